@@ -1,0 +1,257 @@
+#!/usr/bin/env python3
+"""Benchmark of the ragged MoE expert path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload 3] [--no-cpu-baseline]
+
+A step is one pass of the path over the workload's routed batch: the grouped
+dynamic quantize of the bf16 activations, then the grouped GEMM (with its
+in-kernel tile map), or the fused gate/up GEMM + SwiGLU + requant for the
+fused workload.  Inputs are seeded synthetics already resident in HBM; the
+weights are quantized once before timing (offline preparation).
+
+Default workload: prefill_fp8_rowwise (8192 tokens x top-8 of 128 experts,
+Zipf(1.1), K=4096, N=1536) -- the configuration the FP8 MFMA target is quoted
+on.  `value` is GEMM FLOP per step / step time (TFLOP/s).  The roofline object
+describes the GEMM kernel from HIP events recorded around each launch inside
+the timed region; the CPU baseline times the oracle on a bounded sample.
+Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+# MI355X published dense peaks (TFLOP/s) and HBM bandwidth (GB/s)
+PEAK_TFLOPS = {"fp8": 5000.0, "fp4": 10100.0}
+PEAK_HBM_GBS = 8000.0
+
+METRIC = "ragged MoE grouped GEMM TFLOP/s + % FP8/MXFP4 MFMA peak; quantize GB/s"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", type=int, default=3, help="1..5 (default: 3, prefill FP8 rowwise)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU baseline")
+    return p.parse_args()
+
+
+def algorithmic_gemm_bytes(w, counts, K, N, T, fmt):
+    """Each operand read once, output written once; experts with no rows are not read."""
+    active = int((counts > 0).sum())
+    row_bytes = K // 2 if fmt == 2 else K
+    if fmt == 0:
+        a = T * row_bytes + T * 4
+        b = active * N * (row_bytes + 4)
+    else:
+        a = T * (row_bytes + K // 32)
+        b = active * N * (row_bytes + K // 32)
+    out = T * (N // 4 + N // 64) if w.swiglu else T * N * 2
+    return a + b + out
+
+
+def kernel_sources_sha():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "fp4_grouped_gemm_quantize_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def counter_traffic(workload_name):
+    """HBM bytes per GEMM launch from the committed rocprofv3 counter summary,
+    or None when the kernels changed after the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload_name}.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    if fields.get("kernel_sources_sha256") != kernel_sources_sha():
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, r, x_gpu, target_s):
+    """The oracle, as it stands, on a bounded sample of the same workload:
+    rows from a few groups (quantize + GEMM of those rows against their
+    experts).  Returns the value in TFLOP/s of GEMM work."""
+    import numpy as np
+
+    import oracle
+    import workloads as W
+
+    rng = np.random.default_rng(w.seed)
+    nonempty = np.nonzero(r.counts > 0)[0]
+    sel = np.sort(rng.choice(nonempty, size=min(4, nonempty.size), replace=False))
+    wt = W.bf16_bits(W.weights(w, device="cuda", experts=list(sel)))
+    E_s = len(sel)
+    b, sb = oracle.quantize(w.fmt, wt.reshape(E_s * w.N, w.K), np.array([0, E_s * w.N], np.uint32))
+    b = b.reshape(E_s, w.N, -1)
+    sb = sb.reshape(E_s, w.N) if w.fmt == 0 else sb.reshape(E_s, w.N, w.K // 32)
+    del wt
+
+    def run(rows_per_group):
+        rows = []
+        for e in sel:
+            lo = int(r.row_offsets[e])
+            n = min(rows_per_group, int(r.counts[e]))
+            rows += list(range(lo, lo + n))
+        xs = W.bf16_bits(x_gpu[rows])
+        counts = [min(rows_per_group, int(r.counts[e])) for e in sel]
+        off = np.r_[0, np.cumsum(counts)].astype(np.uint32)
+        ids = np.arange(E_s, dtype=np.int32)
+        t0 = time.perf_counter()
+        a, sa = oracle.quantize(w.fmt, xs, off)
+        if w.swiglu:
+            oracle.gemm_swiglu_rows(w.fmt, a, sa, b, sb, off, ids, w.N // 2, w.K, np.arange(len(rows)),
+                                    want_exact=False)
+        else:
+            oracle.gemm_rows(w.fmt, a, sa, b, sb, off, ids, w.N, w.K, np.arange(len(rows)), want_exact=False)
+        dt = time.perf_counter() - t0
+        return len(rows), dt
+
+    n, dt = run(1)
+    per_row = dt / max(n, 1)
+    rows_per_group = max(1, int(target_s / per_row / E_s))
+    n, dt = run(rows_per_group)
+    flops = 2.0 * n * w.N * w.K
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{n} routed rows ({rows_per_group} from each of {E_s} experts) of the same workload: "
+                      f"oracle quantize + grouped GEMM, {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import fp4_grouped_gemm_quantize_amd as mxg
+    import workloads as W
+
+    torch.cuda.set_device(0)
+    w = W.WORKLOADS[args.workload]
+    r = W.routing(w)
+    T, K, N, fmt = r.total_rows, w.K, w.N, w.fmt
+
+    # ---- inputs resident in HBM; weights prepared once (untimed)
+    x = W.activations(w, r, device="cuda")
+    wt = W.weights(w, device="cuda")
+    b, sb = mxg.quantize_weights(fmt, wt)
+    del wt
+    torch.cuda.empty_cache()
+    off = torch.from_numpy(r.row_offsets.view(np.int32)).cuda()
+    ids = torch.from_numpy(r.expert_ids).cuda()
+    qcols = K // 2 if fmt == mxg.MXFP4 else K
+    a = torch.empty((T, qcols), dtype=torch.uint8, device="cuda")
+    sa = torch.empty((T,), dtype=torch.float32, device="cuda") if fmt == 0 else \
+        torch.empty((T, K // 32), dtype=torch.uint8, device="cuda")
+    if w.swiglu:
+        yq = torch.empty((T, N // 4), dtype=torch.uint8, device="cuda")
+        ys = torch.empty((T, N // 64), dtype=torch.uint8, device="cuda")
+    else:
+        c = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
+    hint = int(r.counts.max())
+
+    def quant():
+        mxg.mx_grouped_quantize(fmt, x, a, sa, off, ids)
+
+    def gemm():
+        if w.swiglu:
+            mxg.mx_grouped_matmul_swiglu(fmt, a, sa, b, sb, yq, ys, off, ids, hint)
+        else:
+            mxg.mx_grouped_matmul(fmt, a, sa, b, sb, c, off, ids, hint)
+
+    for _ in range(args.warmup):
+        quant()
+        gemm()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        ev[s][0].record(stream)
+        quant()
+        ev[s][1].record(stream)
+        gemm()
+        ev[s][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    q_ms = [ev[s][0].elapsed_time(ev[s][1]) for s in range(args.steps)]
+    g_ms = [ev[s][1].elapsed_time(ev[s][2]) for s in range(args.steps)]
+    step_ms = wall * 1e3 / args.steps
+    flops = 2.0 * T * N * K
+    q_bytes = T * K * 2 + a.numel() + sa.numel() * sa.element_size()
+    g_bytes = algorithmic_gemm_bytes(w, r.counts, K, N, T, fmt)
+    g_avg = float(np.mean(g_ms))
+    q_avg = float(np.mean(q_ms))
+    peak = PEAK_TFLOPS["fp4" if fmt == 2 else "fp8"]
+    g_tflops = flops / (g_avg * 1e-3) / 1e12
+    # the GEMM is MFMA-bound when its intensity exceeds the ridge point
+    ridge = peak * 1e12 / (PEAK_HBM_GBS * 1e9)
+    mfma_bound = flops / g_bytes >= ridge
+    traffic = counter_traffic(w.name)
+    roof = {"bound": "mfma" if mfma_bound else "hbm",
+            "achieved": round(g_tflops if mfma_bound else g_bytes / (g_avg * 1e-3) / 1e9, 2),
+            "peak": peak if mfma_bound else PEAK_HBM_GBS,
+            "unit": "TFLOP/s" if mfma_bound else "GB/s",
+            "traffic": traffic}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    out = {
+        "metric": METRIC,
+        "value": round(flops / (step_ms * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp4_e2m1" if fmt == 2 else "fp8_e4m3",
+        "data": "synthetic (seeded; random-init weights N(0,0.02), activations N(0,1))",
+        "config": {"workload": w.name, "routed_rows": T, "experts": w.E, "active_experts": int((r.counts > 0).sum()),
+                   "tokens": w.tokens or None, "top_k": w.top_k or None, "K": K, "N": N,
+                   "format": mxg.FORMATS[fmt], "routing": w.routing,
+                   "max_rows_per_expert": hint, "min_rows_per_expert": int(r.counts.min())},
+        "kernels": {
+            "quantize_ms": round(q_avg, 4), "quantize_GBps": round(q_bytes / (q_avg * 1e-3) / 1e9, 1),
+            "quantize_frac_hbm": round(q_bytes / (q_avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "gemm_ms": round(g_avg, 4), "gemm_TFLOPs": round(g_tflops, 1),
+            "gemm_frac_mfma_peak": round(g_tflops / peak, 4),
+            "gemm_GBps_algorithmic": round(g_bytes / (g_avg * 1e-3) / 1e9, 1),
+            "gemm_flop": flops, "gemm_algorithmic_bytes": g_bytes, "quantize_bytes": q_bytes,
+        },
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, r, x, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,240 @@
+"""Python binding of libmxg.so -- the ragged MoE expert path on one gfx950 GPU.
+
+Argument marshalling only: torch tensors provide device memory and the current
+HIP stream; every step of the computation runs in the library's HIP kernels.
+There is no CPU fallback: if libmxg.so has not been built, every call raises.
+
+Entry points (same names as the C ABI in include/mxg.h):
+    mx_grouped_quantize(fmt, x, q, scales, row_offsets, expert_ids=None)
+    mx_grouped_matmul(fmt, a_q, a_scales, b_q, b_scales, c, row_offsets, expert_ids, max_rows_per_group_hint=0)
+    mx_grouped_matmul_swiglu(fmt, a_q, a_scales, w_q, w_scales, y_q, y_scales, row_offsets, expert_ids,
+                             max_rows_per_group_hint=0)
+    mx_silu_quantize(h, y_q, y_scales, row_offsets)
+plus allocating conveniences quantize(), grouped_matmul(), grouped_matmul_swiglu(), silu_quantize().
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+FP8_ROWWISE = 0
+MXFP8 = 1
+MXFP4 = 2
+FORMATS = {FP8_ROWWISE: "fp8_e4m3_rowwise", MXFP8: "mxfp8_e4m3", MXFP4: "mxfp4_e2m1"}
+
+SUCCESS, ERROR_INVALID_VALUE, ERROR_NOT_SUPPORTED, ERROR_LAUNCH = 0, 1, 2, 3
+MAX_GROUPS = 1024
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmxg.so")
+
+EXPORTED = ("mx_grouped_quantize", "mx_grouped_matmul", "mx_grouped_matmul_swiglu", "mx_silu_quantize",
+            "mxg_status_string")
+
+
+class MxgError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)}")
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmxg.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libmxg.so not found at {LIB_PATH}: build it with "
+                               "`python -m fp4_grouped_gemm_quantize_amd.build` (there is no CPU fallback)")
+        L = ctypes.CDLL(LIB_PATH)
+        L.mx_grouped_quantize.argtypes = [ctypes.c_int, _P, _P, _P, _P, _P, _I32, _I64, _I64, _P]
+        L.mx_grouped_matmul.argtypes = [ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I64, _I64, _I64,
+                                        _I64, _P]
+        L.mx_grouped_matmul_swiglu.argtypes = [ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I64,
+                                               _I64, _I64, _I64, _P]
+        L.mx_silu_quantize.argtypes = [_P, _P, _P, _P, _I32, _I64, _I64, _P]
+        for name in ("mx_grouped_quantize", "mx_grouped_matmul", "mx_grouped_matmul_swiglu", "mx_silu_quantize"):
+            getattr(L, name).restype = ctypes.c_int
+        L.mxg_status_string.argtypes = [ctypes.c_int]
+        L.mxg_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().mxg_status_string(status).decode()
+
+
+def _check(status: int, what: str) -> None:
+    if status != SUCCESS:
+        raise MxgError(status, what)
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _expect(t: torch.Tensor, name: str, dtypes, shape=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)} != expected {tuple(shape)}")
+
+
+_U8 = (torch.uint8,)
+_F32 = (torch.float32,)
+_BF16 = (torch.bfloat16,)
+_U32 = (torch.uint32, torch.int32)
+_I32T = (torch.int32,)
+
+
+# ----------------------------------------------------------------------------- entry points
+def mx_grouped_quantize(fmt: int, x, q, scales, row_offsets, expert_ids=None) -> None:
+    """Grouped quantize of bf16 x [T, K] into q / scales (only covered rows written)."""
+    _expect(x, "x", _BF16)
+    if x.dim() != 2:
+        raise ValueError("x must be [total_rows, K]")
+    T, K = x.shape
+    dev = x.device
+    qcols = K // 2 if fmt == MXFP4 else K
+    _expect(q, "q", _U8, (T, qcols), dev)
+    if fmt == FP8_ROWWISE:
+        _expect(scales, "scales", _F32, (T,), dev)
+    else:
+        _expect(scales, "scales", _U8, (T, K // 32), dev)
+    _expect(row_offsets, "row_offsets", _U32, None, dev)
+    G = row_offsets.numel() - 1
+    if expert_ids is not None:
+        _expect(expert_ids, "expert_ids", _I32T, (G,), dev)
+    _check(lib().mx_grouped_quantize(fmt, _ptr(x), _ptr(q), _ptr(scales), _ptr(row_offsets), _ptr(expert_ids),
+                                     G, T, K, _stream(x)), "mx_grouped_quantize")
+
+
+def mx_grouped_matmul(fmt: int, a_q, a_scales, b_q, b_scales, c, row_offsets, expert_ids,
+                      max_rows_per_group_hint: int = 0) -> None:
+    """Ragged grouped GEMM into bf16 c [T, N] (only covered rows written)."""
+    _expect(a_q, "a_q", _U8)
+    _expect(b_q, "b_q", _U8)
+    dev = a_q.device
+    T = a_q.shape[0]
+    E, N = b_q.shape[0], b_q.shape[1]
+    K = a_q.shape[1] * (2 if fmt == MXFP4 else 1)
+    _expect(b_q, "b_q", _U8, (E, N, a_q.shape[1]), dev)
+    if fmt == FP8_ROWWISE:
+        _expect(a_scales, "a_scales", _F32, (T,), dev)
+        _expect(b_scales, "b_scales", _F32, (E, N), dev)
+    else:
+        _expect(a_scales, "a_scales", _U8, (T, K // 32), dev)
+        _expect(b_scales, "b_scales", _U8, (E, N, K // 32), dev)
+    _expect(c, "c", _BF16, (T, N), dev)
+    _expect(row_offsets, "row_offsets", _U32, None, dev)
+    G = row_offsets.numel() - 1
+    _expect(expert_ids, "expert_ids", _I32T, (G,), dev)
+    _check(lib().mx_grouped_matmul(fmt, _ptr(a_q), _ptr(a_scales), _ptr(b_q), _ptr(b_scales), _ptr(c),
+                                   _ptr(row_offsets), _ptr(expert_ids), G, E, T, N, K,
+                                   int(max_rows_per_group_hint), _stream(a_q)), "mx_grouped_matmul")
+
+
+def mx_grouped_matmul_swiglu(fmt: int, a_q, a_scales, w_q, w_scales, y_q, y_scales, row_offsets, expert_ids,
+                             max_rows_per_group_hint: int = 0) -> None:
+    """Fused gate/up grouped GEMM + SwiGLU + MXFP4 requant into y_q [T, I/2], y_scales [T, I/32]."""
+    _expect(a_q, "a_q", _U8)
+    _expect(w_q, "w_q", _U8)
+    dev = a_q.device
+    T = a_q.shape[0]
+    E, N2 = w_q.shape[0], w_q.shape[1]
+    I = N2 // 2
+    K = a_q.shape[1] * (2 if fmt == MXFP4 else 1)
+    _expect(w_q, "w_q", _U8, (E, N2, a_q.shape[1]), dev)
+    _expect(a_scales, "a_scales", _U8, (T, K // 32), dev)
+    _expect(w_scales, "w_scales", _U8, (E, N2, K // 32), dev)
+    _expect(y_q, "y_q", _U8, (T, I // 2), dev)
+    _expect(y_scales, "y_scales", _U8, (T, I // 32), dev)
+    _expect(row_offsets, "row_offsets", _U32, None, dev)
+    G = row_offsets.numel() - 1
+    _expect(expert_ids, "expert_ids", _I32T, (G,), dev)
+    _check(lib().mx_grouped_matmul_swiglu(fmt, _ptr(a_q), _ptr(a_scales), _ptr(w_q), _ptr(w_scales), _ptr(y_q),
+                                          _ptr(y_scales), _ptr(row_offsets), _ptr(expert_ids), G, E, T, I, K,
+                                          int(max_rows_per_group_hint), _stream(a_q)),
+           "mx_grouped_matmul_swiglu")
+
+
+def mx_silu_quantize(h, y_q, y_scales, row_offsets) -> None:
+    """SwiGLU + MXFP4 requant of bf16 h [T, 2I] (gate/up interleaved by column)."""
+    _expect(h, "h", _BF16)
+    dev = h.device
+    T, N2 = h.shape
+    I = N2 // 2
+    _expect(y_q, "y_q", _U8, (T, I // 2), dev)
+    _expect(y_scales, "y_scales", _U8, (T, I // 32), dev)
+    _expect(row_offsets, "row_offsets", _U32, None, dev)
+    G = row_offsets.numel() - 1
+    _check(lib().mx_silu_quantize(_ptr(h), _ptr(y_q), _ptr(y_scales), _ptr(row_offsets), G, T, I, _stream(h)),
+           "mx_silu_quantize")
+
+
+# ----------------------------------------------------------------------------- allocating forms
+def quantize(fmt: int, x, row_offsets, expert_ids=None):
+    """Returns (q, scales); rows no group covers are zero."""
+    T, K = x.shape
+    q = torch.zeros((T, K // 2 if fmt == MXFP4 else K), dtype=torch.uint8, device=x.device)
+    if fmt == FP8_ROWWISE:
+        s = torch.zeros((T,), dtype=torch.float32, device=x.device)
+    else:
+        s = torch.zeros((T, K // 32), dtype=torch.uint8, device=x.device)
+    mx_grouped_quantize(fmt, x, q, s, row_offsets, expert_ids)
+    return q, s
+
+
+def grouped_matmul(fmt: int, a_q, a_scales, b_q, b_scales, row_offsets, expert_ids, max_rows_per_group_hint=0):
+    c = torch.zeros((a_q.shape[0], b_q.shape[1]), dtype=torch.bfloat16, device=a_q.device)
+    mx_grouped_matmul(fmt, a_q, a_scales, b_q, b_scales, c, row_offsets, expert_ids, max_rows_per_group_hint)
+    return c
+
+
+def grouped_matmul_swiglu(fmt: int, a_q, a_scales, w_q, w_scales, row_offsets, expert_ids,
+                          max_rows_per_group_hint=0):
+    T, I = a_q.shape[0], w_q.shape[1] // 2
+    yq = torch.zeros((T, I // 2), dtype=torch.uint8, device=a_q.device)
+    ys = torch.zeros((T, I // 32), dtype=torch.uint8, device=a_q.device)
+    mx_grouped_matmul_swiglu(fmt, a_q, a_scales, w_q, w_scales, yq, ys, row_offsets, expert_ids,
+                             max_rows_per_group_hint)
+    return yq, ys
+
+
+def silu_quantize(h, row_offsets):
+    T, I = h.shape[0], h.shape[1] // 2
+    yq = torch.zeros((T, I // 2), dtype=torch.uint8, device=h.device)
+    ys = torch.zeros((T, I // 32), dtype=torch.uint8, device=h.device)
+    mx_silu_quantize(h, yq, ys, row_offsets)
+    return yq, ys
+
+
+def quantize_weights(fmt: int, w):
+    """Quantize bf16 weights [E, N, K] per output row: one group of E*N rows."""
+    E, N, K = w.shape
+    flat = w.reshape(E * N, K)
+    off = torch.tensor([0, E * N], dtype=torch.int32, device=w.device)
+    q, s = quantize(fmt, flat, off)
+    if fmt == FP8_ROWWISE:
+        return q.reshape(E, N, -1), s.reshape(E, N)
+    return q.reshape(E, N, -1), s.reshape(E, N, K // 32)

@@ -1,0 +1,110 @@
+// api.cpp -- the extern "C" entry points of libmxg.so: argument validation on
+// the host (before anything is enqueued), then one launch per call.  No
+// allocation, no host synchronisation, no state.
+#include "mxg.h"
+#include "mxg_internal.h"
+
+#include <stdint.h>
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+mxg_status from_hip(hipError_t e) { return e == hipSuccess ? MXG_SUCCESS : MXG_ERROR_LAUNCH; }
+
+bool valid_fmt(int fmt) { return fmt == MXG_FP8_E4M3_ROWWISE || fmt == MXG_MXFP8_E4M3 || fmt == MXG_MXFP4_E2M1; }
+
+}  // namespace
+
+extern "C" {
+
+const char* mxg_status_string(mxg_status status) {
+    switch (status) {
+        case MXG_SUCCESS:
+            return "MXG_SUCCESS";
+        case MXG_ERROR_INVALID_VALUE:
+            return "MXG_ERROR_INVALID_VALUE: null pointer, bad enum, bad size or misaligned pointer";
+        case MXG_ERROR_NOT_SUPPORTED:
+            return "MXG_ERROR_NOT_SUPPORTED: K or I not a multiple of 32, too many groups, or format not offered";
+        case MXG_ERROR_LAUNCH:
+            return "MXG_ERROR_LAUNCH: the HIP runtime rejected a kernel launch";
+    }
+    return "unknown mxg_status";
+}
+
+mxg_status mx_grouped_quantize(mxg_format fmt, const void* x_bf16, void* q, void* scales,
+                               const uint32_t* row_offsets, const int32_t* expert_ids, int32_t num_groups,
+                               int64_t total_rows, int64_t K, hipStream_t stream) {
+    (void)expert_ids;  // not read by these formats (no per-expert tensor scale)
+    if (!valid_fmt(fmt)) return MXG_ERROR_INVALID_VALUE;
+    if (K <= 0 || total_rows < 0 || num_groups < 0) return MXG_ERROR_INVALID_VALUE;
+    if (K % 32 != 0 || num_groups > MXG_MAX_GROUPS) return MXG_ERROR_NOT_SUPPORTED;
+    if (total_rows == 0 || num_groups == 0) return MXG_SUCCESS;  // nothing is read or written
+    if (!x_bf16 || !q || !scales || !row_offsets) return MXG_ERROR_INVALID_VALUE;
+    if (!aligned(x_bf16, 16) || !aligned(q, 16) || (fmt == MXG_FP8_E4M3_ROWWISE && !aligned(scales, 4)) ||
+        !aligned(row_offsets, 4))
+        return MXG_ERROR_INVALID_VALUE;
+    return from_hip(mxg::launch_quantize((int)fmt, x_bf16, q, scales, row_offsets, num_groups, total_rows, K,
+                                         stream));
+}
+
+static mxg_status check_gemm_common(mxg_format fmt, const void* a_q, const void* a_scales, const void* b_q,
+                                    const void* b_scales, const uint32_t* row_offsets, const int32_t* expert_ids,
+                                    int32_t num_groups, int32_t num_experts, int64_t total_rows, int64_t N,
+                                    int64_t K) {
+    if (!valid_fmt(fmt)) return MXG_ERROR_INVALID_VALUE;
+    if (K <= 0 || N <= 0 || num_experts <= 0 || total_rows < 0 || num_groups < 0) return MXG_ERROR_INVALID_VALUE;
+    if (K % 32 != 0 || num_groups > MXG_MAX_GROUPS) return MXG_ERROR_NOT_SUPPORTED;
+    if (N > INT32_MAX / 2 || total_rows > INT32_MAX) return MXG_ERROR_NOT_SUPPORTED;
+    if (total_rows == 0 || num_groups == 0) return MXG_SUCCESS;  // checked again by the caller: no-op
+    if (!a_q || !a_scales || !b_q || !b_scales || !row_offsets || !expert_ids) return MXG_ERROR_INVALID_VALUE;
+    if (!aligned(a_q, 16) || !aligned(b_q, 16) || !aligned(row_offsets, 4) || !aligned(expert_ids, 4))
+        return MXG_ERROR_INVALID_VALUE;
+    if (fmt == MXG_FP8_E4M3_ROWWISE && (!aligned(a_scales, 4) || !aligned(b_scales, 4)))
+        return MXG_ERROR_INVALID_VALUE;
+    return MXG_SUCCESS;
+}
+
+mxg_status mx_grouped_matmul(mxg_format fmt, const void* a_q, const void* a_scales, const void* b_q,
+                             const void* b_scales, void* c_bf16, const uint32_t* row_offsets,
+                             const int32_t* expert_ids, int32_t num_groups, int32_t num_experts,
+                             int64_t total_rows, int64_t N, int64_t K, int64_t max_rows_per_group_hint,
+                             hipStream_t stream) {
+    mxg_status st = check_gemm_common(fmt, a_q, a_scales, b_q, b_scales, row_offsets, expert_ids, num_groups,
+                                      num_experts, total_rows, N, K);
+    if (st != MXG_SUCCESS) return st;
+    if (total_rows == 0 || num_groups == 0) return MXG_SUCCESS;
+    if (!c_bf16 || !aligned(c_bf16, 16)) return MXG_ERROR_INVALID_VALUE;
+    mxg::GemmProblem p{(int)fmt, a_q, a_scales, b_q, b_scales, c_bf16, nullptr, nullptr, row_offsets, expert_ids,
+                       num_groups, num_experts, total_rows, N, K, max_rows_per_group_hint};
+    return from_hip(mxg::launch_grouped_gemm(p, stream));
+}
+
+mxg_status mx_grouped_matmul_swiglu(mxg_format fmt, const void* a_q, const void* a_scales, const void* w_q,
+                                    const void* w_scales, void* y_q, void* y_scales,
+                                    const uint32_t* row_offsets, const int32_t* expert_ids, int32_t num_groups,
+                                    int32_t num_experts, int64_t total_rows, int64_t I, int64_t K,
+                                    int64_t max_rows_per_group_hint, hipStream_t stream) {
+    if (I <= 0) return MXG_ERROR_INVALID_VALUE;
+    mxg_status st = check_gemm_common(fmt, a_q, a_scales, w_q, w_scales, row_offsets, expert_ids, num_groups,
+                                      num_experts, total_rows, 2 * I, K);
+    if (st != MXG_SUCCESS) return st;
+    if (fmt == MXG_FP8_E4M3_ROWWISE || I % 32 != 0) return MXG_ERROR_NOT_SUPPORTED;
+    if (total_rows == 0 || num_groups == 0) return MXG_SUCCESS;
+    if (!y_q || !y_scales || !aligned(y_q, 16)) return MXG_ERROR_INVALID_VALUE;
+    mxg::GemmProblem p{(int)fmt, a_q, a_scales, w_q, w_scales, nullptr, y_q, y_scales, row_offsets, expert_ids,
+                       num_groups, num_experts, total_rows, 2 * I, K, max_rows_per_group_hint};
+    return from_hip(mxg::launch_grouped_gemm(p, stream));
+}
+
+mxg_status mx_silu_quantize(const void* h_bf16, void* y_q, void* y_scales, const uint32_t* row_offsets,
+                            int32_t num_groups, int64_t total_rows, int64_t I, hipStream_t stream) {
+    if (I <= 0 || total_rows < 0 || num_groups < 0) return MXG_ERROR_INVALID_VALUE;
+    if (I % 32 != 0 || num_groups > MXG_MAX_GROUPS) return MXG_ERROR_NOT_SUPPORTED;
+    if (total_rows == 0 || num_groups == 0) return MXG_SUCCESS;
+    if (!h_bf16 || !y_q || !y_scales || !row_offsets) return MXG_ERROR_INVALID_VALUE;
+    if (!aligned(h_bf16, 16) || !aligned(y_q, 16) || !aligned(row_offsets, 4)) return MXG_ERROR_INVALID_VALUE;
+    return from_hip(mxg::launch_silu_quantize(h_bf16, y_q, y_scales, row_offsets, num_groups, total_rows, I, stream));
+}
+
+}  // extern "C"

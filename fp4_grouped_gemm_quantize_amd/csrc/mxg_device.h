@@ -1,0 +1,171 @@
+// mxg_device.h -- gfx950 device helpers shared by the quantize and GEMM kernels:
+// bit-level element encoders, bf16 rounding, wave reductions and the group
+// bookkeeping every kernel does on row_offsets / expert_ids.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxg {
+
+constexpr int kWave = 64;
+constexpr int kMaxGroups = 1024;
+
+// ---------------------------------------------------------------------------
+// bf16 <-> fp32.  bf16 is the upper half of binary32; fp32 -> bf16 rounds to
+// nearest, ties to even (overflow goes to infinity as IEEE rounding does).
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;  // quiet NaN
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// ---------------------------------------------------------------------------
+// OCP OFP8 E4M3 ("fn": no infinities, max 448) from fp32, round to nearest
+// even, saturating.  Bit manipulation on the binary32 pattern:
+//   |v| >= 448           -> 0x7e
+//   |v| <  2^-6          -> subnormal: m = rne(|v| * 2^9) in 0..8 (8 is 0x08)
+//   otherwise            -> round the pattern at bit 20 (3 mantissa bits kept,
+//                           carries run into the exponent), rebias 127 -> 7.
+__device__ __forceinline__ uint32_t enc_e4m3(float v) {
+    uint32_t u = __float_as_uint(v);
+    uint32_t s = (u >> 24) & 0x80u;
+    uint32_t a = u & 0x7fffffffu;
+    // (the min() keeps the unused branch's float->int conversion in range)
+    uint32_t sub = (uint32_t)__builtin_rintf(fminf(__uint_as_float(a), 0.015625f) * 512.0f);
+    uint32_t nrm = ((a + 0x7ffffu + ((a >> 20) & 1u)) >> 20) - (120u << 3);
+    uint32_t c = a < 0x3c800000u ? sub : nrm;
+    c = a >= 0x43e00000u ? 0x7eu : c;
+    return s | c;
+}
+
+// OCP MX E2M1 (max 6) from fp32, round to nearest even, saturating.
+//   |v| >= 6  -> 7;  |v| < 1 -> rne(2|v|) in 0..2;  else round at bit 22.
+__device__ __forceinline__ uint32_t enc_e2m1(float v) {
+    uint32_t u = __float_as_uint(v);
+    uint32_t s = (u >> 28) & 0x8u;
+    uint32_t a = u & 0x7fffffffu;
+    uint32_t sub = (uint32_t)__builtin_rintf(fminf(__uint_as_float(a), 1.0f) * 2.0f);
+    uint32_t nrm = ((a + 0x1fffffu + ((a >> 22) & 1u)) >> 22) - (126u << 1);
+    uint32_t c = a < 0x3f800000u ? sub : nrm;
+    c = a >= 0x40c00000u ? 7u : c;
+    return s | c;
+}
+
+// floor(log2(a)) of a positive finite fp32 (normal or subnormal), exactly.
+__device__ __forceinline__ int floor_log2_f32(float a) {
+    uint32_t u = __float_as_uint(a);
+    int e = (int)(u >> 23);
+    if (e != 0) return e - 127;
+    uint32_t m = u & 0x7fffffu;
+    return (31 - __clz(m)) - 149;
+}
+
+// MX shared exponent of a block with maximum magnitude amax (OCP MX v1.0):
+// X = clamp(floor(log2 amax) - emax_elem, -127, 127); the E8M0 code is X+127,
+// and an all-zero block gets code 0 (elements are then signed zeros anyway).
+__device__ __forceinline__ int mx_shared_exp(float amax, int emax_elem) {
+    if (amax == 0.0f) return -127;
+    int x = floor_log2_f32(amax) - emax_elem;
+    return x < -127 ? -127 : (x > 127 ? 127 : x);
+}
+
+// ---------------------------------------------------------------------------
+// Wave reductions (wave64).
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+
+// Gated activation in fp32, the one formula both the fused GEMM epilogue and
+// the standalone activation kernel use: silu(g) * u with silu(z) = z/(1+e^-z).
+__device__ __forceinline__ float silu_mul(float g, float u) { return (g / (1.0f + expf(-g))) * u; }
+
+// ---------------------------------------------------------------------------
+// Group bookkeeping.  Group g is taken when its (clamped) start does not
+// exceed its end and, if experts are checked (num_experts > 0), its id is in
+// range; its rows are [lo, hi).
+struct GroupRange {
+    int64_t lo, hi;
+};
+
+__device__ __forceinline__ GroupRange group_range(const uint32_t* off, const int32_t* ids, int g, int64_t T,
+                                                  int num_experts) {
+    int64_t lo = (int64_t)off[g], hi = (int64_t)off[g + 1];
+    lo = lo < T ? lo : T;
+    hi = hi < T ? hi : T;
+    if (hi < lo) hi = lo;
+    if (num_experts > 0) {
+        int e = ids[g];
+        if (e < 0 || e >= num_experts) hi = lo;
+    }
+    return {lo, hi};
+}
+
+// Whether any taken group covers row t.  The whole wave cooperates: lane i
+// tests groups i, i+64, ...; the result is wave-uniform.  Offsets are read
+// from LDS (s_off holds row_offsets[0..G]).
+__device__ __forceinline__ bool wave_row_covered(const uint32_t* s_off, int G, int64_t T, int64_t t) {
+    int lane = threadIdx.x & (kWave - 1);
+    bool hit = false;
+    for (int g = lane; g < G; g += kWave) {
+        int64_t lo = (int64_t)s_off[g], hi = (int64_t)s_off[g + 1];
+        lo = lo < T ? lo : T;
+        hi = hi < T ? hi : T;
+        hit |= (t >= lo) && (t < hi);
+    }
+    return __any(hit);
+}
+
+// Unpack a 16-byte vector of 8 bf16 into fp32.
+__device__ __forceinline__ void unpack8(const uint4& v, float* f) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = bf16_to_f32(w[i] & 0xffffu);
+        f[2 * i + 1] = bf16_to_f32(w[i] >> 16);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// MX: 4 lanes x 8 elements form one 32-element block.  Given the 8 values of
+// this lane, returns the block's shared exponent X (after the 4-lane
+// reduction) and writes the 8 element codes.
+template <bool FP4>
+__device__ __forceinline__ int mx_encode8(const float* f, uint32_t* code) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
+    const int X = mx_shared_exp(amax, FP4 ? 2 : 8);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float e = ldexpf(f[i], -X);  // exact power-of-two shift
+        code[i] = FP4 ? enc_e2m1(e) : enc_e4m3(e);
+    }
+    return X;
+}
+
+template <bool FP4>
+__device__ __forceinline__ void mx_store8(const uint32_t* code, int X, uint8_t* qrow, uint8_t* srow, int64_t idx,
+                                          int lane) {
+    if (FP4) {
+        uint32_t packed = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) packed |= code[i] << (4 * i);
+        *reinterpret_cast<uint32_t*>(qrow + idx * 4) = packed;
+    } else {
+        uint2 packed;
+        packed.x = code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
+        packed.y = code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24);
+        *reinterpret_cast<uint2*>(qrow + idx * 8) = packed;
+    }
+    if ((lane & 3) == 0) srow[idx >> 2] = (uint8_t)(X + 127);
+}
+
+}  // namespace mxg

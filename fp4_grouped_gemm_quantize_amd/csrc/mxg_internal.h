@@ -1,0 +1,38 @@
+// mxg_internal.h -- launchers the C ABI layer calls; host-side only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxg {
+
+hipError_t launch_quantize(int fmt, const void* x, void* q, void* scales, const uint32_t* off, int G, int64_t T,
+                           int64_t K, hipStream_t stream);
+
+hipError_t launch_silu_quantize(const void* h, void* yq, void* ys, const uint32_t* off, int G, int64_t T,
+                                int64_t I, hipStream_t stream);
+
+// Grouped GEMM; when yq != nullptr the SwiGLU + MXFP4 requant epilogue runs
+// (N = 2I) and c is not written.
+struct GemmProblem {
+    int fmt;
+    const void* a;
+    const void* a_scales;
+    const void* b;
+    const void* b_scales;
+    void* c;
+    void* yq;
+    void* ys;
+    const uint32_t* off;
+    const int32_t* ids;
+    int G;
+    int E;
+    int64_t T;
+    int64_t N;
+    int64_t K;
+    int64_t max_rows_hint;
+};
+
+hipError_t launch_grouped_gemm(const GemmProblem& p, hipStream_t stream);
+
+}  // namespace mxg

@@ -1,0 +1,188 @@
+/*
+ * mxg.h -- C ABI of libmxg.so: the ragged MoE expert path on one gfx950 GPU.
+ *
+ * Four operations, each one asynchronous launch sequence on the caller's HIP
+ * stream:
+ *   mx_grouped_quantize       BF16 activations -> FP8 e4m3 + per-row fp32 scale,
+ *                             or MX (32-element blocks, E8M0 scale, e4m3 or e2m1)
+ *   mx_grouped_matmul         ragged grouped GEMM, FP8 rowwise or MX block-scaled,
+ *                             fp32 accumulation, BF16 output
+ *   mx_grouped_matmul_swiglu  MX grouped GEMM against interleaved gate/up weights,
+ *                             fused with SwiGLU and an MXFP4 requant
+ *   mx_silu_quantize          the unfused second half: SwiGLU + MXFP4 requant of a
+ *                             BF16 gate/up tensor
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller; the library
+ *     allocates no memory and keeps no state between calls.  Tensors are dense
+ *     and row-major with the last-named dimension innermost.  Code and BF16
+ *     tensors must start on a 16-byte boundary; fp32 scale tensors on 4 bytes.
+ *   - Calls only enqueue work on `stream` (0 = the null stream) and return; no
+ *     host synchronisation and no device-to-host copy happens inside a call.
+ *   - Groups.  row_offsets is uint32 [num_groups + 1]; group g owns the rows
+ *     [row_offsets[g], row_offsets[g+1]) of the routed-row dimension, and
+ *     expert_ids[g] (int32) names the expert whose weights those rows use
+ *     (grouped_matmul_rowwise_dynamic_scaled_fp8, Args: a_offsets, expert_ids).
+ *     Offsets are expected non-decreasing and <= total_rows.  Malformed device
+ *     data never causes an out-of-bounds access: offsets are clamped to
+ *     total_rows, a group whose start exceeds its end or whose expert id lies
+ *     outside [0, num_experts) is skipped, and output rows that no taken group
+ *     covers are left untouched.  Overlapping groups give unspecified values
+ *     in the overlap.
+ *   - FP4 (e2m1) tensors hold two elements per byte, element 2i in bits 0..3
+ *     and element 2i+1 in bits 4..7.  E8M0 scales are one byte, 2^(code-127).
+ *   - Element encodings: e4m3 is OCP OFP8 E4M3 (no infinities, max 448), e2m1
+ *     is OCP MX E2M1 (max 6).  Encoding rounds to nearest, ties to even, and
+ *     saturates to the largest finite code; the sign of a value that rounds to
+ *     zero is kept.
+ *   - Errors are returned before anything is enqueued (nothing is launched on
+ *     an error).  MXG_ERROR_LAUNCH reports a failed kernel launch.  With
+ *     total_rows == 0 or num_groups == 0 a call (after its enum and size
+ *     checks) is a no-op that examines no pointer.
+ */
+#ifndef MXG_H
+#define MXG_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MXG_SUCCESS = 0,
+    MXG_ERROR_INVALID_VALUE = 1, /* null pointer, bad enum, bad size, misaligned pointer */
+    MXG_ERROR_NOT_SUPPORTED = 2, /* K or I not a multiple of 32, too many groups, format not offered */
+    MXG_ERROR_LAUNCH = 3         /* the HIP runtime refused a launch */
+} mxg_status;
+
+typedef enum {
+    MXG_FP8_E4M3_ROWWISE = 0, /* e4m3 codes, one fp32 scale per row (per-token / per-channel) */
+    MXG_MXFP8_E4M3 = 1,       /* e4m3 codes, one E8M0 scale per 32 elements along K */
+    MXG_MXFP4_E2M1 = 2        /* e2m1 codes packed 2 per byte, one E8M0 scale per 32 elements */
+} mxg_format;
+
+/* Largest num_groups any entry point accepts. */
+#define MXG_MAX_GROUPS 1024
+
+/*
+ * mx_grouped_quantize -- per-expert dynamic quantization of BF16 rows.
+ * (grouped_quantize_dynamic_scaled_fp4_async_kernel, description;
+ *  NvMxf4f8Strategy, grouped_quantize() and quantize() -- the latter is the
+ *  num_groups = 1, row_offsets = {0, total_rows} case;
+ *  grouped_matmul_rowwise_dynamic_scaled_fp8, Args: a_scales.)
+ *
+ *   x_bf16   [total_rows, K] bf16 input.
+ *   q        MXG_FP8_E4M3_ROWWISE, MXG_MXFP8_E4M3: [total_rows, K] u8;
+ *            MXG_MXFP4_E2M1: [total_rows, K/2] u8.
+ *   scales   MXG_FP8_E4M3_ROWWISE: fp32 [total_rows]; MX: u8 E8M0 [total_rows, K/32].
+ *   row_offsets / num_groups as above.  Only covered rows of q and scales are
+ *            written.
+ *   expert_ids may be NULL; it is not read (these formats carry no per-expert
+ *            tensor scale) and is accepted so the same routing tuple can be
+ *            handed to quantize and matmul.
+ *
+ * Rowwise: amax = max |x| over the row; scale = amax / 448 (IEEE fp32
+ * division); code = e4m3(x / scale) (IEEE fp32 division); a zero row gets
+ * scale 0 and signed-zero codes.  MX: per 32-element block, X =
+ * clamp(floor(log2 amax) - emax, -127, 127) with emax = 8 (e4m3) or 2 (e2m1),
+ * scale code X + 127 (0 for an all-zero block), code = enc(x * 2^-X).
+ * Weights are prepared with the same call (one group of num_experts*N rows).
+ *
+ * Errors: INVALID_VALUE for a null x/q/scales/row_offsets, a bad fmt,
+ * K <= 0, total_rows < 0, num_groups < 0, misalignment; NOT_SUPPORTED for
+ * K % 32 != 0 or num_groups > MXG_MAX_GROUPS.
+ */
+mxg_status mx_grouped_quantize(mxg_format fmt, const void* x_bf16, void* q, void* scales,
+                               const uint32_t* row_offsets, const int32_t* expert_ids, int32_t num_groups,
+                               int64_t total_rows, int64_t K, hipStream_t stream);
+
+/*
+ * mx_grouped_matmul -- ragged grouped GEMM with BF16 output.
+ * (grouped_matmul_rowwise_dynamic_scaled_fp8, description and Args;
+ *  NvMxf4f8Strategy, grouped_matmul().)
+ *
+ * For each taken group g with e = expert_ids[g], each row t it owns and each
+ * n in [0, N):
+ *   MXG_FP8_E4M3_ROWWISE:
+ *     c[t,n] = bf16( (sum_k a[t,k] * b[e,n,k]) * a_scales[t] * b_scales[e,n] )
+ *     with the sum accumulated in fp32 and the two scales applied once after
+ *     it, in that order, in fp32.
+ *   MX formats:
+ *     c[t,n] = bf16( sum_blocks 2^(sa[t,blk]-127) * 2^(sb[e,n,blk]-127)
+ *                    * sum_{k in blk} a[t,k] * b[e,n,k] ), fp32 accumulation.
+ *
+ *   a_q       [total_rows, K] u8 (e4m3) or [total_rows, K/2] u8 (e2m1).
+ *   a_scales  fp32 [total_rows] (rowwise) or u8 [total_rows, K/32] (MX).
+ *   b_q       [num_experts, N, K] u8 or [num_experts, N, K/2] u8 -- K innermost
+ *             (the weight is already transposed).
+ *   b_scales  fp32 [num_experts, N] (rowwise) or u8 [num_experts, N, K/32] (MX).
+ *   c_bf16    [total_rows, N] bf16 output; only covered rows are written.
+ *   max_rows_per_group_hint  largest group size if the host knows it, else 0.
+ *             It only steers the choice of tile shape; results never depend
+ *             on it (grouped_matmul_rowwise_dynamic_scaled_fp8, Args:
+ *             max_num_tokens_per_expert).
+ *
+ * Errors: INVALID_VALUE for null pointers, a bad fmt, K/N/num_experts <= 0,
+ * total_rows/num_groups < 0, misalignment; NOT_SUPPORTED for K % 32 != 0 or
+ * num_groups > MXG_MAX_GROUPS.
+ */
+mxg_status mx_grouped_matmul(mxg_format fmt, const void* a_q, const void* a_scales, const void* b_q,
+                             const void* b_scales, void* c_bf16, const uint32_t* row_offsets,
+                             const int32_t* expert_ids, int32_t num_groups, int32_t num_experts,
+                             int64_t total_rows, int64_t N, int64_t K, int64_t max_rows_per_group_hint,
+                             hipStream_t stream);
+
+/*
+ * mx_grouped_matmul_swiglu -- fused gate/up grouped GEMM + SwiGLU + MXFP4 requant.
+ * (NvMxf4f8Strategy, grouped_matmul_swiglu(): the grouped matmul followed by
+ *  fused_silu_quantize(), folded into one kernel, byte-identical to the
+ *  chained path; weights arrive (gate, up)-interleaved.)
+ *
+ *   fmt       MXG_MXFP4_E2M1 or MXG_MXFP8_E4M3 (the input format of a_q / w_q).
+ *   a_q, a_scales  as mx_grouped_matmul (MX layouts).
+ *   w_q       [num_experts, 2I, K] u8 (e4m3) or [num_experts, 2I, K/2] u8 (e2m1);
+ *             row 2j is gate_j and row 2j+1 is up_j.
+ *   w_scales  u8 [num_experts, 2I, K/32], rows as w_q.
+ *   y_q       [total_rows, I/2] u8, e2m1 codes of y (element 2i low nibble).
+ *   y_scales  [total_rows, I/32] u8 E8M0.
+ *
+ * g_j and u_j are the BF16 outputs mx_grouped_matmul would produce for
+ * columns 2j and 2j+1 (bit-identical: same accumulation order), y_j =
+ * bf16( g_j / (1 + e^-g_j) * u_j ) computed in fp32, and (y_q, y_scales) is
+ * the MXFP4 quantization of y along j in blocks of 32 -- exactly what
+ * mx_grouped_matmul followed by mx_silu_quantize produces.
+ *
+ * Errors: as mx_grouped_matmul; NOT_SUPPORTED also for I % 32 != 0 or a
+ * rowwise fmt.
+ */
+mxg_status mx_grouped_matmul_swiglu(mxg_format fmt, const void* a_q, const void* a_scales, const void* w_q,
+                                    const void* w_scales, void* y_q, void* y_scales,
+                                    const uint32_t* row_offsets, const int32_t* expert_ids, int32_t num_groups,
+                                    int32_t num_experts, int64_t total_rows, int64_t I, int64_t K,
+                                    int64_t max_rows_per_group_hint, hipStream_t stream);
+
+/*
+ * mx_silu_quantize -- SwiGLU + MXFP4 requant of a BF16 gate/up tensor.
+ * (NvMxf4f8Strategy, fused_silu_quantize(): apply the gated activation, then
+ *  quantize.)
+ *
+ *   h_bf16    [total_rows, 2I] bf16; column 2j is gate_j, column 2j+1 is up_j
+ *             (the output of mx_grouped_matmul against interleaved weights).
+ *   y_q, y_scales  as mx_grouped_matmul_swiglu.  Only covered rows are written.
+ *
+ * Errors: INVALID_VALUE for null pointers, I <= 0, total_rows/num_groups < 0,
+ * misalignment; NOT_SUPPORTED for I % 32 != 0 or num_groups > MXG_MAX_GROUPS.
+ */
+mxg_status mx_silu_quantize(const void* h_bf16, void* y_q, void* y_scales, const uint32_t* row_offsets,
+                            int32_t num_groups, int64_t total_rows, int64_t I, hipStream_t stream);
+
+/* Static, human-readable name of a status code. */
+const char* mxg_status_string(mxg_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXG_H */

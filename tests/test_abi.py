@@ -1,0 +1,107 @@
+"""The C ABI boundary, on the CPU: the library loads, exports every entry point
+include/mxg.h declares, and rejects bad arguments with the documented status
+before touching the GPU (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import fp4_grouped_gemm_quantize_amd as mxg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxg.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(mxg.LIB_PATH), reason="libmxg.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted(mxg.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    L = mxg.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_status_strings():
+    assert mxg.status_string(0) == "MXG_SUCCESS"
+    for s in (1, 2, 3):
+        assert mxg.status_string(s).startswith("MXG_ERROR")
+    assert "unknown" in mxg.status_string(99)
+
+
+P = ctypes.c_void_p
+FAKE = P(0x10000)      # never dereferenced: validation fails before any launch
+FAKE_ODD = P(0x10001)  # misaligned
+
+
+def q(fmt=0, x=FAKE, qq=FAKE, s=FAKE, off=FAKE, ids=None, G=1, T=4, K=64):
+    return mxg.lib().mx_grouped_quantize(fmt, x, qq, s, off, ids, G, T, K, None)
+
+
+def test_quantize_argument_errors():
+    assert q(x=None) == mxg.ERROR_INVALID_VALUE
+    assert q(qq=None) == mxg.ERROR_INVALID_VALUE
+    assert q(s=None) == mxg.ERROR_INVALID_VALUE
+    assert q(off=None) == mxg.ERROR_INVALID_VALUE
+    assert q(fmt=3) == mxg.ERROR_INVALID_VALUE
+    assert q(fmt=-1) == mxg.ERROR_INVALID_VALUE
+    assert q(K=0) == mxg.ERROR_INVALID_VALUE
+    assert q(T=-1) == mxg.ERROR_INVALID_VALUE
+    assert q(G=-1) == mxg.ERROR_INVALID_VALUE
+    assert q(x=FAKE_ODD) == mxg.ERROR_INVALID_VALUE
+    assert q(K=48) == mxg.ERROR_NOT_SUPPORTED
+    assert q(G=1025) == mxg.ERROR_NOT_SUPPORTED
+    # nothing to do: returns success without launching
+    assert q(T=0) == mxg.SUCCESS
+    assert q(G=0) == mxg.SUCCESS
+
+
+def mm(fmt=0, a=FAKE, sa=FAKE, b=FAKE, sb=FAKE, c=FAKE, off=FAKE, ids=FAKE, G=1, E=1, T=4, N=32, K=64):
+    return mxg.lib().mx_grouped_matmul(fmt, a, sa, b, sb, c, off, ids, G, E, T, N, K, 0, None)
+
+
+def test_matmul_argument_errors():
+    for kw in [dict(a=None), dict(sa=None), dict(b=None), dict(sb=None), dict(c=None), dict(off=None),
+               dict(ids=None), dict(fmt=7), dict(K=0), dict(N=0), dict(E=0), dict(T=-1), dict(G=-1),
+               dict(a=FAKE_ODD), dict(c=FAKE_ODD)]:
+        assert mm(**kw) == mxg.ERROR_INVALID_VALUE, kw
+    assert mm(K=40) == mxg.ERROR_NOT_SUPPORTED
+    assert mm(G=2000) == mxg.ERROR_NOT_SUPPORTED
+    assert mm(T=0) == mxg.SUCCESS
+
+
+def sw(fmt=2, a=FAKE, sa=FAKE, w=FAKE, sw_=FAKE, yq=FAKE, ys=FAKE, off=FAKE, ids=FAKE, G=1, E=1, T=4, I=64, K=64):
+    return mxg.lib().mx_grouped_matmul_swiglu(fmt, a, sa, w, sw_, yq, ys, off, ids, G, E, T, I, K, 0, None)
+
+
+def test_swiglu_argument_errors():
+    for kw in [dict(a=None), dict(yq=None), dict(ys=None), dict(I=0), dict(fmt=9), dict(yq=FAKE_ODD)]:
+        assert sw(**kw) == mxg.ERROR_INVALID_VALUE, kw
+    assert sw(fmt=0) == mxg.ERROR_NOT_SUPPORTED
+    assert sw(I=48) == mxg.ERROR_NOT_SUPPORTED
+    assert sw(K=16) == mxg.ERROR_NOT_SUPPORTED
+    assert sw(T=0) == mxg.SUCCESS
+
+
+def test_silu_quantize_argument_errors():
+    f = mxg.lib().mx_silu_quantize
+    assert f(None, FAKE, FAKE, FAKE, 1, 4, 64, None) == mxg.ERROR_INVALID_VALUE
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 4, 0, None) == mxg.ERROR_INVALID_VALUE
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 4, 40, None) == mxg.ERROR_NOT_SUPPORTED
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 0, 64, None) == mxg.SUCCESS
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros((4, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        mxg.quantize(0, x, torch.tensor([0, 4], dtype=torch.int32))

@@ -1,0 +1,81 @@
+"""GPU parity: ragged grouped GEMM (FP8 rowwise, MXFP8, MXFP4) against the CPU
+oracle, element by element within |gpu - exact| <= 1e-2 * sum_k |a*b| *
+scales + 1 bf16 ulp; uncovered rows must keep their sentinel."""
+import numpy as np
+import pytest
+import torch
+
+import fp4_grouped_gemm_quantize_amd as mxg
+import oracle
+import workloads as W
+from common import GemmCase, check_gemm_rows, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+SENT_BF16 = 0x7FA5  # a NaN pattern no result can produce
+
+
+def run_gemm(case: GemmCase, N=None, hint=0):
+    inp = case.gpu_inputs()
+    N = N if N is not None else case.w.N
+    c = torch.full((case.T, N), SENT_BF16, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    mxg.mx_grouped_matmul(case.fmt, c=c, max_rows_per_group_hint=hint, **inp)
+    torch.cuda.synchronize()
+    return c.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def check_all_rows(case: GemmCase, c: np.ndarray, label: str):
+    rows = np.arange(case.T)
+    ref = case.oracle_rows(rows)
+    covered = ref["group"] >= 0
+    assert np.all(c[~covered] == SENT_BF16), f"{label}: uncovered rows were written"
+    worst, exact = check_gemm_rows(c[covered], {k: v[covered] for k, v in ref.items() if k != "group"}, label)
+    print(f"{label}: max |err|/tol = {worst:.3g}, bf16-exact fraction = {exact:.4f}")
+    return worst, exact
+
+
+# Reduced copies of the workloads: several tiles, ragged M tails (group sizes
+# not multiples of the tile), N and K not multiples of the tile or stage.
+SMALL = {
+    "tiny_fp8": W.WORKLOADS[1],
+    "decode_fp8": W.WORKLOADS[2].scaled(tokens=32, N=320, K=1056),
+    "prefill_fp8": W.WORKLOADS[3].scaled(tokens=160, E=16, N=384, K=1024),
+    "mxfp8": W.WORKLOADS[4].scaled(rows=700, E=8, N=288, K=608),
+    "mxfp4": W.WORKLOADS[5].scaled(tokens=96, E=16, N=256, K=1344),
+    "mxfp4_ktail": W.WORKLOADS[5].scaled(tokens=40, E=6, masked=1, top_k=4, N=192, K=800, swiglu=False),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_gemm_matches_oracle_all_rows(name):
+    case = GemmCase(SMALL[name])
+    c = run_gemm(case)
+    worst, exact = check_all_rows(case, c, name)
+    assert exact > 0.9, "most outputs should round to the same bf16 as the exact value"
+
+
+@pytest.mark.parametrize("name", ["prefill_fp8", "mxfp4"])
+def test_gemm_hint_does_not_change_results(name):
+    case = GemmCase(SMALL[name])
+    c0 = run_gemm(case, hint=0)
+    c1 = run_gemm(case, hint=int(case.r.counts.max()))
+    c2 = run_gemm(case, hint=1)
+    assert np.array_equal(c0, c1) and np.array_equal(c0, c2)
+
+
+@pytest.mark.parametrize("widx", [1, 2, 3, 4, 5])
+def test_gemm_full_size_sampled_rows(widx):
+    """Full-size workloads in the benchmark's launch configuration; the oracle
+    computes whole output rows for the first and last row of every group plus
+    random rows.  Workload 5 runs here as a plain MXFP4 GEMM with N = 2I."""
+    w = W.WORKLOADS[widx]
+    case = GemmCase(w, gen_device="cuda")
+    c = run_gemm(case)
+    rng = np.random.default_rng(widx)
+    rows = sample_rows(case.off, rng, per_group_extra=1, extra=32)
+    ref = case.oracle_rows(rows)
+    assert np.all(ref["group"] >= 0)
+    worst, exact = check_gemm_rows(c[rows], ref, f"workload {widx}")
+    print(f"workload {widx}: {rows.size} rows, max |err|/tol = {worst:.3g}, bf16-exact = {exact:.4f}")
+    # rows beyond the routed total do not exist here; every row is covered
+    assert not np.any(c == SENT_BF16)

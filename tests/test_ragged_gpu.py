@@ -1,0 +1,92 @@
+"""Ragged-group edge cases of the grouped GEMM on the GPU, against the oracle:
+empty groups, a single group, one-row groups, permuted / repeated / subset
+expert ids, out-of-range ids and malformed offsets (skipped, never read out of
+bounds), uncovered rows (left untouched) and N / K tails."""
+import numpy as np
+import pytest
+import torch
+
+import fp4_grouped_gemm_quantize_amd as mxg
+import oracle
+from common import check_gemm_rows, ids_gpu, offsets_gpu, to_gpu
+
+pytestmark = pytest.mark.gpu
+
+SENT = 0x7FA5
+
+
+def random_operands(rng, fmt, T, E, N, K):
+    x = oracle.bf16_round_array(rng.standard_normal((T, K)))
+    wt = oracle.bf16_round_array(rng.standard_normal((E * N, K)) * 0.02)
+    a, sa = oracle.quantize(fmt, x, np.array([0, T], np.uint32))
+    b, sb = oracle.quantize(fmt, wt, np.array([0, E * N], np.uint32))
+    b = b.reshape(E, N, -1)
+    sb = sb.reshape(E, N) if fmt == 0 else sb.reshape(E, N, K // 32)
+    return a, sa, b, sb
+
+
+def run_case(fmt, a, sa, b, sb, off, ids, N, K):
+    T = a.shape[0]
+    E = b.shape[0]
+    c = torch.full((T, N), SENT, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    mxg.mx_grouped_matmul(fmt, to_gpu(a), to_gpu(sa), to_gpu(b), to_gpu(sb), c, offsets_gpu(off), ids_gpu(ids))
+    torch.cuda.synchronize()
+    c = c.view(torch.int16).cpu().numpy().view(np.uint16)
+    ref = oracle.gemm_rows(fmt, a, sa, b, sb, off, ids, N, K, np.arange(T))
+    cov = ref["group"] >= 0
+    assert np.all(c[~cov] == SENT), "a row no valid group covers was written"
+    if cov.any():
+        check_gemm_rows(c[cov], {k: v[cov] for k, v in ref.items() if k != "group"})
+    return cov
+
+
+GROUPINGS = {
+    "empty_groups": ([0, 0, 50, 50, 50, 130, 130], [0, 1, 2, 3, 1, 0]),
+    "single_group": ([0, 130], [2]),
+    "one_row_groups": ([0, 1, 2, 3, 4, 130], [3, 0, 3, 1, 2]),
+    "permuted_and_repeated": ([0, 33, 64, 65, 129, 130], [3, 3, 0, 2, 3]),
+    "subset_with_gaps": ([5, 40, 40, 90], [1, 1, 2]),           # rows 0..4 and 90.. uncovered
+    "out_of_range_ids": ([0, 40, 80, 130], [4, -1, 1]),         # groups 0 and 1 skipped
+    "inverted_and_past_end": ([60, 20, 100, 500], [0, 1, 2]),   # g0 inverted; g2 clamped to T
+    "all_empty": ([7, 7, 7], [0, 1]),
+}
+
+
+@pytest.mark.parametrize("fmt", [0, 1, 2])
+@pytest.mark.parametrize("name", list(GROUPINGS))
+def test_groupings(fmt, name):
+    rng = np.random.default_rng(len(name) * 7 + fmt)
+    T, E, N, K = 130, 4, 200, 288
+    a, sa, b, sb = random_operands(rng, fmt, T, E, N, K)
+    off, ids = GROUPINGS[name]
+    run_case(fmt, a, sa, b, sb, np.array(off, np.uint32), np.array(ids, np.int32), N, K)
+
+
+@pytest.mark.parametrize("fmt", [0, 1, 2])
+@pytest.mark.parametrize("N,K", [(32, 32), (96, 64), (129, 160), (1000, 96)])
+def test_shape_tails(fmt, N, K):
+    rng = np.random.default_rng(N * K + fmt)
+    T, E = 77, 3
+    a, sa, b, sb = random_operands(rng, fmt, T, E, N, K)
+    run_case(fmt, a, sa, b, sb, np.array([0, 20, 21, 77], np.uint32), np.array([2, 0, 1], np.int32), N, K)
+
+
+def test_many_groups():
+    """The largest group count (1024 groups, many of them empty)."""
+    rng = np.random.default_rng(99)
+    G, E, T, N, K = 1024, 8, 600, 64, 64
+    counts = rng.multinomial(T, np.ones(G) / G)
+    off = np.r_[0, np.cumsum(counts)].astype(np.uint32)
+    ids = rng.integers(0, E, G).astype(np.int32)
+    a, sa, b, sb = random_operands(rng, 2, T, E, N, K)
+    cov = run_case(2, a, sa, b, sb, off, ids, N, K)
+    assert cov.all()
+
+
+def test_zero_rows_is_a_no_op():
+    e = torch.empty((0, 64), dtype=torch.uint8, device="cuda")
+    c = torch.empty((0, 32), dtype=torch.bfloat16, device="cuda")
+    b = torch.zeros((1, 32, 64), dtype=torch.uint8, device="cuda")
+    mxg.mx_grouped_matmul(0, e, torch.empty((0,), device="cuda"), b, torch.zeros((1, 32), device="cuda"), c,
+                          offsets_gpu(np.array([0, 0], np.uint32)), ids_gpu(np.array([0], np.int32)))
+    torch.cuda.synchronize()
