@@ -44,6 +44,9 @@ def parse():
     p.add_argument("--workload", type=int, default=3, help="1..5 (default: 3, prefill FP8 rowwise)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU baseline")
+    p.add_argument("--copy-calibration-mib", type=int, default=0,
+                   help="before the workload, run a plain device copy of this many MiB three times "
+                        "(a known-size kernel for scaling rocprofv3 byte counters)")
     return p.parse_args()
 
 
@@ -151,6 +154,14 @@ def main():
     import workloads as W
 
     torch.cuda.set_device(0)
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     w = W.WORKLOADS[args.workload]
     r = W.routing(w)
     T, K, N, fmt = r.total_rows, w.K, w.N, w.fmt
