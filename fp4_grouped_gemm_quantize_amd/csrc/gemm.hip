@@ -18,16 +18,26 @@
 //            K 32+16h .. 32+16h+15 (block 1).
 //    FP8 rowwise runs the same instruction without block scales and applies
 //    a_scale * b_scale in the epilogue.
-//  * Tiles: a workgroup of 4 waves (2 x 2) owns a BM x BN output tile; each
-//    wave a (BM/2) x (BN/2) sub-tile of 32 x 32 accumulators.  K streams in
-//    stages of 128 bytes per row (128 e4m3 or 256 e2m1 elements) through a
-//    double-buffered LDS ring: global -> registers for stage k+1 is in flight
-//    while stage k feeds the matrix cores.  16-byte chunks are XOR-swizzled by
-//    row so the 16-byte LDS reads of 8 consecutive rows hit distinct banks.
+//  * Tiles: a workgroup of WGM x WGN waves owns a BM x BN output tile; each
+//    wave a (BM/WGM) x (BN/WGN) sub-tile of 32 x 32 accumulators.  K streams
+//    in stages of 128 bytes per row (128 e4m3 or 256 e2m1 elements) through a
+//    double-buffered LDS ring filled by direct global->LDS loads
+//    (global_load_lds_dwordx4: each lane's 16 bytes land at LDS base + 16 *
+//    lane, no VGPR staging), issued one stage ahead of the matrix cores.  The
+//    16-byte chunks of a row are XOR-swizzled by row (chunk c of row r sits
+//    at slot c ^ (r & 7)) so the 16-byte fragment reads of 8 consecutive rows
+//    hit distinct banks; the swizzle is realised by choosing which global
+//    chunk each lane fetches.  A stage that runs past the end of K (only the
+//    last one, when K bytes are not a multiple of 128) goes through VGPRs so
+//    its tail can be zero-filled.
+//  * MX scales: each lane loads the 4 (e4m3) or 8 (e2m1) scale bytes of its
+//    own row for the next stage straight into registers and shifts out the
+//    byte of its block per step; no LDS traffic.
 //  * Ragged groups without host sync: every workgroup derives the per-group
 //    M-tile counts from row_offsets into an LDS prefix sum; a tile index is
 //    mapped to (group, m-tile) by binary search.  Empty or invalid groups own
-//    no tiles, partial M tiles are masked, not padded in memory.
+//    no tiles; in a partial M (or N) tile each wave skips the matrix-core work
+//    of its 32-row (32-column) slices that hold no real rows.
 //  * Persistent, XCD-aware schedule: the grid is sized to the resident
 //    capacity; workgroup b (dispatched to XCD b % 8) walks logical tiles so
 //    that the workgroups resident on one XCD hold consecutive tiles (same
@@ -43,7 +53,6 @@ namespace {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-constexpr int kThreads = 256;
 constexpr int kStageBytes = 128;  // K bytes per row per stage
 constexpr int kNumXcd = 8;
 
@@ -64,6 +73,7 @@ struct GemmArgs {
     int64_t K;
     int64_t row_bytes;  // bytes per row of a and b
     int ntiles_n;
+    int n_outer;        // tile order within a group: 0 = M tiles outer, 1 = N tiles outer
 };
 
 // FMT: 0 = FP8 rowwise, 1 = MXFP8, 2 = MXFP4.
@@ -71,12 +81,34 @@ template <int FMT>
 struct Fmt {
     static constexpr bool kMX = FMT != 0;
     static constexpr bool kFP4 = FMT == 2;
-    static constexpr int kSteps = kFP4 ? 4 : 2;           // 64-deep MFMA steps per stage
-    static constexpr int kBlocks = kFP4 ? 8 : 4;          // 32-element scale blocks per stage
-    static constexpr int kTypeCode = kFP4 ? 4 : 0;        // cbsz / blgp: 0 = e4m3, 4 = e2m1
+    static constexpr int kSteps = kFP4 ? 4 : 2;   // 64-deep MFMA steps per stage
+    static constexpr int kBlocks = kFP4 ? 8 : 4;  // 32-element scale blocks per stage
+    static constexpr int kTypeCode = kFP4 ? 4 : 0;  // cbsz / blgp: 0 = e4m3, 4 = e2m1
 };
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * kStageBytes + ((chunk ^ (row & 7)) << 4); }
+// BM x BN output tile, WGM x WGN waves, SLOTS stages of LDS ring (2: one stage
+// in flight while one is consumed; 3: two in flight).
+template <int BM_, int BN_, int WGM_, int WGN_, int SLOTS_ = 3, int MINB_ = 1>
+struct Tile {
+    static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_, kMinBlocks = MINB_, kSlots = SLOTS_;
+    // Fragment buffers per wave: with one wave per SIMD the fragments of step
+    // s+1 are read while step s computes (2); with two waves per SIMD the
+    // other wave covers the LDS latency and the registers go to accumulators.
+    static_assert(SLOTS_ == 2 || SLOTS_ == 3, "2- or 3-slot LDS ring");
+    static constexpr int kWaves = WGM * WGN, kThreads = kWave * kWaves;
+    static constexpr int WTM = BM / WGM, WTN = BN / WGN;
+    static constexpr int TM = WTM / 32, TN = WTN / 32;
+    static constexpr int kFragBufs = kWaves >= 8 ? 1 : 2;
+    static_assert(TM >= 1 && TN >= 1, "wave tile below one 32x32 accumulator");
+    static_assert(BM % (8 * kWaves) == 0 && BN % (8 * kWaves) == 0, "loader: whole 8-row groups per wave");
+};
+
+// LDS byte offset of 16-byte chunk `chunk` of stage row `row`.  A row is 128
+// bytes (32 of the 64 four-byte banks), so even and odd rows fall in opposite
+// bank halves; XOR-ing the chunk with bits 1..3 of the row gives the 16 rows a
+// 16-lane slice of a fragment read touches 16 distinct 4-bank groups.
+__device__ __forceinline__ int swz_chunk(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
+__device__ __forceinline__ int swz(int row, int chunk) { return row * kStageBytes + (swz_chunk(row, chunk) << 4); }
 
 // Bijective remap so that the workgroups the dispatcher sends to one XCD
 // (b, b + 8, b + 16, ...) get consecutive logical indices.
@@ -86,7 +118,8 @@ __device__ __forceinline__ int xcd_remap(int b, int n) {
     return xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
 }
 
-// Exclusive block-wide scan (256 threads).
+// Exclusive block-wide scan over NT threads.
+template <int NT>
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s_wave, uint32_t* total) {
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     uint32_t inc = v;
@@ -99,7 +132,7 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s
     __syncthreads();
     uint32_t before = 0, all = 0;
 #pragma unroll
-    for (int w = 0; w < kThreads / kWave; ++w) {
+    for (int w = 0; w < NT / kWave; ++w) {
         uint32_t s = s_wave[w];
         before += w < wave ? s : 0;
         all += s;
@@ -108,35 +141,161 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s
     return before + inc - v;
 }
 
-template <int BM, int BN, int FMT, bool SWIGLU>
-__global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(const GemmArgs args) {
+// Scale bytes p[0 .. 4) as one word; bytes at or past `avail` read as 127
+// (2^0: they only ever multiply zero-filled K tails).
+__device__ __forceinline__ uint32_t scale_word(const uint8_t* p, int64_t avail) {
+    if (avail >= 4 && (reinterpret_cast<uintptr_t>(p) & 3) == 0) return *reinterpret_cast<const uint32_t*>(p);
+    uint32_t w = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w |= (uint32_t)(i < avail ? p[i] : (uint8_t)127) << (8 * i);
+    return w;
+}
+
+// s_waitcnt vmcnt(N) (expcnt / lgkmcnt left at their maxima): wait until at
+// most N vector-memory loads of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 0xf) | (0x7 << 4) | (0xf << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier for the K loop.  __syncthreads() carries a workgroup
+// release fence, and because direct-to-LDS loads count as LDS writes that
+// fence waits for ALL of them (vmcnt(0)), draining the prefetch in flight.
+// Here each wave waits only until at most N of its loads are outstanding
+// (the stage being prefetched) and for its own LDS writes (lgkmcnt(0)); the
+// empty asm statements keep the compiler from moving memory accesses across.
+template <int N>
+__device__ __forceinline__ void stage_barrier() {
+    wait_vmem<N>();
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+}
+
+typedef const void __attribute__((address_space(1)))* gptr_t;
+typedef void __attribute__((address_space(3)))* lptr_t;
+
+// Fragments of one 64-deep K step for one wave, read from LDS slot sa / sb.
+template <class TL, int FMT>
+__device__ __forceinline__ void load_frags(const uint8_t* __restrict__ sa, const uint8_t* __restrict__ sb, int s,
+                                           int wm, int wn, int h, int r32, v8i (&af)[TL::TM], v8i (&bf)[TL::TN]) {
     using F = Fmt<FMT>;
-    constexpr int WM = BM / 2, WN = BN / 2;
-    constexpr int TM = WM / 32, TN = WN / 32;
-    constexpr int A_CH = BM * 8 / kThreads;  // 16-byte chunks per thread per stage
-    constexpr int B_CH = BN * 8 / kThreads;
-    constexpr int A_SC = F::kMX ? BM * F::kBlocks / kThreads : 0;  // scale bytes per thread per stage
-    constexpr int B_SC = F::kMX ? BN * F::kBlocks / kThreads : 0;
-    static_assert(A_CH >= 1 && B_CH >= 1, "tile too small for the loader");
-    static_assert(!F::kMX || (A_SC >= 1 && B_SC >= 1), "tile too small for the scale loader");
+#pragma unroll
+    for (int i = 0; i < TL::TM; ++i) {
+        const int row = wm * TL::WTM + i * 32 + r32;
+        if constexpr (F::kFP4) {
+            const uint4 x = *reinterpret_cast<const uint4*>(sa + swz(row, 2 * s + h));
+            af[i] = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
+        } else {
+            const uint4 x0 = *reinterpret_cast<const uint4*>(sa + swz(row, 4 * s + h));
+            const uint4 x1 = *reinterpret_cast<const uint4*>(sa + swz(row, 4 * s + 2 + h));
+            af[i] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < TL::TN; ++j) {
+        const int row = wn * TL::WTN + j * 32 + r32;
+        if constexpr (F::kFP4) {
+            const uint4 x = *reinterpret_cast<const uint4*>(sb + swz(row, 2 * s + h));
+            bf[j] = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
+        } else {
+            const uint4 x0 = *reinterpret_cast<const uint4*>(sb + swz(row, 4 * s + h));
+            const uint4 x1 = *reinterpret_cast<const uint4*>(sb + swz(row, 4 * s + 2 + h));
+            bf[j] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+        }
+    }
+}
+
+// The TM x TN matrix-core ops of step s (scale byte of block 2s + h of the
+// stage: word s/2, byte 2(s%2) + h).
+template <class TL, int FMT>
+__device__ __forceinline__ void mma_step(int s, int h, const v8i (&af)[TL::TM], const v8i (&bf)[TL::TN],
+                                         const uint32_t (&wa)[TL::TM][Fmt<FMT>::kFP4 ? 2 : 1],
+                                         const uint32_t (&wb)[TL::TN][Fmt<FMT>::kFP4 ? 2 : 1],
+                                         v16f (&acc)[TL::TM][TL::TN]) {
+    using F = Fmt<FMT>;
+    const int shift = 8 * (2 * (s & 1) + h);
+#pragma unroll
+    for (int i = 0; i < TL::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TL::TN; ++j) {
+            if constexpr (F::kMX)
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    af[i], bf[j], acc[i][j], F::kTypeCode, F::kTypeCode, 0, (int)(wa[i][s >> 1] >> shift), 0,
+                    (int)(wb[j][s >> 1] >> shift));
+            else
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], 0, 0, 0, 0,
+                                                                             0, 0);
+        }
+}
+
+// All K steps of one stage with the fragments of step s+1 read from LDS
+// while the matrix cores work on step s.
+template <class TL, int FMT>
+__device__ __forceinline__ void mma_stage(const uint8_t* __restrict__ sa, const uint8_t* __restrict__ sb, int wm,
+                                          int wn, int h, int r32,
+                                          const uint32_t (&wa)[TL::TM][Fmt<FMT>::kFP4 ? 2 : 1],
+                                          const uint32_t (&wb)[TL::TN][Fmt<FMT>::kFP4 ? 2 : 1],
+                                          v16f (&acc)[TL::TM][TL::TN]) {
+    using F = Fmt<FMT>;
+    constexpr int NB = TL::kFragBufs;
+    v8i af[NB][TL::TM], bf[NB][TL::TN];
+    load_frags<TL, FMT>(sa, sb, 0, wm, wn, h, r32, af[0], bf[0]);
+#pragma unroll
+    for (int s = 0; s < F::kSteps; ++s) {
+        if (NB == 2 && s + 1 < F::kSteps)
+            load_frags<TL, FMT>(sa, sb, s + 1, wm, wn, h, r32, af[(s + 1) % NB], bf[(s + 1) % NB]);
+        mma_step<TL, FMT>(s, h, af[s % NB], bf[s % NB], wa, wb, acc);
+        if (NB == 1 && s + 1 < F::kSteps) load_frags<TL, FMT>(sa, sb, s + 1, wm, wn, h, r32, af[0], bf[0]);
+        // interleave: one matrix-core op, then a share of the next step's LDS reads
+        constexpr int kMfma = TL::TM * TL::TN;
+        constexpr int kReads = (TL::TM + TL::TN) * (F::kFP4 ? 1 : 2);
+        if (NB == 2 && s + 1 < F::kSteps) {
+#pragma unroll
+            for (int q = 0; q < kMfma; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                            // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, (kReads + kMfma - 1) / kMfma, 0);  // DS read
+            }
+        }
+    }
+}
+
+template <class TL, int FMT, bool SWIGLU>
+__global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_kernel(const GemmArgs args) {
+    using F = Fmt<FMT>;
+    constexpr int BM = TL::BM, BN = TL::BN, NW = TL::kWaves, NT = TL::kThreads;
+    constexpr int WTM = TL::WTM, WTN = TL::WTN, TM = TL::TM, TN = TL::TN;
     constexpr int kAStage = BM * kStageBytes, kBStage = BN * kStageBytes;
-    constexpr int kSStride = 8;  // LDS bytes per row of a stage's scales
+    constexpr int kStage = kAStage + kBStage;
+    constexpr int A_J = BM / 8 / NW, B_J = BN / 8 / NW;  // 1 KiB load instructions per wave per stage
+    constexpr int kWords = F::kFP4 ? 2 : 1;              // scale words per row per stage
+    constexpr int kGroupsPerThread = (kMaxGroups + NT - 1) / NT;
 
-    __shared__ __attribute__((aligned(16))) uint8_t s_ab[2 * (kAStage + kBStage)];
-    __shared__ uint8_t s_sc[F::kMX ? 2 * (BM + BN) * kSStride : 4];
+    // Ring slots as distinct objects: the compiler can then tell the
+    // direct-to-LDS loads into one slot from the fragment reads of another and
+    // does not serialise them.  kSlots - 1 stages are in flight while one is
+    // consumed.
+    constexpr int kSlots = TL::kSlots;
+    __shared__ __attribute__((aligned(16))) uint8_t s_ring0[kStage];
+    __shared__ __attribute__((aligned(16))) uint8_t s_ring1[kStage];
+    __shared__ __attribute__((aligned(16))) uint8_t s_ring2[kSlots > 2 ? kStage : 16];
     __shared__ uint32_t s_pre[kMaxGroups + 1];
-    __shared__ uint32_t s_wave[kThreads / kWave];
+    __shared__ uint32_t s_wave[NW];
 
-    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int wm = wave / TL::WGN, wn = wave % TL::WGN;
+    const int h = lane >> 5, r32 = lane & 31;
     const int G = args.G;
 
     // ---- per-group M-tile prefix (ragged schedule, no host sync)
     {
-        uint32_t cnt[4], local = 0;
+        uint32_t cnt[kGroupsPerThread], local = 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int g = tid * 4 + i;
+        for (int i = 0; i < kGroupsPerThread; ++i) {
+            const int g = tid * kGroupsPerThread + i;
             cnt[i] = 0;
             if (g < G) {
                 GroupRange r = group_range(args.off, args.ids, g, args.T, args.E);
@@ -145,10 +304,10 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(const GemmArgs a
             local += cnt[i];
         }
         uint32_t total;
-        uint32_t ex = block_exclusive_scan(local, s_wave, &total);
+        uint32_t ex = block_exclusive_scan<NT>(local, s_wave, &total);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int g = tid * 4 + i;
+        for (int i = 0; i < kGroupsPerThread; ++i) {
+            const int g = tid * kGroupsPerThread + i;
             if (g < G) s_pre[g] = ex;
             ex += cnt[i];
         }
@@ -156,106 +315,119 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(const GemmArgs a
         __syncthreads();
     }
     const int64_t total_tiles = (int64_t)s_pre[G] * args.ntiles_n;
-    const int nkt = (int)((args.row_bytes + kStageBytes - 1) / kStageBytes);
+    const int64_t row_bytes = args.row_bytes;
+    const int nkt = (int)((row_bytes + kStageBytes - 1) / kStageBytes);
+    const bool k_tail = (row_bytes % kStageBytes) != 0;  // the last stage is partial
+    const int64_t nblk = args.K / 32;
 
+    const int ntn = args.ntiles_n;
     for (int64_t L = xcd_remap(blockIdx.x, gridDim.x); L < total_tiles; L += gridDim.x) {
-        const int mt = (int)(L / args.ntiles_n);
-        const int nt = (int)(L % args.ntiles_n);
-        // group owning m-tile mt: largest g with s_pre[g] <= mt
-        int lo = 0, hi = G;  // invariant: s_pre[lo] <= mt < s_pre[hi]
+        // group owning tile L: largest g with s_pre[g] * ntn <= L (groups own
+        // contiguous tile ranges; empty groups own none)
+        int lo = 0, hi = G;  // invariant: s_pre[lo] * ntn <= L < s_pre[hi] * ntn
         while (hi - lo > 1) {
             const int mid = (lo + hi) >> 1;
-            if (s_pre[mid] <= (uint32_t)mt) lo = mid; else hi = mid;
+            if ((int64_t)s_pre[mid] * ntn <= L) lo = mid; else hi = mid;
         }
         const int g = lo;
+        const int mtiles = (int)(s_pre[g + 1] - s_pre[g]);
+        const int local = (int)(L - (int64_t)s_pre[g] * ntn);
+        // M-outer: consecutive tiles share an A panel; N-outer: consecutive
+        // tiles share a weight panel (weight streaming)
+        const int mt = args.n_outer ? local % mtiles : local / ntn;
+        const int nt = args.n_outer ? local / mtiles : local % ntn;
         const GroupRange gr = group_range(args.off, args.ids, g, args.T, args.E);
         const int e = args.ids[g];
-        const int64_t m0 = gr.lo + (int64_t)(mt - (int)s_pre[g]) * BM;
+        const int64_t m0 = gr.lo + (int64_t)mt * BM;
         const int64_t m_end = m0 + BM < gr.hi ? m0 + BM : gr.hi;
         const int64_t n0 = (int64_t)nt * BN;
+        const int rows_in = (int)(m_end - m0);
+        const int cols_in = (int)(args.N - n0 < BN ? args.N - n0 : BN);
 
-        // ---- global load plan for this tile
-        const uint8_t* a_row[A_CH];
-        const uint8_t* b_row[B_CH];
+        // ---- operand sources: tile base (uniform) + 32-bit per-lane offsets;
+        // each load instruction covers 8 rows x 8 chunks (1 KiB of the slot).
+        // Rows past the group / columns past N re-read the last real one.
+        const uint8_t* a_base = args.a + m0 * row_bytes;
+        const uint8_t* b_base = args.b + ((int64_t)e * args.N + n0) * row_bytes;
+        uint32_t a_off[A_J], b_off[B_J];
+        {
+            const int rr = lane >> 3, pc = lane & 7;
 #pragma unroll
-        for (int i = 0; i < A_CH; ++i) {
-            const int q = tid + kThreads * i, r = q >> 3;
-            int64_t row = m0 + r;
-            row = row < m_end ? row : m_end - 1;
-            a_row[i] = args.a + row * args.row_bytes + ((q & 7) << 4);
-        }
+            for (int j = 0; j < A_J; ++j) {
+                const int r = (wave + NW * j) * 8 + rr;
+                const int rc = r < rows_in ? r : rows_in - 1;
+                a_off[j] = (uint32_t)(rc * row_bytes) + (swz_chunk(r, pc) << 4);
+            }
 #pragma unroll
-        for (int i = 0; i < B_CH; ++i) {
-            const int q = tid + kThreads * i, r = q >> 3;
-            int64_t n = n0 + r;
-            n = n < args.N ? n : args.N - 1;
-            b_row[i] = args.b + ((int64_t)e * args.N + n) * args.row_bytes + ((q & 7) << 4);
+            for (int j = 0; j < B_J; ++j) {
+                const int r = (wave + NW * j) * 8 + rr;
+                const int rc = r < cols_in ? r : cols_in - 1;
+                b_off[j] = (uint32_t)(rc * row_bytes) + (swz_chunk(r, pc) << 4);
+            }
         }
-        uint4 ra[A_CH], rb[B_CH];
-        uint8_t rsa[A_SC > 0 ? A_SC : 1], rsb[B_SC > 0 ? B_SC : 1];
-
-        auto load_stage = [&](int kt) {
+        auto issue_stage = [&](int kt, uint8_t* slot) {
+            const uint8_t* ak = a_base + (int64_t)kt * kStageBytes;
+            const uint8_t* bk = b_base + (int64_t)kt * kStageBytes;
+#pragma unroll
+            for (int j = 0; j < A_J; ++j)
+                __builtin_amdgcn_global_load_lds((gptr_t)(ak + a_off[j]), (lptr_t)(slot + (wave + NW * j) * 1024), 16,
+                                                 0, 0);
+#pragma unroll
+            for (int j = 0; j < B_J; ++j)
+                __builtin_amdgcn_global_load_lds((gptr_t)(bk + b_off[j]),
+                                                 (lptr_t)(slot + kAStage + (wave + NW * j) * 1024), 16, 0, 0);
+        };
+        // The partial last stage: VGPR loads with the K tail zero-filled.
+        uint4 ta[A_J], tb[B_J];
+        auto load_tail = [&](int kt) {
             const int64_t kb = (int64_t)kt * kStageBytes;
+            const int c_lo = lane & 7;  // physical chunk; the logical one depends on the row
 #pragma unroll
-            for (int i = 0; i < A_CH; ++i) {
-                const int c = (tid + kThreads * i) & 7;
-                ra[i] = kb + c * 16 < args.row_bytes ? *reinterpret_cast<const uint4*>(a_row[i] + kb)
-                                                     : make_uint4(0, 0, 0, 0);
+            for (int j = 0; j < A_J; ++j) {
+                const int r = (wave + NW * j) * 8 + (lane >> 3);
+                const bool in = kb + swz_chunk(r, c_lo) * 16 < row_bytes;
+                ta[j] = in ? *reinterpret_cast<const uint4*>(a_base + kb + a_off[j]) : make_uint4(0, 0, 0, 0);
             }
 #pragma unroll
-            for (int i = 0; i < B_CH; ++i) {
-                const int c = (tid + kThreads * i) & 7;
-                rb[i] = kb + c * 16 < args.row_bytes ? *reinterpret_cast<const uint4*>(b_row[i] + kb)
-                                                     : make_uint4(0, 0, 0, 0);
-            }
-            if constexpr (F::kMX) {
-                const int64_t nblk = args.K / 32;
-                const uint8_t* as = static_cast<const uint8_t*>(args.as);
-                const uint8_t* bs = static_cast<const uint8_t*>(args.bs);
-#pragma unroll
-                for (int i = 0; i < A_SC; ++i) {
-                    const int q = tid + kThreads * i, r = q / F::kBlocks, j = q % F::kBlocks;
-                    int64_t row = m0 + r;
-                    row = row < m_end ? row : m_end - 1;
-                    const int64_t blk = (int64_t)kt * F::kBlocks + j;
-                    rsa[i] = blk < nblk ? as[row * nblk + blk] : (uint8_t)127;
-                }
-#pragma unroll
-                for (int i = 0; i < B_SC; ++i) {
-                    const int q = tid + kThreads * i, r = q / F::kBlocks, j = q % F::kBlocks;
-                    int64_t n = n0 + r;
-                    n = n < args.N ? n : args.N - 1;
-                    const int64_t blk = (int64_t)kt * F::kBlocks + j;
-                    rsb[i] = blk < nblk ? bs[((int64_t)e * args.N + n) * nblk + blk] : (uint8_t)127;
-                }
+            for (int j = 0; j < B_J; ++j) {
+                const int r = (wave + NW * j) * 8 + (lane >> 3);
+                const bool in = kb + swz_chunk(r, c_lo) * 16 < row_bytes;
+                tb[j] = in ? *reinterpret_cast<const uint4*>(b_base + kb + b_off[j]) : make_uint4(0, 0, 0, 0);
             }
         };
-        auto store_stage = [&](int st) {
-            uint8_t* sa = s_ab + st * (kAStage + kBStage);
-            uint8_t* sb = sa + kAStage;
+        auto store_tail = [&](uint8_t* slot) {
 #pragma unroll
-            for (int i = 0; i < A_CH; ++i) {
-                const int q = tid + kThreads * i;
-                *reinterpret_cast<uint4*>(sa + swz(q >> 3, q & 7)) = ra[i];
+            for (int j = 0; j < A_J; ++j) *reinterpret_cast<uint4*>(slot + (wave + NW * j) * 1024 + lane * 16) = ta[j];
+#pragma unroll
+            for (int j = 0; j < B_J; ++j)
+                *reinterpret_cast<uint4*>(slot + kAStage + (wave + NW * j) * 1024 + lane * 16) = tb[j];
+        };
+
+        // ---- MX scale words of this lane's rows / columns, one stage ahead
+        const uint8_t* sa_base = static_cast<const uint8_t*>(args.as) + m0 * nblk;
+        const uint8_t* sb_base = static_cast<const uint8_t*>(args.bs) + ((int64_t)e * args.N + n0) * nblk;
+        uint32_t sa_off[TM], sb_off[TN];
+        uint32_t wa[TM][kWords], wb[TN][kWords];
+        if constexpr (F::kMX) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const int r = wm * WTM + i * 32 + r32;
+                sa_off[i] = (uint32_t)((r < rows_in ? r : rows_in - 1) * nblk);
             }
 #pragma unroll
-            for (int i = 0; i < B_CH; ++i) {
-                const int q = tid + kThreads * i;
-                *reinterpret_cast<uint4*>(sb + swz(q >> 3, q & 7)) = rb[i];
+            for (int j = 0; j < TN; ++j) {
+                const int r = wn * WTN + j * 32 + r32;
+                sb_off[j] = (uint32_t)((r < cols_in ? r : cols_in - 1) * nblk);
             }
-            if constexpr (F::kMX) {
-                uint8_t* ssa = s_sc + st * (BM + BN) * kSStride;
-                uint8_t* ssb = ssa + BM * kSStride;
+        }
+        auto load_scales = [&](int kt, uint32_t (&xa)[TM][kWords], uint32_t (&xb)[TN][kWords]) {
+            const int64_t b0 = (int64_t)kt * F::kBlocks;
 #pragma unroll
-                for (int i = 0; i < A_SC; ++i) {
-                    const int q = tid + kThreads * i;
-                    ssa[(q / F::kBlocks) * kSStride + q % F::kBlocks] = rsa[i];
-                }
+            for (int w = 0; w < kWords; ++w) {
 #pragma unroll
-                for (int i = 0; i < B_SC; ++i) {
-                    const int q = tid + kThreads * i;
-                    ssb[(q / F::kBlocks) * kSStride + q % F::kBlocks] = rsb[i];
-                }
+                for (int i = 0; i < TM; ++i) xa[i][w] = scale_word(sa_base + b0 + 4 * w + sa_off[i], nblk - b0 - 4 * w);
+#pragma unroll
+                for (int j = 0; j < TN; ++j) xb[j][w] = scale_word(sb_base + b0 + 4 * w + sb_off[j], nblk - b0 - 4 * w);
             }
         };
 
@@ -265,79 +437,79 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(const GemmArgs a
 #pragma unroll
             for (int j = 0; j < TN; ++j) acc[i][j] = v16f{};
 
-        load_stage(0);
-        store_stage(0);
+        // ---- prologue: stages 0 .. kSlots-2 into the first slots
+        auto put_stage = [&](int kt, uint8_t* slot) {
+            if (k_tail && kt == nkt - 1) {
+                load_tail(kt);
+                store_tail(slot);
+            } else {
+                issue_stage(kt, slot);
+            }
+        };
+        put_stage(0, s_ring0);
+        if (kSlots > 2 && nkt > 1) put_stage(1, s_ring1);
+        if constexpr (F::kMX) load_scales(0, wa, wb);
+        wait_vmem<0>();
         __syncthreads();
 
-        const int h = lane >> 5, r32 = lane & 31;
-        for (int kt = 0; kt < nkt; ++kt) {
-            const int st = kt & 1;
-            if (kt + 1 < nkt) load_stage(kt + 1);
-            const uint8_t* sa = s_ab + st * (kAStage + kBStage);
-            const uint8_t* sb = sa + kAStage;
-            const uint8_t* ssa = s_sc + st * (BM + BN) * kSStride;
-            const uint8_t* ssb = ssa + BM * kSStride;
-#pragma unroll
-            for (int s = 0; s < F::kSteps; ++s) {
-                v8i af[TM], bf[TN];
-                int sca[TM], scb[TN];
-#pragma unroll
-                for (int i = 0; i < TM; ++i) {
-                    const int row = wm * WM + i * 32 + r32;
-                    if constexpr (F::kFP4) {
-                        const uint4 x = *reinterpret_cast<const uint4*>(sa + swz(row, 2 * s + h));
-                        af[i] = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
-                    } else {
-                        const uint4 x0 = *reinterpret_cast<const uint4*>(sa + swz(row, 4 * s + h));
-                        const uint4 x1 = *reinterpret_cast<const uint4*>(sa + swz(row, 4 * s + 2 + h));
-                        af[i] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
-                                    (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-                    }
-                    if constexpr (F::kMX) sca[i] = ssa[row * kSStride + 2 * s + h];
-                }
-#pragma unroll
-                for (int j = 0; j < TN; ++j) {
-                    const int row = wn * WN + j * 32 + r32;
-                    if constexpr (F::kFP4) {
-                        const uint4 x = *reinterpret_cast<const uint4*>(sb + swz(row, 2 * s + h));
-                        bf[j] = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
-                    } else {
-                        const uint4 x0 = *reinterpret_cast<const uint4*>(sb + swz(row, 4 * s + h));
-                        const uint4 x1 = *reinterpret_cast<const uint4*>(sb + swz(row, 4 * s + 2 + h));
-                        bf[j] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
-                                    (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-                    }
-                    if constexpr (F::kMX) scb[j] = ssb[row * kSStride + 2 * s + h];
-                }
-#pragma unroll
-                for (int i = 0; i < TM; ++i)
-#pragma unroll
-                    for (int j = 0; j < TN; ++j) {
-                        if constexpr (F::kMX)
-                            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                                af[i], bf[j], acc[i][j], F::kTypeCode, F::kTypeCode, 0, sca[i], 0, scb[j]);
-                        else
-                            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                                af[i], bf[j], acc[i][j], 0, 0, 0, 0, 0, 0);
-                    }
+        // One stage: the matrix cores consume `cur` (stage kt) while stage
+        // kt + kSlots - 1 streams into `pf` (and, with three slots, stage kt+1,
+        // issued one stage earlier, lands); the slots rotate, so the loop is
+        // unrolled by kSlots.
+        constexpr int D = kSlots - 1;  // prefetch distance in stages
+        auto stage = [&](int kt, const uint8_t* cur, uint8_t* pf) {
+            const bool pf_on = kt + D < nkt;
+            const bool pf_tail = pf_on && k_tail && kt + D == nkt - 1;
+            uint32_t na[TM][kWords], nb[TN][kWords];
+            if constexpr (F::kMX)
+                if (kt + 1 < nkt) load_scales(kt + 1, na, nb);
+            if (pf_on) {
+                if (pf_tail) load_tail(kt + D);
+                else issue_stage(kt + D, pf);
             }
-            if (kt + 1 < nkt) store_stage(st ^ 1);
-            __syncthreads();
+            mma_stage<TL, FMT>(cur, cur + kAStage, wm, wn, h, r32, wa, wb, acc);
+            if (pf_tail) store_tail(pf);
+            if constexpr (F::kMX)
+                if (kt + 1 < nkt) {
+#pragma unroll
+                    for (int w = 0; w < kWords; ++w) {
+#pragma unroll
+                        for (int i = 0; i < TM; ++i) wa[i][w] = na[i][w];
+#pragma unroll
+                        for (int j = 0; j < TN; ++j) wb[j][w] = nb[j][w];
+                    }
+                }
+            // stage kt+1 (and its scales) must have landed; with three slots
+            // stage kt+2's direct loads, the most recent ones, may stay in flight
+            if (D == 2 && pf_on && !pf_tail) stage_barrier<A_J + B_J>();
+            else stage_barrier<0>();
+        };
+        if constexpr (kSlots == 3) {
+            for (int kt = 0; kt < nkt; kt += 3) {
+                stage(kt, s_ring0, s_ring2);
+                if (kt + 1 < nkt) stage(kt + 1, s_ring1, s_ring0);
+                if (kt + 2 < nkt) stage(kt + 2, s_ring2, s_ring1);
+            }
+        } else {
+            for (int kt = 0; kt < nkt; kt += 2) {
+                stage(kt, s_ring0, s_ring1);
+                if (kt + 1 < nkt) stage(kt + 1, s_ring1, s_ring0);
+            }
         }
 
         // ---- epilogue
         if constexpr (!SWIGLU) {
 #pragma unroll
-            for (int i = 0; i < TM; ++i)
+            for (int i = 0; i < TM; ++i) {
 #pragma unroll
                 for (int j = 0; j < TN; ++j) {
-                    const int64_t col = n0 + wn * WN + j * 32 + r32;
+                    const int64_t col = n0 + wn * WTN + j * 32 + r32;
                     float sbv = 1.0f;
                     if constexpr (!F::kMX)
                         if (col < args.N) sbv = static_cast<const float*>(args.bs)[(int64_t)e * args.N + col];
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const int64_t row = m0 + wm * WM + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                        const int64_t row = m0 + wm * WTM + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
                         if (row < m_end && col < args.N) {
                             float v = acc[i][j][r];
                             if constexpr (!F::kMX) {
@@ -348,46 +520,52 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(const GemmArgs a
                         }
                     }
                 }
+            }
         } else {
-            // Stage the bf16 gate/up tile in LDS, then requant rows of 32 outputs
-            // with the same code the standalone activation kernel runs.
+            // Stage the bf16 gate/up tile in LDS (rows spread over the slots),
+            // then requant rows of 32 outputs with the same code the standalone
+            // activation kernel runs.
             static_assert(BN % 64 == 0, "fused tile must hold whole 32-output blocks");
-            static_assert(BM * BN * 2 <= 2 * (kAStage + kBStage), "staging tile must fit the LDS ring");
-            uint16_t* s_c = reinterpret_cast<uint16_t*>(s_ab);
+            constexpr int kRowsPerSlot = kStage / (BN * 2);
+            static_assert(kSlots * kRowsPerSlot >= BM, "staging tile must fit the LDS ring");
+            auto srow = [&](int row) -> uint16_t* {
+                uint8_t* base = row < kRowsPerSlot ? s_ring0 : row < 2 * kRowsPerSlot ? s_ring1 : s_ring2;
+                return reinterpret_cast<uint16_t*>(base + (row % kRowsPerSlot) * BN * 2);
+            };
 #pragma unroll
-            for (int i = 0; i < TM; ++i)
+            for (int i = 0; i < TM; ++i) {
 #pragma unroll
                 for (int j = 0; j < TN; ++j) {
-                    const int col = wn * WN + j * 32 + r32;
+                    const int col = wn * WTN + j * 32 + r32;
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const int row = wm * WM + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                        s_c[row * BN + col] = (uint16_t)f32_to_bf16(acc[i][j][r]);
+                        const int row = wm * WTM + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                        srow(row)[col] = (uint16_t)f32_to_bf16(acc[i][j][r]);
                     }
                 }
+            }
             __syncthreads();
             constexpr int kBlk = BN / 64;  // 32-output blocks per tile row
             constexpr int kUnits = BM * kBlk;
             const int l4 = tid & 3;
             const int64_t I = args.N / 2;
+            // units cover whole 4-lane groups, so every lane runs the shuffles
 #pragma unroll 1
-            for (int u = tid >> 2; u < kUnits; u += kThreads / 4) {
+            for (int u = tid >> 2; u < kUnits; u += NT / 4) {
                 const int row = u / kBlk, blk = u % kBlk;
-                const uint4* src = reinterpret_cast<const uint4*>(s_c + row * BN + blk * 64 + l4 * 16);
+                const uint4* src = reinterpret_cast<const uint4*>(srow(row) + blk * 64 + l4 * 16);
                 float gu[16];
                 unpack8(src[0], gu);
                 unpack8(src[1], gu + 8);
                 float y[8];
 #pragma unroll
                 for (int k = 0; k < 8; ++k) y[k] = bf16_to_f32(f32_to_bf16(silu_mul(gu[2 * k], gu[2 * k + 1])));
-                uint32_t code[8];
+                uint2 code;
                 const int X = mx_encode8<true>(y, code);
                 const int64_t grow = m0 + row;
                 const int64_t gblk = n0 / 64 + blk;
-                if (grow < m_end && n0 + blk * 64 < args.N) {
-                    // unit index within the output row, in 8-output lane units
+                if (grow < m_end && n0 + blk * 64 < args.N)
                     mx_store8<true>(code, X, args.yq + grow * (I / 2), args.ys + grow * (I / 32), gblk * 4 + l4, l4);
-                }
             }
         }
         __syncthreads();  // LDS is reused by the next tile's prologue
@@ -395,33 +573,28 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(const GemmArgs a
 }
 
 // ---------------------------------------------------------------------------
-struct LaunchCache {
-    int device = -1;
-    int cus = 0;
-};
-
 int device_cus() {
-    static thread_local LaunchCache cache;
+    static thread_local int cached_device = -1, cached_cus = 0;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
-    if (cache.device != dev) {
+    if (cached_device != dev) {
         int cus = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-        cache.device = dev;
-        cache.cus = cus;
+        cached_device = dev;
+        cached_cus = cus;
     }
-    return cache.cus;
+    return cached_cus;
 }
 
-template <int BM, int BN, int FMT, bool SWIGLU>
-hipError_t launch_tile(const GemmProblem& p, hipStream_t stream) {
-    auto kernel = grouped_gemm_kernel<BM, BN, FMT, SWIGLU>;
+template <class TL, int FMT, bool SWIGLU>
+hipError_t launch_tile(const GemmProblem& p, hipStream_t stream, bool n_outer) {
+    auto kernel = grouped_gemm_kernel<TL, FMT, SWIGLU>;
     static thread_local int occ_device = -1, occ = 0;
     int dev = 0;
     hipError_t err = hipGetDevice(&dev);
     if (err != hipSuccess) return err;
     if (occ_device != dev) {
-        err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, kThreads, 0);
+        err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, TL::kThreads, 0);
         if (err != hipSuccess) return err;
         occ_device = dev;
     }
@@ -442,16 +615,42 @@ hipError_t launch_tile(const GemmProblem& p, hipStream_t stream) {
     a.N = p.N;
     a.K = p.K;
     a.row_bytes = FMT == 2 ? p.K / 2 : p.K;
-    a.ntiles_n = (int)((p.N + BN - 1) / BN);
+    a.ntiles_n = (int)((p.N + TL::BN - 1) / TL::BN);
+    a.n_outer = n_outer ? 1 : 0;
     // Upper bound on M tiles: each non-empty group adds at most one partial tile.
     const int64_t groups_nonempty = p.G < p.T ? p.G : p.T;
-    const int64_t mtiles_bound = p.T / BM + groups_nonempty;
+    const int64_t mtiles_bound = p.T / TL::BM + groups_nonempty;
     const int64_t tiles_bound = mtiles_bound * a.ntiles_n;
     int64_t grid = (int64_t)(cus > 0 ? cus : 256) * (occ > 0 ? occ : 1);
     if (grid > tiles_bound) grid = tiles_bound;
     if (grid <= 0) return hipSuccess;
-    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(TL::kThreads), 0, stream, a);
     return hipGetLastError();
+}
+
+// Tile shapes, chosen by measurement on MI355X (ragged workloads of the
+// benchmark): FP8 rowwise with many rows per group -> 256 x 256 with eight
+// waves (fewest operand bytes per FLOP; two ring slots fit 160 KiB of LDS);
+// MX formats -> 128 x 256 with four waves and three slots (the MX scale words
+// leave no room for the 256 x 256 accumulators); few rows per group
+// (decode-like, weight streaming) -> 32 x 128 tiles, many of them, walked
+// N-outer so the M tiles of an expert share each weight panel in L2.
+using TileLargeFp8 = Tile<256, 256, 2, 4, 2>;
+using TileLargeMx = Tile<128, 256, 2, 2, 3>;
+using TileSmall = Tile<32, 128, 1, 4, 3>;
+
+template <int FMT, bool SWIGLU>
+hipError_t launch_fmt(const GemmProblem& p, hipStream_t stream) {
+    // Average rows per non-empty group decides the regime; the optional host
+    // hint (largest group) can only move a problem to the larger tile.
+    const int64_t groups = p.G < p.T ? p.G : p.T;
+    const int64_t avg_rows = groups > 0 ? p.T / groups : p.T;
+    const int64_t rows = p.max_rows_hint > avg_rows ? (avg_rows + p.max_rows_hint) / 2 : avg_rows;
+    if (rows >= 128) {
+        if constexpr (FMT == 0) return launch_tile<TileLargeFp8, FMT, SWIGLU>(p, stream, false);
+        else return launch_tile<TileLargeMx, FMT, SWIGLU>(p, stream, true);
+    }
+    return launch_tile<TileSmall, FMT, SWIGLU>(p, stream, true);
 }
 
 }  // namespace
@@ -460,11 +659,11 @@ hipError_t launch_grouped_gemm(const GemmProblem& p, hipStream_t stream) {
     const bool swiglu = p.yq != nullptr;
     switch (p.fmt) {
         case 0:
-            return launch_tile<128, 128, 0, false>(p, stream);
+            return launch_fmt<0, false>(p, stream);
         case 1:
-            return swiglu ? launch_tile<128, 128, 1, true>(p, stream) : launch_tile<128, 128, 1, false>(p, stream);
+            return swiglu ? launch_fmt<1, true>(p, stream) : launch_fmt<1, false>(p, stream);
         case 2:
-            return swiglu ? launch_tile<128, 128, 2, true>(p, stream) : launch_tile<128, 128, 2, false>(p, stream);
+            return swiglu ? launch_fmt<2, true>(p, stream) : launch_fmt<2, false>(p, stream);
         default:
             return hipErrorInvalidValue;
     }

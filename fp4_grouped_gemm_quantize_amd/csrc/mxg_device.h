@@ -132,39 +132,59 @@ __device__ __forceinline__ void unpack8(const uint4& v, float* f) {
 }
 
 // ---------------------------------------------------------------------------
+// Hardware packing converts.  Checked exhaustively on gfx950 against the
+// bit-level encoders above: v_cvt_pk_fp8_f32 equals enc_e4m3 for every fp32
+// input of magnitude <= 448 + 1/2 ulp (beyond that it does not saturate, so
+// callers clamp first), and v_cvt_scalef32_pk_fp4_f32 with scale 1 equals
+// enc_e2m1 for every fp32 input, saturation included.  The first element of
+// each pair lands in the low byte / low nibble.
+__device__ __forceinline__ uint2 pack8_e4m3(const float* f) {
+    uint32_t lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0u, false);
+    lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], lo, true);
+    uint32_t hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[4], f[5], 0u, false);
+    hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[6], f[7], hi, true);
+    return make_uint2(lo, hi);
+}
+
+__device__ __forceinline__ uint32_t pack8_e2m1(const float* f) {
+    uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, f[0], f[1], 1.0f, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, f[2], f[3], 1.0f, 1);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, f[4], f[5], 1.0f, 2);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, f[6], f[7], 1.0f, 3);
+    return w;
+}
+
+// ---------------------------------------------------------------------------
 // MX: 4 lanes x 8 elements form one 32-element block.  Given the 8 values of
 // this lane, returns the block's shared exponent X (after the 4-lane
-// reduction) and writes the 8 element codes.
+// reduction) and the lane's packed codes of x * 2^-X (e4m3: 8 bytes; e2m1:
+// 8 nibbles in word .x).  Every lane of the 4-lane group must call it.
 template <bool FP4>
-__device__ __forceinline__ int mx_encode8(const float* f, uint32_t* code) {
+__device__ __forceinline__ int mx_encode8(const float* f, uint2& packed) {
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
     amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
     amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
     const int X = mx_shared_exp(amax, FP4 ? 2 : 8);
+    float e[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const float e = ldexpf(f[i], -X);  // exact power-of-two shift
-        code[i] = FP4 ? enc_e2m1(e) : enc_e4m3(e);
+        e[i] = ldexpf(f[i], -X);  // exact power-of-two shift
+        if (!FP4) e[i] = fminf(fmaxf(e[i], -448.0f), 448.0f);  // saturate (the convert does not)
     }
+    if (FP4) packed = make_uint2(pack8_e2m1(e), 0u);
+    else packed = pack8_e4m3(e);
     return X;
 }
 
+// Store one lane's 8 codes (unit `idx` of 8 elements in the row) and, from the
+// first lane of the block, the block's E8M0 scale.
 template <bool FP4>
-__device__ __forceinline__ void mx_store8(const uint32_t* code, int X, uint8_t* qrow, uint8_t* srow, int64_t idx,
+__device__ __forceinline__ void mx_store8(const uint2& packed, int X, uint8_t* qrow, uint8_t* srow, int64_t idx,
                                           int lane) {
-    if (FP4) {
-        uint32_t packed = 0;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) packed |= code[i] << (4 * i);
-        *reinterpret_cast<uint32_t*>(qrow + idx * 4) = packed;
-    } else {
-        uint2 packed;
-        packed.x = code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
-        packed.y = code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24);
-        *reinterpret_cast<uint2*>(qrow + idx * 8) = packed;
-    }
+    if (FP4) *reinterpret_cast<uint32_t*>(qrow + idx * 4) = packed.x;
+    else *reinterpret_cast<uint2*>(qrow + idx * 8) = packed;
     if ((lane & 3) == 0) srow[idx >> 2] = (uint8_t)(X + 127);
 }
 

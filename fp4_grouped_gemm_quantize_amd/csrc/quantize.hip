@@ -1,12 +1,14 @@
 // quantize.hip -- grouped dynamic quantization of BF16 rows (FP8 rowwise, MXFP8,
 // MXFP4) and the standalone SwiGLU + MXFP4 requant, for gfx950.
 //
-// Both passes are HBM-bound streams.  One wave owns one row: each lane loads
-// 16-byte vectors (8 bf16) so a wave reads 1 KiB per instruction, fully
-// coalesced; all of a row's loads are issued before any is consumed.  MX block
-// maxima are reduced across the 4 lanes that share a 32-element block; the
-// rowwise maximum across the whole wave.  Codes are packed in registers and
-// written as 8-byte (e4m3) or 4-byte (e2m1) stores per lane.
+// Both passes are HBM-bound streams.  One wave owns one row at a time: each
+// lane loads 16-byte vectors (8 bf16), so a wave reads 1 KiB per instruction,
+// fully coalesced.  Waves are persistent (the grid is sized to the resident
+// capacity) and load the next row they own while they encode the current one,
+// so row loads stay in flight behind the arithmetic.  MX block maxima are
+// reduced across the 4 lanes that share a 32-element block; the rowwise
+// maximum across the whole wave.  Codes are packed by the hardware converts
+// and written as 8-byte (e4m3) or 4-byte (e2m1) stores per lane.
 //
 // (grouped_quantize_dynamic_scaled_fp4_async_kernel, description;
 //  NvMxf4f8Strategy, grouped_quantize() / fused_silu_quantize().)
@@ -18,143 +20,155 @@ namespace mxg {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kRowsPerBlock = kThreads / kWave;  // one row per wave
-constexpr int kVecElems = 8;                     // bf16 per 16-byte vector
-constexpr int kChunk = kWave * kVecElems;        // 512 elements per wave-wide load
+constexpr int kWavesPerBlock = kThreads / kWave;  // one row per wave at a time
+constexpr int kVecElems = 8;                      // bf16 per 16-byte vector
+constexpr int kChunk = kWave * kVecElems;         // 512 elements per wave-wide load
 
 __device__ __forceinline__ void load_offsets(uint32_t* s_off, const uint32_t* off, int G) {
     for (int i = threadIdx.x; i <= G; i += blockDim.x) s_off[i] = off[i];
     __syncthreads();
 }
 
+// The rowwise quotient x / scale (scale > 0) as IEEE binary32 division rounds
+// it, computed as one fp64 product with the fp64 reciprocal of the scale
+// followed by the binary64 -> binary32 rounding.  Equality with the binary32
+// division was checked exhaustively on gfx950 for every bf16 amax (scale =
+// amax / 448) and every bf16 x with |x| <= amax.
+__device__ __forceinline__ float div_by_scale(float x, double inv_scale) { return (float)((double)x * inv_scale); }
+
 // ---------------------------------------------------------------------------
-// FP8 rowwise: amax over the row, scale = amax / 448, code = e4m3(x / scale).
-// NC = 16-byte vectors per lane held in registers (K <= NC * 512).
-template <int NC>
-__global__ __launch_bounds__(kThreads) void quantize_rowwise_kernel(const uint16_t* __restrict__ x,
-                                                                    uint8_t* __restrict__ q,
-                                                                    float* __restrict__ scales,
-                                                                    const uint32_t* __restrict__ off, int G,
-                                                                    int64_t T, int64_t K) {
+// FP8 rowwise and MX, rows of K <= NC * 512 held in registers.
+// FMT: 0 = FP8 rowwise (scale = amax / 448, code = e4m3(x / scale)),
+//      1 = MXFP8, 2 = MXFP4.
+template <int FMT, int NC>
+__global__ __launch_bounds__(kThreads) void quantize_rows_kernel(const uint16_t* __restrict__ x,
+                                                                 uint8_t* __restrict__ q, void* __restrict__ scales,
+                                                                 const uint32_t* __restrict__ off, int G,
+                                                                 int64_t T, int64_t K) {
     __shared__ uint32_t s_off[kMaxGroups + 1];
     load_offsets(s_off, off, G);
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t t = (int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / kWave;
-    if (t >= T || !wave_row_covered(s_off, G, T, t)) return;
-
+    const int64_t nw = (int64_t)gridDim.x * kWavesPerBlock;
     const int nvec = (int)(K / kVecElems);
-    const uint4* xr = reinterpret_cast<const uint4*>(x + t * K);
-    uint4 v[NC];
+
+    auto load_row = [&](int64_t t, uint4 (&v)[NC]) {
+        const uint4* xr = reinterpret_cast<const uint4*>(x + t * K);
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-        int idx = c * kWave + lane;
-        v[c] = idx < nvec ? xr[idx] : make_uint4(0, 0, 0, 0);
-    }
-    // bf16 magnitudes compare like their bit patterns with the sign cleared.
-    uint32_t amax_bits = 0;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-        const uint32_t w[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            amax_bits = max(amax_bits, w[i] & 0x7fffu);
-            amax_bits = max(amax_bits, (w[i] >> 16) & 0x7fffu);
+        for (int c = 0; c < NC; ++c) {
+            const int idx = c * kWave + lane;
+            v[c] = idx < nvec ? xr[idx] : make_uint4(0, 0, 0, 0);
         }
-    }
-    const float amax = wave_max(bf16_to_f32(amax_bits));
-    const float scale = amax / 448.0f;  // IEEE binary32 division
-    uint8_t* qr = q + t * K;
+    };
+
+    uint4 v[NC], vn[NC];
+    int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+    if (t < T) load_row(t, v);
+    for (; t < T; t += nw) {
+        const int64_t tn = t + nw;
+        if (tn < T) load_row(tn, vn);
+        if (wave_row_covered(s_off, G, T, t)) {
+            if constexpr (FMT == 0) {
+                // bf16 magnitudes order like their bit patterns with the sign cleared
+                uint32_t amax_bits = 0;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-        int idx = c * kWave + lane;
-        if (idx >= nvec) continue;
-        float f[8];
-        unpack8(v[c], f);
-        uint32_t code[8];
+                for (int c = 0; c < NC; ++c) {
+                    const uint32_t w[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            code[i] = amax == 0.0f ? (__float_as_uint(f[i]) >> 24) & 0x80u : enc_e4m3(f[i] / scale);
-        uint2 packed;
-        packed.x = code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
-        packed.y = code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24);
-        *reinterpret_cast<uint2*>(qr + (int64_t)idx * 8) = packed;
+                    for (int i = 0; i < 4; ++i) {
+                        amax_bits = max(amax_bits, w[i] & 0x7fffu);
+                        amax_bits = max(amax_bits, (w[i] >> 16) & 0x7fffu);
+                    }
+                }
+                const float amax = wave_max(bf16_to_f32(amax_bits));
+                const float scale = amax / 448.0f;  // IEEE binary32 division
+                const double inv = amax == 0.0f ? 0.0 : 1.0 / (double)scale;
+                uint8_t* qr = q + t * K;
+#pragma unroll
+                for (int c = 0; c < NC; ++c) {
+                    const int idx = c * kWave + lane;
+                    if (idx >= nvec) continue;
+                    float f[8];
+                    unpack8(v[c], f);
+                    // a zero row keeps its signed zeros (the convert keeps the sign)
+                    if (amax != 0.0f) {
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) f[i] = div_by_scale(f[i], inv);
+                    }
+                    *reinterpret_cast<uint2*>(qr + (int64_t)idx * 8) = pack8_e4m3(f);
+                }
+                if (lane == 0) static_cast<float*>(scales)[t] = amax == 0.0f ? 0.0f : scale;
+            } else {
+                constexpr bool FP4 = FMT == 2;
+                uint8_t* qrow = q + t * (FP4 ? K / 2 : K);
+                uint8_t* srow = static_cast<uint8_t*>(scales) + t * (K / 32);
+#pragma unroll
+                for (int c = 0; c < NC; ++c) {
+                    const int idx = c * kWave + lane;
+                    // a block's 4 lanes are all in or all out (K is a multiple
+                    // of 32), so the shuffles only mix lanes of one block
+                    float f[8];
+                    unpack8(v[c], f);
+                    uint2 packed;
+                    const int X = mx_encode8<FP4>(f, packed);
+                    if (idx < nvec) mx_store8<FP4>(packed, X, qrow, srow, idx, lane);
+                }
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < NC; ++c) v[c] = vn[c];
     }
-    if (lane == 0) scales[t] = amax == 0.0f ? 0.0f : scale;
 }
 
-// Rows longer than the register budget: two passes over the row (the second
-// one re-reads from cache).
-__global__ __launch_bounds__(kThreads) void quantize_rowwise_long_kernel(const uint16_t* __restrict__ x,
-                                                                         uint8_t* __restrict__ q,
-                                                                         float* __restrict__ scales,
-                                                                         const uint32_t* __restrict__ off,
-                                                                         int G, int64_t T, int64_t K) {
+// Rows longer than the register budget: rowwise reads the row twice (the
+// second pass from cache); MX streams 512-element chunks.
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void quantize_long_kernel(const uint16_t* __restrict__ x,
+                                                                 uint8_t* __restrict__ q, void* __restrict__ scales,
+                                                                 const uint32_t* __restrict__ off, int G,
+                                                                 int64_t T, int64_t K) {
     __shared__ uint32_t s_off[kMaxGroups + 1];
     load_offsets(s_off, off, G);
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t t = (int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / kWave;
-    if (t >= T || !wave_row_covered(s_off, G, T, t)) return;
+    const int64_t nw = (int64_t)gridDim.x * kWavesPerBlock;
     const int64_t nvec = K / kVecElems;
-    const uint4* xr = reinterpret_cast<const uint4*>(x + t * K);
-    uint32_t amax_bits = 0;
-    for (int64_t idx = lane; idx < nvec; idx += kWave) {
-        uint4 v = xr[idx];
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-        for (int i = 0; i < 4; ++i) {
-            amax_bits = max(amax_bits, w[i] & 0x7fffu);
-            amax_bits = max(amax_bits, (w[i] >> 16) & 0x7fffu);
-        }
-    }
-    const float amax = wave_max(bf16_to_f32(amax_bits));
-    const float scale = amax / 448.0f;
-    uint8_t* qr = q + t * K;
-    for (int64_t idx = lane; idx < nvec; idx += kWave) {
-        float f[8];
-        unpack8(xr[idx], f);
-        uint32_t code[8];
-        for (int i = 0; i < 8; ++i)
-            code[i] = amax == 0.0f ? (__float_as_uint(f[i]) >> 24) & 0x80u : enc_e4m3(f[i] / scale);
-        uint2 packed;
-        packed.x = code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
-        packed.y = code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24);
-        *reinterpret_cast<uint2*>(qr + idx * 8) = packed;
-    }
-    if (lane == 0) scales[t] = amax == 0.0f ? 0.0f : scale;
-}
-
-// U = vectors per lane loaded before any is encoded.
-template <bool FP4, int U>
-__global__ __launch_bounds__(kThreads) void quantize_mx_kernel(const uint16_t* __restrict__ x,
-                                                               uint8_t* __restrict__ q,
-                                                               uint8_t* __restrict__ scales,
-                                                               const uint32_t* __restrict__ off, int G, int64_t T,
-                                                               int64_t K) {
-    __shared__ uint32_t s_off[kMaxGroups + 1];
-    load_offsets(s_off, off, G);
-    const int lane = threadIdx.x & (kWave - 1);
-    const int64_t t = (int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / kWave;
-    if (t >= T || !wave_row_covered(s_off, G, T, t)) return;
-    const int64_t nvec = K / kVecElems;
-    const uint4* xr = reinterpret_cast<const uint4*>(x + t * K);
-    uint8_t* qrow = q + t * (FP4 ? K / 2 : K);
-    uint8_t* srow = scales + t * (K / 32);
-    for (int64_t base = 0; base < nvec; base += (int64_t)U * kWave) {
-        uint4 v[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            int64_t idx = base + u * kWave + lane;
-            v[u] = idx < nvec ? xr[idx] : make_uint4(0, 0, 0, 0);
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            int64_t idx = base + u * kWave + lane;
-            // a block's 4 lanes are all in or all out (K is a multiple of 32),
-            // so the shuffles inside mx_encode8 only mix lanes of one block
-            float f[8];
-            unpack8(v[u], f);
-            uint32_t code[8];
-            int X = mx_encode8<FP4>(f, code);
-            if (idx < nvec) mx_store8<FP4>(code, X, qrow, srow, idx, lane);
+    for (int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave; t < T; t += nw) {
+        if (!wave_row_covered(s_off, G, T, t)) continue;
+        const uint4* xr = reinterpret_cast<const uint4*>(x + t * K);
+        if constexpr (FMT == 0) {
+            uint32_t amax_bits = 0;
+            for (int64_t idx = lane; idx < nvec; idx += kWave) {
+                const uint4 v = xr[idx];
+                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+                for (int i = 0; i < 4; ++i) {
+                    amax_bits = max(amax_bits, w[i] & 0x7fffu);
+                    amax_bits = max(amax_bits, (w[i] >> 16) & 0x7fffu);
+                }
+            }
+            const float amax = wave_max(bf16_to_f32(amax_bits));
+            const float scale = amax / 448.0f;
+            const double inv = amax == 0.0f ? 0.0 : 1.0 / (double)scale;
+            uint8_t* qr = q + t * K;
+            for (int64_t idx = lane; idx < nvec; idx += kWave) {
+                float f[8];
+                unpack8(xr[idx], f);
+                if (amax != 0.0f)
+                    for (int i = 0; i < 8; ++i) f[i] = div_by_scale(f[i], inv);
+                *reinterpret_cast<uint2*>(qr + idx * 8) = pack8_e4m3(f);
+            }
+            if (lane == 0) static_cast<float*>(scales)[t] = amax == 0.0f ? 0.0f : scale;
+        } else {
+            constexpr bool FP4 = FMT == 2;
+            uint8_t* qrow = q + t * (FP4 ? K / 2 : K);
+            uint8_t* srow = static_cast<uint8_t*>(scales) + t * (K / 32);
+            // whole 512-element chunks per iteration keep every lane in the loop
+            for (int64_t base = 0; base < nvec; base += kWave) {
+                const int64_t idx = base + lane;
+                float f[8];
+                unpack8(idx < nvec ? xr[idx] : make_uint4(0, 0, 0, 0), f);
+                uint2 packed;
+                const int X = mx_encode8<FP4>(f, packed);
+                if (idx < nvec) mx_store8<FP4>(packed, X, qrow, srow, idx, lane);
+            }
         }
     }
 }
@@ -170,29 +184,65 @@ __global__ __launch_bounds__(kThreads) void silu_quantize_kernel(const uint16_t*
     __shared__ uint32_t s_off[kMaxGroups + 1];
     load_offsets(s_off, off, G);
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t t = (int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / kWave;
-    if (t >= T || !wave_row_covered(s_off, G, T, t)) return;
+    const int64_t nw = (int64_t)gridDim.x * kWavesPerBlock;
     const int64_t nunits = I / 8;  // 8 outputs per lane-unit
-    const uint4* hr = reinterpret_cast<const uint4*>(h + t * 2 * I);
-    uint8_t* qrow = yq + t * (I / 2);
-    uint8_t* srow = ys + t * (I / 32);
-    for (int64_t base = 0; base < nunits; base += kWave) {
-        const int64_t idx = base + lane;
-        uint4 v0 = make_uint4(0, 0, 0, 0), v1 = make_uint4(0, 0, 0, 0);
-        if (idx < nunits) {
-            v0 = hr[2 * idx];
-            v1 = hr[2 * idx + 1];
-        }
-        float gu[16];
-        unpack8(v0, gu);
-        unpack8(v1, gu + 8);
-        float y[8];
+    for (int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave; t < T; t += nw) {
+        if (!wave_row_covered(s_off, G, T, t)) continue;
+        const uint4* hr = reinterpret_cast<const uint4*>(h + t * 2 * I);
+        uint8_t* qrow = yq + t * (I / 2);
+        uint8_t* srow = ys + t * (I / 32);
+        for (int64_t base = 0; base < nunits; base += kWave) {
+            const int64_t idx = base + lane;
+            uint4 v0 = make_uint4(0, 0, 0, 0), v1 = make_uint4(0, 0, 0, 0);
+            if (idx < nunits) {
+                v0 = hr[2 * idx];
+                v1 = hr[2 * idx + 1];
+            }
+            float gu[16];
+            unpack8(v0, gu);
+            unpack8(v1, gu + 8);
+            float y[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) y[i] = bf16_to_f32(f32_to_bf16(silu_mul(gu[2 * i], gu[2 * i + 1])));
-        uint32_t code[8];
-        int X = mx_encode8<true>(y, code);
-        if (idx < nunits) mx_store8<true>(code, X, qrow, srow, idx, lane);
+            for (int i = 0; i < 8; ++i) y[i] = bf16_to_f32(f32_to_bf16(silu_mul(gu[2 * i], gu[2 * i + 1])));
+            uint2 packed;
+            const int X = mx_encode8<true>(y, packed);
+            if (idx < nunits) mx_store8<true>(packed, X, qrow, srow, idx, lane);
+        }
     }
+}
+
+// Persistent grid: as many blocks as can be resident, at most one wave per row.
+template <class Kern>
+int64_t persistent_grid(Kern kernel, int64_t T) {
+    int dev = 0, cus = 0, occ = 0;
+    int64_t cap = 2048;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, kThreads, 0) == hipSuccess && cus > 0)
+        cap = (int64_t)cus * (occ > 0 ? occ : 1);
+    const int64_t need = (T + kWavesPerBlock - 1) / kWavesPerBlock;
+    return need < cap ? need : cap;
+}
+
+template <class Kern>
+hipError_t launch_persistent(Kern kernel, const uint16_t* x, uint8_t* q, void* s, const uint32_t* off, int G,
+                             int64_t T, int64_t K, hipStream_t stream) {
+    hipLaunchKernelGGL(kernel, dim3((unsigned)persistent_grid(kernel, T)), dim3(kThreads), 0, stream, x, q, s, off,
+                       G, T, K);
+    return hipGetLastError();
+}
+
+template <int FMT>
+hipError_t launch_fmt(const uint16_t* x, uint8_t* q, void* s, const uint32_t* off, int G, int64_t T, int64_t K,
+                      hipStream_t stream) {
+    const int64_t nc = (K + kChunk - 1) / kChunk;
+    if (nc <= 1) return launch_persistent(quantize_rows_kernel<FMT, 1>, x, q, s, off, G, T, K, stream);
+    if (nc <= 2) return launch_persistent(quantize_rows_kernel<FMT, 2>, x, q, s, off, G, T, K, stream);
+    if (nc <= 4) return launch_persistent(quantize_rows_kernel<FMT, 4>, x, q, s, off, G, T, K, stream);
+    if (nc <= 8) return launch_persistent(quantize_rows_kernel<FMT, 8>, x, q, s, off, G, T, K, stream);
+    if (nc <= 14) return launch_persistent(quantize_rows_kernel<FMT, 14>, x, q, s, off, G, T, K, stream);
+    if (nc <= 16) return launch_persistent(quantize_rows_kernel<FMT, 16>, x, q, s, off, G, T, K, stream);
+    return launch_persistent(quantize_long_kernel<FMT>, x, q, s, off, G, T, K, stream);
 }
 
 }  // namespace
@@ -200,43 +250,18 @@ __global__ __launch_bounds__(kThreads) void silu_quantize_kernel(const uint16_t*
 // ---------------------------------------------------------------------------
 hipError_t launch_quantize(int fmt, const void* x, void* q, void* scales, const uint32_t* off, int G, int64_t T,
                            int64_t K, hipStream_t stream) {
-    const dim3 block(kThreads);
-    const dim3 grid((unsigned)((T + kRowsPerBlock - 1) / kRowsPerBlock));
     const uint16_t* xb = static_cast<const uint16_t*>(x);
     uint8_t* qb = static_cast<uint8_t*>(q);
-    if (fmt == 0) {
-        float* sf = static_cast<float*>(scales);
-        const int64_t nc = (K + kChunk - 1) / kChunk;
-        if (nc <= 1)
-            hipLaunchKernelGGL(quantize_rowwise_kernel<1>, grid, block, 0, stream, xb, qb, sf, off, G, T, K);
-        else if (nc <= 2)
-            hipLaunchKernelGGL(quantize_rowwise_kernel<2>, grid, block, 0, stream, xb, qb, sf, off, G, T, K);
-        else if (nc <= 4)
-            hipLaunchKernelGGL(quantize_rowwise_kernel<4>, grid, block, 0, stream, xb, qb, sf, off, G, T, K);
-        else if (nc <= 8)
-            hipLaunchKernelGGL(quantize_rowwise_kernel<8>, grid, block, 0, stream, xb, qb, sf, off, G, T, K);
-        else if (nc <= 14)
-            hipLaunchKernelGGL(quantize_rowwise_kernel<14>, grid, block, 0, stream, xb, qb, sf, off, G, T, K);
-        else if (nc <= 16)
-            hipLaunchKernelGGL(quantize_rowwise_kernel<16>, grid, block, 0, stream, xb, qb, sf, off, G, T, K);
-        else
-            hipLaunchKernelGGL(quantize_rowwise_long_kernel, grid, block, 0, stream, xb, qb, sf, off, G, T, K);
-    } else if (fmt == 1) {
-        hipLaunchKernelGGL((quantize_mx_kernel<false, 7>), grid, block, 0, stream, xb, qb,
-                           static_cast<uint8_t*>(scales), off, G, T, K);
-    } else {
-        hipLaunchKernelGGL((quantize_mx_kernel<true, 7>), grid, block, 0, stream, xb, qb,
-                           static_cast<uint8_t*>(scales), off, G, T, K);
-    }
-    return hipGetLastError();
+    if (fmt == 0) return launch_fmt<0>(xb, qb, scales, off, G, T, K, stream);
+    if (fmt == 1) return launch_fmt<1>(xb, qb, scales, off, G, T, K, stream);
+    return launch_fmt<2>(xb, qb, scales, off, G, T, K, stream);
 }
 
 hipError_t launch_silu_quantize(const void* h, void* yq, void* ys, const uint32_t* off, int G, int64_t T,
                                 int64_t I, hipStream_t stream) {
-    const dim3 block(kThreads);
-    const dim3 grid((unsigned)((T + kRowsPerBlock - 1) / kRowsPerBlock));
-    hipLaunchKernelGGL(silu_quantize_kernel, grid, block, 0, stream, static_cast<const uint16_t*>(h),
-                       static_cast<uint8_t*>(yq), static_cast<uint8_t*>(ys), off, G, T, I);
+    hipLaunchKernelGGL(silu_quantize_kernel, dim3((unsigned)persistent_grid(silu_quantize_kernel, T)), dim3(kThreads),
+                       0, stream, static_cast<const uint16_t*>(h), static_cast<uint8_t*>(yq), static_cast<uint8_t*>(ys),
+                       off, G, T, I);
     return hipGetLastError();
 }
 
