@@ -45,8 +45,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU baseline")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
-                   help="before the workload, run a plain device copy of this many MiB three times "
-                        "(a known-size kernel for scaling rocprofv3 byte counters)")
+                   help="before the workload, run torch.bitwise_not over this many MiB of int32 three times: a "
+                        "streaming kernel that reads and writes a known number of bytes, for scaling rocprofv3's "
+                        "FETCH_SIZE / WRITE_SIZE counters")
     return p.parse_args()
 
 
@@ -132,9 +133,9 @@ def cpu_baseline(w, r, x_gpu, target_s):
         dt = time.perf_counter() - t0
         return len(rows), dt
 
-    n, dt = run(1)
+    n, dt = run(8)
     per_row = dt / max(n, 1)
-    rows_per_group = max(1, int(target_s / per_row / E_s))
+    rows_per_group = max(8, int(target_s / per_row / E_s))
     n, dt = run(rows_per_group)
     flops = 2.0 * n * w.N * w.K
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
@@ -155,11 +156,11 @@ def main():
 
     torch.cuda.set_device(0)
     if args.copy_calibration_mib:
-        n = args.copy_calibration_mib << 20
-        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        n = (args.copy_calibration_mib << 20) // 4
+        src = torch.ones(n, dtype=torch.int32, device="cuda")
         dst = torch.empty_like(src)
         for _ in range(3):
-            dst.copy_(src)
+            torch.bitwise_not(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
     w = W.WORKLOADS[args.workload]

@@ -46,15 +46,23 @@ SMALL = {
 }
 
 
+# The row-count hint selects the tile shape: 0 lets small reduced problems use
+# the decode-regime tile, a large hint forces the prefill-regime tile (FP8:
+# 256 x 256 with eight waves; MX: 128 x 256), so both code paths see every
+# case, including partial M / N tiles and K tails.
+HINTS = [0, 1 << 20]
+
+
+@pytest.mark.parametrize("hint", HINTS)
 @pytest.mark.parametrize("name", list(SMALL))
-def test_gemm_matches_oracle_all_rows(name):
+def test_gemm_matches_oracle_all_rows(name, hint):
     case = GemmCase(SMALL[name])
-    c = run_gemm(case)
-    worst, exact = check_all_rows(case, c, name)
+    c = run_gemm(case, hint=hint)
+    worst, exact = check_all_rows(case, c, f"{name} hint={hint}")
     assert exact > 0.9, "most outputs should round to the same bf16 as the exact value"
 
 
-@pytest.mark.parametrize("name", ["prefill_fp8", "mxfp4"])
+@pytest.mark.parametrize("name", list(SMALL))
 def test_gemm_hint_does_not_change_results(name):
     case = GemmCase(SMALL[name])
     c0 = run_gemm(case, hint=0)

@@ -26,12 +26,18 @@ def random_operands(rng, fmt, T, E, N, K):
 
 
 def run_case(fmt, a, sa, b, sb, off, ids, N, K):
+    """Both tile regimes (hint 0 and a hint that forces the large tile) must
+    agree bit for bit and match the oracle; uncovered rows keep the sentinel."""
     T = a.shape[0]
-    E = b.shape[0]
-    c = torch.full((T, N), SENT, dtype=torch.int16, device="cuda").view(torch.bfloat16)
-    mxg.mx_grouped_matmul(fmt, to_gpu(a), to_gpu(sa), to_gpu(b), to_gpu(sb), c, offsets_gpu(off), ids_gpu(ids))
-    torch.cuda.synchronize()
-    c = c.view(torch.int16).cpu().numpy().view(np.uint16)
+    outs = []
+    for hint in (0, 1 << 20):
+        c = torch.full((T, N), SENT, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+        mxg.mx_grouped_matmul(fmt, to_gpu(a), to_gpu(sa), to_gpu(b), to_gpu(sb), c, offsets_gpu(off), ids_gpu(ids),
+                              hint)
+        torch.cuda.synchronize()
+        outs.append(c.view(torch.int16).cpu().numpy().view(np.uint16))
+    assert np.array_equal(outs[0], outs[1]), "tile regimes disagree"
+    c = outs[0]
     ref = oracle.gemm_rows(fmt, a, sa, b, sb, off, ids, N, K, np.arange(T))
     cov = ref["group"] >= 0
     assert np.all(c[~cov] == SENT), "a row no valid group covers was written"

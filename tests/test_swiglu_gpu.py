@@ -69,15 +69,15 @@ FUSED = {
 }
 
 
-def run_fused_and_chained(case: GemmCase):
+def run_fused_and_chained(case: GemmCase, hint: int = 0):
     inp = case.gpu_inputs()
     T, I = case.T, case.w.N // 2
     yq = torch.full((T, I // 2), 0xA5, dtype=torch.uint8, device="cuda")
     ys = torch.full((T, I // 32), 0x5A, dtype=torch.uint8, device="cuda")
     mxg.mx_grouped_matmul_swiglu(case.fmt, inp["a_q"], inp["a_scales"], inp["b_q"], inp["b_scales"], yq, ys,
-                                 inp["row_offsets"], inp["expert_ids"])
+                                 inp["row_offsets"], inp["expert_ids"], hint)
     c = torch.zeros((T, 2 * I), dtype=torch.bfloat16, device="cuda")
-    mxg.mx_grouped_matmul(case.fmt, c=c, **inp)
+    mxg.mx_grouped_matmul(case.fmt, c=c, max_rows_per_group_hint=hint, **inp)
     yq2 = torch.full((T, I // 2), 0xA5, dtype=torch.uint8, device="cuda")
     ys2 = torch.full((T, I // 32), 0x5A, dtype=torch.uint8, device="cuda")
     mxg.mx_silu_quantize(c, yq2, ys2, inp["row_offsets"])
@@ -96,10 +96,11 @@ def check_against_oracle(case: GemmCase, yq, ys, rows):
     assert code_eq > 0.98 and scale_eq > 0.98
 
 
+@pytest.mark.parametrize("hint", [0, 1 << 20])
 @pytest.mark.parametrize("name", list(FUSED))
-def test_fused_equals_chained_and_oracle(name):
+def test_fused_equals_chained_and_oracle(name, hint):
     case = GemmCase(FUSED[name])
-    (yq, ys), (yq2, ys2) = run_fused_and_chained(case)
+    (yq, ys), (yq2, ys2) = run_fused_and_chained(case, hint)
     assert np.array_equal(yq, yq2) and np.array_equal(ys, ys2), "fused and chained paths differ"
     check_against_oracle(case, yq, ys, np.arange(case.T))
 
