@@ -1,5 +1,6 @@
 // gemm.hip -- ragged grouped GEMM for gfx950 (FP8 rowwise, MXFP8, MXFP4), with
-// a BF16 epilogue or the fused SwiGLU + MXFP4 requant epilogue.
+// a BF16 epilogue or the fused SwiGLU + MXFP4 requant epilogue, and the
+// dispatcher that picks its tile shape.
 //
 // (grouped_matmul_rowwise_dynamic_scaled_fp8, description: out[t,n] =
 //  (sum_k a[t,k] b[expert_ids[g],n,k]) a_scale[t] b_scale[expert_ids[g],n],
@@ -21,70 +22,33 @@
 //  * Tiles: a workgroup of WGM x WGN waves owns a BM x BN output tile; each
 //    wave a (BM/WGM) x (BN/WGN) sub-tile of 32 x 32 accumulators.  K streams
 //    in stages of 128 bytes per row (128 e4m3 or 256 e2m1 elements) through a
-//    double-buffered LDS ring filled by direct global->LDS loads
+//    2- or 3-slot LDS ring filled by direct global->LDS loads
 //    (global_load_lds_dwordx4: each lane's 16 bytes land at LDS base + 16 *
-//    lane, no VGPR staging), issued one stage ahead of the matrix cores.  The
-//    16-byte chunks of a row are XOR-swizzled by row (chunk c of row r sits
-//    at slot c ^ (r & 7)) so the 16-byte fragment reads of 8 consecutive rows
-//    hit distinct banks; the swizzle is realised by choosing which global
-//    chunk each lane fetches.  A stage that runs past the end of K (only the
-//    last one, when K bytes are not a multiple of 128) goes through VGPRs so
-//    its tail can be zero-filled.
+//    lane, no VGPR staging), issued one or two stages ahead of the matrix
+//    cores.  The 16-byte chunks of a row are XOR-swizzled (chunk c of row r
+//    sits at slot c ^ ((r >> 1) & 7)) so the 16-byte fragment reads of 16
+//    consecutive rows hit distinct bank groups; the swizzle is realised by
+//    choosing which global chunk each lane fetches.  A stage that runs past
+//    the end of K (only the last one, when K bytes are not a multiple of 128)
+//    goes through VGPRs so its tail can be zero-filled.
 //  * MX scales: each lane loads the 4 (e4m3) or 8 (e2m1) scale bytes of its
 //    own row for the next stage straight into registers and shifts out the
 //    byte of its block per step; no LDS traffic.
-//  * Ragged groups without host sync: every workgroup derives the per-group
-//    M-tile counts from row_offsets into an LDS prefix sum; a tile index is
-//    mapped to (group, m-tile) by binary search.  Empty or invalid groups own
-//    no tiles; in a partial M (or N) tile each wave skips the matrix-core work
-//    of its 32-row (32-column) slices that hold no real rows.
+//  * Ragged groups without host sync: the tile map of gemm_common.h.  Rows
+//    past a group's end (columns past N) re-read the last real one and are
+//    never stored.
 //  * Persistent, XCD-aware schedule: the grid is sized to the resident
 //    capacity; workgroup b (dispatched to XCD b % 8) walks logical tiles so
 //    that the workgroups resident on one XCD hold consecutive tiles (same
 //    expert, neighbouring N tiles), which keeps shared A/B panels in that
 //    XCD's L2.
-#include "mxg_device.h"
-#include "mxg_internal.h"
+#include "gemm_common.h"
 
 namespace mxg {
 
+using namespace gemm;
+
 namespace {
-
-typedef int v8i __attribute__((ext_vector_type(8)));
-typedef float v16f __attribute__((ext_vector_type(16)));
-
-constexpr int kStageBytes = 128;  // K bytes per row per stage
-constexpr int kNumXcd = 8;
-
-struct GemmArgs {
-    const uint8_t* a;
-    const void* as;
-    const uint8_t* b;
-    const void* bs;
-    uint16_t* c;
-    uint8_t* yq;
-    uint8_t* ys;
-    const uint32_t* off;
-    const int32_t* ids;
-    int G;
-    int E;
-    int64_t T;
-    int64_t N;
-    int64_t K;
-    int64_t row_bytes;  // bytes per row of a and b
-    int ntiles_n;
-    int n_outer;        // tile order within a group: 0 = M tiles outer, 1 = N tiles outer
-};
-
-// FMT: 0 = FP8 rowwise, 1 = MXFP8, 2 = MXFP4.
-template <int FMT>
-struct Fmt {
-    static constexpr bool kMX = FMT != 0;
-    static constexpr bool kFP4 = FMT == 2;
-    static constexpr int kSteps = kFP4 ? 4 : 2;   // 64-deep MFMA steps per stage
-    static constexpr int kBlocks = kFP4 ? 8 : 4;  // 32-element scale blocks per stage
-    static constexpr int kTypeCode = kFP4 ? 4 : 0;  // cbsz / blgp: 0 = e4m3, 4 = e2m1
-};
 
 // BM x BN output tile, WGM x WGN waves, SLOTS stages of LDS ring (2: one stage
 // in flight while one is consumed; 3: two in flight).
@@ -102,80 +66,6 @@ struct Tile {
     static_assert(TM >= 1 && TN >= 1, "wave tile below one 32x32 accumulator");
     static_assert(BM % (8 * kWaves) == 0 && BN % (8 * kWaves) == 0, "loader: whole 8-row groups per wave");
 };
-
-// LDS byte offset of 16-byte chunk `chunk` of stage row `row`.  A row is 128
-// bytes (32 of the 64 four-byte banks), so even and odd rows fall in opposite
-// bank halves; XOR-ing the chunk with bits 1..3 of the row gives the 16 rows a
-// 16-lane slice of a fragment read touches 16 distinct 4-bank groups.
-__device__ __forceinline__ int swz_chunk(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
-__device__ __forceinline__ int swz(int row, int chunk) { return row * kStageBytes + (swz_chunk(row, chunk) << 4); }
-
-// Bijective remap so that the workgroups the dispatcher sends to one XCD
-// (b, b + 8, b + 16, ...) get consecutive logical indices.
-__device__ __forceinline__ int xcd_remap(int b, int n) {
-    const int per = n / kNumXcd, rem = n % kNumXcd;
-    const int xcd = b % kNumXcd, idx = b / kNumXcd;
-    return xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
-}
-
-// Exclusive block-wide scan over NT threads.
-template <int NT>
-__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s_wave, uint32_t* total) {
-    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-    uint32_t inc = v;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        uint32_t n = __shfl_up(inc, o, kWave);
-        if (lane >= o) inc += n;
-    }
-    if (lane == kWave - 1) s_wave[wave] = inc;
-    __syncthreads();
-    uint32_t before = 0, all = 0;
-#pragma unroll
-    for (int w = 0; w < NT / kWave; ++w) {
-        uint32_t s = s_wave[w];
-        before += w < wave ? s : 0;
-        all += s;
-    }
-    *total = all;
-    return before + inc - v;
-}
-
-// Scale bytes p[0 .. 4) as one word; bytes at or past `avail` read as 127
-// (2^0: they only ever multiply zero-filled K tails).
-__device__ __forceinline__ uint32_t scale_word(const uint8_t* p, int64_t avail) {
-    if (avail >= 4 && (reinterpret_cast<uintptr_t>(p) & 3) == 0) return *reinterpret_cast<const uint32_t*>(p);
-    uint32_t w = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) w |= (uint32_t)(i < avail ? p[i] : (uint8_t)127) << (8 * i);
-    return w;
-}
-
-// s_waitcnt vmcnt(N) (expcnt / lgkmcnt left at their maxima): wait until at
-// most N vector-memory loads of this wave are outstanding.
-template <int N>
-__device__ __forceinline__ void wait_vmem() {
-    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
-    __builtin_amdgcn_s_waitcnt((N & 0xf) | (0x7 << 4) | (0xf << 8) | ((N >> 4) << 14));
-}
-
-// Workgroup barrier for the K loop.  __syncthreads() carries a workgroup
-// release fence, and because direct-to-LDS loads count as LDS writes that
-// fence waits for ALL of them (vmcnt(0)), draining the prefetch in flight.
-// Here each wave waits only until at most N of its loads are outstanding
-// (the stage being prefetched) and for its own LDS writes (lgkmcnt(0)); the
-// empty asm statements keep the compiler from moving memory accesses across.
-template <int N>
-__device__ __forceinline__ void stage_barrier() {
-    wait_vmem<N>();
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-    __asm__ volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    __asm__ volatile("" ::: "memory");
-}
-
-typedef const void __attribute__((address_space(1)))* gptr_t;
-typedef void __attribute__((address_space(3)))* lptr_t;
 
 // Fragments of one 64-deep K step for one wave, read from LDS slot sa / sb.
 template <class TL, int FMT>
@@ -262,7 +152,10 @@ __device__ __forceinline__ void mma_stage(const uint8_t* __restrict__ sa, const 
     }
 }
 
-template <class TL, int FMT, bool SWIGLU>
+// KA: K is a multiple of 512 (K bytes a whole number of stages, scale rows a
+// whole number of 16-byte chunks): no partial stage, and MX scales are staged
+// through LDS (see below) instead of per-lane loads.
+template <class TL, int FMT, bool SWIGLU, bool KA>
 __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_kernel(const GemmArgs args) {
     using F = Fmt<FMT>;
     constexpr int BM = TL::BM, BN = TL::BN, NW = TL::kWaves, NT = TL::kThreads;
@@ -271,7 +164,16 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
     constexpr int kStage = kAStage + kBStage;
     constexpr int A_J = BM / 8 / NW, B_J = BN / 8 / NW;  // 1 KiB load instructions per wave per stage
     constexpr int kWords = F::kFP4 ? 2 : 1;              // scale words per row per stage
-    constexpr int kGroupsPerThread = (kMaxGroups + NT - 1) / NT;
+    // MX scales through LDS: every kSclStages stages the workgroup loads the
+    // next 16 scale bytes (16 blocks) of each of its BM + BN rows with direct
+    // loads (lane i of an instruction: row i of 64), into one of two buffers;
+    // lanes then read their words from LDS.  One 16-byte request per row per
+    // 16 blocks instead of a 4-byte load per row, stage and wave.
+    constexpr bool kLdsScales = F::kMX && KA;
+    constexpr int kSclRows = BM + BN;
+    constexpr int kSclStages = 16 / F::kBlocks;
+    static_assert(!kLdsScales || (TL::kSlots == 2 && BM % 64 == 0 && BN % 64 == 0),
+                  "LDS scales: two ring slots, whole 64-row groups");
 
     // Ring slots as distinct objects: the compiler can then tell the
     // direct-to-LDS loads into one slot from the fragment reads of another and
@@ -281,6 +183,8 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
     __shared__ __attribute__((aligned(16))) uint8_t s_ring0[kStage];
     __shared__ __attribute__((aligned(16))) uint8_t s_ring1[kStage];
     __shared__ __attribute__((aligned(16))) uint8_t s_ring2[kSlots > 2 ? kStage : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t s_scl0[kLdsScales ? kSclRows * 16 : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t s_scl1[kLdsScales ? kSclRows * 16 : 16];
     __shared__ uint32_t s_pre[kMaxGroups + 1];
     __shared__ uint32_t s_wave[NW];
 
@@ -290,59 +194,18 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
     const int h = lane >> 5, r32 = lane & 31;
     const int G = args.G;
 
-    // ---- per-group M-tile prefix (ragged schedule, no host sync)
-    {
-        uint32_t cnt[kGroupsPerThread], local = 0;
-#pragma unroll
-        for (int i = 0; i < kGroupsPerThread; ++i) {
-            const int g = tid * kGroupsPerThread + i;
-            cnt[i] = 0;
-            if (g < G) {
-                GroupRange r = group_range(args.off, args.ids, g, args.T, args.E);
-                cnt[i] = (uint32_t)((r.hi - r.lo + BM - 1) / BM);
-            }
-            local += cnt[i];
-        }
-        uint32_t total;
-        uint32_t ex = block_exclusive_scan<NT>(local, s_wave, &total);
-#pragma unroll
-        for (int i = 0; i < kGroupsPerThread; ++i) {
-            const int g = tid * kGroupsPerThread + i;
-            if (g < G) s_pre[g] = ex;
-            ex += cnt[i];
-        }
-        if (tid == 0) s_pre[G] = total;
-        __syncthreads();
-    }
+    build_tile_prefix<NT, BM>(args, s_pre, s_wave);
     const int64_t total_tiles = (int64_t)s_pre[G] * args.ntiles_n;
     const int64_t row_bytes = args.row_bytes;
     const int nkt = (int)((row_bytes + kStageBytes - 1) / kStageBytes);
-    const bool k_tail = (row_bytes % kStageBytes) != 0;  // the last stage is partial
+    const bool k_tail = !KA && (row_bytes % kStageBytes) != 0;  // the last stage is partial
     const int64_t nblk = args.K / 32;
 
-    const int ntn = args.ntiles_n;
     for (int64_t L = xcd_remap(blockIdx.x, gridDim.x); L < total_tiles; L += gridDim.x) {
-        // group owning tile L: largest g with s_pre[g] * ntn <= L (groups own
-        // contiguous tile ranges; empty groups own none)
-        int lo = 0, hi = G;  // invariant: s_pre[lo] * ntn <= L < s_pre[hi] * ntn
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if ((int64_t)s_pre[mid] * ntn <= L) lo = mid; else hi = mid;
-        }
-        const int g = lo;
-        const int mtiles = (int)(s_pre[g + 1] - s_pre[g]);
-        const int local = (int)(L - (int64_t)s_pre[g] * ntn);
-        // M-outer: consecutive tiles share an A panel; N-outer: consecutive
-        // tiles share a weight panel (weight streaming)
-        const int mt = args.n_outer ? local % mtiles : local / ntn;
-        const int nt = args.n_outer ? local / mtiles : local % ntn;
-        const GroupRange gr = group_range(args.off, args.ids, g, args.T, args.E);
-        const int e = args.ids[g];
-        const int64_t m0 = gr.lo + (int64_t)mt * BM;
-        const int64_t m_end = m0 + BM < gr.hi ? m0 + BM : gr.hi;
-        const int64_t n0 = (int64_t)nt * BN;
-        const int rows_in = (int)(m_end - m0);
-        const int cols_in = (int)(args.N - n0 < BN ? args.N - n0 : BN);
+        const TileCoord tc = locate_tile<BM, BN>(args, s_pre, L);
+        const int e = tc.e;
+        const int64_t m0 = tc.m0, m_end = tc.m_end, n0 = tc.n0;
+        const int rows_in = tc.rows_in, cols_in = tc.cols_in;
 
         // ---- operand sources: tile base (uniform) + 32-bit per-lane offsets;
         // each load instruction covers 8 rows x 8 chunks (1 KiB of the slot).
@@ -365,16 +228,23 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
                 b_off[j] = (uint32_t)(rc * row_bytes) + (swz_chunk(r, pc) << 4);
             }
         }
+        // An offset passes through an empty asm statement where it is used,
+        // so the compiler keeps it a 32-bit offset to a uniform base instead
+        // of hoisting a 64-bit per-lane address out of the K loop.
+        auto opaque = [](uint32_t v) {
+            __asm__ volatile("" : "+v"(v));
+            return v;
+        };
         auto issue_stage = [&](int kt, uint8_t* slot) {
             const uint8_t* ak = a_base + (int64_t)kt * kStageBytes;
             const uint8_t* bk = b_base + (int64_t)kt * kStageBytes;
 #pragma unroll
             for (int j = 0; j < A_J; ++j)
-                __builtin_amdgcn_global_load_lds((gptr_t)(ak + a_off[j]), (lptr_t)(slot + (wave + NW * j) * 1024), 16,
-                                                 0, 0);
+                __builtin_amdgcn_global_load_lds((gptr_t)(ak + opaque(a_off[j])),
+                                                 (lptr_t)(slot + (wave + NW * j) * 1024), 16, 0, 0);
 #pragma unroll
             for (int j = 0; j < B_J; ++j)
-                __builtin_amdgcn_global_load_lds((gptr_t)(bk + b_off[j]),
+                __builtin_amdgcn_global_load_lds((gptr_t)(bk + opaque(b_off[j])),
                                                  (lptr_t)(slot + kAStage + (wave + NW * j) * 1024), 16, 0, 0);
         };
         // The partial last stage: VGPR loads with the K tail zero-filled.
@@ -420,6 +290,45 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
                 sb_off[j] = (uint32_t)((r < cols_in ? r : cols_in - 1) * nblk);
             }
         }
+        // LDS-staged scales: chunk c (16 bytes per row from block 16c) into
+        // buffer `buf`, rows 0 .. BM-1 of A then BM .. BM+BN-1 of B; 64-row
+        // group q is loaded by wave q % NW (this lane: row 64q + lane).
+        constexpr int kSclGroups = kSclRows / 64;
+        constexpr int kSclPerWave = (kSclGroups + NW - 1) / NW;
+        const uint8_t* scl_base[kSclPerWave];
+        uint32_t scl_off[kSclPerWave];
+        if constexpr (kLdsScales) {
+#pragma unroll
+            for (int k = 0; k < kSclPerWave; ++k) {
+                const int q = wave + NW * k;
+                const int r = q * 64 + lane;
+                const bool in_a = q * 64 < BM;  // wave-uniform
+                scl_base[k] = in_a ? sa_base : sb_base;
+                scl_off[k] = in_a ? (uint32_t)((r < rows_in ? r : rows_in - 1) * nblk)
+                                  : (uint32_t)((r - BM < cols_in ? r - BM : cols_in - 1) * nblk);
+            }
+        }
+        auto issue_scales = [&](int c, uint8_t* buf) {
+#pragma unroll
+            for (int k = 0; k < kSclPerWave; ++k)
+                if (wave + NW * k < kSclGroups)  // wave-uniform
+                    __builtin_amdgcn_global_load_lds((gptr_t)(scl_base[k] + 16 * c + opaque(scl_off[k])),
+                                                     (lptr_t)(buf + (wave + NW * k) * 1024), 16, 0, 0);
+        };
+        // this lane's scale words for position `pos` (stage within a chunk)
+        auto read_scales = [&](const uint8_t* buf, int pos, uint32_t (&xa)[TM][kWords], uint32_t (&xb)[TN][kWords]) {
+#pragma unroll
+            for (int w = 0; w < kWords; ++w) {
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+                    xa[i][w] = *reinterpret_cast<const uint32_t*>(buf + (wm * WTM + i * 32 + r32) * 16 +
+                                                                  (pos * kWords + w) * 4);
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    xb[j][w] = *reinterpret_cast<const uint32_t*>(buf + (BM + wn * WTN + j * 32 + r32) * 16 +
+                                                                  (pos * kWords + w) * 4);
+            }
+        };
         auto load_scales = [&](int kt, uint32_t (&xa)[TM][kWords], uint32_t (&xb)[TN][kWords]) {
             const int64_t b0 = (int64_t)kt * F::kBlocks;
 #pragma unroll
@@ -448,7 +357,8 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
         };
         put_stage(0, s_ring0);
         if (kSlots > 2 && nkt > 1) put_stage(1, s_ring1);
-        if constexpr (F::kMX) load_scales(0, wa, wb);
+        if constexpr (kLdsScales) issue_scales(0, s_scl0);
+        else if constexpr (F::kMX) load_scales(0, wa, wb);
         wait_vmem<0>();
         __syncthreads();
 
@@ -484,7 +394,32 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
             if (D == 2 && pf_on && !pf_tail) stage_barrier<A_J + B_J>();
             else stage_barrier<0>();
         };
-        if constexpr (kSlots == 3) {
+        // With LDS scales: the stage also reads its scale words from `scur`
+        // (position pos of the chunk) and, in a chunk's last stage, starts the
+        // next chunk into `snext`, which the chunk before last used.  Slots
+        // and scale buffers rotate, so that loop is unrolled by
+        // 2 * kSclStages.
+        auto stage_lds = [&](int kt, const uint8_t* cur, uint8_t* pf, const uint8_t* scur, uint8_t* snext,
+                             int pos) {
+            const bool pf_on = kt + 1 < nkt;
+            uint32_t xa[TM][kWords], xb[TN][kWords];
+            read_scales(scur, pos, xa, xb);
+            if (pf_on) issue_stage(kt + 1, pf);
+            if (pos == kSclStages - 1 && pf_on) issue_scales((kt + 1) / kSclStages, snext);
+            mma_stage<TL, FMT>(cur, cur + kAStage, wm, wn, h, r32, xa, xb, acc);
+            stage_barrier<0>();
+        };
+        if constexpr (kLdsScales) {
+            constexpr int U = 2 * kSclStages;
+            for (int kt = 0; kt < nkt; kt += U) {
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    if (kt + u < nkt)
+                        stage_lds(kt + u, u % 2 ? s_ring1 : s_ring0, u % 2 ? s_ring0 : s_ring1,
+                                  (u / kSclStages) % 2 ? s_scl1 : s_scl0, (u / kSclStages) % 2 ? s_scl0 : s_scl1,
+                                  u % kSclStages);
+            }
+        } else if constexpr (kSlots == 3) {
             for (int kt = 0; kt < nkt; kt += 3) {
                 stage(kt, s_ring0, s_ring2);
                 if (kt + 1 < nkt) stage(kt + 1, s_ring1, s_ring0);
@@ -572,7 +507,61 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
     }
 }
 
-// ---------------------------------------------------------------------------
+template <class TL, int FMT, bool SWIGLU, bool KA>
+hipError_t launch_tile(const GemmProblem& p, hipStream_t stream, bool n_outer) {
+    auto kernel = grouped_gemm_kernel<TL, FMT, SWIGLU, KA>;
+    static thread_local int occ_device = -1, occ = 0;
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    if (occ_device != dev) {
+        err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, TL::kThreads, 0);
+        if (err != hipSuccess) return err;
+        occ_device = dev;
+    }
+    int64_t grid = 0;
+    const GemmArgs a = make_args(p, TL::BM, TL::BN, n_outer, occ, &grid);
+    if (grid <= 0) return hipSuccess;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(TL::kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+// Tile shapes, chosen by measurement on MI355X (ragged workloads of the
+// benchmark): FP8 rowwise with many rows per group -> 256 x 256 with eight
+// waves (fewest operand bytes per FLOP; two ring slots fit 160 KiB of LDS);
+// MX formats -> 128 x 256 with four waves and three slots;
+// few rows per group (decode-like, weight streaming) -> 32 x 128 tiles, many
+// of them, walked N-outer so the M tiles of an expert share each weight panel
+// in L2.
+using TileLargeFp8 = Tile<256, 256, 2, 4, 2>;
+using TileLargeMx = Tile<128, 256, 2, 2, 3>;
+using TileLargeMxKA = Tile<128, 256, 2, 2, 2>;
+using TileSmall = Tile<32, 128, 1, 4, 3>;
+
+template <int FMT, bool SWIGLU>
+hipError_t launch_fmt(const GemmProblem& p, hipStream_t stream) {
+    // Average rows per non-empty group decides the regime; the optional host
+    // hint (largest group) can only move a problem to the larger tile.
+    const int64_t groups = p.G < p.T ? p.G : p.T;
+    const int64_t avg_rows = groups > 0 ? p.T / groups : p.T;
+    const int64_t rows = p.max_rows_hint > avg_rows ? (avg_rows + p.max_rows_hint) / 2 : avg_rows;
+    const bool ka = p.K % 512 == 0;
+    if (rows >= 128) {
+        if constexpr (FMT == 0) {
+            return ka ? launch_tile<TileLargeFp8, FMT, SWIGLU, true>(p, stream, false)
+                      : launch_tile<TileLargeFp8, FMT, SWIGLU, false>(p, stream, false);
+        } else {
+            return ka ? launch_tile<TileLargeMxKA, FMT, SWIGLU, true>(p, stream, true)
+                      : launch_tile<TileLargeMx, FMT, SWIGLU, false>(p, stream, true);
+        }
+    }
+    return launch_tile<TileSmall, FMT, SWIGLU, false>(p, stream, true);
+}
+
+}  // namespace
+
+namespace gemm {
+
 int device_cus() {
     static thread_local int cached_device = -1, cached_cus = 0;
     int dev = 0;
@@ -586,19 +575,7 @@ int device_cus() {
     return cached_cus;
 }
 
-template <class TL, int FMT, bool SWIGLU>
-hipError_t launch_tile(const GemmProblem& p, hipStream_t stream, bool n_outer) {
-    auto kernel = grouped_gemm_kernel<TL, FMT, SWIGLU>;
-    static thread_local int occ_device = -1, occ = 0;
-    int dev = 0;
-    hipError_t err = hipGetDevice(&dev);
-    if (err != hipSuccess) return err;
-    if (occ_device != dev) {
-        err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, TL::kThreads, 0);
-        if (err != hipSuccess) return err;
-        occ_device = dev;
-    }
-    const int cus = device_cus();
+GemmArgs make_args(const GemmProblem& p, int BM, int BN, bool n_outer, int per_cu, int64_t* grid) {
     GemmArgs a;
     a.a = static_cast<const uint8_t*>(p.a);
     a.as = p.a_scales;
@@ -614,46 +591,20 @@ hipError_t launch_tile(const GemmProblem& p, hipStream_t stream, bool n_outer) {
     a.T = p.T;
     a.N = p.N;
     a.K = p.K;
-    a.row_bytes = FMT == 2 ? p.K / 2 : p.K;
-    a.ntiles_n = (int)((p.N + TL::BN - 1) / TL::BN);
+    a.row_bytes = p.fmt == 2 ? p.K / 2 : p.K;
+    a.ntiles_n = (int)((p.N + BN - 1) / BN);
     a.n_outer = n_outer ? 1 : 0;
     // Upper bound on M tiles: each non-empty group adds at most one partial tile.
     const int64_t groups_nonempty = p.G < p.T ? p.G : p.T;
-    const int64_t mtiles_bound = p.T / TL::BM + groups_nonempty;
+    const int64_t mtiles_bound = p.T / BM + groups_nonempty;
     const int64_t tiles_bound = mtiles_bound * a.ntiles_n;
-    int64_t grid = (int64_t)(cus > 0 ? cus : 256) * (occ > 0 ? occ : 1);
-    if (grid > tiles_bound) grid = tiles_bound;
-    if (grid <= 0) return hipSuccess;
-    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(TL::kThreads), 0, stream, a);
-    return hipGetLastError();
+    const int cus = device_cus();
+    int64_t g = (int64_t)(cus > 0 ? cus : 256) * (per_cu > 0 ? per_cu : 1);
+    *grid = g < tiles_bound ? g : tiles_bound;
+    return a;
 }
 
-// Tile shapes, chosen by measurement on MI355X (ragged workloads of the
-// benchmark): FP8 rowwise with many rows per group -> 256 x 256 with eight
-// waves (fewest operand bytes per FLOP; two ring slots fit 160 KiB of LDS);
-// MX formats -> 128 x 256 with four waves and three slots (the MX scale words
-// leave no room for the 256 x 256 accumulators); few rows per group
-// (decode-like, weight streaming) -> 32 x 128 tiles, many of them, walked
-// N-outer so the M tiles of an expert share each weight panel in L2.
-using TileLargeFp8 = Tile<256, 256, 2, 4, 2>;
-using TileLargeMx = Tile<128, 256, 2, 2, 3>;
-using TileSmall = Tile<32, 128, 1, 4, 3>;
-
-template <int FMT, bool SWIGLU>
-hipError_t launch_fmt(const GemmProblem& p, hipStream_t stream) {
-    // Average rows per non-empty group decides the regime; the optional host
-    // hint (largest group) can only move a problem to the larger tile.
-    const int64_t groups = p.G < p.T ? p.G : p.T;
-    const int64_t avg_rows = groups > 0 ? p.T / groups : p.T;
-    const int64_t rows = p.max_rows_hint > avg_rows ? (avg_rows + p.max_rows_hint) / 2 : avg_rows;
-    if (rows >= 128) {
-        if constexpr (FMT == 0) return launch_tile<TileLargeFp8, FMT, SWIGLU>(p, stream, false);
-        else return launch_tile<TileLargeMx, FMT, SWIGLU>(p, stream, true);
-    }
-    return launch_tile<TileSmall, FMT, SWIGLU>(p, stream, true);
-}
-
-}  // namespace
+}  // namespace gemm
 
 hipError_t launch_grouped_gemm(const GemmProblem& p, hipStream_t stream) {
     const bool swiglu = p.yq != nullptr;

@@ -1,0 +1,199 @@
+// gemm_common.h -- pieces both grouped-GEMM kernels share: argument block,
+// per-format constants, the LDS swizzle, the XCD-aware tile order, the ragged
+// tile map (per-group M-tile prefix in LDS + binary search) and the counted
+// wait / barrier primitives of the K pipeline.  Device code for gfx950.
+#pragma once
+
+#include "mxg_device.h"
+#include "mxg_internal.h"
+
+namespace mxg {
+namespace gemm {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+constexpr int kStageBytes = 128;  // K bytes per row per stage
+constexpr int kNumXcd = 8;
+
+struct GemmArgs {
+    const uint8_t* a;
+    const void* as;
+    const uint8_t* b;
+    const void* bs;
+    uint16_t* c;
+    uint8_t* yq;
+    uint8_t* ys;
+    const uint32_t* off;
+    const int32_t* ids;
+    int G;
+    int E;
+    int64_t T;
+    int64_t N;
+    int64_t K;
+    int64_t row_bytes;  // bytes per row of a and b
+    int ntiles_n;
+    int n_outer;        // tile order within a group: 0 = M tiles outer, 1 = N tiles outer
+};
+
+// FMT: 0 = FP8 rowwise, 1 = MXFP8, 2 = MXFP4.
+template <int FMT>
+struct Fmt {
+    static constexpr bool kMX = FMT != 0;
+    static constexpr bool kFP4 = FMT == 2;
+    static constexpr int kSteps = kFP4 ? 4 : 2;   // 64-deep MFMA steps per stage
+    static constexpr int kBlocks = kFP4 ? 8 : 4;  // 32-element scale blocks per stage
+    static constexpr int kTypeCode = kFP4 ? 4 : 0;  // cbsz / blgp: 0 = e4m3, 4 = e2m1
+};
+
+// LDS byte offset of 16-byte chunk `chunk` of stage row `row`.  A row is 128
+// bytes (32 of the 64 four-byte banks), so even and odd rows fall in opposite
+// bank halves; XOR-ing the chunk with bits 1..3 of the row gives the 16 rows a
+// 16-lane slice of a fragment read touches 16 distinct 4-bank groups.
+__device__ __forceinline__ int swz_chunk(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
+__device__ __forceinline__ int swz(int row, int chunk) { return row * kStageBytes + (swz_chunk(row, chunk) << 4); }
+
+// Bijective remap so that the workgroups the dispatcher sends to one XCD
+// (b, b + 8, b + 16, ...) get consecutive logical indices.
+__device__ __forceinline__ int xcd_remap(int b, int n) {
+    const int per = n / kNumXcd, rem = n % kNumXcd;
+    const int xcd = b % kNumXcd, idx = b / kNumXcd;
+    return xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+}
+
+// Exclusive block-wide scan over NT threads.
+template <int NT>
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s_wave, uint32_t* total) {
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    uint32_t inc = v;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        uint32_t n = __shfl_up(inc, o, kWave);
+        if (lane >= o) inc += n;
+    }
+    if (lane == kWave - 1) s_wave[wave] = inc;
+    __syncthreads();
+    uint32_t before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < NT / kWave; ++w) {
+        uint32_t s = s_wave[w];
+        before += w < wave ? s : 0;
+        all += s;
+    }
+    *total = all;
+    return before + inc - v;
+}
+
+// Scale bytes p[0 .. 4) as one word; bytes at or past `avail` read as 127
+// (2^0: they only ever multiply zero-filled K tails).
+__device__ __forceinline__ uint32_t scale_word(const uint8_t* p, int64_t avail) {
+    if (avail >= 4 && (reinterpret_cast<uintptr_t>(p) & 3) == 0) return *reinterpret_cast<const uint32_t*>(p);
+    uint32_t w = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w |= (uint32_t)(i < avail ? p[i] : (uint8_t)127) << (8 * i);
+    return w;
+}
+
+// s_waitcnt vmcnt(N) (expcnt / lgkmcnt left at their maxima): wait until at
+// most N vector-memory loads of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 0xf) | (0x7 << 4) | (0xf << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier for the K loop.  __syncthreads() carries a workgroup
+// release fence, and because direct-to-LDS loads count as LDS writes that
+// fence waits for ALL of them (vmcnt(0)), draining the prefetch in flight.
+// Here each wave waits only until at most N of its loads are outstanding
+// (the stage being prefetched) and for its own LDS writes (lgkmcnt(0)); the
+// empty asm statements keep the compiler from moving memory accesses across.
+template <int N>
+__device__ __forceinline__ void stage_barrier() {
+    wait_vmem<N>();
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+}
+
+typedef const void __attribute__((address_space(1)))* gptr_t;
+typedef void __attribute__((address_space(3)))* lptr_t;
+
+// ---------------------------------------------------------------------------
+// Ragged tile map.  Each workgroup turns row_offsets into a prefix over the
+// per-group M-tile counts (in LDS; groups that are empty, inverted or carry an
+// out-of-range expert id own no tiles).  Tile L of the launch is then found by
+// binary search; the N index is taken inner (M-outer order: consecutive tiles
+// share an A panel) or outer (consecutive tiles share a weight panel).
+template <int NT, int BM>
+__device__ __forceinline__ void build_tile_prefix(const GemmArgs& args, uint32_t* s_pre, uint32_t* s_wave) {
+    constexpr int kPer = (kMaxGroups + NT - 1) / NT;
+    const int tid = threadIdx.x, G = args.G;
+    uint32_t cnt[kPer], local = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int g = tid * kPer + i;
+        cnt[i] = 0;
+        if (g < G) {
+            const GroupRange r = group_range(args.off, args.ids, g, args.T, args.E);
+            cnt[i] = (uint32_t)((r.hi - r.lo + BM - 1) / BM);
+        }
+        local += cnt[i];
+    }
+    uint32_t total;
+    uint32_t ex = block_exclusive_scan<NT>(local, s_wave, &total);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int g = tid * kPer + i;
+        if (g < G) s_pre[g] = ex;
+        ex += cnt[i];
+    }
+    if (tid == 0) s_pre[G] = total;
+    __syncthreads();
+}
+
+struct TileCoord {
+    int e;           // expert
+    int64_t m0;      // first row of the tile
+    int64_t m_end;   // one past its last real row
+    int64_t n0;      // first column
+    int rows_in;     // real rows (1 .. BM)
+    int cols_in;     // real columns (1 .. BN)
+};
+
+template <int BM, int BN>
+__device__ __forceinline__ TileCoord locate_tile(const GemmArgs& args, const uint32_t* s_pre, int64_t L) {
+    const int ntn = args.ntiles_n;
+    int lo = 0, hi = args.G;  // invariant: s_pre[lo] * ntn <= L < s_pre[hi] * ntn
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if ((int64_t)s_pre[mid] * ntn <= L) lo = mid; else hi = mid;
+    }
+    const int g = lo;
+    const int mtiles = (int)(s_pre[g + 1] - s_pre[g]);
+    const int local = (int)(L - (int64_t)s_pre[g] * ntn);
+    const int mt = args.n_outer ? local % mtiles : local / ntn;
+    const int nt = args.n_outer ? local / mtiles : local % ntn;
+    const GroupRange gr = group_range(args.off, args.ids, g, args.T, args.E);
+    TileCoord t;
+    t.e = args.ids[g];
+    t.m0 = gr.lo + (int64_t)mt * BM;
+    t.m_end = t.m0 + BM < gr.hi ? t.m0 + BM : gr.hi;
+    t.n0 = (int64_t)nt * BN;
+    t.rows_in = (int)(t.m_end - t.m0);
+    t.cols_in = (int)(args.N - t.n0 < BN ? args.N - t.n0 : BN);
+    return t;
+}
+
+// ---------------------------------------------------------------------------
+// Host side.
+int device_cus();
+
+// Argument block for a BM x BN tiling of problem p; also returns the launch
+// grid (resident capacity `per_cu` x CUs, capped by an upper bound on the
+// tile count).  grid == 0 means there is nothing to do.
+GemmArgs make_args(const GemmProblem& p, int BM, int BN, bool n_outer, int per_cu, int64_t* grid);
+
+}  // namespace gemm
+}  // namespace mxg
