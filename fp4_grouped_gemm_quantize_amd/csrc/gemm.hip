@@ -152,9 +152,10 @@ __device__ __forceinline__ void mma_stage(const uint8_t* __restrict__ sa, const 
     }
 }
 
-// KA: K is a multiple of 512 (K bytes a whole number of stages, scale rows a
-// whole number of 16-byte chunks): no partial stage, and MX scales are staged
-// through LDS (see below) instead of per-lane loads.
+// KA: K bytes are a whole number of stages (no partial last stage) and, for
+// the MX formats, K is a multiple of 1024 (scale rows a whole number of
+// 32-byte chunks), so the scales are staged through LDS (see below) instead
+// of loaded per lane.
 template <class TL, int FMT, bool SWIGLU, bool KA>
 __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_kernel(const GemmArgs args) {
     using F = Fmt<FMT>;
@@ -165,15 +166,16 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
     constexpr int A_J = BM / 8 / NW, B_J = BN / 8 / NW;  // 1 KiB load instructions per wave per stage
     constexpr int kWords = F::kFP4 ? 2 : 1;              // scale words per row per stage
     // MX scales through LDS: every kSclStages stages the workgroup loads the
-    // next 16 scale bytes (16 blocks) of each of its BM + BN rows with direct
-    // loads (lane i of an instruction: row i of 64), into one of two buffers;
-    // lanes then read their words from LDS.  One 16-byte request per row per
-    // 16 blocks instead of a 4-byte load per row, stage and wave.
+    // next 32 scale bytes (32 blocks) of each of its BM + BN rows with direct
+    // loads (an instruction covers 32 rows, two lanes per row), into one of
+    // two buffers; lanes then read their words from LDS.  One request per
+    // row per 32 blocks instead of a 4-byte load per row, stage and wave.
     constexpr bool kLdsScales = F::kMX && KA;
     constexpr int kSclRows = BM + BN;
-    constexpr int kSclStages = 16 / F::kBlocks;
-    static_assert(!kLdsScales || (TL::kSlots == 2 && BM % 64 == 0 && BN % 64 == 0),
-                  "LDS scales: two ring slots, whole 64-row groups");
+    constexpr int kSclBytes = 32;
+    constexpr int kSclStages = kSclBytes / F::kBlocks;
+    static_assert(!kLdsScales || (TL::kSlots == 2 && BM % 32 == 0 && BN % 32 == 0),
+                  "LDS scales: two ring slots, whole 32-row groups");
 
     // Ring slots as distinct objects: the compiler can then tell the
     // direct-to-LDS loads into one slot from the fragment reads of another and
@@ -183,8 +185,8 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
     __shared__ __attribute__((aligned(16))) uint8_t s_ring0[kStage];
     __shared__ __attribute__((aligned(16))) uint8_t s_ring1[kStage];
     __shared__ __attribute__((aligned(16))) uint8_t s_ring2[kSlots > 2 ? kStage : 16];
-    __shared__ __attribute__((aligned(16))) uint8_t s_scl0[kLdsScales ? kSclRows * 16 : 16];
-    __shared__ __attribute__((aligned(16))) uint8_t s_scl1[kLdsScales ? kSclRows * 16 : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t s_scl0[kLdsScales ? kSclRows * kSclBytes : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t s_scl1[kLdsScales ? kSclRows * kSclBytes : 16];
     __shared__ uint32_t s_pre[kMaxGroups + 1];
     __shared__ uint32_t s_wave[NW];
 
@@ -290,10 +292,12 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
                 sb_off[j] = (uint32_t)((r < cols_in ? r : cols_in - 1) * nblk);
             }
         }
-        // LDS-staged scales: chunk c (16 bytes per row from block 16c) into
-        // buffer `buf`, rows 0 .. BM-1 of A then BM .. BM+BN-1 of B; 64-row
-        // group q is loaded by wave q % NW (this lane: row 64q + lane).
-        constexpr int kSclGroups = kSclRows / 64;
+        // LDS-staged scales: chunk c (32 bytes per row from block 32c) into
+        // buffer `buf`, rows 0 .. BM-1 of A then BM .. BM+BN-1 of B, row r at
+        // byte 32r; 32-row group q is loaded by wave q % NW (lane l: row
+        // 32q + l/2, bytes 16(l%2) ..).
+        constexpr int kSclRowsPerLoad = 1024 / kSclBytes;
+        constexpr int kSclGroups = kSclRows / kSclRowsPerLoad;
         constexpr int kSclPerWave = (kSclGroups + NW - 1) / NW;
         const uint8_t* scl_base[kSclPerWave];
         uint32_t scl_off[kSclPerWave];
@@ -301,18 +305,19 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
 #pragma unroll
             for (int k = 0; k < kSclPerWave; ++k) {
                 const int q = wave + NW * k;
-                const int r = q * 64 + lane;
-                const bool in_a = q * 64 < BM;  // wave-uniform
+                const int r = q * kSclRowsPerLoad + lane / (kSclBytes / 16);
+                const bool in_a = q * kSclRowsPerLoad < BM;  // wave-uniform
                 scl_base[k] = in_a ? sa_base : sb_base;
-                scl_off[k] = in_a ? (uint32_t)((r < rows_in ? r : rows_in - 1) * nblk)
-                                  : (uint32_t)((r - BM < cols_in ? r - BM : cols_in - 1) * nblk);
+                scl_off[k] = (in_a ? (uint32_t)((r < rows_in ? r : rows_in - 1) * nblk)
+                                   : (uint32_t)((r - BM < cols_in ? r - BM : cols_in - 1) * nblk)) +
+                             16 * (lane % (kSclBytes / 16));
             }
         }
         auto issue_scales = [&](int c, uint8_t* buf) {
 #pragma unroll
             for (int k = 0; k < kSclPerWave; ++k)
                 if (wave + NW * k < kSclGroups)  // wave-uniform
-                    __builtin_amdgcn_global_load_lds((gptr_t)(scl_base[k] + 16 * c + opaque(scl_off[k])),
+                    __builtin_amdgcn_global_load_lds((gptr_t)(scl_base[k] + kSclBytes * c + opaque(scl_off[k])),
                                                      (lptr_t)(buf + (wave + NW * k) * 1024), 16, 0, 0);
         };
         // this lane's scale words for position `pos` (stage within a chunk)
@@ -321,11 +326,11 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
             for (int w = 0; w < kWords; ++w) {
 #pragma unroll
                 for (int i = 0; i < TM; ++i)
-                    xa[i][w] = *reinterpret_cast<const uint32_t*>(buf + (wm * WTM + i * 32 + r32) * 16 +
+                    xa[i][w] = *reinterpret_cast<const uint32_t*>(buf + (wm * WTM + i * 32 + r32) * kSclBytes +
                                                                   (pos * kWords + w) * 4);
 #pragma unroll
                 for (int j = 0; j < TN; ++j)
-                    xb[j][w] = *reinterpret_cast<const uint32_t*>(buf + (BM + wn * WTN + j * 32 + r32) * 16 +
+                    xb[j][w] = *reinterpret_cast<const uint32_t*>(buf + (BM + wn * WTN + j * 32 + r32) * kSclBytes +
                                                                   (pos * kWords + w) * 4);
             }
         };
@@ -545,7 +550,8 @@ hipError_t launch_fmt(const GemmProblem& p, hipStream_t stream) {
     const int64_t groups = p.G < p.T ? p.G : p.T;
     const int64_t avg_rows = groups > 0 ? p.T / groups : p.T;
     const int64_t rows = p.max_rows_hint > avg_rows ? (avg_rows + p.max_rows_hint) / 2 : avg_rows;
-    const bool ka = p.K % 512 == 0;
+    // whole stages; for MX also whole 32-byte scale chunks (LDS-staged scales)
+    const bool ka = FMT == 0 ? p.K % kStageBytes == 0 : p.K % 1024 == 0;
     if (rows >= 128) {
         if constexpr (FMT == 0) {
             return ka ? launch_tile<TileLargeFp8, FMT, SWIGLU, true>(p, stream, false)

@@ -43,9 +43,9 @@ SMALL = {
     "mxfp8": W.WORKLOADS[4].scaled(rows=700, E=8, N=288, K=608),
     "mxfp4": W.WORKLOADS[5].scaled(tokens=96, E=16, N=256, K=1344),
     "mxfp4_ktail": W.WORKLOADS[5].scaled(tokens=40, E=6, masked=1, top_k=4, N=192, K=800, swiglu=False),
-    # K a multiple of 512: whole stages, MX scales staged through LDS
-    "mxfp8_k512": W.WORKLOADS[4].scaled(rows=700, E=8, N=288, K=1024),
-    "mxfp4_k512": W.WORKLOADS[5].scaled(tokens=96, E=16, N=320, K=1536, swiglu=False),
+    # K a multiple of 1024: whole stages, MX scales staged through LDS
+    "mxfp8_k1024": W.WORKLOADS[4].scaled(rows=700, E=8, N=288, K=1024),
+    "mxfp4_k2048": W.WORKLOADS[5].scaled(tokens=96, E=16, N=320, K=2048, swiglu=False),
 }
 
 

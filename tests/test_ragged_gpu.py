@@ -58,9 +58,9 @@ GROUPINGS = {
 }
 
 
-# K = 512 sends FP8 rowwise through the kernel that needs K to be a multiple
-# of 512 (with the large-tile hint of run_case); K = 288 through the others.
-@pytest.mark.parametrize("K", [288, 512])
+# K = 288 has a partial last stage; K = 512 does not; with K = 1024 the MX
+# formats also stage their scales through LDS (large-tile hint of run_case).
+@pytest.mark.parametrize("K", [288, 512, 1024])
 @pytest.mark.parametrize("fmt", [0, 1, 2])
 @pytest.mark.parametrize("name", list(GROUPINGS))
 def test_groupings(fmt, name, K):
@@ -72,7 +72,7 @@ def test_groupings(fmt, name, K):
 
 
 @pytest.mark.parametrize("fmt", [0, 1, 2])
-@pytest.mark.parametrize("N,K", [(32, 32), (96, 64), (129, 160), (1000, 96), (300, 512), (40, 1536)])
+@pytest.mark.parametrize("N,K", [(32, 32), (96, 64), (129, 160), (1000, 96), (300, 512), (300, 1024), (40, 3072)])
 def test_shape_tails(fmt, N, K):
     rng = np.random.default_rng(N * K + fmt)
     T, E = 77, 3

@@ -66,7 +66,7 @@ def test_silu_quantize_matches_oracle(I, T):
 FUSED = {
     "small_mxfp4": W.WORKLOADS[5].scaled(tokens=96, E=16, N=256, K=1344),
     "small_mxfp8": W.WORKLOADS[5].scaled(tokens=64, E=8, N=192, K=640, fmt=W.MXFP8),
-    "small_mxfp4_k512": W.WORKLOADS[5].scaled(tokens=96, E=16, N=384, K=1024),
+    "small_mxfp4_k1024": W.WORKLOADS[5].scaled(tokens=96, E=16, N=384, K=1024),
 }
 
 
