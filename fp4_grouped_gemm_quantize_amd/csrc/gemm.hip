@@ -67,86 +67,112 @@ struct Tile {
     static_assert(BM % (8 * kWaves) == 0 && BN % (8 * kWaves) == 0, "loader: whole 8-row groups per wave");
 };
 
-// Fragments of one 64-deep K step for one wave, read from LDS slot sa / sb.
+// One fragment of a 64-deep K step, read from LDS: A row block i (from sa)
+// or B column block j (from sb) of this wave's sub-tile.
 template <class TL, int FMT>
-__device__ __forceinline__ void load_frags(const uint8_t* __restrict__ sa, const uint8_t* __restrict__ sb, int s,
-                                           int wm, int wn, int h, int r32, v8i (&af)[TL::TM], v8i (&bf)[TL::TN]) {
-    using F = Fmt<FMT>;
-#pragma unroll
-    for (int i = 0; i < TL::TM; ++i) {
-        const int row = wm * TL::WTM + i * 32 + r32;
-        if constexpr (F::kFP4) {
-            const uint4 x = *reinterpret_cast<const uint4*>(sa + swz(row, 2 * s + h));
-            af[i] = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
-        } else {
-            const uint4 x0 = *reinterpret_cast<const uint4*>(sa + swz(row, 4 * s + h));
-            const uint4 x1 = *reinterpret_cast<const uint4*>(sa + swz(row, 4 * s + 2 + h));
-            af[i] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-        }
+__device__ __forceinline__ v8i load_frag(const uint8_t* __restrict__ base, int s, int row, int h) {
+    if constexpr (Fmt<FMT>::kFP4) {
+        const uint4 x = *reinterpret_cast<const uint4*>(base + swz(row, 2 * s + h));
+        return v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
+    } else {
+        const uint4 x0 = *reinterpret_cast<const uint4*>(base + swz(row, 4 * s + h));
+        const uint4 x1 = *reinterpret_cast<const uint4*>(base + swz(row, 4 * s + 2 + h));
+        return v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
     }
+}
+
+// The TM x TN matrix-core ops of row block i at step s.  Scale words arrive
+// shifted right by 8h (h = lane half), so block 2s + h of the stage is byte
+// 2(s%2) of word s/2 for every lane: a constant byte select.
+template <class TL, int FMT, int SEL>
+__device__ __forceinline__ void mma_row_sel(int i, int s, const v8i& a, const v8i (&bf)[TL::TN],
+                                            const uint32_t (&wa)[TL::TM][Fmt<FMT>::kFP4 ? 2 : 1],
+                                            const uint32_t (&wb)[TL::TN][Fmt<FMT>::kFP4 ? 2 : 1],
+                                            v16f (&acc)[TL::TM][TL::TN]) {
+    using F = Fmt<FMT>;
 #pragma unroll
     for (int j = 0; j < TL::TN; ++j) {
-        const int row = wn * TL::WTN + j * 32 + r32;
-        if constexpr (F::kFP4) {
-            const uint4 x = *reinterpret_cast<const uint4*>(sb + swz(row, 2 * s + h));
-            bf[j] = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
-        } else {
-            const uint4 x0 = *reinterpret_cast<const uint4*>(sb + swz(row, 4 * s + h));
-            const uint4 x1 = *reinterpret_cast<const uint4*>(sb + swz(row, 4 * s + 2 + h));
-            bf[j] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-        }
+        if constexpr (F::kMX)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bf[j], acc[i][j], F::kTypeCode,
+                                                                         F::kTypeCode, SEL, (int)wa[i][s >> 1], SEL,
+                                                                         (int)wb[j][s >> 1]);
+        else
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bf[j], acc[i][j], 0, 0, 0, 0, 0, 0);
     }
 }
-
-// The TM x TN matrix-core ops of step s (scale byte of block 2s + h of the
-// stage: word s/2, byte 2(s%2) + h).
 template <class TL, int FMT>
-__device__ __forceinline__ void mma_step(int s, int h, const v8i (&af)[TL::TM], const v8i (&bf)[TL::TN],
-                                         const uint32_t (&wa)[TL::TM][Fmt<FMT>::kFP4 ? 2 : 1],
-                                         const uint32_t (&wb)[TL::TN][Fmt<FMT>::kFP4 ? 2 : 1],
-                                         v16f (&acc)[TL::TM][TL::TN]) {
-    using F = Fmt<FMT>;
-    const int shift = 8 * (2 * (s & 1) + h);
-#pragma unroll
-    for (int i = 0; i < TL::TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TL::TN; ++j) {
-            if constexpr (F::kMX)
-                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    af[i], bf[j], acc[i][j], F::kTypeCode, F::kTypeCode, 0, (int)(wa[i][s >> 1] >> shift), 0,
-                    (int)(wb[j][s >> 1] >> shift));
-            else
-                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], 0, 0, 0, 0,
-                                                                             0, 0);
-        }
+__device__ __forceinline__ void mma_row(int i, int s, const v8i& a, const v8i (&bf)[TL::TN],
+                                        const uint32_t (&wa)[TL::TM][Fmt<FMT>::kFP4 ? 2 : 1],
+                                        const uint32_t (&wb)[TL::TN][Fmt<FMT>::kFP4 ? 2 : 1],
+                                        v16f (&acc)[TL::TM][TL::TN]) {
+    if (s & 1) mma_row_sel<TL, FMT, 2>(i, s, a, bf, wa, wb, acc);  // s is unrolled: the branch folds
+    else mma_row_sel<TL, FMT, 0>(i, s, a, bf, wa, wb, acc);
 }
 
-// All K steps of one stage with the fragments of step s+1 read from LDS
-// while the matrix cores work on step s.
+// All K steps of one stage.  Two waves per SIMD (one fragment set): the
+// other wave covers the LDS latency.  One wave per SIMD: the next step's
+// fragments are read while the matrix cores work -- each A fragment is
+// replaced right after the ops of its row block, B fragments alternate
+// between two sets.
 template <class TL, int FMT>
 __device__ __forceinline__ void mma_stage(const uint8_t* __restrict__ sa, const uint8_t* __restrict__ sb, int wm,
                                           int wn, int h, int r32,
-                                          const uint32_t (&wa)[TL::TM][Fmt<FMT>::kFP4 ? 2 : 1],
-                                          const uint32_t (&wb)[TL::TN][Fmt<FMT>::kFP4 ? 2 : 1],
+                                          const uint32_t (&wa_in)[TL::TM][Fmt<FMT>::kFP4 ? 2 : 1],
+                                          const uint32_t (&wb_in)[TL::TN][Fmt<FMT>::kFP4 ? 2 : 1],
                                           v16f (&acc)[TL::TM][TL::TN]) {
     using F = Fmt<FMT>;
-    constexpr int NB = TL::kFragBufs;
-    v8i af[NB][TL::TM], bf[NB][TL::TN];
-    load_frags<TL, FMT>(sa, sb, 0, wm, wn, h, r32, af[0], bf[0]);
+    constexpr int TM = TL::TM, TN = TL::TN, kW = F::kFP4 ? 2 : 1;
+    uint32_t wa[TM][kW], wb[TN][kW];
+    if constexpr (F::kMX) {
+#pragma unroll
+        for (int w = 0; w < kW; ++w) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i) wa[i][w] = wa_in[i][w] >> (8 * h);
+#pragma unroll
+            for (int j = 0; j < TN; ++j) wb[j][w] = wb_in[j][w] >> (8 * h);
+        }
+    }
+    auto arow = [&](int i) { return wm * TL::WTM + i * 32 + r32; };
+    auto brow = [&](int j) { return wn * TL::WTN + j * 32 + r32; };
+    v8i af[TM], bf[2][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) af[i] = load_frag<TL, FMT>(sa, 0, arow(i), h);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) bf[0][j] = load_frag<TL, FMT>(sb, 0, brow(j), h);
 #pragma unroll
     for (int s = 0; s < F::kSteps; ++s) {
-        if (NB == 2 && s + 1 < F::kSteps)
-            load_frags<TL, FMT>(sa, sb, s + 1, wm, wn, h, r32, af[(s + 1) % NB], bf[(s + 1) % NB]);
-        mma_step<TL, FMT>(s, h, af[s % NB], bf[s % NB], wa, wb, acc);
-        if (NB == 1 && s + 1 < F::kSteps) load_frags<TL, FMT>(sa, sb, s + 1, wm, wn, h, r32, af[0], bf[0]);
-        // interleave: one matrix-core op, then a share of the next step's LDS reads
-        constexpr int kMfma = TL::TM * TL::TN;
-        constexpr int kReads = (TL::TM + TL::TN) * (F::kFP4 ? 1 : 2);
-        if (NB == 2 && s + 1 < F::kSteps) {
+        const int c = s & 1, n = c ^ 1;
+        if constexpr (TL::kFragBufs == 1) {
 #pragma unroll
-            for (int q = 0; q < kMfma; ++q) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                            // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x100, (kReads + kMfma - 1) / kMfma, 0);  // DS read
+            for (int i = 0; i < TM; ++i) mma_row<TL, FMT>(i, s, af[i], bf[c], wa, wb, acc);
+            if (s + 1 < F::kSteps) {
+#pragma unroll
+                for (int i = 0; i < TM; ++i) af[i] = load_frag<TL, FMT>(sa, s + 1, arow(i), h);
+#pragma unroll
+                for (int j = 0; j < TN; ++j) bf[n][j] = load_frag<TL, FMT>(sb, s + 1, brow(j), h);
+            }
+        } else {
+            constexpr int kBPerRow = (TN + TM - 1) / TM;
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                mma_row<TL, FMT>(i, s, af[i], bf[c], wa, wb, acc);
+                if (s + 1 < F::kSteps) {
+                    af[i] = load_frag<TL, FMT>(sa, s + 1, arow(i), h);
+#pragma unroll
+                    for (int k = 0; k < kBPerRow; ++k)
+                        if (i * kBPerRow + k < TN)
+                            bf[n][i * kBPerRow + k] = load_frag<TL, FMT>(sb, s + 1, brow(i * kBPerRow + k), h);
+                }
+            }
+            if (s + 1 < F::kSteps) {
+                // interleave: one matrix-core op, then a share of the next step's LDS reads
+                constexpr int kMfma = TM * TN;
+                constexpr int kReads = (TM + TN) * (F::kFP4 ? 1 : 2);
+#pragma unroll
+                for (int q = 0; q < kMfma; ++q) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                            // MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x100, (kReads + kMfma - 1) / kMfma, 0);  // DS read
+                }
             }
         }
     }
