@@ -260,6 +260,30 @@ def main():
         },
         "roofline": roof,
     }
+    if r.token_of_row is not None:
+        # the gathered form (routed rows read straight from the token rows),
+        # timed on its own; algorithmic bytes: token rows once, codes,
+        # scales and indices
+        xs = W.source_activations(w, r, device="cuda")
+        idx = torch.from_numpy(W.slot_indices(r, w.top_k)).cuda()
+
+        def quant_gather():
+            mxg.mx_grouped_quantize_gather(fmt, xs, idx, w.top_k, a, sa, off, ids)
+
+        for _ in range(args.warmup):
+            quant_gather()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            quant_gather()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        qg_avg = e0.elapsed_time(e1) / args.steps
+        qg_bytes = xs.numel() * 2 + a.numel() + sa.numel() * sa.element_size() + idx.numel() * 4
+        out["kernels"].update({"quantize_gather_ms": round(qg_avg, 4),
+                               "quantize_gather_GBps": round(qg_bytes / (qg_avg * 1e-3) / 1e9, 1),
+                               "quantize_gather_bytes": qg_bytes})
+        del xs, idx
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, r, x, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -30,8 +30,8 @@ MAX_GROUPS = 1024
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmxg.so")
 
-EXPORTED = ("mx_grouped_quantize", "mx_grouped_matmul", "mx_grouped_matmul_swiglu", "mx_silu_quantize",
-            "mxg_status_string")
+EXPORTED = ("mx_grouped_quantize", "mx_grouped_quantize_gather", "mx_grouped_matmul", "mx_grouped_matmul_swiglu",
+            "mx_silu_quantize", "mxg_status_string")
 
 
 class MxgError(RuntimeError):
@@ -55,12 +55,15 @@ def lib() -> ctypes.CDLL:
                                "`python -m fp4_grouped_gemm_quantize_amd.build` (there is no CPU fallback)")
         L = ctypes.CDLL(LIB_PATH)
         L.mx_grouped_quantize.argtypes = [ctypes.c_int, _P, _P, _P, _P, _P, _I32, _I64, _I64, _P]
+        L.mx_grouped_quantize_gather.argtypes = [ctypes.c_int, _P, _I64, _P, _I32, _P, _P, _P, _P, _I32, _I64, _I64,
+                                                 _P]
         L.mx_grouped_matmul.argtypes = [ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I64, _I64, _I64,
                                         _I64, _P]
         L.mx_grouped_matmul_swiglu.argtypes = [ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I64,
                                                _I64, _I64, _I64, _P]
         L.mx_silu_quantize.argtypes = [_P, _P, _P, _P, _I32, _I64, _I64, _P]
-        for name in ("mx_grouped_quantize", "mx_grouped_matmul", "mx_grouped_matmul_swiglu", "mx_silu_quantize"):
+        for name in ("mx_grouped_quantize", "mx_grouped_quantize_gather", "mx_grouped_matmul",
+                     "mx_grouped_matmul_swiglu", "mx_silu_quantize"):
             getattr(L, name).restype = ctypes.c_int
         L.mxg_status_string.argtypes = [ctypes.c_int]
         L.mxg_status_string.restype = ctypes.c_char_p
@@ -127,6 +130,35 @@ def mx_grouped_quantize(fmt: int, x, q, scales, row_offsets, expert_ids=None) ->
         _expect(expert_ids, "expert_ids", _I32T, (G,), dev)
     _check(lib().mx_grouped_quantize(fmt, _ptr(x), _ptr(q), _ptr(scales), _ptr(row_offsets), _ptr(expert_ids),
                                      G, T, K, _stream(x)), "mx_grouped_quantize")
+
+
+def mx_grouped_quantize_gather(fmt: int, x_src, indices, indices_divisor: int, q, scales, row_offsets,
+                               expert_ids=None) -> None:
+    """Grouped quantize of the routed rows x_src[indices[t] // indices_divisor] (x_src bf16
+    [S, K], indices int32 [T]) into q / scales [T, ...]; covered rows with an index that
+    names no source row are left untouched."""
+    _expect(x_src, "x_src", _BF16)
+    if x_src.dim() != 2:
+        raise ValueError("x_src must be [num_src_rows, K]")
+    S, K = x_src.shape
+    dev = x_src.device
+    _expect(indices, "indices", _I32T, None, dev)
+    if indices.dim() != 1:
+        raise ValueError("indices must be [total_rows]")
+    T = indices.shape[0]
+    qcols = K // 2 if fmt == MXFP4 else K
+    _expect(q, "q", _U8, (T, qcols), dev)
+    if fmt == FP8_ROWWISE:
+        _expect(scales, "scales", _F32, (T,), dev)
+    else:
+        _expect(scales, "scales", _U8, (T, K // 32), dev)
+    _expect(row_offsets, "row_offsets", _U32, None, dev)
+    G = row_offsets.numel() - 1
+    if expert_ids is not None:
+        _expect(expert_ids, "expert_ids", _I32T, (G,), dev)
+    _check(lib().mx_grouped_quantize_gather(fmt, _ptr(x_src), S, _ptr(indices), int(indices_divisor), _ptr(q),
+                                            _ptr(scales), _ptr(row_offsets), _ptr(expert_ids), G, T, K,
+                                            _stream(x_src)), "mx_grouped_quantize_gather")
 
 
 def mx_grouped_matmul(fmt: int, a_q, a_scales, b_q, b_scales, c, row_offsets, expert_ids,
@@ -202,6 +234,19 @@ def quantize(fmt: int, x, row_offsets, expert_ids=None):
     else:
         s = torch.zeros((T, K // 32), dtype=torch.uint8, device=x.device)
     mx_grouped_quantize(fmt, x, q, s, row_offsets, expert_ids)
+    return q, s
+
+
+def quantize_gather(fmt: int, x_src, indices, indices_divisor: int, row_offsets, expert_ids=None):
+    """Returns (q, scales) for the routed rows x_src[indices // indices_divisor]; rows no
+    group covers (or whose index names no source row) are zero."""
+    T, K = indices.shape[0], x_src.shape[1]
+    q = torch.zeros((T, K // 2 if fmt == MXFP4 else K), dtype=torch.uint8, device=x_src.device)
+    if fmt == FP8_ROWWISE:
+        s = torch.zeros((T,), dtype=torch.float32, device=x_src.device)
+    else:
+        s = torch.zeros((T, K // 32), dtype=torch.uint8, device=x_src.device)
+    mx_grouped_quantize_gather(fmt, x_src, indices, indices_divisor, q, s, row_offsets, expert_ids)
     return q, s
 
 

@@ -48,6 +48,24 @@ mxg_status mx_grouped_quantize(mxg_format fmt, const void* x_bf16, void* q, void
                                          stream));
 }
 
+mxg_status mx_grouped_quantize_gather(mxg_format fmt, const void* x_bf16, int64_t num_src_rows,
+                                      const int32_t* indices, int32_t indices_divisor, void* q, void* scales,
+                                      const uint32_t* row_offsets, const int32_t* expert_ids, int32_t num_groups,
+                                      int64_t total_rows, int64_t K, hipStream_t stream) {
+    (void)expert_ids;  // not read, as in mx_grouped_quantize
+    if (!valid_fmt(fmt)) return MXG_ERROR_INVALID_VALUE;
+    if (K <= 0 || total_rows < 0 || num_groups < 0 || num_src_rows < 0 || indices_divisor < 1)
+        return MXG_ERROR_INVALID_VALUE;
+    if (K % 32 != 0 || num_groups > MXG_MAX_GROUPS) return MXG_ERROR_NOT_SUPPORTED;
+    if (total_rows == 0 || num_groups == 0) return MXG_SUCCESS;  // nothing is read or written
+    if (!indices || !q || !scales || !row_offsets || (num_src_rows > 0 && !x_bf16)) return MXG_ERROR_INVALID_VALUE;
+    if (!aligned(x_bf16, 16) || !aligned(q, 16) || (fmt == MXG_FP8_E4M3_ROWWISE && !aligned(scales, 4)) ||
+        !aligned(row_offsets, 4) || !aligned(indices, 4))
+        return MXG_ERROR_INVALID_VALUE;
+    return from_hip(mxg::launch_quantize_gather((int)fmt, x_bf16, num_src_rows, indices, indices_divisor, q, scales,
+                                                row_offsets, num_groups, total_rows, K, stream));
+}
+
 static mxg_status check_gemm_common(mxg_format fmt, const void* a_q, const void* a_scales, const void* b_q,
                                     const void* b_scales, const uint32_t* row_offsets, const int32_t* expert_ids,
                                     int32_t num_groups, int32_t num_experts, int64_t total_rows, int64_t N,

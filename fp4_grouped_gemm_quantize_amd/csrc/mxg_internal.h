@@ -9,6 +9,11 @@ namespace mxg {
 hipError_t launch_quantize(int fmt, const void* x, void* q, void* scales, const uint32_t* off, int G, int64_t T,
                            int64_t K, hipStream_t stream);
 
+// The same with row t read from row indices[t] / divisor of x (nsrc rows).
+hipError_t launch_quantize_gather(int fmt, const void* x, int64_t nsrc, const int32_t* indices, int32_t divisor,
+                                  void* q, void* scales, const uint32_t* off, int G, int64_t T, int64_t K,
+                                  hipStream_t stream);
+
 hipError_t launch_silu_quantize(const void* h, void* yq, void* ys, const uint32_t* off, int G, int64_t T,
                                 int64_t I, hipStream_t stream);
 

@@ -36,23 +36,47 @@ __device__ __forceinline__ void load_offsets(uint32_t* s_off, const uint32_t* of
 // amax / 448) and every bf16 x with |x| <= amax.
 __device__ __forceinline__ float div_by_scale(float x, double inv_scale) { return (float)((double)x * inv_scale); }
 
+// Gathered input (grouped_quantize(): indices, indices_divisor): routed row
+// t reads source row indices[t] / divisor of x, which has nsrc rows; a row
+// whose index is negative or names no source row is skipped (left
+// untouched), so no read leaves x.  Without GATHER, row t reads row t.
+struct Gather {
+    const int32_t* idx;
+    int32_t div;
+    int64_t nsrc;
+};
+
+template <bool GATHER>
+__device__ __forceinline__ int64_t source_row(const Gather& g, int64_t t) {
+    if constexpr (!GATHER) {
+        return t;
+    } else {
+        const int32_t v = g.idx[t];
+        if (v < 0) return -1;
+        const int64_t s = v / g.div;
+        return s < g.nsrc ? s : -1;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // FP8 rowwise and MX, rows of K <= NC * 512 held in registers.
 // FMT: 0 = FP8 rowwise (scale = amax / 448, code = e4m3(x / scale)),
 //      1 = MXFP8, 2 = MXFP4.
-template <int FMT, int NC>
+template <int FMT, int NC, bool GATHER>
 __global__ __launch_bounds__(kThreads) void quantize_rows_kernel(const uint16_t* __restrict__ x,
                                                                  uint8_t* __restrict__ q, void* __restrict__ scales,
                                                                  const uint32_t* __restrict__ off, int G,
-                                                                 int64_t T, int64_t K) {
+                                                                 int64_t T, int64_t K, Gather ga) {
     __shared__ uint32_t s_off[kMaxGroups + 1];
     load_offsets(s_off, off, G);
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t nw = (int64_t)gridDim.x * kWavesPerBlock;
     const int nvec = (int)(K / kVecElems);
 
-    auto load_row = [&](int64_t t, uint4 (&v)[NC]) {
-        const uint4* xr = reinterpret_cast<const uint4*>(x + t * K);
+    // source row sr of x (-1: none; the registers are then left as they are)
+    auto load_row = [&](int64_t sr, uint4 (&v)[NC]) {
+        if (sr < 0) return;
+        const uint4* xr = reinterpret_cast<const uint4*>(x + sr * K);
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
             const int idx = c * kWave + lane;
@@ -62,11 +86,13 @@ __global__ __launch_bounds__(kThreads) void quantize_rows_kernel(const uint16_t*
 
     uint4 v[NC], vn[NC];
     int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
-    if (t < T) load_row(t, v);
+    int64_t sr = t < T ? source_row<GATHER>(ga, t) : -1;
+    load_row(sr, v);
     for (; t < T; t += nw) {
         const int64_t tn = t + nw;
-        if (tn < T) load_row(tn, vn);
-        if (wave_row_covered(s_off, G, T, t)) {
+        const int64_t srn = tn < T ? source_row<GATHER>(ga, tn) : -1;
+        load_row(srn, vn);
+        if (sr >= 0 && wave_row_covered(s_off, G, T, t)) {
             if constexpr (FMT == 0) {
                 // bf16 magnitudes order like their bit patterns with the sign cleared
                 uint32_t amax_bits = 0;
@@ -116,24 +142,26 @@ __global__ __launch_bounds__(kThreads) void quantize_rows_kernel(const uint16_t*
         }
 #pragma unroll
         for (int c = 0; c < NC; ++c) v[c] = vn[c];
+        sr = srn;
     }
 }
 
 // Rows longer than the register budget: rowwise reads the row twice (the
 // second pass from cache); MX streams 512-element chunks.
-template <int FMT>
+template <int FMT, bool GATHER>
 __global__ __launch_bounds__(kThreads) void quantize_long_kernel(const uint16_t* __restrict__ x,
                                                                  uint8_t* __restrict__ q, void* __restrict__ scales,
                                                                  const uint32_t* __restrict__ off, int G,
-                                                                 int64_t T, int64_t K) {
+                                                                 int64_t T, int64_t K, Gather ga) {
     __shared__ uint32_t s_off[kMaxGroups + 1];
     load_offsets(s_off, off, G);
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t nw = (int64_t)gridDim.x * kWavesPerBlock;
     const int64_t nvec = K / kVecElems;
     for (int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave; t < T; t += nw) {
-        if (!wave_row_covered(s_off, G, T, t)) continue;
-        const uint4* xr = reinterpret_cast<const uint4*>(x + t * K);
+        const int64_t sr = source_row<GATHER>(ga, t);
+        if (sr < 0 || !wave_row_covered(s_off, G, T, t)) continue;
+        const uint4* xr = reinterpret_cast<const uint4*>(x + sr * K);
         if constexpr (FMT == 0) {
             uint32_t amax_bits = 0;
             for (int64_t idx = lane; idx < nvec; idx += kWave) {
@@ -226,23 +254,33 @@ int64_t persistent_grid(Kern kernel, int64_t T) {
 
 template <class Kern>
 hipError_t launch_persistent(Kern kernel, const uint16_t* x, uint8_t* q, void* s, const uint32_t* off, int G,
-                             int64_t T, int64_t K, hipStream_t stream) {
+                             int64_t T, int64_t K, const Gather& ga, hipStream_t stream) {
     hipLaunchKernelGGL(kernel, dim3((unsigned)persistent_grid(kernel, T)), dim3(kThreads), 0, stream, x, q, s, off,
-                       G, T, K);
+                       G, T, K, ga);
     return hipGetLastError();
 }
 
-template <int FMT>
+template <int FMT, bool GATHER>
 hipError_t launch_fmt(const uint16_t* x, uint8_t* q, void* s, const uint32_t* off, int G, int64_t T, int64_t K,
-                      hipStream_t stream) {
+                      const Gather& ga, hipStream_t stream) {
     const int64_t nc = (K + kChunk - 1) / kChunk;
-    if (nc <= 1) return launch_persistent(quantize_rows_kernel<FMT, 1>, x, q, s, off, G, T, K, stream);
-    if (nc <= 2) return launch_persistent(quantize_rows_kernel<FMT, 2>, x, q, s, off, G, T, K, stream);
-    if (nc <= 4) return launch_persistent(quantize_rows_kernel<FMT, 4>, x, q, s, off, G, T, K, stream);
-    if (nc <= 8) return launch_persistent(quantize_rows_kernel<FMT, 8>, x, q, s, off, G, T, K, stream);
-    if (nc <= 14) return launch_persistent(quantize_rows_kernel<FMT, 14>, x, q, s, off, G, T, K, stream);
-    if (nc <= 16) return launch_persistent(quantize_rows_kernel<FMT, 16>, x, q, s, off, G, T, K, stream);
-    return launch_persistent(quantize_long_kernel<FMT>, x, q, s, off, G, T, K, stream);
+    if (nc <= 1) return launch_persistent(quantize_rows_kernel<FMT, 1, GATHER>, x, q, s, off, G, T, K, ga, stream);
+    if (nc <= 2) return launch_persistent(quantize_rows_kernel<FMT, 2, GATHER>, x, q, s, off, G, T, K, ga, stream);
+    if (nc <= 4) return launch_persistent(quantize_rows_kernel<FMT, 4, GATHER>, x, q, s, off, G, T, K, ga, stream);
+    if (nc <= 8) return launch_persistent(quantize_rows_kernel<FMT, 8, GATHER>, x, q, s, off, G, T, K, ga, stream);
+    if (nc <= 14) return launch_persistent(quantize_rows_kernel<FMT, 14, GATHER>, x, q, s, off, G, T, K, ga, stream);
+    if (nc <= 16) return launch_persistent(quantize_rows_kernel<FMT, 16, GATHER>, x, q, s, off, G, T, K, ga, stream);
+    return launch_persistent(quantize_long_kernel<FMT, GATHER>, x, q, s, off, G, T, K, ga, stream);
+}
+
+template <bool GATHER>
+hipError_t launch_any(int fmt, const void* x, void* q, void* scales, const uint32_t* off, int G, int64_t T,
+                      int64_t K, const Gather& ga, hipStream_t stream) {
+    const uint16_t* xb = static_cast<const uint16_t*>(x);
+    uint8_t* qb = static_cast<uint8_t*>(q);
+    if (fmt == 0) return launch_fmt<0, GATHER>(xb, qb, scales, off, G, T, K, ga, stream);
+    if (fmt == 1) return launch_fmt<1, GATHER>(xb, qb, scales, off, G, T, K, ga, stream);
+    return launch_fmt<2, GATHER>(xb, qb, scales, off, G, T, K, ga, stream);
 }
 
 }  // namespace
@@ -250,11 +288,13 @@ hipError_t launch_fmt(const uint16_t* x, uint8_t* q, void* s, const uint32_t* of
 // ---------------------------------------------------------------------------
 hipError_t launch_quantize(int fmt, const void* x, void* q, void* scales, const uint32_t* off, int G, int64_t T,
                            int64_t K, hipStream_t stream) {
-    const uint16_t* xb = static_cast<const uint16_t*>(x);
-    uint8_t* qb = static_cast<uint8_t*>(q);
-    if (fmt == 0) return launch_fmt<0>(xb, qb, scales, off, G, T, K, stream);
-    if (fmt == 1) return launch_fmt<1>(xb, qb, scales, off, G, T, K, stream);
-    return launch_fmt<2>(xb, qb, scales, off, G, T, K, stream);
+    return launch_any<false>(fmt, x, q, scales, off, G, T, K, Gather{nullptr, 1, T}, stream);
+}
+
+hipError_t launch_quantize_gather(int fmt, const void* x, int64_t nsrc, const int32_t* indices, int32_t divisor,
+                                  void* q, void* scales, const uint32_t* off, int G, int64_t T, int64_t K,
+                                  hipStream_t stream) {
+    return launch_any<true>(fmt, x, q, scales, off, G, T, K, Gather{indices, divisor, nsrc}, stream);
 }
 
 hipError_t launch_silu_quantize(const void* h, void* yq, void* ys, const uint32_t* off, int G, int64_t T,

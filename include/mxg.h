@@ -1,10 +1,12 @@
 /*
  * mxg.h -- C ABI of libmxg.so: the ragged MoE expert path on one gfx950 GPU.
  *
- * Four operations, each one asynchronous launch sequence on the caller's HIP
+ * Five operations, each one asynchronous launch sequence on the caller's HIP
  * stream:
  *   mx_grouped_quantize       BF16 activations -> FP8 e4m3 + per-row fp32 scale,
  *                             or MX (32-element blocks, E8M0 scale, e4m3 or e2m1)
+ *   mx_grouped_quantize_gather  the same, reading each routed row from its
+ *                             source row (token) through an index list
  *   mx_grouped_matmul         ragged grouped GEMM, FP8 rowwise or MX block-scaled,
  *                             fp32 accumulation, BF16 output
  *   mx_grouped_matmul_swiglu  MX grouped GEMM against interleaved gate/up weights,
@@ -97,6 +99,35 @@ typedef enum {
 mxg_status mx_grouped_quantize(mxg_format fmt, const void* x_bf16, void* q, void* scales,
                                const uint32_t* row_offsets, const int32_t* expert_ids, int32_t num_groups,
                                int64_t total_rows, int64_t K, hipStream_t stream);
+
+/*
+ * mx_grouped_quantize_gather -- mx_grouped_quantize with the routed rows
+ * gathered from the source activations on the fly, so the permuted BF16
+ * copy of the activations is never written.
+ * (NvMxf4f8Strategy, grouped_quantize(): parameters indices and
+ *  indices_divisor.  The page names them without defining them; the reading
+ *  taken here: routed row t is source row indices[t] / indices_divisor,
+ *  integer division -- with indices holding flat (token * top_k + k) slots
+ *  and indices_divisor = top_k, the token's row.)
+ *
+ *   x_bf16          [num_src_rows, K] bf16 source rows (e.g. one per token).
+ *   num_src_rows    rows of x_bf16.
+ *   indices         [total_rows] int32, device.  Read for every row below
+ *                   total_rows; a row whose entry is negative or whose
+ *                   quotient is >= num_src_rows is skipped (left untouched),
+ *                   so no read leaves x_bf16.
+ *   indices_divisor >= 1.
+ *   q, scales, row_offsets, expert_ids, num_groups, total_rows, K, stream:
+ *                   as in mx_grouped_quantize; the results of a covered row
+ *                   equal mx_grouped_quantize applied to its source row.
+ *
+ * Errors: those of mx_grouped_quantize, plus INVALID_VALUE for a null
+ * indices, num_src_rows < 0, indices_divisor < 1 or a misaligned indices.
+ */
+mxg_status mx_grouped_quantize_gather(mxg_format fmt, const void* x_bf16, int64_t num_src_rows,
+                                      const int32_t* indices, int32_t indices_divisor, void* q, void* scales,
+                                      const uint32_t* row_offsets, const int32_t* expert_ids, int32_t num_groups,
+                                      int64_t total_rows, int64_t K, hipStream_t stream);
 
 /*
  * mx_grouped_matmul -- ragged grouped GEMM with BF16 output.

@@ -83,6 +83,8 @@ def lib() -> ctypes.CDLL:
         L.mxo_group_of_row.restype = _I32
         L.mxo_quantize.argtypes = [ctypes.c_int, _P, _P, _P, _P, _I32, _I64, _I64]
         L.mxo_quantize.restype = ctypes.c_int
+        L.mxo_quantize_gather.argtypes = [ctypes.c_int, _P, _I64, _P, _I32, _P, _P, _P, _I32, _I64, _I64]
+        L.mxo_quantize_gather.restype = ctypes.c_int
         L.mxo_gemm_rows.argtypes = [ctypes.c_int, _P, _P, _P, _P, _P, _P, _I32, _I32, _I64, _I64, _I64,
                                     _P, _I64, _P, _P, _P, _P]
         L.mxo_gemm_rows.restype = ctypes.c_int
@@ -198,6 +200,28 @@ def quantize(fmt: int, x_bf16, offsets, q=None, scales=None):
     rc = lib().mxo_quantize(fmt, _ptr(x), _ptr(q), _ptr(scales), _ptr(off), off.size - 1, T, K)
     if rc != 0:
         raise ValueError("oracle quantize: invalid arguments")
+    return q, scales
+
+
+def quantize_gather(fmt: int, x_src, indices, divisor: int, offsets, q=None, scales=None):
+    """Grouped quantize of the routed rows x_src[indices[t] // divisor] (x_src bf16 bits
+    [S, K] uint16, indices int32 [T]).  Returns (q, scales) [T, ...]; covered rows whose
+    index is negative or names no source row keep their contents, as do uncovered rows."""
+    x = _c(x_src, np.uint16)
+    S, K = x.shape
+    idx = _c(indices, np.int32)
+    T = idx.shape[0]
+    off = _c(offsets, np.uint32)
+    qcols = K // 2 if fmt == MXFP4 else K
+    if q is None:
+        q = np.zeros((T, qcols), np.uint8)
+    if scales is None:
+        scales = np.zeros((T,), np.float32) if fmt == FP8_ROWWISE else np.zeros((T, K // 32), np.uint8)
+    assert q.shape == (T, qcols) and q.dtype == np.uint8
+    rc = lib().mxo_quantize_gather(fmt, _ptr(x), S, _ptr(idx), int(divisor), _ptr(q), _ptr(scales), _ptr(off),
+                                   off.size - 1, T, K)
+    if rc != 0:
+        raise ValueError("oracle quantize_gather: invalid arguments")
     return q, scales
 
 

@@ -303,6 +303,40 @@ int mxo_quantize(int fmt, const uint16_t* x, uint8_t* q, void* scales, const uin
     return MXO_OK;
 }
 
+/* Gathered grouped quantize (NvMxf4f8Strategy, grouped_quantize(): indices,
+ * indices_divisor; the pages name the two parameters without defining them,
+ * and the reading taken is: routed row t is source row idx[t] / div of x,
+ * which has nsrc rows).  Row t of q / scales is what mxo_quantize writes for
+ * that source row; a covered row whose index is negative or names no source
+ * row is left untouched, as is every uncovered row.                        */
+int mxo_quantize_gather(int fmt, const uint16_t* x, int64_t nsrc, const int32_t* idx, int32_t div, uint8_t* q,
+                        void* scales, const uint32_t* off, int32_t G, int64_t T, int64_t K) {
+    if (!q || !scales || !off || !idx || G < 0 || T < 0 || nsrc < 0 || div < 1 || K <= 0 || (K % 32) != 0)
+        return MXO_EINVAL;
+    if (nsrc > 0 && !x) return MXO_EINVAL;
+    if (fmt < 0 || fmt > 2) return MXO_EINVAL;
+    for (int32_t g = 0; g < G; ++g) {
+        int64_t lo, hi;
+        group_range(off, g, T, &lo, &hi);
+        if (lo > hi) continue;
+#pragma omp parallel for schedule(dynamic, 16)
+        for (int64_t t = lo; t < hi; ++t) {
+            if (idx[t] < 0) continue;
+            const int64_t src = (int64_t)idx[t] / div;
+            if (src >= nsrc) continue;
+            const uint16_t* xr = x + src * K;
+            if (fmt == 0) {
+                quantize_row_fp8(xr, K, q + t * K, (float*)scales + t);
+            } else if (fmt == 1) {
+                quantize_row_mx(MXO_E4M3, xr, K, q + t * K, (uint8_t*)scales + t * (K / 32));
+            } else {
+                quantize_row_mx(MXO_E2M1, xr, K, q + t * (K / 2), (uint8_t*)scales + t * (K / 32));
+            }
+        }
+    }
+    return MXO_OK;
+}
+
 /* ------------------------------------------------------------------------- */
 /* Grouped GEMM on a list of rows (grouped_matmul_rowwise_dynamic_scaled_fp8,
  * description; NvMxf4f8Strategy grouped_matmul()).  For each listed row t the

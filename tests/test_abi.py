@@ -65,6 +65,28 @@ def test_quantize_argument_errors():
     assert q(G=0) == mxg.SUCCESS
 
 
+def qg(fmt=0, x=FAKE, S=8, idx=FAKE, div=2, qq=FAKE, s=FAKE, off=FAKE, ids=None, G=1, T=4, K=64):
+    return mxg.lib().mx_grouped_quantize_gather(fmt, x, S, idx, div, qq, s, off, ids, G, T, K, None)
+
+
+def test_quantize_gather_argument_errors():
+    assert qg(idx=None) == mxg.ERROR_INVALID_VALUE
+    assert qg(x=None) == mxg.ERROR_INVALID_VALUE
+    assert qg(qq=None) == mxg.ERROR_INVALID_VALUE
+    assert qg(s=None) == mxg.ERROR_INVALID_VALUE
+    assert qg(off=None) == mxg.ERROR_INVALID_VALUE
+    assert qg(div=0) == mxg.ERROR_INVALID_VALUE
+    assert qg(div=-2) == mxg.ERROR_INVALID_VALUE
+    assert qg(S=-1) == mxg.ERROR_INVALID_VALUE
+    assert qg(fmt=3) == mxg.ERROR_INVALID_VALUE
+    assert qg(idx=FAKE_ODD) == mxg.ERROR_INVALID_VALUE
+    assert qg(x=FAKE_ODD) == mxg.ERROR_INVALID_VALUE
+    assert qg(K=48) == mxg.ERROR_NOT_SUPPORTED
+    assert qg(G=1025) == mxg.ERROR_NOT_SUPPORTED
+    assert qg(T=0) == mxg.SUCCESS
+    assert qg(G=0) == mxg.SUCCESS
+
+
 def mm(fmt=0, a=FAKE, sa=FAKE, b=FAKE, sb=FAKE, c=FAKE, off=FAKE, ids=FAKE, G=1, E=1, T=4, N=32, K=64):
     return mxg.lib().mx_grouped_matmul(fmt, a, sa, b, sb, c, off, ids, G, E, T, N, K, 0, None)
 

@@ -9,6 +9,7 @@ import json
 import os
 
 import numpy as np
+import pytest
 import torch
 
 import oracle
@@ -198,3 +199,56 @@ def test_quantize_clamps_offsets_and_skips_inverted_groups():
     qa, sa = oracle.quantize(oracle.FP8_ROWWISE, x, one_group(6))
     assert np.all(q[0] == 0xA5) and s[0] == -1.0
     assert np.array_equal(q[1:], qa[1:]) and np.array_equal(s[1:], sa[1:])
+
+
+# ---------------------------------------------------------------- gathered quantize
+# (NvMxf4f8Strategy, grouped_quantize(): indices / indices_divisor.  Reading:
+#  routed row t is source row indices[t] // indices_divisor.)  The gathered
+# form must equal the pinned plain quantize of the rows it names, and rows
+# whose index names no source row must keep their contents.
+@pytest.mark.parametrize("fmt", [0, 1, 2])
+def test_quantize_gather_identity_equals_quantize(fmt):
+    rng = np.random.default_rng(40 + fmt)
+    T, K = 37, 96
+    x = oracle.bf16_round_array(rng.standard_normal((T, K)) * np.exp(rng.uniform(-4, 4, (T, 1))))
+    off = np.array([0, 10, 10, 30, T], np.uint32)
+    q0, s0 = oracle.quantize(fmt, x, off)
+    q1, s1 = oracle.quantize_gather(fmt, x, np.arange(T, dtype=np.int32), 1, off)
+    assert np.array_equal(q0, q1) and np.array_equal(s0.view(np.uint8), s1.view(np.uint8))
+
+
+@pytest.mark.parametrize("fmt", [0, 1, 2])
+def test_quantize_gather_follows_indices_and_divisor(fmt):
+    rng = np.random.default_rng(50 + fmt)
+    S, top_k, K = 23, 4, 64
+    x = oracle.bf16_round_array(rng.standard_normal((S, K)))
+    # every (token, k) slot once, sorted by a random expert -> routed rows
+    slots = rng.permutation(S * top_k).astype(np.int32)
+    T = slots.size
+    off = np.array([0, 30, 31, 60, T], np.uint32)
+    q, s = oracle.quantize_gather(fmt, x, slots, top_k, off)
+    qr, sr = oracle.quantize(fmt, x[slots // top_k], off)
+    assert np.array_equal(q, qr) and np.array_equal(s.view(np.uint8), sr.view(np.uint8))
+
+
+@pytest.mark.parametrize("fmt", [0, 1, 2])
+def test_quantize_gather_skips_rows_without_a_source(fmt):
+    rng = np.random.default_rng(60 + fmt)
+    S, K = 5, 32
+    x = oracle.bf16_round_array(rng.standard_normal((S, K)))
+    idx = np.array([0, -1, 9, 10, 4, 2**31 - 1, 7], np.int32)  # divisor 2: sources 0, -, 4, 5(out), 2, out, 3
+    T = idx.size
+    off = np.array([0, T], np.uint32)
+    qcols = K // 2 if fmt == 2 else K
+    q0 = np.full((T, qcols), 0xA5, np.uint8)
+    s0 = np.full((T,), -3.0, np.float32) if fmt == 0 else np.full((T, K // 32), 0x5A, np.uint8)
+    q, s = oracle.quantize_gather(fmt, x, idx, 2, off, q0.copy(), s0.copy())
+    for t, v in enumerate(idx):
+        src = v // 2
+        if v < 0 or src >= S:
+            assert np.all(q[t] == 0xA5) and np.array_equal(np.atleast_1d(s[t]).view(np.uint8),
+                                                           np.atleast_1d(s0[t]).view(np.uint8))
+        else:
+            qr, sr = oracle.quantize(fmt, x[src:src + 1], np.array([0, 1], np.uint32))
+            assert np.array_equal(q[t], qr[0]) and np.array_equal(np.atleast_1d(s[t]).view(np.uint8),
+                                                                  np.atleast_1d(sr[0]).view(np.uint8))

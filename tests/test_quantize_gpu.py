@@ -134,3 +134,67 @@ def test_weight_preparation_full_size(widx):
     torch.cuda.synchronize()
     q_ref, s_ref = oracle_quantize_weights(w.fmt, bits(wt))
     assert_same((qg.cpu().numpy(), sg.cpu().numpy()), (q_ref, s_ref), f"weights {widx}")
+
+
+# ---------------------------------------------------------------- gathered quantize
+def run_gather_both(fmt, x_src_bits: np.ndarray, idx: np.ndarray, div: int, off: np.ndarray):
+    S, K = x_src_bits.shape
+    T = idx.size
+    qcols = K // 2 if fmt == mxg.MXFP4 else K
+    s0 = np.full((T,), -3.0, np.float32) if fmt == mxg.FP8_ROWWISE else sentinel_like((T, K // 32), value=0x5A)
+    q_ref, s_ref = oracle.quantize_gather(fmt, x_src_bits, idx, div, off, sentinel_like((T, qcols)), s0.copy())
+    x = to_gpu(x_src_bits.view(np.int16)).view(torch.bfloat16)
+    q = to_gpu(sentinel_like((T, qcols)))
+    s = to_gpu(s0.copy())
+    mxg.mx_grouped_quantize_gather(fmt, x, to_gpu(idx.astype(np.int32)), div, q, s, offsets_gpu(off))
+    torch.cuda.synchronize()
+    return (q.cpu().numpy(), s.cpu().numpy()), (q_ref, s_ref)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("case", ["prefill", "mxfp4"])
+def test_quantize_gather_matches_oracle(fmt, case):
+    """Routed rows read from the token rows through flat slot indices (divisor top_k)."""
+    widx, kw = CASES[case]
+    w = W.WORKLOADS[widx].scaled(**kw)
+    r = W.routing(w)
+    xs = bits(W.source_activations(w, r))
+    idx = W.slot_indices(r, w.top_k)
+    gpu, ref = run_gather_both(fmt, xs, idx, w.top_k, r.row_offsets)
+    assert_same(gpu, ref, f"gather {case} fmt={fmt}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("K", [32, 1024, 8704])
+def test_quantize_gather_edge_rows(fmt, K):
+    """Uncovered rows, negative indices and indices past the source rows are
+    left untouched; K = 8704 takes the long-row kernel."""
+    rng = np.random.default_rng(K + fmt)
+    S, div, T = 19, 3, 70
+    xs = oracle.bf16_round_array(rng.standard_normal((S, K)) * np.exp(rng.uniform(-3, 3, (S, 1))))
+    idx = rng.integers(0, S * div, T).astype(np.int32)
+    idx[[3, 11, 40]] = -7
+    idx[[5, 50]] = S * div + 4
+    idx[60] = np.iinfo(np.int32).max
+    off = np.array([2, 20, 20, 64], np.uint32)  # rows 0-1 and 64.. uncovered
+    gpu, ref = run_gather_both(fmt, xs, idx, div, off)
+    assert_same(gpu, ref, f"gather edges K={K} fmt={fmt}")
+
+
+def test_quantize_gather_full_size_prefill():
+    """The prefill workload's 65,536 routed rows read straight from its 8192
+    token rows, in the benchmark's launch configuration."""
+    w = W.WORKLOADS[3]
+    r = W.routing(w)
+    xs_gpu = W.source_activations(w, r, device="cuda")
+    idx = W.slot_indices(r, w.top_k)
+    q, s = mxg.quantize_gather(w.fmt, xs_gpu, to_gpu(idx), w.top_k, offsets_gpu(r.row_offsets))
+    torch.cuda.synchronize()
+    rows = np.unique(np.r_[r.row_offsets[:-1], r.row_offsets[1:] - 1,
+                           np.random.default_rng(7).integers(0, r.total_rows, 256)]).astype(np.int64)
+    rows = rows[rows < r.total_rows]
+    xs = bits(xs_gpu)
+    sub_idx = idx[rows]
+    q_ref, s_ref = oracle.quantize_gather(w.fmt, xs, sub_idx, w.top_k, np.array([0, rows.size], np.uint32))
+    assert np.array_equal(q.cpu().numpy()[rows], q_ref)
+    assert np.array_equal(s.cpu().numpy()[rows].view(np.uint8), s_ref.view(np.uint8))

@@ -149,8 +149,9 @@ def _gen(device, seed):
     return g
 
 
-def activations(w: Workload, r: Routing, device="cpu") -> torch.Tensor:
-    """bf16 [T, K] routed activations, N(0, 1) (with the stated outliers)."""
+def source_activations(w: Workload, r: Routing, device="cpu") -> torch.Tensor:
+    """bf16 source rows, N(0, 1) (with the stated outliers): one per token for
+    the tokens x top-k workloads, else one per routed row."""
     _, seed_a, _ = _streams(w.seed)
     g = _gen(device, seed_a)
     n_src = w.tokens if r.token_of_row is not None else r.total_rows
@@ -158,10 +159,27 @@ def activations(w: Workload, r: Routing, device="cpu") -> torch.Tensor:
     if w.outlier_p > 0:
         mask = torch.rand((n_src, w.K), generator=g, device=device) < w.outlier_p
         x = torch.where(mask, x * w.outlier_mult, x)
-    x = x.to(torch.bfloat16)
+    return x.to(torch.bfloat16)
+
+
+def activations(w: Workload, r: Routing, device="cpu") -> torch.Tensor:
+    """bf16 [T, K] routed activations: source row token_of_row[t] for row t."""
+    x = source_activations(w, r, device)
     if r.token_of_row is not None:
         x = x[torch.as_tensor(r.token_of_row, device=device)]
     return x.contiguous()
+
+
+def slot_indices(r: Routing, top_k: int) -> np.ndarray:
+    """int32 [T] flat slot index token * top_k + k of each routed row, k being
+    the row's rank among its token's rows; slot // top_k is the token."""
+    tok = np.asarray(r.token_of_row, np.int64)
+    seen = np.zeros(int(tok.max()) + 1 if tok.size else 0, np.int64)
+    k = np.empty_like(tok)
+    for i, t in enumerate(tok):
+        k[i] = seen[t]
+        seen[t] += 1
+    return (tok * top_k + k).astype(np.int32)
 
 
 def weights(w: Workload, device="cpu", experts=None) -> torch.Tensor:
