@@ -284,6 +284,48 @@ def main():
                                "quantize_gather_GBps": round(qg_bytes / (qg_avg * 1e-3) / 1e9, 1),
                                "quantize_gather_bytes": qg_bytes})
         del xs, idx
+    if w.swiglu and r.token_of_row is not None:
+        # the rest of the expert FFN, timed on its own: the down-projection
+        # (MX grouped GEMM with K = I on the fused output, weights [E, H, I])
+        # and the combine of each token's top-k rows with router weights
+        H, I = K, N // 2
+        wd = w.scaled(N=H, K=I, seed=w.seed + 17)
+        wdt = W.weights(wd, device="cuda")
+        bd, sbd = mxg.quantize_weights(fmt, wdt)
+        del wdt
+        torch.cuda.empty_cache()
+        yd = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+        ros = torch.from_numpy(W.rows_of_slots(r, w.top_k, w.tokens)).cuda()
+        wts = torch.from_numpy(W.router_weights(w, w.tokens)).cuda()
+        comb = torch.empty((w.tokens, H), dtype=torch.bfloat16, device="cuda")
+
+        def down():
+            mxg.mx_grouped_matmul(fmt, yq, ys, bd, sbd, yd, off, ids, hint)
+
+        def combine():
+            mxg.mx_moe_combine(yd, ros, wts, comb)
+
+        for _ in range(args.warmup):
+            down()
+            combine()
+        ed = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        d_ms, c_ms = [], []
+        for _ in range(args.steps):
+            ed[0].record(stream)
+            down()
+            ed[1].record(stream)
+            combine()
+            ed[2].record(stream)
+            torch.cuda.synchronize()
+            d_ms.append(ed[0].elapsed_time(ed[1]))
+            c_ms.append(ed[1].elapsed_time(ed[2]))
+        d_avg, c_avg = float(np.mean(d_ms)), float(np.mean(c_ms))
+        d_flops = 2.0 * T * H * I
+        c_bytes = yd.numel() * 2 + comb.numel() * 2 + ros.numel() * 8
+        out["kernels"].update({"down_proj_ms": round(d_avg, 4), "down_proj_TFLOPs": round(d_flops / (d_avg * 1e-3) / 1e12, 1),
+                               "down_proj_flop": d_flops, "combine_ms": round(c_avg, 4),
+                               "combine_GBps": round(c_bytes / (c_avg * 1e-3) / 1e9, 1), "combine_bytes": c_bytes})
+        del bd, sbd, yd, comb
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, r, x, args.cpu_seconds)
     print(json.dumps(out), flush=True)

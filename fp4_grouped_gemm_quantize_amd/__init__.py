@@ -31,7 +31,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmxg.so")
 
 EXPORTED = ("mx_grouped_quantize", "mx_grouped_quantize_gather", "mx_grouped_matmul", "mx_grouped_matmul_swiglu",
-            "mx_silu_quantize", "mxg_status_string")
+            "mx_silu_quantize", "mx_moe_combine", "mxg_status_string")
 
 
 class MxgError(RuntimeError):
@@ -62,8 +62,9 @@ def lib() -> ctypes.CDLL:
         L.mx_grouped_matmul_swiglu.argtypes = [ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I64,
                                                _I64, _I64, _I64, _P]
         L.mx_silu_quantize.argtypes = [_P, _P, _P, _P, _I32, _I64, _I64, _P]
+        L.mx_moe_combine.argtypes = [_P, _I64, _I64, _P, _P, _I64, _I32, _P, _P]
         for name in ("mx_grouped_quantize", "mx_grouped_quantize_gather", "mx_grouped_matmul",
-                     "mx_grouped_matmul_swiglu", "mx_silu_quantize"):
+                     "mx_grouped_matmul_swiglu", "mx_silu_quantize", "mx_moe_combine"):
             getattr(L, name).restype = ctypes.c_int
         L.mxg_status_string.argtypes = [ctypes.c_int]
         L.mxg_status_string.restype = ctypes.c_char_p
@@ -224,6 +225,26 @@ def mx_silu_quantize(h, y_q, y_scales, row_offsets) -> None:
            "mx_silu_quantize")
 
 
+def mx_moe_combine(y, row_of_slot, weights, out) -> None:
+    """out [tokens, H] bf16 = router-weighted sum over each token's slots of the routed rows
+    y [T, H] bf16; row_of_slot int32 / weights fp32 [tokens * top_k] (top_k from out)."""
+    _expect(y, "y", _BF16)
+    dev = y.device
+    T, H = y.shape
+    _expect(out, "out", _BF16, None, dev)
+    if out.dim() != 2 or out.shape[1] != H:
+        raise ValueError("out must be [num_tokens, H]")
+    ntok = out.shape[0]
+    _expect(row_of_slot, "row_of_slot", _I32T, None, dev)
+    _expect(weights, "weights", _F32, None, dev)
+    if ntok == 0 or row_of_slot.numel() % ntok != 0 or weights.numel() != row_of_slot.numel():
+        if ntok != 0:
+            raise ValueError("row_of_slot and weights must hold num_tokens * top_k entries")
+    top_k = row_of_slot.numel() // ntok if ntok else 1
+    _check(lib().mx_moe_combine(_ptr(y), T, H, _ptr(row_of_slot), _ptr(weights), ntok, top_k, _ptr(out),
+                                _stream(y)), "mx_moe_combine")
+
+
 # ----------------------------------------------------------------------------- allocating forms
 def quantize(fmt: int, x, row_offsets, expert_ids=None):
     """Returns (q, scales); rows no group covers are zero."""
@@ -272,6 +293,12 @@ def silu_quantize(h, row_offsets):
     ys = torch.zeros((T, I // 32), dtype=torch.uint8, device=h.device)
     mx_silu_quantize(h, yq, ys, row_offsets)
     return yq, ys
+
+
+def moe_combine(y, row_of_slot, weights, num_tokens: int):
+    out = torch.empty((num_tokens, y.shape[1]), dtype=torch.bfloat16, device=y.device)
+    mx_moe_combine(y, row_of_slot, weights, out)
+    return out
 
 
 def quantize_weights(fmt: int, w):

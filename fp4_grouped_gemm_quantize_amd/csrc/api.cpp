@@ -66,6 +66,19 @@ mxg_status mx_grouped_quantize_gather(mxg_format fmt, const void* x_bf16, int64_
                                                 row_offsets, num_groups, total_rows, K, stream));
 }
 
+mxg_status mx_moe_combine(const void* y_bf16, int64_t total_rows, int64_t H, const int32_t* row_of_slot,
+                          const float* weights, int64_t num_tokens, int32_t top_k, void* out_bf16,
+                          hipStream_t stream) {
+    if (H <= 0 || total_rows < 0 || num_tokens < 0 || top_k < 1) return MXG_ERROR_INVALID_VALUE;
+    if (H % 8 != 0 || (int64_t)top_k * num_tokens > INT32_MAX) return MXG_ERROR_NOT_SUPPORTED;
+    if (num_tokens == 0) return MXG_SUCCESS;  // nothing is read or written
+    if (!row_of_slot || !weights || !out_bf16 || (total_rows > 0 && !y_bf16)) return MXG_ERROR_INVALID_VALUE;
+    if (!aligned(y_bf16, 16) || !aligned(out_bf16, 16) || !aligned(row_of_slot, 4) || !aligned(weights, 4))
+        return MXG_ERROR_INVALID_VALUE;
+    return from_hip(mxg::launch_combine(y_bf16, total_rows, H, row_of_slot, weights, num_tokens, top_k, out_bf16,
+                                        stream));
+}
+
 static mxg_status check_gemm_common(mxg_format fmt, const void* a_q, const void* a_scales, const void* b_q,
                                     const void* b_scales, const uint32_t* row_offsets, const int32_t* expert_ids,
                                     int32_t num_groups, int32_t num_experts, int64_t total_rows, int64_t N,

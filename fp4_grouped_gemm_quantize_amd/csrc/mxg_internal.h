@@ -14,6 +14,10 @@ hipError_t launch_quantize_gather(int fmt, const void* x, int64_t nsrc, const in
                                   void* q, void* scales, const uint32_t* off, int G, int64_t T, int64_t K,
                                   hipStream_t stream);
 
+// out[t, :] = bf16(sum_k weights[t*top_k + k] * y[row_of_slot[t*top_k + k], :]).
+hipError_t launch_combine(const void* y, int64_t T, int64_t H, const int32_t* row_of_slot, const float* weights,
+                          int64_t ntok, int top_k, void* out, hipStream_t stream);
+
 hipError_t launch_silu_quantize(const void* h, void* yq, void* ys, const uint32_t* off, int G, int64_t T,
                                 int64_t I, hipStream_t stream);
 

@@ -1,7 +1,7 @@
 /*
  * mxg.h -- C ABI of libmxg.so: the ragged MoE expert path on one gfx950 GPU.
  *
- * Five operations, each one asynchronous launch sequence on the caller's HIP
+ * Six operations, each one asynchronous launch sequence on the caller's HIP
  * stream:
  *   mx_grouped_quantize       BF16 activations -> FP8 e4m3 + per-row fp32 scale,
  *                             or MX (32-element blocks, E8M0 scale, e4m3 or e2m1)
@@ -13,6 +13,8 @@
  *                             fused with SwiGLU and an MXFP4 requant
  *   mx_silu_quantize          the unfused second half: SwiGLU + MXFP4 requant of a
  *                             BF16 gate/up tensor
+ *   mx_moe_combine            after the down-projection: each token's row is the
+ *                             router-weighted sum of its routed rows
  *
  * Conventions shared by every entry point
  *   - Every tensor pointer is a DEVICE pointer owned by the caller; the library
@@ -208,6 +210,37 @@ mxg_status mx_grouped_matmul_swiglu(mxg_format fmt, const void* a_q, const void*
  */
 mxg_status mx_silu_quantize(const void* h_bf16, void* y_q, void* y_scales, const uint32_t* row_offsets,
                             int32_t num_groups, int64_t total_rows, int64_t I, hipStream_t stream);
+
+/*
+ * mx_moe_combine -- the MoE combine after the down-projection (itself
+ * mx_grouped_matmul with K = I on the fused output): for every token t,
+ *   out[t, n] = bf16( sum_{k < top_k} weights[t*top_k + k] *
+ *                                     y[row_of_slot[t*top_k + k], n] ).
+ * (grouped_matmul_rowwise_dynamic_scaled_fp8, Parameters:
+ *  elementwise_lambda_fn, the output epilogue at (global_row, n) where the
+ *  weighting and combine attach; NvMxf4f8Strategy, prepare_swiglu_operands(),
+ *  the EP-combine path; Struct_ep_dispatch_mxfp4, src_info.  The pages name
+ *  the combine without defining it; the reading taken is the router-weighted
+ *  sum above, with the token's slots summed in order k = 0, 1, ....)
+ *
+ *   y_bf16       [total_rows, H] bf16 routed rows (the down-projection output).
+ *   row_of_slot  int32 [num_tokens * top_k]: the routed row of slot
+ *                (t, k), or any value outside [0, total_rows) for a slot
+ *                that was dropped (it contributes nothing).
+ *   weights      fp32 [num_tokens * top_k] router weights.
+ *   out_bf16     [num_tokens, H] bf16; every row is written (a token with no
+ *                live slot gets zeros).
+ * The sum is accumulated in fp32 (fused multiply-add per slot) and rounded
+ * once to bf16, nearest-even.  Deterministic: no atomics.
+ *
+ * Errors: INVALID_VALUE for H <= 0, total_rows < 0, num_tokens < 0,
+ * top_k < 1, a null row_of_slot / weights / out_bf16 (or y_bf16 with
+ * total_rows > 0) or misalignment; NOT_SUPPORTED for H % 8 != 0 or
+ * num_tokens * top_k > INT32_MAX.  num_tokens == 0 is a no-op.
+ */
+mxg_status mx_moe_combine(const void* y_bf16, int64_t total_rows, int64_t H, const int32_t* row_of_slot,
+                          const float* weights, int64_t num_tokens, int32_t top_k, void* out_bf16,
+                          hipStream_t stream);
 
 /* Static, human-readable name of a status code. */
 const char* mxg_status_string(mxg_status status);

@@ -85,6 +85,8 @@ def lib() -> ctypes.CDLL:
         L.mxo_quantize.restype = ctypes.c_int
         L.mxo_quantize_gather.argtypes = [ctypes.c_int, _P, _I64, _P, _I32, _P, _P, _P, _I32, _I64, _I64]
         L.mxo_quantize_gather.restype = ctypes.c_int
+        L.mxo_combine.argtypes = [_P, _I64, _I64, _P, _P, _I64, _I32, _P, _P, _P]
+        L.mxo_combine.restype = ctypes.c_int
         L.mxo_gemm_rows.argtypes = [ctypes.c_int, _P, _P, _P, _P, _P, _P, _I32, _I32, _I64, _I64, _I64,
                                     _P, _I64, _P, _P, _P, _P]
         L.mxo_gemm_rows.restype = ctypes.c_int
@@ -223,6 +225,26 @@ def quantize_gather(fmt: int, x_src, indices, divisor: int, offsets, q=None, sca
     if rc != 0:
         raise ValueError("oracle quantize_gather: invalid arguments")
     return q, scales
+
+
+def combine(y_bf16, row_of_slot, weights, num_tokens: int):
+    """MoE combine: out[t] = sum_k weights[t*top_k + k] * y[row_of_slot[t*top_k + k]] over
+    slots whose row lies in [0, T).  Returns dict with ``out`` (bf16 bits [tokens, H]),
+    ``exact`` and ``bound`` (fp64 [tokens, H], bound = sum of |products|)."""
+    y = _c(y_bf16, np.uint16)
+    T, H = y.shape
+    ros = _c(row_of_slot, np.int32)
+    w = _c(weights, np.float32)
+    assert ros.size == w.size and num_tokens > 0 and ros.size % num_tokens == 0
+    top_k = ros.size // num_tokens
+    out = np.zeros((num_tokens, H), np.uint16)
+    exact = np.zeros((num_tokens, H), np.float64)
+    bound = np.zeros((num_tokens, H), np.float64)
+    rc = lib().mxo_combine(_ptr(y), T, H, _ptr(ros), _ptr(w), num_tokens, top_k, _ptr(out), _ptr(exact),
+                           _ptr(bound))
+    if rc != 0:
+        raise ValueError("oracle combine: invalid arguments")
+    return {"out": out, "exact": exact, "bound": bound}
 
 
 # ---------------------------------------------------------------- grouped GEMM

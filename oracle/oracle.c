@@ -488,6 +488,38 @@ void mxo_e4m3_encode_array(const double* v, uint8_t* out, int64_t n) {
 void mxo_e2m1_encode_array(const double* v, uint8_t* out, int64_t n) {
     for (int64_t i = 0; i < n; ++i) out[i] = mxo_e2m1_encode(v[i]);
 }
+/* MoE combine after the down-projection (grouped_matmul_rowwise_dynamic_
+ * scaled_fp8, Parameters: elementwise_lambda_fn -- the output epilogue at
+ * (global_row, n); NvMxf4f8Strategy, the EP-combine path; the pages do not
+ * define the combine, and the reading taken is the router-weighted sum):
+ *   exact[t, n] = sum_k w[t*top_k + k] * y[row_of_slot[t*top_k + k], n]
+ * over the slots whose row lies in [0, T) -- each product of an fp32 weight
+ * and a bf16 value is exact in fp64 --, bound[t, n] = the same sum of
+ * |products|, out = bf16 round-to-nearest-even of exact.  Any of out /
+ * exact / bound may be NULL.                                               */
+int mxo_combine(const uint16_t* y, int64_t T, int64_t H, const int32_t* row_of_slot, const float* w,
+                int64_t ntok, int32_t top_k, uint16_t* out, double* exact, double* bound) {
+    if (H <= 0 || T < 0 || ntok < 0 || top_k < 1 || !row_of_slot || !w) return MXO_EINVAL;
+    if (T > 0 && !y) return MXO_EINVAL;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < ntok; ++t) {
+        for (int64_t n = 0; n < H; ++n) {
+            double e = 0.0, b = 0.0;
+            for (int32_t k = 0; k < top_k; ++k) {
+                const int32_t r = row_of_slot[t * top_k + k];
+                if (r < 0 || (int64_t)r >= T) continue;
+                const double p = (double)w[t * top_k + k] * mxo_bf16_value(y[(int64_t)r * H + n]);
+                e += p;
+                b += fabs(p);
+            }
+            if (out) out[t * H + n] = mxo_bf16_round(e);
+            if (exact) exact[t * H + n] = e;
+            if (bound) bound[t * H + n] = b;
+        }
+    }
+    return MXO_OK;
+}
+
 void mxo_bf16_round_array(const double* v, uint16_t* out, int64_t n) {
     for (int64_t i = 0; i < n; ++i) out[i] = mxo_bf16_round(v[i]);
 }

@@ -87,6 +87,24 @@ def test_quantize_gather_argument_errors():
     assert qg(G=0) == mxg.SUCCESS
 
 
+def cb(y=FAKE, T=8, H=64, ros=FAKE, w=FAKE, ntok=2, k=4, out=FAKE):
+    return mxg.lib().mx_moe_combine(y, T, H, ros, w, ntok, k, out, None)
+
+
+def test_combine_argument_errors():
+    assert cb(ros=None) == mxg.ERROR_INVALID_VALUE
+    assert cb(w=None) == mxg.ERROR_INVALID_VALUE
+    assert cb(out=None) == mxg.ERROR_INVALID_VALUE
+    assert cb(y=None) == mxg.ERROR_INVALID_VALUE
+    assert cb(H=0) == mxg.ERROR_INVALID_VALUE
+    assert cb(k=0) == mxg.ERROR_INVALID_VALUE
+    assert cb(T=-1) == mxg.ERROR_INVALID_VALUE
+    assert cb(ntok=-1) == mxg.ERROR_INVALID_VALUE
+    assert cb(out=FAKE_ODD) == mxg.ERROR_INVALID_VALUE
+    assert cb(H=12) == mxg.ERROR_NOT_SUPPORTED
+    assert cb(ntok=0) == mxg.SUCCESS
+
+
 def mm(fmt=0, a=FAKE, sa=FAKE, b=FAKE, sb=FAKE, c=FAKE, off=FAKE, ids=FAKE, G=1, E=1, T=4, N=32, K=64):
     return mxg.lib().mx_grouped_matmul(fmt, a, sa, b, sb, c, off, ids, G, E, T, N, K, 0, None)
 

@@ -46,6 +46,8 @@ SMALL = {
     # K a multiple of 1024: whole stages, MX scales staged through LDS
     "mxfp8_k1024": W.WORKLOADS[4].scaled(rows=700, E=8, N=288, K=1024),
     "mxfp4_k2048": W.WORKLOADS[5].scaled(tokens=96, E=16, N=320, K=2048, swiglu=False),
+    # the down-projection after the fused SwiGLU: K = I = 2048, N = hidden = 7168
+    "mxfp4_down_proj": W.WORKLOADS[5].scaled(tokens=24, E=8, N=7168, K=2048, swiglu=False),
 }
 
 

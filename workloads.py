@@ -182,6 +182,23 @@ def slot_indices(r: Routing, top_k: int) -> np.ndarray:
     return (tok * top_k + k).astype(np.int32)
 
 
+def rows_of_slots(r: Routing, top_k: int, num_tokens: int) -> np.ndarray:
+    """int32 [num_tokens * top_k]: the routed row of each flat slot (the inverse
+    of slot_indices); -1 for a slot no row took."""
+    ros = np.full(num_tokens * top_k, -1, np.int32)
+    ros[slot_indices(r, top_k)] = np.arange(r.total_rows, dtype=np.int32)
+    return ros
+
+
+def router_weights(w: Workload, num_tokens: int) -> np.ndarray:
+    """fp32 [num_tokens * top_k] router weights: a softmax over top_k seeded
+    N(0, 1) logits per token (a token's weights sum to about 1)."""
+    rng = np.random.default_rng(w.seed + 1000)
+    logits = rng.standard_normal((num_tokens, w.top_k))
+    p = np.exp(logits - logits.max(axis=1, keepdims=True))
+    return (p / p.sum(axis=1, keepdims=True)).astype(np.float32).reshape(-1)
+
+
 def weights(w: Workload, device="cpu", experts=None) -> torch.Tensor:
     """bf16 [E, N, K] weights, N(0, w_std^2), drawn one expert at a time.
 
