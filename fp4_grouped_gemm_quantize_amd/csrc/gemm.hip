@@ -463,41 +463,75 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
             }
         }
 
-        // ---- epilogue
+        // ---- epilogue.  The output tile is staged in LDS as bf16 rows (the
+        // ring is free: the last stage ended at a barrier), spread over the
+        // slots, then written out in coalesced 16-byte pieces -- or, fused,
+        // requantized from there.
+        constexpr int kRowsPerSlot = kStage / (BN * 2);
+        static_assert(kSlots * kRowsPerSlot >= BM, "staging tile must fit the LDS ring");
+        auto srow = [&](int row) -> uint16_t* {
+            uint8_t* base = row < kRowsPerSlot ? s_ring0 : row < 2 * kRowsPerSlot ? s_ring1 : s_ring2;
+            return reinterpret_cast<uint16_t*>(base + (row % kRowsPerSlot) * BN * 2);
+        };
         if constexpr (!SWIGLU) {
+            // out = bf16((acc * a_scale[row]) * b_scale[col]) for FP8 rowwise
+            auto value = [&](int i, int j, int r, float sbv) {
+                float v = acc[i][j][r];
+                if constexpr (!F::kMX) {
+                    const int64_t row = m0 + wm * WTM + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                    v = v * static_cast<const float*>(args.as)[row < m_end ? row : m_end - 1];
+                    v = v * sbv;
+                }
+                return (uint16_t)f32_to_bf16(v);
+            };
+            auto b_scale = [&](int j) {
+                const int64_t col = n0 + wn * WTN + j * 32 + r32;
+                float sbv = 1.0f;
+                if constexpr (!F::kMX)
+                    if (col < args.N) sbv = static_cast<const float*>(args.bs)[(int64_t)e * args.N + col];
+                return sbv;
+            };
+            if ((args.N & 7) == 0) {  // rows of c start on 16 bytes
 #pragma unroll
-            for (int i = 0; i < TM; ++i) {
+                for (int i = 0; i < TM; ++i) {
 #pragma unroll
-                for (int j = 0; j < TN; ++j) {
-                    const int64_t col = n0 + wn * WTN + j * 32 + r32;
-                    float sbv = 1.0f;
-                    if constexpr (!F::kMX)
-                        if (col < args.N) sbv = static_cast<const float*>(args.bs)[(int64_t)e * args.N + col];
+                    for (int j = 0; j < TN; ++j) {
+                        const float sbv = b_scale(j);
+                        const int col = wn * WTN + j * 32 + r32;
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int64_t row = m0 + wm * WTM + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                        if (row < m_end && col < args.N) {
-                            float v = acc[i][j][r];
-                            if constexpr (!F::kMX) {
-                                v = v * static_cast<const float*>(args.as)[row];
-                                v = v * sbv;
-                            }
-                            args.c[row * args.N + col] = (uint16_t)f32_to_bf16(v);
+                        for (int r = 0; r < 16; ++r)
+                            srow(wm * WTM + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3))[col] = value(i, j, r, sbv);
+                    }
+                }
+                __syncthreads();
+                constexpr int kPieces = BN / 8;  // 16-byte pieces per tile row
+#pragma unroll 1
+                for (int q = tid; q < BM * kPieces; q += NT) {
+                    const int row = q / kPieces, pc = q % kPieces;
+                    const int64_t grow = m0 + row, gcol = n0 + pc * 8;
+                    if (grow < m_end && gcol < args.N)
+                        *reinterpret_cast<uint4*>(args.c + grow * args.N + gcol) =
+                            *reinterpret_cast<const uint4*>(srow(row) + pc * 8);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < TM; ++i) {
+#pragma unroll
+                    for (int j = 0; j < TN; ++j) {
+                        const int64_t col = n0 + wn * WTN + j * 32 + r32;
+                        const float sbv = b_scale(j);
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int64_t row = m0 + wm * WTM + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                            if (row < m_end && col < args.N) args.c[row * args.N + col] = value(i, j, r, sbv);
                         }
                     }
                 }
             }
         } else {
-            // Stage the bf16 gate/up tile in LDS (rows spread over the slots),
-            // then requant rows of 32 outputs with the same code the standalone
+            // Requant rows of 32 outputs with the same code the standalone
             // activation kernel runs.
             static_assert(BN % 64 == 0, "fused tile must hold whole 32-output blocks");
-            constexpr int kRowsPerSlot = kStage / (BN * 2);
-            static_assert(kSlots * kRowsPerSlot >= BM, "staging tile must fit the LDS ring");
-            auto srow = [&](int row) -> uint16_t* {
-                uint8_t* base = row < kRowsPerSlot ? s_ring0 : row < 2 * kRowsPerSlot ? s_ring1 : s_ring2;
-                return reinterpret_cast<uint16_t*>(base + (row % kRowsPerSlot) * BN * 2);
-            };
 #pragma unroll
             for (int i = 0; i < TM; ++i) {
 #pragma unroll
