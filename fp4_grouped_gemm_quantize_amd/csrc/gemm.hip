@@ -229,10 +229,12 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
     const bool k_tail = !KA && (row_bytes % kStageBytes) != 0;  // the last stage is partial
     const int64_t nblk = args.K / 32;
 
-    for (int64_t L = xcd_remap(blockIdx.x, gridDim.x); L < total_tiles; L += gridDim.x) {
-        const TileCoord tc = locate_tile<BM, BN>(args, s_pre, L);
+    const WorkSplit ws = work_split(total_tiles, gridDim.x);
+    for (int64_t W = xcd_remap(blockIdx.x, gridDim.x); W < ws.items; W += gridDim.x) {
+        const TileCoord tc = locate_item<BM, BN>(args, s_pre, ws, W);
+        if (tc.cols_in <= 0) continue;  // the empty second half of a last, narrow tile (uniform)
         const int e = tc.e;
-        const int64_t m0 = tc.m0, m_end = tc.m_end, n0 = tc.n0;
+        const int64_t m0 = tc.m0, m_end = tc.m_end, n0 = tc.n0, n_end = tc.n_end;
         const int rows_in = tc.rows_in, cols_in = tc.cols_in;
 
         // ---- operand sources: tile base (uniform) + 32-bit per-lane offsets;
@@ -488,7 +490,7 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
                 const int64_t col = n0 + wn * WTN + j * 32 + r32;
                 float sbv = 1.0f;
                 if constexpr (!F::kMX)
-                    if (col < args.N) sbv = static_cast<const float*>(args.bs)[(int64_t)e * args.N + col];
+                    if (col < n_end) sbv = static_cast<const float*>(args.bs)[(int64_t)e * args.N + col];
                 return sbv;
             };
             if ((args.N & 7) == 0) {  // rows of c start on 16 bytes
@@ -509,7 +511,7 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
                 for (int q = tid; q < BM * kPieces; q += NT) {
                     const int row = q / kPieces, pc = q % kPieces;
                     const int64_t grow = m0 + row, gcol = n0 + pc * 8;
-                    if (grow < m_end && gcol < args.N)
+                    if (grow < m_end && gcol < n_end)
                         *reinterpret_cast<uint4*>(args.c + grow * args.N + gcol) =
                             *reinterpret_cast<const uint4*>(srow(row) + pc * 8);
                 }
@@ -523,7 +525,7 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
 #pragma unroll
                         for (int r = 0; r < 16; ++r) {
                             const int64_t row = m0 + wm * WTM + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                            if (row < m_end && col < args.N) args.c[row * args.N + col] = value(i, j, r, sbv);
+                            if (row < m_end && col < n_end) args.c[row * args.N + col] = value(i, j, r, sbv);
                         }
                     }
                 }
@@ -564,7 +566,7 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
                 const int X = mx_encode8<true>(y, code);
                 const int64_t grow = m0 + row;
                 const int64_t gblk = n0 / 64 + blk;
-                if (grow < m_end && n0 + blk * 64 < args.N)
+                if (grow < m_end && n0 + blk * 64 < n_end)
                     mx_store8<true>(code, X, args.yq + grow * (I / 2), args.ys + grow * (I / 32), gblk * 4 + l4, l4);
             }
         }

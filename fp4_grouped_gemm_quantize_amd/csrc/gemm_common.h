@@ -158,9 +158,29 @@ struct TileCoord {
     int64_t m0;      // first row of the tile
     int64_t m_end;   // one past its last real row
     int64_t n0;      // first column
+    int64_t n_end;   // one past its last real column
     int rows_in;     // real rows (1 .. BM)
-    int cols_in;     // real columns (1 .. BN)
+    int cols_in;     // real columns (0 .. BN; 0: an empty half tile)
 };
+
+// Work items of a persistent launch.  When the tiles leave a last round
+// that is at most half full, each of its R tiles is split into two half
+// tiles along N (columns [n0, n0 + BN/2) and [n0 + BN/2, n0 + BN)): 2R items
+// of about 3/4 of a tile's load time each fill the round better than R
+// whole tiles.
+struct WorkSplit {
+    int64_t full;   // items before the split round (whole tiles)
+    int64_t items;  // all items
+};
+
+__device__ __forceinline__ WorkSplit work_split(int64_t total_tiles, int64_t grid) {
+    const int64_t rem = total_tiles % grid;
+    WorkSplit w;
+    w.full = total_tiles - rem;
+    w.items = (rem > 0 && 2 * rem <= grid) ? w.full + 2 * rem : total_tiles;
+    if (w.items == total_tiles) w.full = total_tiles;
+    return w;
+}
 
 template <int BM, int BN>
 __device__ __forceinline__ TileCoord locate_tile(const GemmArgs& args, const uint32_t* s_pre, int64_t L) {
@@ -183,6 +203,21 @@ __device__ __forceinline__ TileCoord locate_tile(const GemmArgs& args, const uin
     t.n0 = (int64_t)nt * BN;
     t.rows_in = (int)(t.m_end - t.m0);
     t.cols_in = (int)(args.N - t.n0 < BN ? args.N - t.n0 : BN);
+    t.n_end = t.n0 + t.cols_in;
+    return t;
+}
+
+// Item W of a launch split as work_split describes.
+template <int BM, int BN>
+__device__ __forceinline__ TileCoord locate_item(const GemmArgs& args, const uint32_t* s_pre, const WorkSplit& ws,
+                                                 int64_t W) {
+    if (W < ws.full) return locate_tile<BM, BN>(args, s_pre, W);
+    TileCoord t = locate_tile<BM, BN>(args, s_pre, ws.full + (W - ws.full) / 2);
+    const int half = (int)((W - ws.full) % 2);
+    t.n0 += half * (BN / 2);
+    const int64_t left = t.n_end - t.n0;
+    t.cols_in = (int)(left < BN / 2 ? (left > 0 ? left : 0) : BN / 2);
+    t.n_end = t.n0 + t.cols_in;
     return t;
 }
 
