@@ -31,17 +31,21 @@
 //    choosing which global chunk each lane fetches.  A stage that runs past
 //    the end of K (only the last one, when K bytes are not a multiple of 128)
 //    goes through VGPRs so its tail can be zero-filled.
-//  * MX scales: each lane loads the 4 (e4m3) or 8 (e2m1) scale bytes of its
-//    own row for the next stage straight into registers and shifts out the
-//    byte of its block per step; no LDS traffic.
+//  * MX scales: when K is a multiple of 1024 the workgroup stages 32 (or, for
+//    the 256 x 256 tile, 16) scale bytes of each of its rows through two LDS
+//    buffers with direct loads, one chunk per 32 (16) blocks, and each lane
+//    reads its words from there per stage; otherwise each lane loads the 4
+//    (e4m3) or 8 (e2m1) scale bytes of its own row for the next stage into
+//    registers.  Either way the byte of a lane's block is selected per step.
 //  * Ragged groups without host sync: the tile map of gemm_common.h.  Rows
 //    past a group's end (columns past N) re-read the last real one and are
 //    never stored.
 //  * Persistent, XCD-aware schedule: the grid is sized to the resident
 //    capacity; workgroup b (dispatched to XCD b % 8) walks logical tiles so
-//    that the workgroups resident on one XCD hold consecutive tiles (same
-//    expert, neighbouring N tiles), which keeps shared A/B panels in that
-//    XCD's L2.
+//    that the workgroups resident on one XCD hold consecutive tiles, and the
+//    tiles of an expert run in bands of a few M tiles (N outer inside a
+//    band), so the tiles on one XCD at a time form a block that shares A and
+//    weight panels in that XCD's L2.
 #include "gemm_common.h"
 
 namespace mxg {
@@ -198,7 +202,8 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
     // row per 32 blocks instead of a 4-byte load per row, stage and wave.
     constexpr bool kLdsScales = F::kMX && KA;
     constexpr int kSclRows = BM + BN;
-    constexpr int kSclBytes = 32;
+    // 32-byte chunks where both buffers fit beside the ring, else 16
+    constexpr int kSclBytes = TL::kSlots * kStage + 2 * kSclRows * 32 + 8192 <= 160 * 1024 ? 32 : 16;
     constexpr int kSclStages = kSclBytes / F::kBlocks;
     static_assert(!kLdsScales || (TL::kSlots == 2 && BM % 32 == 0 && BN % 32 == 0),
                   "LDS scales: two ring slots, whole 32-row groups");
@@ -575,7 +580,7 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
 }
 
 template <class TL, int FMT, bool SWIGLU, bool KA>
-hipError_t launch_tile(const GemmProblem& p, hipStream_t stream, bool n_outer) {
+hipError_t launch_tile(const GemmProblem& p, hipStream_t stream, int mband) {
     auto kernel = grouped_gemm_kernel<TL, FMT, SWIGLU, KA>;
     static thread_local int occ_device = -1, occ = 0;
     int dev = 0;
@@ -587,23 +592,30 @@ hipError_t launch_tile(const GemmProblem& p, hipStream_t stream, bool n_outer) {
         occ_device = dev;
     }
     int64_t grid = 0;
-    const GemmArgs a = make_args(p, TL::BM, TL::BN, n_outer, occ, &grid);
+    const GemmArgs a = make_args(p, TL::BM, TL::BN, mband, occ, &grid);
     if (grid <= 0) return hipSuccess;
     hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(TL::kThreads), 0, stream, a);
     return hipGetLastError();
 }
 
-// Tile shapes, chosen by measurement on MI355X (ragged workloads of the
-// benchmark): FP8 rowwise with many rows per group -> 256 x 256 with eight
-// waves (fewest operand bytes per FLOP; two ring slots fit 160 KiB of LDS);
-// MX formats -> 128 x 256 with four waves and three slots;
+// Tile shapes and tile orders, chosen by measurement on MI355X (ragged
+// workloads of the benchmark): FP8 rowwise with many rows per group ->
+// 256 x 256 with eight waves (fewest operand bytes per FLOP; two ring slots
+// fit 160 KiB of LDS) in bands of 4 M tiles; MX formats -> 128 x 256 with
+// four waves in bands of 8 M tiles, or, with at least 384 rows per group on
+// average, the eight-wave 256 x 256 tile with 16-byte scale chunks
+// (measured: 5-16 % faster at 512-1024 rows per group for N = 1536 .. 7168;
+// at ~256 rows per group its partial M tiles cost more than it saves);
 // few rows per group (decode-like, weight streaming) -> 32 x 128 tiles, many
 // of them, walked N-outer so the M tiles of an expert share each weight panel
 // in L2.
 using TileLargeFp8 = Tile<256, 256, 2, 4, 2>;
 using TileLargeMx = Tile<128, 256, 2, 2, 3>;
 using TileLargeMxKA = Tile<128, 256, 2, 2, 2>;
+using TileLargeMxKA8 = Tile<256, 256, 2, 4, 2>;
 using TileSmall = Tile<32, 128, 1, 4, 3>;
+constexpr int kBandLarge = 4, kBandMx = 8, kBandNOuter = 1 << 30;
+constexpr int64_t kTallRows = 384;
 
 template <int FMT, bool SWIGLU>
 hipError_t launch_fmt(const GemmProblem& p, hipStream_t stream) {
@@ -616,14 +628,16 @@ hipError_t launch_fmt(const GemmProblem& p, hipStream_t stream) {
     const bool ka = FMT == 0 ? p.K % kStageBytes == 0 : p.K % 1024 == 0;
     if (rows >= 128) {
         if constexpr (FMT == 0) {
-            return ka ? launch_tile<TileLargeFp8, FMT, SWIGLU, true>(p, stream, false)
-                      : launch_tile<TileLargeFp8, FMT, SWIGLU, false>(p, stream, false);
+            return ka ? launch_tile<TileLargeFp8, FMT, SWIGLU, true>(p, stream, kBandLarge)
+                      : launch_tile<TileLargeFp8, FMT, SWIGLU, false>(p, stream, kBandLarge);
         } else {
-            return ka ? launch_tile<TileLargeMxKA, FMT, SWIGLU, true>(p, stream, true)
-                      : launch_tile<TileLargeMx, FMT, SWIGLU, false>(p, stream, true);
+            if (ka && avg_rows >= kTallRows)
+                return launch_tile<TileLargeMxKA8, FMT, SWIGLU, true>(p, stream, kBandLarge);
+            return ka ? launch_tile<TileLargeMxKA, FMT, SWIGLU, true>(p, stream, kBandMx)
+                      : launch_tile<TileLargeMx, FMT, SWIGLU, false>(p, stream, kBandMx);
         }
     }
-    return launch_tile<TileSmall, FMT, SWIGLU, false>(p, stream, true);
+    return launch_tile<TileSmall, FMT, SWIGLU, false>(p, stream, kBandNOuter);
 }
 
 }  // namespace
@@ -643,7 +657,7 @@ int device_cus() {
     return cached_cus;
 }
 
-GemmArgs make_args(const GemmProblem& p, int BM, int BN, bool n_outer, int per_cu, int64_t* grid) {
+GemmArgs make_args(const GemmProblem& p, int BM, int BN, int mband, int per_cu, int64_t* grid) {
     GemmArgs a;
     a.a = static_cast<const uint8_t*>(p.a);
     a.as = p.a_scales;
@@ -661,7 +675,7 @@ GemmArgs make_args(const GemmProblem& p, int BM, int BN, bool n_outer, int per_c
     a.K = p.K;
     a.row_bytes = p.fmt == 2 ? p.K / 2 : p.K;
     a.ntiles_n = (int)((p.N + BN - 1) / BN);
-    a.n_outer = n_outer ? 1 : 0;
+    a.mband = mband > 0 ? mband : 1;
     // Upper bound on M tiles: each non-empty group adds at most one partial tile.
     const int64_t groups_nonempty = p.G < p.T ? p.G : p.T;
     const int64_t mtiles_bound = p.T / BM + groups_nonempty;

@@ -33,7 +33,8 @@ struct GemmArgs {
     int64_t K;
     int64_t row_bytes;  // bytes per row of a and b
     int ntiles_n;
-    int n_outer;        // tile order within a group: 0 = M tiles outer, 1 = N tiles outer
+    int mband;          // tile order within a group: bands of mband M tiles, N walked within a band
+                        // (1: M tiles outer; >= the group's M tiles: N tiles outer)
 };
 
 // FMT: 0 = FP8 rowwise, 1 = MXFP8, 2 = MXFP4.
@@ -124,8 +125,11 @@ typedef void __attribute__((address_space(3)))* lptr_t;
 // Ragged tile map.  Each workgroup turns row_offsets into a prefix over the
 // per-group M-tile counts (in LDS; groups that are empty, inverted or carry an
 // out-of-range expert id own no tiles).  Tile L of the launch is then found by
-// binary search; the N index is taken inner (M-outer order: consecutive tiles
-// share an A panel) or outer (consecutive tiles share a weight panel).
+// binary search.  Within a group the tiles run in bands of mband M tiles
+// with the N index outer inside a band, so the tiles in flight together on
+// one XCD cover about mband M tiles by (tiles per XCD / mband) N tiles and
+// share both A and weight panels in that XCD's L2 (mband = 1: M-outer;
+// mband at least the group's M tiles: N-outer).
 template <int NT, int BM>
 __device__ __forceinline__ void build_tile_prefix(const GemmArgs& args, uint32_t* s_pre, uint32_t* s_wave) {
     constexpr int kPer = (kMaxGroups + NT - 1) / NT;
@@ -193,8 +197,13 @@ __device__ __forceinline__ TileCoord locate_tile(const GemmArgs& args, const uin
     const int g = lo;
     const int mtiles = (int)(s_pre[g + 1] - s_pre[g]);
     const int local = (int)(L - (int64_t)s_pre[g] * ntn);
-    const int mt = args.n_outer ? local % mtiles : local / ntn;
-    const int nt = args.n_outer ? local / mtiles : local % ntn;
+    const int mb = args.mband < mtiles ? args.mband : mtiles;  // mb * ntn <= the group's tiles
+    const int band = local / (mb * ntn);
+    const int r = local - band * mb * ntn;
+    const int left = mtiles - band * mb;
+    const int gm = left < mb ? left : mb;  // M tiles in this band
+    const int mt = band * mb + r % gm;
+    const int nt = r / gm;
     const GroupRange gr = group_range(args.off, args.ids, g, args.T, args.E);
     TileCoord t;
     t.e = args.ids[g];
@@ -228,7 +237,7 @@ int device_cus();
 // Argument block for a BM x BN tiling of problem p; also returns the launch
 // grid (resident capacity `per_cu` x CUs, capped by an upper bound on the
 // tile count).  grid == 0 means there is nothing to do.
-GemmArgs make_args(const GemmProblem& p, int BM, int BN, bool n_outer, int per_cu, int64_t* grid);
+GemmArgs make_args(const GemmProblem& p, int BM, int BN, int mband, int per_cu, int64_t* grid);
 
 }  // namespace gemm
 }  // namespace mxg

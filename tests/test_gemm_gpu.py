@@ -48,6 +48,9 @@ SMALL = {
     "mxfp4_k2048": W.WORKLOADS[5].scaled(tokens=96, E=16, N=320, K=2048, swiglu=False),
     # the down-projection after the fused SwiGLU: K = I = 2048, N = hidden = 7168
     "mxfp4_down_proj": W.WORKLOADS[5].scaled(tokens=24, E=8, N=7168, K=2048, swiglu=False),
+    # 384+ rows per group on average: the MX formats take the eight-wave 256 x 256 tile
+    "mxfp8_tall": W.WORKLOADS[4].scaled(rows=4096, E=8, N=288, K=1024),
+    "mxfp4_tall": W.WORKLOADS[5].scaled(tokens=1024, E=8, masked=1, top_k=4, N=320, K=1024, swiglu=False),
 }
 
 
@@ -91,4 +94,20 @@ def test_gemm_full_size_sampled_rows(widx):
     worst, exact = check_gemm_rows(c[rows], ref, f"workload {widx}")
     print(f"workload {widx}: {rows.size} rows, max |err|/tol = {worst:.3g}, bf16-exact = {exact:.4f}")
     # rows beyond the routed total do not exist here; every row is covered
+    assert not np.any(c == SENT_BF16)
+
+
+@pytest.mark.parametrize("fmt", [W.MXFP8, W.MXFP4])
+def test_gemm_mx_on_prefill_shape_sampled_rows(fmt):
+    """The prefill routing and shape (128 experts, 512 rows per expert on
+    average, K = 4096, N = 1536) in the MX formats: the regime of the
+    eight-wave MX tile, at full size, sampled rows."""
+    w = W.WORKLOADS[3].scaled(fmt=fmt)
+    case = GemmCase(w, gen_device="cuda")
+    c = run_gemm(case, hint=int(case.r.counts.max()))
+    rng = np.random.default_rng(30 + fmt)
+    rows = sample_rows(case.off, rng, per_group_extra=1, extra=32)
+    ref = case.oracle_rows(rows)
+    worst, exact = check_gemm_rows(c[rows], ref, f"prefill shape fmt {fmt}")
+    print(f"prefill shape fmt {fmt}: {rows.size} rows, max |err|/tol = {worst:.3g}, bf16-exact = {exact:.4f}")
     assert not np.any(c == SENT_BF16)

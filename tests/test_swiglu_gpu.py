@@ -67,6 +67,9 @@ FUSED = {
     "small_mxfp4": W.WORKLOADS[5].scaled(tokens=96, E=16, N=256, K=1344),
     "small_mxfp8": W.WORKLOADS[5].scaled(tokens=64, E=8, N=192, K=640, fmt=W.MXFP8),
     "small_mxfp4_k1024": W.WORKLOADS[5].scaled(tokens=96, E=16, N=384, K=1024),
+    # 384+ rows per group on average: the eight-wave 256 x 256 MX tile
+    "tall_mxfp4": W.WORKLOADS[5].scaled(tokens=1024, E=8, masked=1, top_k=4, N=320, K=1024),
+    "tall_mxfp8": W.WORKLOADS[5].scaled(tokens=1024, E=8, masked=1, top_k=4, N=256, K=1024, fmt=W.MXFP8),
 }
 
 
