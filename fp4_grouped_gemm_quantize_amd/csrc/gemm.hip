@@ -243,29 +243,36 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
         const int rows_in = tc.rows_in, cols_in = tc.cols_in;
 
         // ---- operand sources: tile base (uniform) + 32-bit per-lane offsets;
-        // each load instruction covers 8 rows x 8 chunks (1 KiB of the slot).
-        // Rows past the group / columns past N re-read the last real one.
+        // load j of a wave covers rows r0 + 8 NW j .. +7 x 8 chunks (1 KiB of
+        // the slot).  Rows past the group / columns past N re-read the last
+        // real one.  With an even wave count the swizzled chunk of a lane is
+        // the same for every j.  The offsets are held in registers (one per
+        // load) through the K loop, except in the eight-wave MX kernel, which
+        // runs out of registers (spills in the K loop stall it on the
+        // prefetch): there they are recomputed per stage from two registers.
+        static_assert(NW % 2 == 0, "per-lane chunk independent of the load index");
+        constexpr bool kLeanOffsets = F::kMX && NW >= 8;
         const uint8_t* a_base = args.a + m0 * row_bytes;
         const uint8_t* b_base = args.b + ((int64_t)e * args.N + n0) * row_bytes;
+        const int r0 = wave * 8 + (lane >> 3);
+        const uint32_t chunk16 = (uint32_t)swz_chunk(r0, lane & 7) << 4;
+        const uint32_t rb32 = (uint32_t)row_bytes;
+        auto op_off = [&](int rbase, int j, int live) {
+            const int r = rbase + 8 * NW * j;
+            return (uint32_t)(r < live ? r : live - 1) * rb32 + chunk16;
+        };
         uint32_t a_off[A_J], b_off[B_J];
-        {
-            const int rr = lane >> 3, pc = lane & 7;
+        if constexpr (!kLeanOffsets) {
 #pragma unroll
-            for (int j = 0; j < A_J; ++j) {
-                const int r = (wave + NW * j) * 8 + rr;
-                const int rc = r < rows_in ? r : rows_in - 1;
-                a_off[j] = (uint32_t)(rc * row_bytes) + (swz_chunk(r, pc) << 4);
-            }
+            for (int j = 0; j < A_J; ++j) a_off[j] = op_off(r0, j, rows_in);
 #pragma unroll
-            for (int j = 0; j < B_J; ++j) {
-                const int r = (wave + NW * j) * 8 + rr;
-                const int rc = r < cols_in ? r : cols_in - 1;
-                b_off[j] = (uint32_t)(rc * row_bytes) + (swz_chunk(r, pc) << 4);
-            }
+            for (int j = 0; j < B_J; ++j) b_off[j] = op_off(r0, j, cols_in);
         }
-        // An offset passes through an empty asm statement where it is used,
-        // so the compiler keeps it a 32-bit offset to a uniform base instead
-        // of hoisting a 64-bit per-lane address out of the K loop.
+        // Offsets (or, lean, the row base) pass through an empty asm
+        // statement in each stage, so the compiler does not hoist 64-bit
+        // per-lane addresses out of the K loop (nor, lean, keep every offset
+        // live through it); addresses stay a uniform base plus a 32-bit
+        // offset.
         auto opaque = [](uint32_t v) {
             __asm__ volatile("" : "+v"(v));
             return v;
@@ -273,14 +280,17 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
         auto issue_stage = [&](int kt, uint8_t* slot) {
             const uint8_t* ak = a_base + (int64_t)kt * kStageBytes;
             const uint8_t* bk = b_base + (int64_t)kt * kStageBytes;
+            const int rb = kLeanOffsets ? (int)opaque((uint32_t)r0) : r0;
 #pragma unroll
             for (int j = 0; j < A_J; ++j)
-                __builtin_amdgcn_global_load_lds((gptr_t)(ak + opaque(a_off[j])),
-                                                 (lptr_t)(slot + (wave + NW * j) * 1024), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(
+                    (gptr_t)(ak + (kLeanOffsets ? op_off(rb, j, rows_in) : opaque(a_off[j]))),
+                    (lptr_t)(slot + (wave + NW * j) * 1024), 16, 0, 0);
 #pragma unroll
             for (int j = 0; j < B_J; ++j)
-                __builtin_amdgcn_global_load_lds((gptr_t)(bk + opaque(b_off[j])),
-                                                 (lptr_t)(slot + kAStage + (wave + NW * j) * 1024), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(
+                    (gptr_t)(bk + (kLeanOffsets ? op_off(rb, j, cols_in) : opaque(b_off[j]))),
+                    (lptr_t)(slot + kAStage + (wave + NW * j) * 1024), 16, 0, 0);
         };
         // The partial last stage: VGPR loads with the K tail zero-filled.
         uint4 ta[A_J], tb[B_J];
@@ -291,13 +301,13 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
             for (int j = 0; j < A_J; ++j) {
                 const int r = (wave + NW * j) * 8 + (lane >> 3);
                 const bool in = kb + swz_chunk(r, c_lo) * 16 < row_bytes;
-                ta[j] = in ? *reinterpret_cast<const uint4*>(a_base + kb + a_off[j]) : make_uint4(0, 0, 0, 0);
+                ta[j] = in ? *reinterpret_cast<const uint4*>(a_base + kb + op_off(r0, j, rows_in)) : make_uint4(0, 0, 0, 0);
             }
 #pragma unroll
             for (int j = 0; j < B_J; ++j) {
                 const int r = (wave + NW * j) * 8 + (lane >> 3);
                 const bool in = kb + swz_chunk(r, c_lo) * 16 < row_bytes;
-                tb[j] = in ? *reinterpret_cast<const uint4*>(b_base + kb + b_off[j]) : make_uint4(0, 0, 0, 0);
+                tb[j] = in ? *reinterpret_cast<const uint4*>(b_base + kb + op_off(r0, j, cols_in)) : make_uint4(0, 0, 0, 0);
             }
         };
         auto store_tail = [&](uint8_t* slot) {
