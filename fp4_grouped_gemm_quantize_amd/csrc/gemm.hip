@@ -241,6 +241,10 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
         const int e = tc.e;
         const int64_t m0 = tc.m0, m_end = tc.m_end, n0 = tc.n0, n_end = tc.n_end;
         const int rows_in = tc.rows_in, cols_in = tc.cols_in;
+        // A wave whose sub-tile lies wholly past the group's last row or past
+        // the last column (partial M tiles, half tiles of a split round)
+        // skips its matrix-core work; the loads stay shared.
+        const bool wave_live = wm * WTM < rows_in && wn * WTN < cols_in;  // wave-uniform
 
         // ---- operand sources: tile base (uniform) + 32-bit per-lane offsets;
         // load j of a wave covers rows r0 + 8 NW j .. +7 x 8 chunks (1 KiB of
@@ -425,7 +429,7 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
                 if (pf_tail) load_tail(kt + D);
                 else issue_stage(kt + D, pf);
             }
-            mma_stage<TL, FMT>(cur, cur + kAStage, wm, wn, h, r32, wa, wb, acc);
+            if (wave_live) mma_stage<TL, FMT>(cur, cur + kAStage, wm, wn, h, r32, wa, wb, acc);
             if (pf_tail) store_tail(pf);
             if constexpr (F::kMX)
                 if (kt + 1 < nkt) {
@@ -451,10 +455,10 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
                              int pos) {
             const bool pf_on = kt + 1 < nkt;
             uint32_t xa[TM][kWords], xb[TN][kWords];
-            read_scales(scur, pos, xa, xb);
+            if (wave_live) read_scales(scur, pos, xa, xb);
             if (pf_on) issue_stage(kt + 1, pf);
             if (pos == kSclStages - 1 && pf_on) issue_scales((kt + 1) / kSclStages, snext);
-            mma_stage<TL, FMT>(cur, cur + kAStage, wm, wn, h, r32, xa, xb, acc);
+            if (wave_live) mma_stage<TL, FMT>(cur, cur + kAStage, wm, wn, h, r32, xa, xb, acc);
             stage_barrier<0>();
         };
         if constexpr (kLdsScales) {
