@@ -16,6 +16,10 @@ Pages followed (cited by title and section):
   * NvMxf4f8Strategy -- grouped_quantize(), quantize(), grouped_matmul(),
     fused_silu_quantize(), grouped_matmul_swiglu().
   * Struct_ep_dispatch_mxfp4 -- execute (E8M0 activation scales, K_SCALES).
+  * NvMxf4f8Strategy -- is_nvfp4, grouped_quantize(input_scale),
+    grouped_matmul(expert_scales); the quantize kernel's sf_tensor: NVFP4
+    (16-element blocks, E4M3 block scales, per-expert tensor scale; the
+    readings are stated in oracle.c).
 """
 from __future__ import annotations
 
@@ -95,6 +99,11 @@ def lib() -> ctypes.CDLL:
         L.mxo_gemm_swiglu_rows.argtypes = [ctypes.c_int, _P, _P, _P, _P, _P, _P, _I32, _I32, _I64, _I64,
                                            _I64, _P, _I64, _P, _P, _P, _P, _P]
         L.mxo_gemm_swiglu_rows.restype = ctypes.c_int
+        L.mxo_quantize_nvfp4.argtypes = [_P, _P, _P, _P, _P, _P, _I32, _I32, _I64, _I64]
+        L.mxo_quantize_nvfp4.restype = ctypes.c_int
+        L.mxo_gemm_rows_nvfp4.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I64, _I64, _I64, _P, _I64,
+                                          _P, _P, _P, _P]
+        L.mxo_gemm_rows_nvfp4.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -327,3 +336,57 @@ def gemm_swiglu_rows(fmt: int, a, a_scale, w, w_scale, offsets, expert_ids, I: i
     if rc != 0:
         raise ValueError("oracle gemm_swiglu: invalid arguments")
     return {"yq": yq, "ys": ys, "gu_exact": gu_exact, "gu_bound": gu_bound, "group": group}
+
+
+# ---------------------------------------------------------------- NVFP4
+NVFP4 = 3
+
+
+def quantize_nvfp4(x_bf16, offsets, expert_ids, tensor_scales, q=None, scales=None):
+    """NVFP4 grouped quantize of bf16 bits ``x_bf16`` [T, K]: rows of group g use
+    tensor_scales[expert_ids[g]] (fp32 [E], the encode-side tensor scale).
+    Returns (q u8 [T, K/2], scales u8 E4M3 [T, K/16]); uncovered rows keep the
+    passed contents (zero-filled when not passed)."""
+    x = _c(x_bf16, np.uint16)
+    T, K = x.shape
+    off = _c(offsets, np.uint32)
+    ids = _c(expert_ids, np.int32)
+    sf = _c(tensor_scales, np.float32).ravel()
+    if q is None:
+        q = np.zeros((T, K // 2), np.uint8)
+    if scales is None:
+        scales = np.zeros((T, K // 16), np.uint8)
+    assert q.shape == (T, K // 2) and scales.shape == (T, K // 16)
+    rc = lib().mxo_quantize_nvfp4(_ptr(x), _ptr(q), _ptr(scales), _ptr(sf), _ptr(off), _ptr(ids), off.size - 1,
+                                  sf.size, T, K)
+    if rc != 0:
+        raise ValueError("oracle quantize_nvfp4: invalid arguments")
+    return q, scales
+
+
+def gemm_rows_nvfp4(a, a_scale, b, b_scale, expert_scales, offsets, expert_ids, N: int, K: int, rows,
+                    want_exact: bool = True):
+    """NVFP4 grouped GEMM output rows ``rows``: a u8 [T, K/2], a_scale u8 [T, K/16],
+    b u8 [E, N, K/2], b_scale u8 [E, N, K/16], expert_scales fp32 [E].  Same
+    return dict as gemm_rows."""
+    a = _c(a, np.uint8)
+    b = _c(b, np.uint8)
+    a_scale = _c(a_scale, np.uint8)
+    b_scale = _c(b_scale, np.uint8)
+    es = _c(expert_scales, np.float32).ravel()
+    T = a.shape[0]
+    E = b.shape[0]
+    off = _c(offsets, np.uint32)
+    ids = _c(expert_ids, np.int32)
+    r = _c(rows, np.int64).ravel()
+    n = r.size
+    out = np.zeros((n, N), np.uint16)
+    exact = np.zeros((n, N), np.float64) if want_exact else None
+    bound = np.zeros((n, N), np.float64) if want_exact else None
+    group = np.zeros((n,), np.int32)
+    rc = lib().mxo_gemm_rows_nvfp4(_ptr(a), _ptr(a_scale), _ptr(b), _ptr(b_scale), _ptr(es), _ptr(off), _ptr(ids),
+                                   off.size - 1, E, T, N, K, _ptr(r), n, _ptr(out), _ptr(exact), _ptr(bound),
+                                   _ptr(group))
+    if rc != 0:
+        raise ValueError("oracle gemm_nvfp4: invalid arguments")
+    return {"out": out, "exact": exact, "bound": bound, "group": group}

@@ -19,6 +19,9 @@
  *     grouped_matmul_swiglu(): the same two steps fused, byte-identical.
  *   - Struct_ep_dispatch_mxfp4, execute: MX activation scales are E8M0 and one
  *     scale covers a K block (K_SCALES per row).
+ *   - NvMxf4f8Strategy, is_nvfp4 / grouped_quantize(input_scale) /
+ *     grouped_matmul(expert_scales) and the kernel's sf_tensor: the NVFP4
+ *     variant (readings at its functions below).
  *   - Element and scale encodings follow the public OCP 8-bit floating point
  *     (OFP8, "E4M3" with no infinities) and OCP Microscaling v1.0 (E2M1, E8M0,
  *     32-element blocks, shared exponent = floor(log2 amax) - emax_elem)
@@ -478,6 +481,109 @@ int mxo_gemm_swiglu_rows(int fmt, const uint8_t* a, const uint8_t* a_scale, cons
     free(grp);
     free(h);
     return rc;
+}
+
+/* ------------------------------------------------------------------------- */
+/* NVFP4 (NvMxf4f8Strategy: is_nvfp4, grouped_quantize(input_scale),
+ * grouped_matmul(expert_scales); grouped_quantize_dynamic_scaled_fp4_async_
+ * kernel, Args: sf_tensor, the per-expert tensor-wise scale factor).  The pages
+ * name the format and its scales but state no arithmetic; the readings taken
+ * (listed with the design notes):
+ *   - elements are E2M1 as in MXFP4, in blocks of 16 along K, each block with
+ *     an E4M3 scale code;
+ *   - sf, per expert, is the encode-side tensor scale: with amax the block's
+ *     largest |x|, the block scale is s = e4m3(min(fl32(fl32(amax / 6) * sf),
+ *     448)) and an element is e2m1(fl32(x * r)) with r = fl32(sf / s) (r = 0
+ *     when s decodes to 0); so x ~ e2m1 * s / sf;
+ *   - the grouped GEMM returns expert_scale[e] * sum_b sa[t,b] sb[e,n,b]
+ *     sum_{k in b} qa[t,k] qb[e,n,k], expert_scale per expert (the epilogue
+ *     factor, typically 1 / (sf_a * sf_b)).
+ * Every fl32 step is one IEEE binary32 operation, round to nearest even.    */
+static void quantize_row_nvfp4(const uint16_t* x, int64_t K, float sf, uint8_t* q, uint8_t* s) {
+    for (int64_t b = 0; b < K / 16; ++b) {
+        float amax = 0.0f;
+        for (int i = 0; i < 16; ++i) {
+            float a = fabsf((float)mxo_bf16_value(x[b * 16 + i]));
+            if (a > amax) amax = a;
+        }
+        volatile float t = amax / 6.0f;
+        volatile float u = t * sf;
+        float uc = (u < 448.0f) ? u : 448.0f;
+        uint8_t code = mxo_e4m3_encode((double)uc);
+        s[b] = code;
+        double sv = mxo_e4m3_value(code);
+        volatile float r = 0.0f;
+        if (sv != 0.0) r = sf / (float)sv;
+        uint8_t c[16];
+        for (int i = 0; i < 16; ++i) {
+            volatile float v = (float)mxo_bf16_value(x[b * 16 + i]) * r;
+            c[i] = mxo_e2m1_encode((double)v);
+        }
+        for (int i = 0; i < 8; ++i) q[b * 8 + i] = (uint8_t)(c[2 * i] | (c[2 * i + 1] << 4));
+    }
+}
+
+/* Rows of group g use sf[expert_ids[g]]; a group whose expert id lies outside
+ * [0, E) or whose start exceeds its end is skipped; uncovered rows are left
+ * as they were.  q u8 [T, K/2], scales u8 E4M3 [T, K/16].                    */
+int mxo_quantize_nvfp4(const uint16_t* x, uint8_t* q, uint8_t* scales, const float* sf, const uint32_t* off,
+                       const int32_t* ids, int32_t G, int32_t E, int64_t T, int64_t K) {
+    if (!x || !q || !scales || !sf || !off || !ids || G < 0 || E <= 0 || T < 0 || K <= 0 || (K % 16) != 0)
+        return MXO_EINVAL;
+    for (int32_t g = 0; g < G; ++g) {
+        int64_t lo, hi;
+        group_range(off, g, T, &lo, &hi);
+        if (lo > hi || ids[g] < 0 || ids[g] >= E) continue;
+        const float f = sf[ids[g]];
+#pragma omp parallel for schedule(dynamic, 16)
+        for (int64_t t = lo; t < hi; ++t) quantize_row_nvfp4(x + t * K, K, f, q + t * (K / 2), scales + t * (K / 16));
+    }
+    return MXO_OK;
+}
+
+/* Grouped GEMM rows, NVFP4 operands (same outputs as mxo_gemm_rows).
+ * a u8 [T, K/2], a_scale u8 E4M3 [T, K/16]; b u8 [E, N, K/2], b_scale u8
+ * [E, N, K/16]; expert_scale fp32 [E].                                      */
+int mxo_gemm_rows_nvfp4(const uint8_t* a, const uint8_t* a_scale, const uint8_t* b, const uint8_t* b_scale,
+                        const float* expert_scale, const uint32_t* off, const int32_t* ids, int32_t G, int32_t E,
+                        int64_t T, int64_t N, int64_t K, const int64_t* rows, int64_t nrows, uint16_t* out,
+                        double* exact, double* bound, int32_t* group) {
+    if (!a || !a_scale || !b || !b_scale || !expert_scale || !off || !ids || !rows) return MXO_EINVAL;
+    if (G < 0 || E <= 0 || T < 0 || N <= 0 || K <= 0 || (K % 16) != 0) return MXO_EINVAL;
+    const int64_t row_bytes = K / 2, nblk = K / 16;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < nrows; ++i) {
+        int64_t t = rows[i];
+        int32_t g = (t >= 0 && t < T) ? group_of_row(off, ids, G, E, T, t) : -1;
+        if (group) group[i] = g;
+        if (g < 0) continue;
+        int32_t e = ids[g];
+        const uint8_t* arow = a + t * row_bytes;
+        const uint8_t* sa = a_scale + t * nblk;
+        const double es = (double)expert_scale[e];
+        for (int64_t n = 0; n < N; ++n) {
+            const uint8_t* brow = b + ((int64_t)e * N + n) * row_bytes;
+            const uint8_t* sb = b_scale + ((int64_t)e * N + n) * nblk;
+            double acc = 0.0, mag = 0.0;
+            for (int64_t blk = 0; blk < nblk; ++blk) {
+                double part = 0.0, pmag = 0.0;
+                for (int64_t k = blk * 16; k < blk * 16 + 16; ++k) {
+                    double p = dec_elem(MXO_E2M1, arow, k) * dec_elem(MXO_E2M1, brow, k);
+                    part += p;
+                    pmag += fabs(p);
+                }
+                double sc = mxo_e4m3_value(sa[blk]) * mxo_e4m3_value(sb[blk]);
+                acc += part * sc;
+                mag += pmag * fabs(sc);
+            }
+            acc *= es;
+            mag *= fabs(es);
+            if (exact) exact[i * N + n] = acc;
+            if (bound) bound[i * N + n] = mag;
+            if (out) out[i * N + n] = mxo_bf16_round(acc);
+        }
+    }
+    return MXO_OK;
 }
 
 /* ------------------------------------------------------------------------- */
