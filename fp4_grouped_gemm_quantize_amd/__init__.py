@@ -31,7 +31,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmxg.so")
 
 EXPORTED = ("mx_grouped_quantize", "mx_grouped_quantize_gather", "mx_grouped_matmul", "mx_grouped_matmul_swiglu",
-            "mx_silu_quantize", "mx_moe_combine", "mxg_status_string")
+            "mx_silu_quantize", "mx_moe_combine", "mx_grouped_quantize_nvfp4", "mxg_status_string")
 
 
 class MxgError(RuntimeError):
@@ -63,8 +63,9 @@ def lib() -> ctypes.CDLL:
                                                _I64, _I64, _I64, _P]
         L.mx_silu_quantize.argtypes = [_P, _P, _P, _P, _I32, _I64, _I64, _P]
         L.mx_moe_combine.argtypes = [_P, _I64, _I64, _P, _P, _I64, _I32, _P, _P]
+        L.mx_grouped_quantize_nvfp4.argtypes = [_P, _P, _P, _P, _P, _P, _I32, _I32, _I64, _I64, _P]
         for name in ("mx_grouped_quantize", "mx_grouped_quantize_gather", "mx_grouped_matmul",
-                     "mx_grouped_matmul_swiglu", "mx_silu_quantize", "mx_moe_combine"):
+                     "mx_grouped_matmul_swiglu", "mx_silu_quantize", "mx_moe_combine", "mx_grouped_quantize_nvfp4"):
             getattr(L, name).restype = ctypes.c_int
         L.mxg_status_string.argtypes = [ctypes.c_int]
         L.mxg_status_string.restype = ctypes.c_char_p
@@ -160,6 +161,25 @@ def mx_grouped_quantize_gather(fmt: int, x_src, indices, indices_divisor: int, q
     _check(lib().mx_grouped_quantize_gather(fmt, _ptr(x_src), S, _ptr(indices), int(indices_divisor), _ptr(q),
                                             _ptr(scales), _ptr(row_offsets), _ptr(expert_ids), G, T, K,
                                             _stream(x_src)), "mx_grouped_quantize_gather")
+
+
+def mx_grouped_quantize_nvfp4(x, q, scales, tensor_scales, row_offsets, expert_ids) -> None:
+    """NVFP4 grouped quantize of bf16 x [T, K] into q u8 [T, K/2] and E4M3 scales u8
+    [T, K/16]; the rows of group g use tensor_scales[expert_ids[g]] (fp32 [E])."""
+    _expect(x, "x", _BF16)
+    if x.dim() != 2:
+        raise ValueError("x must be [total_rows, K]")
+    T, K = x.shape
+    dev = x.device
+    _expect(q, "q", _U8, (T, K // 2), dev)
+    _expect(scales, "scales", _U8, (T, K // 16), dev)
+    _expect(tensor_scales, "tensor_scales", _F32, None, dev)
+    _expect(row_offsets, "row_offsets", _U32, None, dev)
+    G = row_offsets.numel() - 1
+    _expect(expert_ids, "expert_ids", _I32T, (G,), dev)
+    _check(lib().mx_grouped_quantize_nvfp4(_ptr(x), _ptr(q), _ptr(scales), _ptr(tensor_scales), _ptr(row_offsets),
+                                           _ptr(expert_ids), G, tensor_scales.numel(), T, K, _stream(x)),
+           "mx_grouped_quantize_nvfp4")
 
 
 def mx_grouped_matmul(fmt: int, a_q, a_scales, b_q, b_scales, c, row_offsets, expert_ids,
@@ -310,3 +330,20 @@ def quantize_weights(fmt: int, w):
     if fmt == FP8_ROWWISE:
         return q.reshape(E, N, -1), s.reshape(E, N)
     return q.reshape(E, N, -1), s.reshape(E, N, K // 32)
+
+
+def quantize_nvfp4(x, row_offsets, expert_ids, tensor_scales):
+    T, K = x.shape
+    q = torch.zeros((T, K // 2), dtype=torch.uint8, device=x.device)
+    s = torch.zeros((T, K // 16), dtype=torch.uint8, device=x.device)
+    mx_grouped_quantize_nvfp4(x, q, s, tensor_scales, row_offsets, expert_ids)
+    return q, s
+
+
+def quantize_weights_nvfp4(w, tensor_scales):
+    """NVFP4 weights [E, N, K]: one group of N rows per expert under tensor_scales[e]."""
+    E, N, K = w.shape
+    off = torch.arange(0, (E + 1) * N, N, dtype=torch.int32, device=w.device)
+    ids = torch.arange(E, dtype=torch.int32, device=w.device)
+    q, s = quantize_nvfp4(w.reshape(E * N, K), off, ids, tensor_scales)
+    return q.reshape(E, N, K // 2), s.reshape(E, N, K // 16)

@@ -66,6 +66,20 @@ mxg_status mx_grouped_quantize_gather(mxg_format fmt, const void* x_bf16, int64_
                                                 row_offsets, num_groups, total_rows, K, stream));
 }
 
+mxg_status mx_grouped_quantize_nvfp4(const void* x_bf16, void* q, void* scales, const float* tensor_scales,
+                                     const uint32_t* row_offsets, const int32_t* expert_ids, int32_t num_groups,
+                                     int32_t num_experts, int64_t total_rows, int64_t K, hipStream_t stream) {
+    if (K <= 0 || total_rows < 0 || num_groups < 0 || num_experts <= 0) return MXG_ERROR_INVALID_VALUE;
+    if (K % 16 != 0 || num_groups > MXG_MAX_GROUPS) return MXG_ERROR_NOT_SUPPORTED;
+    if (total_rows == 0 || num_groups == 0) return MXG_SUCCESS;  // nothing is read or written
+    if (!x_bf16 || !q || !scales || !tensor_scales || !row_offsets || !expert_ids) return MXG_ERROR_INVALID_VALUE;
+    if (!aligned(x_bf16, 16) || !aligned(q, 16) || !aligned(tensor_scales, 4) || !aligned(row_offsets, 4) ||
+        !aligned(expert_ids, 4))
+        return MXG_ERROR_INVALID_VALUE;
+    return from_hip(mxg::launch_quantize_nvfp4(x_bf16, q, scales, tensor_scales, row_offsets, expert_ids, num_groups,
+                                               num_experts, total_rows, K, stream));
+}
+
 mxg_status mx_moe_combine(const void* y_bf16, int64_t total_rows, int64_t H, const int32_t* row_of_slot,
                           const float* weights, int64_t num_tokens, int32_t top_k, void* out_bf16,
                           hipStream_t stream) {

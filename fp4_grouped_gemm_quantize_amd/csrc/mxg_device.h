@@ -188,4 +188,52 @@ __device__ __forceinline__ void mx_store8(const uint2& packed, int X, uint8_t* q
     if ((lane & 3) == 0) srow[idx >> 2] = (uint8_t)(X + 127);
 }
 
+// ---------------------------------------------------------------------------
+// NVFP4: 2 lanes x 8 elements form one 16-element block.  With sf the
+// group's encode-side tensor scale: block scale code = e4m3(min(fl32(
+// fl32(amax / 6) * sf), 448)), element code = e2m1(fl32(x * r)), r =
+// fl32(sf / s) with s the scale code's value (r = 0 when s is 0).  Each step
+// is one IEEE binary32 operation; the e4m3 code comes from the convert above
+// (exact up to 448) and its value from the exact fp8 -> fp32 convert.
+// Returns the lane's 8 packed codes; every lane of the pair must call it.
+__device__ __forceinline__ uint32_t nv_encode8(const float* f, float sf, uint32_t& scode) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
+    const float t = amax / 6.0f;
+    const float u = t * sf;
+    const float uc = u < 448.0f ? u : 448.0f;
+    scode = __builtin_amdgcn_cvt_pk_fp8_f32(uc, 0.0f, 0u, false) & 0xffu;
+    const float s = __builtin_amdgcn_cvt_f32_fp8((int)scode, 0);
+    const float r = s == 0.0f ? 0.0f : sf / s;
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = f[i] * r;
+    return pack8_e2m1(v);
+}
+
+// The group covering row t whose expert id lies in [0, E) (the lowest such
+// group), or -1.  Wave-cooperative, result wave-uniform; offsets from LDS.
+__device__ __forceinline__ int wave_row_group(const uint32_t* s_off, const int32_t* ids, int G, int E, int64_t T,
+                                              int64_t t) {
+    const int lane = threadIdx.x & (kWave - 1);
+    for (int g0 = 0; g0 < G; g0 += kWave) {
+        const int g = g0 + lane;
+        bool hit = false;
+        if (g < G) {
+            int64_t lo = (int64_t)s_off[g], hi = (int64_t)s_off[g + 1];
+            lo = lo < T ? lo : T;
+            hi = hi < T ? hi : T;
+            if (t >= lo && t < hi) {
+                const int e = ids[g];
+                hit = e >= 0 && e < E;
+            }
+        }
+        const uint64_t m = __ballot(hit);
+        if (m) return g0 + __builtin_ctzll(m);
+    }
+    return -1;
+}
+
 }  // namespace mxg

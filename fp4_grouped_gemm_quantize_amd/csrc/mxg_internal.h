@@ -14,6 +14,11 @@ hipError_t launch_quantize_gather(int fmt, const void* x, int64_t nsrc, const in
                                   void* q, void* scales, const uint32_t* off, int G, int64_t T, int64_t K,
                                   hipStream_t stream);
 
+// NVFP4: rows of group g use tensor_scales[ids[g]]; groups with an id outside [0, E) are skipped.
+hipError_t launch_quantize_nvfp4(const void* x, void* q, void* scales, const float* tensor_scales,
+                                  const uint32_t* off, const int32_t* ids, int G, int E, int64_t T, int64_t K,
+                                  hipStream_t stream);
+
 // out[t, :] = bf16(sum_k weights[t*top_k + k] * y[row_of_slot[t*top_k + k], :]).
 hipError_t launch_combine(const void* y, int64_t T, int64_t H, const int32_t* row_of_slot, const float* weights,
                           int64_t ntok, int top_k, void* out, hipStream_t stream);

@@ -46,6 +46,14 @@ struct Gather {
     int64_t nsrc;
 };
 
+// NVFP4 (format 3): the rows of group g use tensor scale sf[ids[g]]; a group
+// whose expert id lies outside [0, E) is skipped.
+struct NvScales {
+    const int32_t* ids;
+    const float* sf;
+    int E;
+};
+
 template <bool GATHER>
 __device__ __forceinline__ int64_t source_row(const Gather& g, int64_t t) {
     if constexpr (!GATHER) {
@@ -61,12 +69,12 @@ __device__ __forceinline__ int64_t source_row(const Gather& g, int64_t t) {
 // ---------------------------------------------------------------------------
 // FP8 rowwise and MX, rows of K <= NC * 512 held in registers.
 // FMT: 0 = FP8 rowwise (scale = amax / 448, code = e4m3(x / scale)),
-//      1 = MXFP8, 2 = MXFP4.
+//      1 = MXFP8, 2 = MXFP4, 3 = NVFP4.
 template <int FMT, int NC, bool GATHER>
 __global__ __launch_bounds__(kThreads) void quantize_rows_kernel(const uint16_t* __restrict__ x,
                                                                  uint8_t* __restrict__ q, void* __restrict__ scales,
                                                                  const uint32_t* __restrict__ off, int G,
-                                                                 int64_t T, int64_t K, Gather ga) {
+                                                                 int64_t T, int64_t K, Gather ga, NvScales nv) {
     __shared__ uint32_t s_off[kMaxGroups + 1];
     load_offsets(s_off, off, G);
     const int lane = threadIdx.x & (kWave - 1);
@@ -92,7 +100,27 @@ __global__ __launch_bounds__(kThreads) void quantize_rows_kernel(const uint16_t*
         const int64_t tn = t + nw;
         const int64_t srn = tn < T ? source_row<GATHER>(ga, tn) : -1;
         load_row(srn, vn);
-        if (sr >= 0 && wave_row_covered(s_off, G, T, t)) {
+        if constexpr (FMT == 3) {
+            const int g = sr >= 0 ? wave_row_group(s_off, nv.ids, G, nv.E, T, t) : -1;
+            if (g >= 0) {
+                const float sf = nv.sf[nv.ids[g]];
+                uint8_t* qrow = q + t * (K / 2);
+                uint8_t* srow = static_cast<uint8_t*>(scales) + t * (K / 16);
+#pragma unroll
+                for (int c = 0; c < NC; ++c) {
+                    const int idx = c * kWave + lane;
+                    // a block's 2 lanes are both in or both out (K a multiple of 16)
+                    float f[8];
+                    unpack8(v[c], f);
+                    uint32_t sc;
+                    const uint32_t packed = nv_encode8(f, sf, sc);
+                    if (idx < nvec) {
+                        *reinterpret_cast<uint32_t*>(qrow + (int64_t)idx * 4) = packed;
+                        if ((lane & 1) == 0) srow[idx >> 1] = (uint8_t)sc;
+                    }
+                }
+            }
+        } else if (sr >= 0 && wave_row_covered(s_off, G, T, t)) {
             if constexpr (FMT == 0) {
                 // bf16 magnitudes order like their bit patterns with the sign cleared
                 uint32_t amax_bits = 0;
@@ -152,7 +180,7 @@ template <int FMT, bool GATHER>
 __global__ __launch_bounds__(kThreads) void quantize_long_kernel(const uint16_t* __restrict__ x,
                                                                  uint8_t* __restrict__ q, void* __restrict__ scales,
                                                                  const uint32_t* __restrict__ off, int G,
-                                                                 int64_t T, int64_t K, Gather ga) {
+                                                                 int64_t T, int64_t K, Gather ga, NvScales nv) {
     __shared__ uint32_t s_off[kMaxGroups + 1];
     load_offsets(s_off, off, G);
     const int lane = threadIdx.x & (kWave - 1);
@@ -160,8 +188,28 @@ __global__ __launch_bounds__(kThreads) void quantize_long_kernel(const uint16_t*
     const int64_t nvec = K / kVecElems;
     for (int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave; t < T; t += nw) {
         const int64_t sr = source_row<GATHER>(ga, t);
-        if (sr < 0 || !wave_row_covered(s_off, G, T, t)) continue;
+        if (sr < 0) continue;
         const uint4* xr = reinterpret_cast<const uint4*>(x + sr * K);
+        if constexpr (FMT == 3) {
+            const int g = wave_row_group(s_off, nv.ids, G, nv.E, T, t);
+            if (g < 0) continue;
+            const float sf = nv.sf[nv.ids[g]];
+            uint8_t* qrow = q + t * (K / 2);
+            uint8_t* srow = static_cast<uint8_t*>(scales) + t * (K / 16);
+            for (int64_t base = 0; base < nvec; base += kWave) {
+                const int64_t idx = base + lane;
+                float f[8];
+                unpack8(idx < nvec ? xr[idx] : make_uint4(0, 0, 0, 0), f);
+                uint32_t sc;
+                const uint32_t packed = nv_encode8(f, sf, sc);
+                if (idx < nvec) {
+                    *reinterpret_cast<uint32_t*>(qrow + idx * 4) = packed;
+                    if ((lane & 1) == 0) srow[idx >> 1] = (uint8_t)sc;
+                }
+            }
+            continue;
+        }
+        if (!wave_row_covered(s_off, G, T, t)) continue;
         if constexpr (FMT == 0) {
             uint32_t amax_bits = 0;
             for (int64_t idx = lane; idx < nvec; idx += kWave) {
@@ -254,23 +302,25 @@ int64_t persistent_grid(Kern kernel, int64_t T) {
 
 template <class Kern>
 hipError_t launch_persistent(Kern kernel, const uint16_t* x, uint8_t* q, void* s, const uint32_t* off, int G,
-                             int64_t T, int64_t K, const Gather& ga, hipStream_t stream) {
+                             int64_t T, int64_t K, const Gather& ga, const NvScales& nv, hipStream_t stream) {
     hipLaunchKernelGGL(kernel, dim3((unsigned)persistent_grid(kernel, T)), dim3(kThreads), 0, stream, x, q, s, off,
-                       G, T, K, ga);
+                       G, T, K, ga, nv);
     return hipGetLastError();
 }
 
 template <int FMT, bool GATHER>
 hipError_t launch_fmt(const uint16_t* x, uint8_t* q, void* s, const uint32_t* off, int G, int64_t T, int64_t K,
-                      const Gather& ga, hipStream_t stream) {
+                      const Gather& ga, hipStream_t stream, const NvScales& nv = NvScales{nullptr, nullptr, 0}) {
     const int64_t nc = (K + kChunk - 1) / kChunk;
-    if (nc <= 1) return launch_persistent(quantize_rows_kernel<FMT, 1, GATHER>, x, q, s, off, G, T, K, ga, stream);
-    if (nc <= 2) return launch_persistent(quantize_rows_kernel<FMT, 2, GATHER>, x, q, s, off, G, T, K, ga, stream);
-    if (nc <= 4) return launch_persistent(quantize_rows_kernel<FMT, 4, GATHER>, x, q, s, off, G, T, K, ga, stream);
-    if (nc <= 8) return launch_persistent(quantize_rows_kernel<FMT, 8, GATHER>, x, q, s, off, G, T, K, ga, stream);
-    if (nc <= 14) return launch_persistent(quantize_rows_kernel<FMT, 14, GATHER>, x, q, s, off, G, T, K, ga, stream);
-    if (nc <= 16) return launch_persistent(quantize_rows_kernel<FMT, 16, GATHER>, x, q, s, off, G, T, K, ga, stream);
-    return launch_persistent(quantize_long_kernel<FMT, GATHER>, x, q, s, off, G, T, K, ga, stream);
+    if (nc <= 1) return launch_persistent(quantize_rows_kernel<FMT, 1, GATHER>, x, q, s, off, G, T, K, ga, nv, stream);
+    if (nc <= 2) return launch_persistent(quantize_rows_kernel<FMT, 2, GATHER>, x, q, s, off, G, T, K, ga, nv, stream);
+    if (nc <= 4) return launch_persistent(quantize_rows_kernel<FMT, 4, GATHER>, x, q, s, off, G, T, K, ga, nv, stream);
+    if (nc <= 8) return launch_persistent(quantize_rows_kernel<FMT, 8, GATHER>, x, q, s, off, G, T, K, ga, nv, stream);
+    if (nc <= 14)
+        return launch_persistent(quantize_rows_kernel<FMT, 14, GATHER>, x, q, s, off, G, T, K, ga, nv, stream);
+    if (nc <= 16)
+        return launch_persistent(quantize_rows_kernel<FMT, 16, GATHER>, x, q, s, off, G, T, K, ga, nv, stream);
+    return launch_persistent(quantize_long_kernel<FMT, GATHER>, x, q, s, off, G, T, K, ga, nv, stream);
 }
 
 template <bool GATHER>
@@ -295,6 +345,13 @@ hipError_t launch_quantize_gather(int fmt, const void* x, int64_t nsrc, const in
                                   void* q, void* scales, const uint32_t* off, int G, int64_t T, int64_t K,
                                   hipStream_t stream) {
     return launch_any<true>(fmt, x, q, scales, off, G, T, K, Gather{indices, divisor, nsrc}, stream);
+}
+
+hipError_t launch_quantize_nvfp4(const void* x, void* q, void* scales, const float* tensor_scales,
+                                  const uint32_t* off, const int32_t* ids, int G, int E, int64_t T, int64_t K,
+                                  hipStream_t stream) {
+    return launch_fmt<3, false>(static_cast<const uint16_t*>(x), static_cast<uint8_t*>(q), scales, off, G, T, K,
+                                Gather{nullptr, 1, T}, stream, NvScales{ids, tensor_scales, E});
 }
 
 hipError_t launch_silu_quantize(const void* h, void* yq, void* ys, const uint32_t* off, int G, int64_t T,

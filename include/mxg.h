@@ -13,6 +13,8 @@
  *                             fused with SwiGLU and an MXFP4 requant
  *   mx_silu_quantize          the unfused second half: SwiGLU + MXFP4 requant of a
  *                             BF16 gate/up tensor
+ *   mx_grouped_quantize_nvfp4 BF16 activations -> NVFP4 (16-element blocks, E4M3
+ *                             scale, e2m1 codes) under a per-expert tensor scale
  *   mx_moe_combine            after the down-projection: each token's row is the
  *                             router-weighted sum of its routed rows
  *
@@ -210,6 +212,38 @@ mxg_status mx_grouped_matmul_swiglu(mxg_format fmt, const void* a_q, const void*
  */
 mxg_status mx_silu_quantize(const void* h_bf16, void* y_q, void* y_scales, const uint32_t* row_offsets,
                             int32_t num_groups, int64_t total_rows, int64_t I, hipStream_t stream);
+
+/*
+ * mx_grouped_quantize_nvfp4 -- per-expert dynamic quantization of BF16 rows to
+ * NVFP4.
+ * (NvMxf4f8Strategy, is_nvfp4 and grouped_quantize(input_scale);
+ *  grouped_quantize_dynamic_scaled_fp4_async_kernel, Args: sf_tensor, the
+ *  per-expert tensor-wise scale factor.  The pages name the format and the
+ *  scale without their arithmetic; the reading taken here follows.)
+ *
+ *   x_bf16         [total_rows, K] bf16 input.
+ *   q              [total_rows, K/2] u8, e2m1 codes, element 2i in bits 0..3.
+ *   scales         [total_rows, K/16] u8, one E4M3 code per 16-element block.
+ *   tensor_scales  fp32 [num_experts]: the encode-side tensor scale sf of each
+ *                  expert; the rows of group g use tensor_scales[expert_ids[g]].
+ *   row_offsets / expert_ids / num_groups as above; a group whose expert id
+ *                  lies outside [0, num_experts) is skipped (its rows are not
+ *                  written), and only covered rows of q and scales are written.
+ *
+ * Per block, with amax its largest |x|: scale code = e4m3(min(fl32(fl32(amax /
+ * 6) * sf), 448)); with s that code's value, r = fl32(sf / s) (0 when s is 0)
+ * and each code = e2m1(fl32(x * r)).  Every fl32 step is one IEEE binary32
+ * operation; so x is about e2m1 * s / sf.  sf is expected finite and > 0.
+ * Weights are prepared with the same call: one group of N rows per expert,
+ * expert_ids = 0 .. E-1, tensor_scales = the weights' own.
+ *
+ * Errors: INVALID_VALUE for a null pointer, K <= 0, total_rows < 0,
+ * num_groups < 0, num_experts <= 0, misalignment; NOT_SUPPORTED for
+ * K % 16 != 0 or num_groups > MXG_MAX_GROUPS.
+ */
+mxg_status mx_grouped_quantize_nvfp4(const void* x_bf16, void* q, void* scales, const float* tensor_scales,
+                                     const uint32_t* row_offsets, const int32_t* expert_ids, int32_t num_groups,
+                                     int32_t num_experts, int64_t total_rows, int64_t K, hipStream_t stream);
 
 /*
  * mx_moe_combine -- the MoE combine after the down-projection (itself

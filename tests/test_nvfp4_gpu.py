@@ -1,0 +1,113 @@
+"""GPU parity for the NVFP4 path: the grouped quantize must match the CPU
+oracle bit for bit (codes and E4M3 block scales) and leave rows of skipped
+or uncovered groups untouched."""
+import numpy as np
+import pytest
+import torch
+
+import fp4_grouped_gemm_quantize_amd as mxg
+import oracle
+import workloads as W
+from common import bits, offsets_gpu, sentinel_like, to_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def tensor_scales(x_bits, off, ids, E, seed):
+    """Calibration-like per-expert tensor scales: 448 * 6 / (largest |x| of the
+    expert's rows), times a seeded factor in [0.5, 2] so that saturating and
+    non-power-of-two block scales occur.  (An input choice, not the method.)"""
+    xv = oracle.bf16_value_array(x_bits)
+    amax = np.ones(E)
+    for g in range(len(ids)):
+        lo, hi = int(off[g]), int(off[g + 1])
+        if 0 <= ids[g] < E and hi > lo:
+            amax[ids[g]] = max(np.abs(xv[lo:hi]).max(), 1e-30)
+    f = np.random.default_rng(seed).uniform(0.5, 2.0, size=E)
+    return (448.0 * 6.0 / amax * f).astype(np.float32)
+
+
+def run_both(x_bits, off, ids, sf):
+    T, K = x_bits.shape
+    q_ref, s_ref = oracle.quantize_nvfp4(x_bits, off, ids, sf, sentinel_like((T, K // 2)),
+                                         sentinel_like((T, K // 16), value=0x5A))
+    x = to_gpu(x_bits.view(np.int16)).view(torch.bfloat16)
+    q = to_gpu(sentinel_like((T, K // 2)))
+    s = to_gpu(sentinel_like((T, K // 16), value=0x5A))
+    mxg.mx_grouped_quantize_nvfp4(x, q, s, to_gpu(sf), offsets_gpu(off), to_gpu(ids.astype(np.int32)))
+    torch.cuda.synchronize()
+    return (q.cpu().numpy(), s.cpu().numpy()), (q_ref, s_ref)
+
+
+def assert_same(gpu, ref, label):
+    (q, s), (qr, sr) = gpu, ref
+    bad = np.argwhere(q != qr)
+    assert bad.size == 0, f"{label}: {len(bad)} code bytes differ, first at {bad[0]}: gpu {q[tuple(bad[0])]:#x} oracle {qr[tuple(bad[0])]:#x}"
+    bad = np.argwhere(s != sr)
+    assert bad.size == 0, f"{label}: {len(bad)} scale bytes differ, first at {bad[0]}: gpu {s[tuple(bad[0])]:#x} oracle {sr[tuple(bad[0])]:#x}"
+
+
+@pytest.mark.parametrize("K", [16, 48, 512, 1040, 7168, 8704])
+def test_quantize_nvfp4_matches_oracle(K):
+    w = W.WORKLOADS[5].scaled(tokens=40, E=8, masked=1, top_k=4, K=K)
+    r = W.routing(w)
+    x = bits(W.activations(w, r))
+    E = w.E
+    sf = tensor_scales(x, r.row_offsets, r.expert_ids, E, seed=K)
+    gpu, ref = run_both(x, r.row_offsets, r.expert_ids, sf)
+    assert_same(gpu, ref, f"K={K}")
+
+
+def test_quantize_nvfp4_special_values():
+    """Zero rows, tiny blocks that underflow, blocks that saturate the E4M3 scale."""
+    T, K = 6, 64
+    xv = np.zeros((T, K))
+    xv[1, :16] = 2.0 ** -14                               # underflow with sf = 1
+    xv[2, :] = np.linspace(-600, 600, K)                  # saturating block scales with sf = 6
+    xv[3, ::2] = -0.0
+    xv[4, :] = np.random.default_rng(1).normal(size=K) * 1e-3
+    xv[5, 16:32] = 6.0
+    x = oracle.bf16_round_array(xv)
+    off = np.array([0, 2, 3, 6], np.uint32)
+    ids = np.array([0, 1, 2], np.int32)
+    sf = np.array([1.0, 6.0, 1000.0], np.float32)
+    gpu, ref = run_both(x, off, ids, sf)
+    assert_same(gpu, ref, "special")
+
+
+def test_quantize_nvfp4_skips_bad_expert_ids_and_uncovered_rows():
+    T, K = 48, 64
+    x = bits(torch.randn(T, K).to(torch.bfloat16))
+    off = np.array([0, 10, 10, 30, 40], np.uint32)        # rows 40..47 uncovered, group 1 empty
+    ids = np.array([1, 0, 7, 2], np.int32)                # expert 7 is out of range (E = 3)
+    sf = np.array([100.0, 50.0, 25.0], np.float32)
+    gpu, ref = run_both(x, off, ids, sf)
+    assert_same(gpu, ref, "skips")
+    # rows of the skipped group (10..29) and the uncovered rows (40..47) keep their sentinels
+    for rows in (slice(10, 30), slice(40, 48)):
+        assert np.all(gpu[0][rows] == 0xA5) and np.all(gpu[1][rows] == 0x5A)
+
+
+def test_quantize_nvfp4_full_size_sampled_rows():
+    """The mxfp4_swiglu routing and shape (32,768 x 7168) in NVFP4; sampled rows
+    checked against the oracle run on those rows (each with its group's scale)."""
+    w = W.WORKLOADS[5]
+    r = W.routing(w)
+    x_gpu = W.activations(w, r, device="cuda")
+    T, K = x_gpu.shape
+    E = w.E
+    xb = bits(x_gpu.cpu())
+    sf = tensor_scales(xb, r.row_offsets, r.expert_ids, E, seed=5)
+    q, s = mxg.quantize_nvfp4(x_gpu, offsets_gpu(r.row_offsets), to_gpu(r.expert_ids.astype(np.int32)), to_gpu(sf))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(55)
+    rows = []
+    for g in range(len(r.expert_ids)):
+        lo, hi = int(r.row_offsets[g]), int(r.row_offsets[g + 1])
+        if hi > lo:
+            rows += [lo, hi - 1]
+    rows = np.unique(np.array(rows + list(rng.integers(0, T, 64))))
+    grp = np.searchsorted(r.row_offsets[1:], rows, side="right")
+    off1 = np.arange(rows.size + 1, dtype=np.uint32)
+    qr, sr = oracle.quantize_nvfp4(xb[rows], off1, r.expert_ids[grp].astype(np.int32), sf)
+    assert_same((q.cpu().numpy()[rows], s.cpu().numpy()[rows]), (qr, sr), "full size")
