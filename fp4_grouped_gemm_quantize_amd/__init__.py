@@ -31,7 +31,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmxg.so")
 
 EXPORTED = ("mx_grouped_quantize", "mx_grouped_quantize_gather", "mx_grouped_matmul", "mx_grouped_matmul_swiglu",
-            "mx_silu_quantize", "mx_moe_combine", "mx_grouped_quantize_nvfp4", "mxg_status_string")
+            "mx_silu_quantize", "mx_moe_combine", "mx_grouped_quantize_nvfp4", "mx_grouped_matmul_nvfp4",
+            "mxg_status_string")
 
 
 class MxgError(RuntimeError):
@@ -64,8 +65,10 @@ def lib() -> ctypes.CDLL:
         L.mx_silu_quantize.argtypes = [_P, _P, _P, _P, _I32, _I64, _I64, _P]
         L.mx_moe_combine.argtypes = [_P, _I64, _I64, _P, _P, _I64, _I32, _P, _P]
         L.mx_grouped_quantize_nvfp4.argtypes = [_P, _P, _P, _P, _P, _P, _I32, _I32, _I64, _I64, _P]
+        L.mx_grouped_matmul_nvfp4.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I64, _I64, _I64, _I64, _P]
         for name in ("mx_grouped_quantize", "mx_grouped_quantize_gather", "mx_grouped_matmul",
-                     "mx_grouped_matmul_swiglu", "mx_silu_quantize", "mx_moe_combine", "mx_grouped_quantize_nvfp4"):
+                     "mx_grouped_matmul_swiglu", "mx_silu_quantize", "mx_moe_combine", "mx_grouped_quantize_nvfp4",
+                     "mx_grouped_matmul_nvfp4"):
             getattr(L, name).restype = ctypes.c_int
         L.mxg_status_string.argtypes = [ctypes.c_int]
         L.mxg_status_string.restype = ctypes.c_char_p
@@ -180,6 +183,29 @@ def mx_grouped_quantize_nvfp4(x, q, scales, tensor_scales, row_offsets, expert_i
     _check(lib().mx_grouped_quantize_nvfp4(_ptr(x), _ptr(q), _ptr(scales), _ptr(tensor_scales), _ptr(row_offsets),
                                            _ptr(expert_ids), G, tensor_scales.numel(), T, K, _stream(x)),
            "mx_grouped_quantize_nvfp4")
+
+
+def mx_grouped_matmul_nvfp4(a_q, a_scales, b_q, b_scales, expert_scales, c, row_offsets, expert_ids,
+                            max_rows_per_group_hint: int = 0) -> None:
+    """NVFP4 ragged grouped GEMM into bf16 c [T, N]: a_q [T, K/2], a_scales [T, K/16],
+    b_q [E, N, K/2], b_scales [E, N, K/16], expert_scales fp32 [E]."""
+    _expect(a_q, "a_q", _U8)
+    _expect(b_q, "b_q", _U8)
+    dev = a_q.device
+    T = a_q.shape[0]
+    E, N = b_q.shape[0], b_q.shape[1]
+    K = a_q.shape[1] * 2
+    _expect(b_q, "b_q", _U8, (E, N, K // 2), dev)
+    _expect(a_scales, "a_scales", _U8, (T, K // 16), dev)
+    _expect(b_scales, "b_scales", _U8, (E, N, K // 16), dev)
+    _expect(expert_scales, "expert_scales", _F32, (E,), dev)
+    _expect(c, "c", _BF16, (T, N), dev)
+    _expect(row_offsets, "row_offsets", _U32, None, dev)
+    G = row_offsets.numel() - 1
+    _expect(expert_ids, "expert_ids", _I32T, (G,), dev)
+    _check(lib().mx_grouped_matmul_nvfp4(_ptr(a_q), _ptr(a_scales), _ptr(b_q), _ptr(b_scales), _ptr(expert_scales),
+                                         _ptr(c), _ptr(row_offsets), _ptr(expert_ids), G, E, T, N, K,
+                                         int(max_rows_per_group_hint), _stream(a_q)), "mx_grouped_matmul_nvfp4")
 
 
 def mx_grouped_matmul(fmt: int, a_q, a_scales, b_q, b_scales, c, row_offsets, expert_ids,

@@ -125,6 +125,25 @@ mxg_status mx_grouped_matmul(mxg_format fmt, const void* a_q, const void* a_scal
     return from_hip(mxg::launch_grouped_gemm(p, stream));
 }
 
+mxg_status mx_grouped_matmul_nvfp4(const void* a_q, const void* a_scales, const void* b_q, const void* b_scales,
+                                   const float* expert_scales, void* c_bf16, const uint32_t* row_offsets,
+                                   const int32_t* expert_ids, int32_t num_groups, int32_t num_experts,
+                                   int64_t total_rows, int64_t N, int64_t K, int64_t max_rows_per_group_hint,
+                                   hipStream_t stream) {
+    if (K <= 0 || N <= 0 || num_experts <= 0 || total_rows < 0 || num_groups < 0) return MXG_ERROR_INVALID_VALUE;
+    if (K % 512 != 0 || num_groups > MXG_MAX_GROUPS) return MXG_ERROR_NOT_SUPPORTED;
+    if (N > INT32_MAX / 2 || total_rows > INT32_MAX) return MXG_ERROR_NOT_SUPPORTED;
+    if (total_rows == 0 || num_groups == 0) return MXG_SUCCESS;  // nothing is read or written
+    if (!a_q || !a_scales || !b_q || !b_scales || !expert_scales || !c_bf16 || !row_offsets || !expert_ids)
+        return MXG_ERROR_INVALID_VALUE;
+    if (!aligned(a_q, 16) || !aligned(b_q, 16) || !aligned(a_scales, 16) || !aligned(b_scales, 16) ||
+        !aligned(c_bf16, 16) || !aligned(expert_scales, 4) || !aligned(row_offsets, 4) || !aligned(expert_ids, 4))
+        return MXG_ERROR_INVALID_VALUE;
+    mxg::GemmProblem p{3, a_q, a_scales, b_q, b_scales, c_bf16, nullptr, nullptr, row_offsets, expert_ids,
+                       num_groups, num_experts, total_rows, N, K, max_rows_per_group_hint, expert_scales};
+    return from_hip(mxg::launch_grouped_gemm(p, stream));
+}
+
 mxg_status mx_grouped_matmul_swiglu(mxg_format fmt, const void* a_q, const void* a_scales, const void* w_q,
                                     const void* w_scales, void* y_q, void* y_scales,
                                     const uint32_t* row_offsets, const int32_t* expert_ids, int32_t num_groups,

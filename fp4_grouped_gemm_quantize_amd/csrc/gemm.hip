@@ -90,8 +90,8 @@ __device__ __forceinline__ v8i load_frag(const uint8_t* __restrict__ base, int s
 // 2(s%2) of word s/2 for every lane: a constant byte select.
 template <class TL, int FMT, int SEL>
 __device__ __forceinline__ void mma_row_sel(int i, int s, const v8i& a, const v8i (&bf)[TL::TN],
-                                            const uint32_t (&wa)[TL::TM][Fmt<FMT>::kFP4 ? 2 : 1],
-                                            const uint32_t (&wb)[TL::TN][Fmt<FMT>::kFP4 ? 2 : 1],
+                                            const uint32_t (&wa)[TL::TM][Fmt<FMT>::kWords],
+                                            const uint32_t (&wb)[TL::TN][Fmt<FMT>::kWords],
                                             v16f (&acc)[TL::TM][TL::TN]) {
     using F = Fmt<FMT>;
 #pragma unroll
@@ -106,11 +106,89 @@ __device__ __forceinline__ void mma_row_sel(int i, int s, const v8i& a, const v8
 }
 template <class TL, int FMT>
 __device__ __forceinline__ void mma_row(int i, int s, const v8i& a, const v8i (&bf)[TL::TN],
-                                        const uint32_t (&wa)[TL::TM][Fmt<FMT>::kFP4 ? 2 : 1],
-                                        const uint32_t (&wb)[TL::TN][Fmt<FMT>::kFP4 ? 2 : 1],
+                                        const uint32_t (&wa)[TL::TM][Fmt<FMT>::kWords],
+                                        const uint32_t (&wb)[TL::TN][Fmt<FMT>::kWords],
                                         v16f (&acc)[TL::TM][TL::TN]) {
     if (s & 1) mma_row_sel<TL, FMT, 2>(i, s, a, bf, wa, wb, acc);  // s is unrolled: the branch folds
     else mma_row_sel<TL, FMT, 0>(i, s, a, bf, wa, wb, acc);
+}
+
+// NVFP4 on the f16 matrix cores.  gfx950's scaled MFMA takes only E8M0
+// block scales per 32 elements, so an NVFP4 element (e2m1 code times its
+// block's E4M3 scale) is turned into an exact f16 value instead: the scaled
+// convert multiplies by the scale's power of two (it uses only the exponent
+// of its fp32 scale operand -- measured), a packed f16 multiply by the scale's
+// 1.xxx mantissa finishes it; the product has at most 6 significant bits and
+// lies in [2^-10, 2688] or is 0, so both steps are exact.  Lane half h holds
+// K 32h .. 32h+31 of each 64-deep step (16 bytes, two 16-element blocks, as
+// the FP4 fragments are laid out); quarter q of them (8 elements) is the
+// lane's operand of the q-th 32x32x16 f16 MFMA, with the same K mapping on
+// the B side, so the products pair up.
+typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+typedef _Float16 h8v __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ void nv_split_scale(uint32_t code, float& pow2, h2v& mant) {
+    const float v = __builtin_amdgcn_cvt_f32_fp8((int)code, 0);
+    const uint32_t b = __float_as_uint(v);
+    pow2 = __uint_as_float(b & 0x7f800000u);
+    const _Float16 m = (_Float16)__uint_as_float((b & 0x007fffffu) | 0x3f800000u);
+    mant = h2v{m, m};
+}
+
+__device__ __forceinline__ h8v nv_dequant8(uint32_t codes, float pow2, h2v mant) {
+    const h2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, pow2, 0) * mant;
+    const h2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, pow2, 1) * mant;
+    const h2v p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, pow2, 2) * mant;
+    const h2v p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, pow2, 3) * mant;
+    return h8v{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+// All K steps of one NVFP4 stage.  wa / wb: the stage's 16 scale bytes of
+// each of this lane's rows / columns, word s = blocks 4s .. 4s+3.
+template <class TL>
+__device__ __forceinline__ void mma_stage_nv(const uint8_t* __restrict__ sa, const uint8_t* __restrict__ sb, int wm,
+                                             int wn, int h, int r32, const uint32_t (&wa)[TL::TM][4],
+                                             const uint32_t (&wb)[TL::TN][4], v16f (&acc)[TL::TM][TL::TN]) {
+    constexpr int TM = TL::TM, TN = TL::TN;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        uint4 ra[TM], rb[TN];
+        float pa[TM][2], pb[TN][2];
+        h2v ma[TM][2], mb[TN][2];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            ra[i] = *reinterpret_cast<const uint4*>(sa + swz(wm * TL::WTM + i * 32 + r32, 2 * s + h));
+            const uint32_t w = wa[i][s] >> (16 * h);  // bytes 0, 1: this lane's two blocks
+            nv_split_scale(w & 0xffu, pa[i][0], ma[i][0]);
+            nv_split_scale((w >> 8) & 0xffu, pa[i][1], ma[i][1]);
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            rb[j] = *reinterpret_cast<const uint4*>(sb + swz(wn * TL::WTN + j * 32 + r32, 2 * s + h));
+            const uint32_t w = wb[j][s] >> (16 * h);
+            nv_split_scale(w & 0xffu, pb[j][0], mb[j][0]);
+            nv_split_scale((w >> 8) & 0xffu, pb[j][1], mb[j][1]);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            h8v av[TM], bv[TN];
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const uint32_t c = q == 0 ? ra[i].x : q == 1 ? ra[i].y : q == 2 ? ra[i].z : ra[i].w;
+                av[i] = nv_dequant8(c, pa[i][q >> 1], ma[i][q >> 1]);
+            }
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const uint32_t c = q == 0 ? rb[j].x : q == 1 ? rb[j].y : q == 2 ? rb[j].z : rb[j].w;
+                bv[j] = nv_dequant8(c, pb[j][q >> 1], mb[j][q >> 1]);
+            }
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
+        }
+    }
 }
 
 // All K steps of one stage.  Two waves per SIMD (one fragment set): the
@@ -121,11 +199,15 @@ __device__ __forceinline__ void mma_row(int i, int s, const v8i& a, const v8i (&
 template <class TL, int FMT>
 __device__ __forceinline__ void mma_stage(const uint8_t* __restrict__ sa, const uint8_t* __restrict__ sb, int wm,
                                           int wn, int h, int r32,
-                                          const uint32_t (&wa_in)[TL::TM][Fmt<FMT>::kFP4 ? 2 : 1],
-                                          const uint32_t (&wb_in)[TL::TN][Fmt<FMT>::kFP4 ? 2 : 1],
+                                          const uint32_t (&wa_in)[TL::TM][Fmt<FMT>::kWords],
+                                          const uint32_t (&wb_in)[TL::TN][Fmt<FMT>::kWords],
                                           v16f (&acc)[TL::TM][TL::TN]) {
     using F = Fmt<FMT>;
-    constexpr int TM = TL::TM, TN = TL::TN, kW = F::kFP4 ? 2 : 1;
+    if constexpr (F::kNV) {
+        mma_stage_nv<TL>(sa, sb, wm, wn, h, r32, wa_in, wb_in, acc);
+        return;
+    }
+    constexpr int TM = TL::TM, TN = TL::TN, kW = F::kWords;
     uint32_t wa[TM][kW], wb[TN][kW];
     if constexpr (F::kMX) {
 #pragma unroll
@@ -194,7 +276,7 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
     constexpr int kAStage = BM * kStageBytes, kBStage = BN * kStageBytes;
     constexpr int kStage = kAStage + kBStage;
     constexpr int A_J = BM / 8 / NW, B_J = BN / 8 / NW;  // 1 KiB load instructions per wave per stage
-    constexpr int kWords = F::kFP4 ? 2 : 1;              // scale words per row per stage
+    constexpr int kWords = F::kWords;                    // scale words per row per stage
     // MX scales through LDS: every kSclStages stages the workgroup loads the
     // next 32 scale bytes (32 blocks) of each of its BM + BN rows with direct
     // loads (an instruction covers 32 rows, two lanes per row), into one of
@@ -232,7 +314,7 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
     const int64_t row_bytes = args.row_bytes;
     const int nkt = (int)((row_bytes + kStageBytes - 1) / kStageBytes);
     const bool k_tail = !KA && (row_bytes % kStageBytes) != 0;  // the last stage is partial
-    const int64_t nblk = args.K / 32;
+    const int64_t nblk = args.K / F::kBlockElems;  // scale bytes per row
 
     const WorkSplit ws = work_split(total_tiles, gridDim.x);
     for (int64_t W = xcd_remap(blockIdx.x, gridDim.x); W < ws.items; W += gridDim.x) {
@@ -495,9 +577,12 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
             return reinterpret_cast<uint16_t*>(base + (row % kRowsPerSlot) * BN * 2);
         };
         if constexpr (!SWIGLU) {
-            // out = bf16((acc * a_scale[row]) * b_scale[col]) for FP8 rowwise
+            // out = bf16((acc * a_scale[row]) * b_scale[col]) for FP8 rowwise,
+            // bf16(acc * expert_scale[e]) for NVFP4
+            const float es_e = F::kNV ? args.es[e] : 1.0f;
             auto value = [&](int i, int j, int r, float sbv) {
                 float v = acc[i][j][r];
+                if constexpr (F::kNV) v = v * es_e;
                 if constexpr (!F::kMX) {
                     const int64_t row = m0 + wm * WTM + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
                     v = v * static_cast<const float*>(args.as)[row < m_end ? row : m_end - 1];
@@ -633,25 +718,31 @@ constexpr int64_t kTallRows = 384;
 
 template <int FMT, bool SWIGLU>
 hipError_t launch_fmt(const GemmProblem& p, hipStream_t stream) {
-    // Average rows per non-empty group decides the regime; the optional host
-    // hint (largest group) can only move a problem to the larger tile.
-    const int64_t groups = p.G < p.T ? p.G : p.T;
-    const int64_t avg_rows = groups > 0 ? p.T / groups : p.T;
-    const int64_t rows = p.max_rows_hint > avg_rows ? (avg_rows + p.max_rows_hint) / 2 : avg_rows;
-    // whole stages; for MX also whole 32-byte scale chunks (LDS-staged scales)
-    const bool ka = FMT == 0 ? p.K % kStageBytes == 0 : p.K % 1024 == 0;
-    if (rows >= 128) {
-        if constexpr (FMT == 0) {
-            return ka ? launch_tile<TileLargeFp8, FMT, SWIGLU, true>(p, stream, kBandLarge)
-                      : launch_tile<TileLargeFp8, FMT, SWIGLU, false>(p, stream, kBandLarge);
-        } else {
-            if (ka && avg_rows >= kTallRows)
-                return launch_tile<TileLargeMxKA8, FMT, SWIGLU, true>(p, stream, kBandLarge);
-            return ka ? launch_tile<TileLargeMxKA, FMT, SWIGLU, true>(p, stream, kBandMx)
-                      : launch_tile<TileLargeMx, FMT, SWIGLU, false>(p, stream, kBandMx);
+    if constexpr (FMT == 3) {
+        // NVFP4: the 128 x 256 tile with LDS-staged scales (K a multiple of 512)
+        static_assert(!SWIGLU, "NVFP4 has no fused epilogue here");
+        return launch_tile<TileLargeMxKA, FMT, false, true>(p, stream, kBandMx);
+    } else {
+        // Average rows per non-empty group decides the regime; the optional host
+        // hint (largest group) can only move a problem to the larger tile.
+        const int64_t groups = p.G < p.T ? p.G : p.T;
+        const int64_t avg_rows = groups > 0 ? p.T / groups : p.T;
+        const int64_t rows = p.max_rows_hint > avg_rows ? (avg_rows + p.max_rows_hint) / 2 : avg_rows;
+        // whole stages; for MX also whole 32-byte scale chunks (LDS-staged scales)
+        const bool ka = FMT == 0 ? p.K % kStageBytes == 0 : p.K % 1024 == 0;
+        if (rows >= 128) {
+            if constexpr (FMT == 0) {
+                return ka ? launch_tile<TileLargeFp8, FMT, SWIGLU, true>(p, stream, kBandLarge)
+                          : launch_tile<TileLargeFp8, FMT, SWIGLU, false>(p, stream, kBandLarge);
+            } else {
+                if (ka && avg_rows >= kTallRows)
+                    return launch_tile<TileLargeMxKA8, FMT, SWIGLU, true>(p, stream, kBandLarge);
+                return ka ? launch_tile<TileLargeMxKA, FMT, SWIGLU, true>(p, stream, kBandMx)
+                          : launch_tile<TileLargeMx, FMT, SWIGLU, false>(p, stream, kBandMx);
+            }
         }
+        return launch_tile<TileSmall, FMT, SWIGLU, false>(p, stream, kBandNOuter);
     }
-    return launch_tile<TileSmall, FMT, SWIGLU, false>(p, stream, kBandNOuter);
 }
 
 }  // namespace
@@ -687,9 +778,10 @@ GemmArgs make_args(const GemmProblem& p, int BM, int BN, int mband, int per_cu, 
     a.T = p.T;
     a.N = p.N;
     a.K = p.K;
-    a.row_bytes = p.fmt == 2 ? p.K / 2 : p.K;
+    a.row_bytes = (p.fmt == 2 || p.fmt == 3) ? p.K / 2 : p.K;
     a.ntiles_n = (int)((p.N + BN - 1) / BN);
     a.mband = mband > 0 ? mband : 1;
+    a.es = p.es;
     // Upper bound on M tiles: each non-empty group adds at most one partial tile.
     const int64_t groups_nonempty = p.G < p.T ? p.G : p.T;
     const int64_t mtiles_bound = p.T / BM + groups_nonempty;
@@ -711,6 +803,8 @@ hipError_t launch_grouped_gemm(const GemmProblem& p, hipStream_t stream) {
             return swiglu ? launch_fmt<1, true>(p, stream) : launch_fmt<1, false>(p, stream);
         case 2:
             return swiglu ? launch_fmt<2, true>(p, stream) : launch_fmt<2, false>(p, stream);
+        case 3:
+            return swiglu ? hipErrorInvalidValue : launch_fmt<3, false>(p, stream);
         default:
             return hipErrorInvalidValue;
     }

@@ -35,15 +35,19 @@ struct GemmArgs {
     int ntiles_n;
     int mband;          // tile order within a group: bands of mband M tiles, N walked within a band
                         // (1: M tiles outer; >= the group's M tiles: N tiles outer)
+    const float* es;    // NVFP4: per-expert epilogue scale (fp32 [E]); unused otherwise
 };
 
-// FMT: 0 = FP8 rowwise, 1 = MXFP8, 2 = MXFP4.
+// FMT: 0 = FP8 rowwise, 1 = MXFP8, 2 = MXFP4, 3 = NVFP4.
 template <int FMT>
 struct Fmt {
-    static constexpr bool kMX = FMT != 0;
-    static constexpr bool kFP4 = FMT == 2;
-    static constexpr int kSteps = kFP4 ? 4 : 2;   // 64-deep MFMA steps per stage
-    static constexpr int kBlocks = kFP4 ? 8 : 4;  // 32-element scale blocks per stage
+    static constexpr bool kMX = FMT != 0;          // block scales (E8M0, or E4M3 for NVFP4)
+    static constexpr bool kNV = FMT == 3;          // 16-element blocks, E4M3 scales, f16 matrix cores
+    static constexpr bool kFP4 = FMT == 2 || FMT == 3;
+    static constexpr int kSteps = kFP4 ? 4 : 2;    // 64-deep K steps per stage
+    static constexpr int kBlockElems = kNV ? 16 : 32;
+    static constexpr int kBlocks = (kFP4 ? 256 : 128) / kBlockElems;  // scale blocks (bytes) per stage
+    static constexpr int kWords = kBlocks / 4;     // scale words per row per stage
     static constexpr int kTypeCode = kFP4 ? 4 : 0;  // cbsz / blgp: 0 = e4m3, 4 = e2m1
 };
 

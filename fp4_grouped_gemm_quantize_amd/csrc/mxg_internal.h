@@ -45,6 +45,7 @@ struct GemmProblem {
     int64_t N;
     int64_t K;
     int64_t max_rows_hint;
+    const float* es;  // NVFP4 (fmt 3): per-expert epilogue scale, fp32 [E]
 };
 
 hipError_t launch_grouped_gemm(const GemmProblem& p, hipStream_t stream);

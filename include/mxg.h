@@ -15,6 +15,8 @@
  *                             BF16 gate/up tensor
  *   mx_grouped_quantize_nvfp4 BF16 activations -> NVFP4 (16-element blocks, E4M3
  *                             scale, e2m1 codes) under a per-expert tensor scale
+ *   mx_grouped_matmul_nvfp4   ragged grouped GEMM of NVFP4 operands with a
+ *                             per-expert epilogue scale, BF16 output
  *   mx_moe_combine            after the down-projection: each token's row is the
  *                             router-weighted sum of its routed rows
  *
@@ -168,6 +170,39 @@ mxg_status mx_grouped_matmul(mxg_format fmt, const void* a_q, const void* a_scal
                              const int32_t* expert_ids, int32_t num_groups, int32_t num_experts,
                              int64_t total_rows, int64_t N, int64_t K, int64_t max_rows_per_group_hint,
                              hipStream_t stream);
+
+/*
+ * mx_grouped_matmul_nvfp4 -- ragged grouped GEMM of NVFP4 operands.
+ * (NvMxf4f8Strategy, grouped_matmul(): block-scaled grouped matmul with
+ *  per-expert scales -- expert_scales, the per-expert matmul-epilogue scaling
+ *  factors; is_nvfp4.  The arithmetic is not given on the pages; reading:)
+ *
+ *   out[t, n] = bf16( expert_scales[e] * sum_b sa[t, b] * sb[e, n, b] *
+ *                     sum_{k in block b} qa[t, k] * qb[e, n, k] )
+ * with e = expert_ids[g] for the group g covering row t, 16-element blocks,
+ * sa / sb the E4M3 values of the scale codes and qa / qb the e2m1 values.
+ *
+ *   a_q       [total_rows, K/2] u8 e2m1 codes (mx_grouped_quantize_nvfp4).
+ *   a_scales  [total_rows, K/16] u8 E4M3.
+ *   b_q       [num_experts, N, K/2] u8; b_scales [num_experts, N, K/16] u8.
+ *   expert_scales  fp32 [num_experts] (e.g. 1 / (sf_a * sf_w) for the tensor
+ *             scales the operands were quantized with).
+ *   c_bf16    [total_rows, N] bf16; only covered rows are written.
+ *
+ * gfx950's scaled matrix-core ops take E8M0 scales per 32 elements only, so
+ * each NVFP4 element becomes an exact f16 value (code times block scale)
+ * and the product runs on the f16 matrix cores with fp32 accumulation.
+ *
+ * Errors: INVALID_VALUE for a null pointer, K/N <= 0, num_experts <= 0,
+ * total_rows/num_groups < 0, misalignment (codes, scales and c on 16 bytes);
+ * NOT_SUPPORTED for K % 512 != 0, num_groups > MXG_MAX_GROUPS or sizes past
+ * the int32 range.
+ */
+mxg_status mx_grouped_matmul_nvfp4(const void* a_q, const void* a_scales, const void* b_q, const void* b_scales,
+                                   const float* expert_scales, void* c_bf16, const uint32_t* row_offsets,
+                                   const int32_t* expert_ids, int32_t num_groups, int32_t num_experts,
+                                   int64_t total_rows, int64_t N, int64_t K, int64_t max_rows_per_group_hint,
+                                   hipStream_t stream);
 
 /*
  * mx_grouped_matmul_swiglu -- fused gate/up grouped GEMM + SwiGLU + MXFP4 requant.

@@ -111,3 +111,100 @@ def test_quantize_nvfp4_full_size_sampled_rows():
     off1 = np.arange(rows.size + 1, dtype=np.uint32)
     qr, sr = oracle.quantize_nvfp4(xb[rows], off1, r.expert_ids[grp].astype(np.int32), sf)
     assert_same((q.cpu().numpy()[rows], s.cpu().numpy()[rows]), (qr, sr), "full size")
+
+
+# ----------------------------------------------------------------------------- grouped GEMM
+from common import check_gemm_rows  # noqa: E402
+
+SENT_BF16 = 0x7FA5  # a NaN pattern no result can produce
+
+
+def nv_gemm_inputs(w, seed, quantized=True):
+    """NVFP4 operands for workload w.  quantized: codes and scales from the
+    oracle's quantize of the seeded activations / weights (tensor scales as in
+    the quantize tests); otherwise seeded random codes and E4M3 scales."""
+    r = W.routing(w)
+    T, E, N, K = r.total_rows, w.E, w.N, w.K
+    rng = np.random.default_rng(seed)
+    if quantized:
+        x = bits(W.activations(w, r))
+        sfa = tensor_scales(x, r.row_offsets, r.expert_ids, E, seed=seed)
+        a, sa = oracle.quantize_nvfp4(x, r.row_offsets, r.expert_ids, sfa)
+        wt = bits(W.weights(w)).reshape(E * N, K)
+        off_w = np.arange(0, (E + 1) * N, N, dtype=np.uint32)
+        ids_w = np.arange(E, dtype=np.int32)
+        sfw = tensor_scales(wt, off_w, ids_w, E, seed=seed + 1)
+        b, sb = oracle.quantize_nvfp4(wt, off_w, ids_w, sfw)
+        b, sb = b.reshape(E, N, K // 2), sb.reshape(E, N, K // 16)
+        es = (1.0 / (sfa.astype(np.float64) * sfw)).astype(np.float32)
+    else:
+        a = rng.integers(0, 256, size=(T, K // 2), dtype=np.uint8)
+        sa = rng.integers(0x28, 0x48, size=(T, K // 16), dtype=np.uint8)
+        b = rng.integers(0, 256, size=(E, N, K // 2), dtype=np.uint8)
+        sb = rng.integers(0x28, 0x48, size=(E, N, K // 16), dtype=np.uint8)
+        es = rng.uniform(0.25, 4.0, size=E).astype(np.float32)
+    return r, a, sa, b, sb, es
+
+
+def run_nv_gemm(r, a, sa, b, sb, es, hint=0):
+    T, N = a.shape[0], b.shape[1]
+    c = torch.full((T, N), SENT_BF16, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    mxg.mx_grouped_matmul_nvfp4(to_gpu(a), to_gpu(sa), to_gpu(b), to_gpu(sb), to_gpu(es), c,
+                                offsets_gpu(r.row_offsets), to_gpu(r.expert_ids.astype(np.int32)), hint)
+    torch.cuda.synchronize()
+    return c.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+NV_SMALL = {
+    # several M and N tiles, ragged M tails, a partial N tile, an empty (masked) expert
+    "k512": W.WORKLOADS[5].scaled(tokens=96, E=8, masked=1, top_k=4, N=288, K=512, swiglu=False),
+    "k1024": W.WORKLOADS[5].scaled(tokens=80, E=6, masked=1, top_k=4, N=320, K=1024, swiglu=False),
+    "k2048_tall": W.WORKLOADS[5].scaled(tokens=512, E=4, masked=0, top_k=2, N=256, K=2048, swiglu=False),
+}
+
+
+@pytest.mark.parametrize("name", list(NV_SMALL))
+def test_nvfp4_gemm_matches_oracle_all_rows(name):
+    w = NV_SMALL[name]
+    r, a, sa, b, sb, es = nv_gemm_inputs(w, seed=21)
+    c = run_nv_gemm(r, a, sa, b, sb, es)
+    rows = np.arange(a.shape[0])
+    ref = oracle.gemm_rows_nvfp4(a, sa, b, sb, es, r.row_offsets, r.expert_ids, w.N, w.K, rows)
+    cov = ref["group"] >= 0
+    assert np.all(c[~cov] == SENT_BF16), "uncovered rows were written"
+    worst, exact = check_gemm_rows(c[cov], {k: v[cov] for k, v in ref.items() if k != "group"}, name)
+    print(f"{name}: max |err|/tol = {worst:.3g}, bf16-exact = {exact:.4f}")
+    assert exact > 0.9
+
+
+def test_nvfp4_gemm_random_codes_and_bad_expert_ids():
+    """Random codes and block scales (every e2m1 code, a wide E4M3 range); a
+    group with an out-of-range expert id leaves its rows untouched."""
+    w = W.WORKLOADS[5].scaled(tokens=64, E=5, masked=0, top_k=4, N=256, K=1024, swiglu=False)
+    r, a, sa, b, sb, es = nv_gemm_inputs(w, seed=4, quantized=False)
+    r.expert_ids = r.expert_ids.copy()
+    r.expert_ids[1] = 9
+    c = run_nv_gemm(r, a, sa, b, sb, es)
+    ref = oracle.gemm_rows_nvfp4(a, sa, b, sb, es, r.row_offsets, r.expert_ids, w.N, w.K, np.arange(a.shape[0]))
+    cov = ref["group"] >= 0
+    assert (~cov).any() and np.all(c[~cov] == SENT_BF16)
+    check_gemm_rows(c[cov], {k: v[cov] for k, v in ref.items() if k != "group"}, "random codes")
+
+
+def test_nvfp4_gemm_full_size_sampled_rows():
+    """The mxfp4_swiglu routing at full size (32,768 routed rows, 128 experts,
+    K = 7168) as a plain NVFP4 GEMM with N = 4096; seeded random operands,
+    sampled rows (first / last of every group and random ones)."""
+    w = W.WORKLOADS[5].scaled(swiglu=False)
+    r, a, sa, b, sb, es = nv_gemm_inputs(w, seed=8, quantized=False)
+    c = run_nv_gemm(r, a, sa, b, sb, es, hint=int(r.counts.max()))
+    rng = np.random.default_rng(88)
+    rows = []
+    for g in range(len(r.expert_ids)):
+        lo, hi = int(r.row_offsets[g]), int(r.row_offsets[g + 1])
+        if hi > lo:
+            rows += [lo, hi - 1]
+    rows = np.unique(np.array(rows + list(rng.integers(0, a.shape[0], 32))))
+    ref = oracle.gemm_rows_nvfp4(a, sa, b, sb, es, r.row_offsets, r.expert_ids, w.N, w.K, rows)
+    worst, exact = check_gemm_rows(c[rows], ref, "full size")
+    print(f"full size: {rows.size} rows, max |err|/tol = {worst:.3g}, bf16-exact = {exact:.4f}")
