@@ -326,6 +326,62 @@ def main():
                                "down_proj_flop": d_flops, "combine_ms": round(c_avg, 4),
                                "combine_GBps": round(c_bytes / (c_avg * 1e-3) / 1e9, 1), "combine_bytes": c_bytes})
         del bd, sbd, yd, comb
+        torch.cuda.empty_cache()
+        # The NVFP4 variant of the gate/up GEMM on the same routing: quantize the
+        # routed rows (per-expert tensor scale 448*6 / the expert's amax, an
+        # input choice) and the plain NVFP4 grouped GEMM with N = 2I (f16
+        # matrix cores; no fused epilogue for this format).
+        def group_amax(t2d, offs, n):
+            am = torch.ones(n, dtype=torch.float32, device=t2d.device)
+            rowmax = t2d.abs().amax(dim=1).float()
+            for g in range(n):
+                lo, hi = int(offs[g]), int(offs[g + 1])
+                if hi > lo:
+                    am[g] = rowmax[lo:hi].max().clamp_min(1e-30)
+            return am
+        E = w.E
+        sfa = torch.ones(E, dtype=torch.float32, device="cuda")
+        am = group_amax(x, r.row_offsets, len(r.expert_ids))
+        for g in range(len(r.expert_ids)):
+            sfa[int(r.expert_ids[g])] = 2688.0 / am[g]
+        wt = W.weights(w, device="cuda")
+        sfw = 2688.0 / wt.reshape(E, -1).abs().amax(dim=1).float().clamp_min(1e-30)
+        bn, sbn = mxg.quantize_weights_nvfp4(wt, sfw)
+        del wt
+        torch.cuda.empty_cache()
+        esn = (1.0 / (sfa.double() * sfw.double())).float()
+        an = torch.empty((T, K // 2), dtype=torch.uint8, device="cuda")
+        san = torch.empty((T, K // 16), dtype=torch.uint8, device="cuda")
+        cn = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
+
+        def nv_quant():
+            mxg.mx_grouped_quantize_nvfp4(x, an, san, sfa, off, ids)
+
+        def nv_gemm():
+            mxg.mx_grouped_matmul_nvfp4(an, san, bn, sbn, esn, cn, off, ids, hint)
+
+        for _ in range(args.warmup):
+            nv_quant()
+            nv_gemm()
+        nq_ms, ng_ms = [], []
+        for _ in range(args.steps):
+            ed[0].record(stream)
+            nv_quant()
+            ed[1].record(stream)
+            nv_gemm()
+            ed[2].record(stream)
+            torch.cuda.synchronize()
+            nq_ms.append(ed[0].elapsed_time(ed[1]))
+            ng_ms.append(ed[1].elapsed_time(ed[2]))
+        nq_avg, ng_avg = float(np.mean(nq_ms)), float(np.mean(ng_ms))
+        nq_bytes = T * K * 2 + T * (K // 2 + K // 16)
+        ng_flops = 2.0 * T * N * K
+        out["kernels"].update({"nvfp4_quantize_ms": round(nq_avg, 4),
+                               "nvfp4_quantize_GBps": round(nq_bytes / (nq_avg * 1e-3) / 1e9, 1),
+                               "nvfp4_gemm_ms": round(ng_avg, 4),
+                               "nvfp4_gemm_TFLOPs": round(ng_flops / (ng_avg * 1e-3) / 1e12, 1),
+                               "nvfp4_gemm_frac_f16_peak": round(ng_flops / (ng_avg * 1e-3) / 2.5e15, 4)})
+        del bn, sbn, an, san, cn
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, r, x, args.cpu_seconds)
     print(json.dumps(out), flush=True)
