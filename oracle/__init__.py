@@ -104,6 +104,11 @@ def lib() -> ctypes.CDLL:
         L.mxo_gemm_rows_nvfp4.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I64, _I64, _I64, _P, _I64,
                                           _P, _P, _P, _P]
         L.mxo_gemm_rows_nvfp4.restype = ctypes.c_int
+        L.mxo_silu_requant_nvfp4.argtypes = [_P, _P, _P, _P, _P, _P, _I32, _I32, _I64, _I64, _P]
+        L.mxo_silu_requant_nvfp4.restype = ctypes.c_int
+        L.mxo_gemm_swiglu_rows_nvfp4.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I64, _I64, _I64,
+                                                 _P, _I64, _P, _P, _P, _P, _P]
+        L.mxo_gemm_swiglu_rows_nvfp4.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -390,3 +395,56 @@ def gemm_rows_nvfp4(a, a_scale, b, b_scale, expert_scales, offsets, expert_ids, 
     if rc != 0:
         raise ValueError("oracle gemm_nvfp4: invalid arguments")
     return {"out": out, "exact": exact, "bound": bound, "group": group}
+
+
+def silu_requant_nvfp4(h_bf16, offsets, expert_ids, y_tensor_scales, yq=None, ys=None, want_y64: bool = False):
+    """Chained gated activation + NVFP4 requant of bf16 [T, 2I] (gate/up interleaved);
+    rows of group g use y_tensor_scales[expert_ids[g]] (encode side).  Returns
+    (yq u8 [T, I/2], ys u8 E4M3 [T, I/16]) and, optionally, fp64 y [T, I]."""
+    h = _c(h_bf16, np.uint16)
+    T, N2 = h.shape
+    I = N2 // 2
+    off = _c(offsets, np.uint32)
+    ids = _c(expert_ids, np.int32)
+    sf = _c(y_tensor_scales, np.float32).ravel()
+    if yq is None:
+        yq = np.zeros((T, I // 2), np.uint8)
+    if ys is None:
+        ys = np.zeros((T, I // 16), np.uint8)
+    y64 = np.full((T, I), np.nan, np.float64) if want_y64 else None
+    rc = lib().mxo_silu_requant_nvfp4(_ptr(h), _ptr(yq), _ptr(ys), _ptr(sf), _ptr(off), _ptr(ids), off.size - 1,
+                                      sf.size, T, I, _ptr(y64))
+    if rc != 0:
+        raise ValueError("oracle silu_requant_nvfp4: invalid arguments")
+    return (yq, ys, y64) if want_y64 else (yq, ys)
+
+
+def gemm_swiglu_rows_nvfp4(a, a_scale, w, w_scale, expert_scales, row_scales_bf16, y_tensor_scales, offsets,
+                           expert_ids, I: int, K: int, rows, want_exact: bool = True):
+    """Fused NVFP4 gate/up GEMM (+ optional bf16 row scales) + SwiGLU + NVFP4 requant
+    for ``rows``.  Returns dict with yq [n, I/2], ys [n, I/16], gu_exact / gu_bound
+    [n, 2I] and group [n]."""
+    a = _c(a, np.uint8)
+    w = _c(w, np.uint8)
+    a_scale = _c(a_scale, np.uint8)
+    w_scale = _c(w_scale, np.uint8)
+    es = _c(expert_scales, np.float32).ravel()
+    rs = None if row_scales_bf16 is None else _c(row_scales_bf16, np.uint16).ravel()
+    sf = _c(y_tensor_scales, np.float32).ravel()
+    T = a.shape[0]
+    E = w.shape[0]
+    off = _c(offsets, np.uint32)
+    ids = _c(expert_ids, np.int32)
+    r = _c(rows, np.int64).ravel()
+    n = r.size
+    yq = np.zeros((n, I // 2), np.uint8)
+    ys = np.zeros((n, I // 16), np.uint8)
+    gu_exact = np.zeros((n, 2 * I), np.float64) if want_exact else None
+    gu_bound = np.zeros((n, 2 * I), np.float64) if want_exact else None
+    group = np.zeros((n,), np.int32)
+    rc = lib().mxo_gemm_swiglu_rows_nvfp4(_ptr(a), _ptr(a_scale), _ptr(w), _ptr(w_scale), _ptr(es), _ptr(rs),
+                                          _ptr(sf), _ptr(off), _ptr(ids), off.size - 1, E, T, I, K, _ptr(r), n,
+                                          _ptr(yq), _ptr(ys), _ptr(gu_exact), _ptr(gu_bound), _ptr(group))
+    if rc != 0:
+        raise ValueError("oracle gemm_swiglu_nvfp4: invalid arguments")
+    return {"yq": yq, "ys": ys, "gu_exact": gu_exact, "gu_bound": gu_bound, "group": group}

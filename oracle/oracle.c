@@ -586,6 +586,91 @@ int mxo_gemm_rows_nvfp4(const uint8_t* a, const uint8_t* a_scale, const uint8_t*
     return MXO_OK;
 }
 
+/* NVFP4 gated activation + requant (NvMxf4f8Strategy fused_silu_quantize()
+ * and grouped_matmul_swiglu() with input_scales, the raw per-expert SiLU-output
+ * scale that the strategy inverts before use; a_row_scales).  Readings: sf_y
+ * below is that inverted (encode-side) scale; y_j = bf16(silu(g_j) u_j) as in
+ * silu_requant_row, quantized to NVFP4 along j in blocks of 16 exactly as
+ * quantize_row_nvfp4 does for a row of bf16 values.                        */
+static void silu_requant_row_nvfp4(const uint16_t* h, int64_t I, float sf, uint8_t* yq, uint8_t* ys, double* y64) {
+    uint16_t yb[16];
+    for (int64_t b = 0; b < I / 16; ++b) {
+        for (int i = 0; i < 16; ++i) {
+            int64_t j = b * 16 + i;
+            double g = mxo_bf16_value(h[2 * j]);
+            double u = mxo_bf16_value(h[2 * j + 1]);
+            double y = g * u / (1.0 + exp(-g));
+            if (y64) y64[j] = y;
+            yb[i] = mxo_bf16_round(y);
+        }
+        quantize_row_nvfp4(yb, 16, sf, yq + b * 8, ys + b);
+    }
+}
+
+/* Rows of group g (expert id in [0, E)) use sf_y[ids[g]]; h bf16 [T, 2I];
+ * yq [T, I/2], ys E4M3 [T, I/16]; uncovered rows are left as they were.   */
+int mxo_silu_requant_nvfp4(const uint16_t* h, uint8_t* yq, uint8_t* ys, const float* sf_y, const uint32_t* off,
+                           const int32_t* ids, int32_t G, int32_t E, int64_t T, int64_t I, double* y64) {
+    if (!h || !yq || !ys || !sf_y || !off || !ids || G < 0 || E <= 0 || T < 0 || I <= 0 || (I % 16) != 0)
+        return MXO_EINVAL;
+    for (int32_t g = 0; g < G; ++g) {
+        int64_t lo, hi;
+        group_range(off, g, T, &lo, &hi);
+        if (lo > hi || ids[g] < 0 || ids[g] >= E) continue;
+        const float f = sf_y[ids[g]];
+#pragma omp parallel for schedule(dynamic, 16)
+        for (int64_t t = lo; t < hi; ++t)
+            silu_requant_row_nvfp4(h + t * 2 * I, I, f, yq + t * (I / 2), ys + t * (I / 16), y64 ? y64 + t * I : NULL);
+    }
+    return MXO_OK;
+}
+
+/* Fused NVFP4 gate/up GEMM + SwiGLU + NVFP4 requant on a list of rows: the
+ * NVFP4 GEMM (expert scale included), times the optional bf16 row scale
+ * rs[t] (reading: "applied with the expert scale before the SwiGLU"), each
+ * output rounded to bf16, then silu_requant_row_nvfp4 with sf_y[e].
+ * gu_exact / gu_bound include the row scale.                                */
+int mxo_gemm_swiglu_rows_nvfp4(const uint8_t* a, const uint8_t* a_scale, const uint8_t* w, const uint8_t* w_scale,
+                               const float* expert_scale, const uint16_t* row_scale, const float* sf_y,
+                               const uint32_t* off, const int32_t* ids, int32_t G, int32_t E, int64_t T, int64_t I,
+                               int64_t K, const int64_t* rows, int64_t nrows, uint8_t* yq, uint8_t* ys,
+                               double* gu_exact, double* gu_bound, int32_t* group) {
+    if (!yq || !ys || !rows || !sf_y || I <= 0 || (I % 16) != 0) return MXO_EINVAL;
+    int64_t N = 2 * I;
+    double* ex = (double*)malloc(sizeof(double) * (size_t)(nrows * N > 0 ? nrows * N : 1));
+    double* bd = (double*)malloc(sizeof(double) * (size_t)(nrows * N > 0 ? nrows * N : 1));
+    int32_t* grp = (int32_t*)malloc(sizeof(int32_t) * (size_t)(nrows > 0 ? nrows : 1));
+    uint16_t* h = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)(N > 0 ? N : 1));
+    if (!ex || !bd || !grp || !h) {
+        free(ex);
+        free(bd);
+        free(grp);
+        free(h);
+        return MXO_EINVAL;
+    }
+    int rc = mxo_gemm_rows_nvfp4(a, a_scale, w, w_scale, expert_scale, off, ids, G, E, T, N, K, rows, nrows, NULL,
+                                 ex, bd, grp);
+    if (rc == MXO_OK) {
+        for (int64_t i = 0; i < nrows; ++i) {
+            if (group) group[i] = grp[i];
+            if (grp[i] < 0) continue;
+            const double rs = row_scale ? mxo_bf16_value(row_scale[rows[i]]) : 1.0;
+            for (int64_t n = 0; n < N; ++n) {
+                const double v = ex[i * N + n] * rs;
+                h[n] = mxo_bf16_round(v);
+                if (gu_exact) gu_exact[i * N + n] = v;
+                if (gu_bound) gu_bound[i * N + n] = bd[i * N + n] * fabs(rs);
+            }
+            silu_requant_row_nvfp4(h, I, sf_y[ids[grp[i]]], yq + i * (I / 2), ys + i * (I / 16), NULL);
+        }
+    }
+    free(h);
+    free(grp);
+    free(bd);
+    free(ex);
+    return rc;
+}
+
 /* ------------------------------------------------------------------------- */
 /* Array forms of the scalar codecs, for exhaustive checks.                    */
 void mxo_e4m3_encode_array(const double* v, uint8_t* out, int64_t n) {

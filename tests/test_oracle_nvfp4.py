@@ -7,7 +7,10 @@ special blocks (zero, underflow, saturation), block locality (16 elements per
 scale), invariance of codes when x and the tensor scale trade a power of two
 (catches a tensor scale applied the wrong way round), the GEMM against a
 numpy matmul of independently decoded operands, and the GEMM against the
-already pinned MXFP4 oracle where every NVFP4 block scale is 1.
+already pinned MXFP4 oracle where every NVFP4 block scale is 1.  The
+SwiGLU + NVFP4 requant is pinned as the NVFP4 quantize of the pinned MXFP4
+path's y, the fused rows as that requant of the pinned NVFP4 GEMM, and the
+row scale by trading a power of two with the expert scale.
 """
 import json
 import os
@@ -186,3 +189,68 @@ def test_gemm_with_unit_block_scales_equals_mxfp4():
     mx = oracle.gemm_rows(oracle.MXFP4, a, np.full((11, K // 32), 127, np.uint8), b,
                           np.full((E, N, K // 32), 127, np.uint8), off, ids, N, K, np.arange(11))
     assert np.array_equal(nv["exact"], mx["exact"]) and np.array_equal(nv["out"], mx["out"])
+
+
+# ----------------------------------------------------------------------------- SwiGLU + NVFP4 requant
+def gate_up(rng, T, I):
+    vals = rng.standard_normal((T, 2 * I)) * np.exp(rng.uniform(-4, 3, (T, 1)))
+    vals[0, :6] = [0.0, 5.0, 20.0, 0.25, -0.0, 3.0]
+    return oracle.bf16_round_array(vals)
+
+
+def test_silu_requant_nvfp4_is_the_nvfp4_quantize_of_y():
+    """The requant is the (pinned) NVFP4 quantize applied to y = bf16(silu(g) u),
+    with y taken from the (pinned) MXFP4 requant's fp64 y."""
+    rng = np.random.default_rng(17)
+    T, I = 9, 64
+    h = gate_up(rng, T, I)
+    off = np.array([0, 4, 9], np.uint32)
+    ids = np.array([1, 0], np.int32)
+    sf = np.array([3.0, 250.0], np.float32)
+    yq, ys = oracle.silu_requant_nvfp4(h, off, ids, sf)
+    _, _, y64 = oracle.silu_requant(h, np.array([0, T], np.uint32), want_y64=True)
+    yb = oracle.bf16_round_array(y64)
+    q_ref, s_ref = oracle.quantize_nvfp4(yb, off, ids, sf)
+    assert np.array_equal(yq, q_ref) and np.array_equal(ys, s_ref)
+    # g = 20, u = 0.25: silu(20) * 0.25 rounds to 5.0 exactly; g = 0 gives 0
+    assert oracle.bf16_value_array(yb[0, :3]).tolist() == [0.0, 5.0, 0.0]
+
+
+def test_gemm_swiglu_nvfp4_composes_gemm_and_requant():
+    rng = np.random.default_rng(23)
+    E, I, K = 3, 32, 64
+    off = np.array([0, 4, 4, 10], np.uint32)
+    ids = np.array([2, 0, 1], np.int32)
+    a, sa = random_nvfp4(rng, (10,), K)
+    w, ws = random_nvfp4(rng, (E, 2 * I), K)
+    es = np.array([0.5, 0.25, 1.0], np.float32)
+    rs = oracle.bf16_round_array(rng.uniform(0.5, 2.0, 10))
+    sfy = np.array([10.0, 2.0, 40.0], np.float32)
+    rows = np.arange(10)
+    fused = oracle.gemm_swiglu_rows_nvfp4(a, sa, w, ws, es, rs, sfy, off, ids, I, K, rows)
+    g = oracle.gemm_rows_nvfp4(a, sa, w, ws, es, off, ids, 2 * I, K, rows)
+    h = oracle.bf16_round_array(g["exact"] * oracle.bf16_value_array(rs)[:, None])
+    yq, ys = oracle.silu_requant_nvfp4(h, off, ids, sfy)
+    cov = fused["group"] >= 0
+    assert np.array_equal(fused["yq"][cov], yq[cov]) and np.array_equal(fused["ys"][cov], ys[cov])
+    np.testing.assert_array_equal(fused["gu_exact"][cov], (g["exact"] * oracle.bf16_value_array(rs)[:, None])[cov])
+
+
+def test_gemm_swiglu_nvfp4_row_scale_trades_with_expert_scale():
+    """Row scale 2^j with expert scale 2^-j leaves every output unchanged (all
+    products exact); no row scale is the row scale 1."""
+    rng = np.random.default_rng(29)
+    E, I, K = 2, 32, 32
+    off = np.array([0, 5, 8], np.uint32)
+    ids = np.array([0, 1], np.int32)
+    a, sa = random_nvfp4(rng, (8,), K)
+    w, ws = random_nvfp4(rng, (E, 2 * I), K)
+    sfy = np.array([5.0, 7.0], np.float32)
+    es = np.array([1.0, 0.5], np.float32)
+    base = oracle.gemm_swiglu_rows_nvfp4(a, sa, w, ws, es, None, sfy, off, ids, I, K, np.arange(8))
+    rs = oracle.bf16_round_array(np.full(8, 4.0))
+    traded = oracle.gemm_swiglu_rows_nvfp4(a, sa, w, ws, es / 4, rs, sfy, off, ids, I, K, np.arange(8))
+    assert np.array_equal(base["yq"], traded["yq"]) and np.array_equal(base["ys"], traded["ys"])
+    ones = oracle.gemm_swiglu_rows_nvfp4(a, sa, w, ws, es, oracle.bf16_round_array(np.ones(8)), sfy, off, ids, I, K,
+                                         np.arange(8))
+    assert np.array_equal(base["yq"], ones["yq"]) and np.array_equal(base["ys"], ones["ys"])
