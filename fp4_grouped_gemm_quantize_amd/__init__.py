@@ -32,7 +32,7 @@ LIB_PATH = os.path.join(_PKG, "libmxg.so")
 
 EXPORTED = ("mx_grouped_quantize", "mx_grouped_quantize_gather", "mx_grouped_matmul", "mx_grouped_matmul_swiglu",
             "mx_silu_quantize", "mx_moe_combine", "mx_grouped_quantize_nvfp4", "mx_grouped_matmul_nvfp4",
-            "mxg_status_string")
+            "mx_grouped_matmul_swiglu_nvfp4", "mx_silu_quantize_nvfp4", "mxg_status_string")
 
 
 class MxgError(RuntimeError):
@@ -66,9 +66,12 @@ def lib() -> ctypes.CDLL:
         L.mx_moe_combine.argtypes = [_P, _I64, _I64, _P, _P, _I64, _I32, _P, _P]
         L.mx_grouped_quantize_nvfp4.argtypes = [_P, _P, _P, _P, _P, _P, _I32, _I32, _I64, _I64, _P]
         L.mx_grouped_matmul_nvfp4.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I64, _I64, _I64, _I64, _P]
+        L.mx_grouped_matmul_swiglu_nvfp4.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I64,
+                                                     _I64, _I64, _I64, _P]
+        L.mx_silu_quantize_nvfp4.argtypes = [_P, _P, _P, _P, _P, _P, _I32, _I32, _I64, _I64, _P]
         for name in ("mx_grouped_quantize", "mx_grouped_quantize_gather", "mx_grouped_matmul",
                      "mx_grouped_matmul_swiglu", "mx_silu_quantize", "mx_moe_combine", "mx_grouped_quantize_nvfp4",
-                     "mx_grouped_matmul_nvfp4"):
+                     "mx_grouped_matmul_nvfp4", "mx_grouped_matmul_swiglu_nvfp4", "mx_silu_quantize_nvfp4"):
             getattr(L, name).restype = ctypes.c_int
         L.mxg_status_string.argtypes = [ctypes.c_int]
         L.mxg_status_string.restype = ctypes.c_char_p
@@ -206,6 +209,53 @@ def mx_grouped_matmul_nvfp4(a_q, a_scales, b_q, b_scales, expert_scales, c, row_
     _check(lib().mx_grouped_matmul_nvfp4(_ptr(a_q), _ptr(a_scales), _ptr(b_q), _ptr(b_scales), _ptr(expert_scales),
                                          _ptr(c), _ptr(row_offsets), _ptr(expert_ids), G, E, T, N, K,
                                          int(max_rows_per_group_hint), _stream(a_q)), "mx_grouped_matmul_nvfp4")
+
+
+def mx_grouped_matmul_swiglu_nvfp4(a_q, a_scales, w_q, w_scales, expert_scales, y_tensor_scales, y_q, y_scales,
+                                   row_offsets, expert_ids, a_row_scales=None, max_rows_per_group_hint: int = 0) -> None:
+    """Fused NVFP4 gate/up grouped GEMM + SwiGLU + NVFP4 requant into y_q [T, I/2],
+    y_scales [T, I/16]; y_tensor_scales fp32 [E] (encode side), a_row_scales bf16 [T] or None."""
+    _expect(a_q, "a_q", _U8)
+    _expect(w_q, "w_q", _U8)
+    dev = a_q.device
+    T = a_q.shape[0]
+    E, N2 = w_q.shape[0], w_q.shape[1]
+    I = N2 // 2
+    K = a_q.shape[1] * 2
+    _expect(w_q, "w_q", _U8, (E, N2, K // 2), dev)
+    _expect(a_scales, "a_scales", _U8, (T, K // 16), dev)
+    _expect(w_scales, "w_scales", _U8, (E, N2, K // 16), dev)
+    _expect(expert_scales, "expert_scales", _F32, (E,), dev)
+    _expect(y_tensor_scales, "y_tensor_scales", _F32, (E,), dev)
+    if a_row_scales is not None:
+        _expect(a_row_scales, "a_row_scales", _BF16, (T,), dev)
+    _expect(y_q, "y_q", _U8, (T, I // 2), dev)
+    _expect(y_scales, "y_scales", _U8, (T, I // 16), dev)
+    _expect(row_offsets, "row_offsets", _U32, None, dev)
+    G = row_offsets.numel() - 1
+    _expect(expert_ids, "expert_ids", _I32T, (G,), dev)
+    _check(lib().mx_grouped_matmul_swiglu_nvfp4(_ptr(a_q), _ptr(a_scales), _ptr(w_q), _ptr(w_scales),
+                                                _ptr(expert_scales), _ptr(a_row_scales), _ptr(y_tensor_scales),
+                                                _ptr(y_q), _ptr(y_scales), _ptr(row_offsets), _ptr(expert_ids), G, E,
+                                                T, I, K, int(max_rows_per_group_hint), _stream(a_q)),
+           "mx_grouped_matmul_swiglu_nvfp4")
+
+
+def mx_silu_quantize_nvfp4(h, y_q, y_scales, y_tensor_scales, row_offsets, expert_ids) -> None:
+    """SwiGLU + NVFP4 requant of bf16 h [T, 2I] into y_q [T, I/2], y_scales [T, I/16]."""
+    _expect(h, "h", _BF16)
+    T, N2 = h.shape
+    I = N2 // 2
+    dev = h.device
+    _expect(y_q, "y_q", _U8, (T, I // 2), dev)
+    _expect(y_scales, "y_scales", _U8, (T, I // 16), dev)
+    _expect(y_tensor_scales, "y_tensor_scales", _F32, None, dev)
+    _expect(row_offsets, "row_offsets", _U32, None, dev)
+    G = row_offsets.numel() - 1
+    _expect(expert_ids, "expert_ids", _I32T, (G,), dev)
+    _check(lib().mx_silu_quantize_nvfp4(_ptr(h), _ptr(y_q), _ptr(y_scales), _ptr(y_tensor_scales), _ptr(row_offsets),
+                                        _ptr(expert_ids), G, y_tensor_scales.numel(), T, I, _stream(h)),
+           "mx_silu_quantize_nvfp4")
 
 
 def mx_grouped_matmul(fmt: int, a_q, a_scales, b_q, b_scales, c, row_offsets, expert_ids,

@@ -144,6 +144,44 @@ mxg_status mx_grouped_matmul_nvfp4(const void* a_q, const void* a_scales, const 
     return from_hip(mxg::launch_grouped_gemm(p, stream));
 }
 
+mxg_status mx_grouped_matmul_swiglu_nvfp4(const void* a_q, const void* a_scales, const void* w_q,
+                                          const void* w_scales, const float* expert_scales,
+                                          const void* a_row_scales_bf16, const float* y_tensor_scales, void* y_q,
+                                          void* y_scales, const uint32_t* row_offsets, const int32_t* expert_ids,
+                                          int32_t num_groups, int32_t num_experts, int64_t total_rows, int64_t I,
+                                          int64_t K, int64_t max_rows_per_group_hint, hipStream_t stream) {
+    if (K <= 0 || I <= 0 || num_experts <= 0 || total_rows < 0 || num_groups < 0) return MXG_ERROR_INVALID_VALUE;
+    if (K % 512 != 0 || I % 32 != 0 || num_groups > MXG_MAX_GROUPS) return MXG_ERROR_NOT_SUPPORTED;
+    if (I > INT32_MAX / 4 || total_rows > INT32_MAX) return MXG_ERROR_NOT_SUPPORTED;
+    if (total_rows == 0 || num_groups == 0) return MXG_SUCCESS;  // nothing is read or written
+    if (!a_q || !a_scales || !w_q || !w_scales || !expert_scales || !y_tensor_scales || !y_q || !y_scales ||
+        !row_offsets || !expert_ids)
+        return MXG_ERROR_INVALID_VALUE;
+    if (!aligned(a_q, 16) || !aligned(a_scales, 16) || !aligned(w_q, 16) || !aligned(w_scales, 16) ||
+        !aligned(y_q, 16) || !aligned(expert_scales, 4) || !aligned(y_tensor_scales, 4) ||
+        !aligned(a_row_scales_bf16, 2) || !aligned(row_offsets, 4) || !aligned(expert_ids, 4))
+        return MXG_ERROR_INVALID_VALUE;
+    mxg::GemmProblem p{3, a_q, a_scales, w_q, w_scales, nullptr, y_q, y_scales, row_offsets, expert_ids,
+                       num_groups, num_experts, total_rows, 2 * I, K, max_rows_per_group_hint, expert_scales,
+                       a_row_scales_bf16, y_tensor_scales};
+    return from_hip(mxg::launch_grouped_gemm(p, stream));
+}
+
+mxg_status mx_silu_quantize_nvfp4(const void* h_bf16, void* y_q, void* y_scales, const float* y_tensor_scales,
+                                  const uint32_t* row_offsets, const int32_t* expert_ids, int32_t num_groups,
+                                  int32_t num_experts, int64_t total_rows, int64_t I, hipStream_t stream) {
+    if (I <= 0 || total_rows < 0 || num_groups < 0 || num_experts <= 0) return MXG_ERROR_INVALID_VALUE;
+    if (I % 16 != 0 || num_groups > MXG_MAX_GROUPS) return MXG_ERROR_NOT_SUPPORTED;
+    if (total_rows == 0 || num_groups == 0) return MXG_SUCCESS;
+    if (!h_bf16 || !y_q || !y_scales || !y_tensor_scales || !row_offsets || !expert_ids)
+        return MXG_ERROR_INVALID_VALUE;
+    if (!aligned(h_bf16, 16) || !aligned(y_q, 16) || !aligned(y_tensor_scales, 4) || !aligned(row_offsets, 4) ||
+        !aligned(expert_ids, 4))
+        return MXG_ERROR_INVALID_VALUE;
+    return from_hip(mxg::launch_silu_quantize_nvfp4(h_bf16, y_q, y_scales, y_tensor_scales, row_offsets, expert_ids,
+                                                    num_groups, num_experts, total_rows, I, stream));
+}
+
 mxg_status mx_grouped_matmul_swiglu(mxg_format fmt, const void* a_q, const void* a_scales, const void* w_q,
                                     const void* w_scales, void* y_q, void* y_scales,
                                     const uint32_t* row_offsets, const int32_t* expert_ids, int32_t num_groups,

@@ -637,7 +637,10 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
         } else {
             // Requant rows of 32 outputs with the same code the standalone
             // activation kernel runs.
+            // (NVFP4: gate/up = bf16(acc * fl32(expert_scale * row_scale)),
+            // requant to NVFP4 blocks of 16 under y's tensor scale.)
             static_assert(BN % 64 == 0, "fused tile must hold whole 32-output blocks");
+            const float es_e = F::kNV ? args.es[e] : 1.0f;
 #pragma unroll
             for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -646,7 +649,16 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int row = wm * WTM + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                        srow(row)[col] = (uint16_t)f32_to_bf16(acc[i][j][r]);
+                        float v = acc[i][j][r];
+                        if constexpr (F::kNV) {
+                            float f = es_e;
+                            if (args.rs) {
+                                const int64_t grow = m0 + row < m_end ? m0 + row : m_end - 1;
+                                f = es_e * bf16_to_f32(args.rs[grow]);
+                            }
+                            v = v * f;
+                        }
+                        srow(row)[col] = (uint16_t)f32_to_bf16(v);
                     }
                 }
             }
@@ -666,12 +678,25 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
                 float y[8];
 #pragma unroll
                 for (int k = 0; k < 8; ++k) y[k] = bf16_to_f32(f32_to_bf16(silu_mul(gu[2 * k], gu[2 * k + 1])));
-                uint2 code;
-                const int X = mx_encode8<true>(y, code);
                 const int64_t grow = m0 + row;
                 const int64_t gblk = n0 / 64 + blk;
-                if (grow < m_end && n0 + blk * 64 < n_end)
-                    mx_store8<true>(code, X, args.yq + grow * (I / 2), args.ys + grow * (I / 32), gblk * 4 + l4, l4);
+                const bool store = grow < m_end && n0 + blk * 64 < n_end;
+                if constexpr (F::kNV) {
+                    // lanes (0, 1) and (2, 3) of the group each form a 16-output block
+                    uint32_t sc;
+                    const uint32_t code = nv_encode8(y, args.ysf[e], sc);
+                    const int64_t unit = gblk * 4 + l4;  // 8-output unit within the row
+                    if (store) {
+                        *reinterpret_cast<uint32_t*>(args.yq + grow * (I / 2) + unit * 4) = code;
+                        if ((l4 & 1) == 0) args.ys[grow * (I / 16) + (unit >> 1)] = (uint8_t)sc;
+                    }
+                } else {
+                    uint2 code;
+                    const int X = mx_encode8<true>(y, code);
+                    if (store)
+                        mx_store8<true>(code, X, args.yq + grow * (I / 2), args.ys + grow * (I / 32), gblk * 4 + l4,
+                                        l4);
+                }
             }
         }
         __syncthreads();  // LDS is reused by the next tile's prologue
@@ -720,8 +745,7 @@ template <int FMT, bool SWIGLU>
 hipError_t launch_fmt(const GemmProblem& p, hipStream_t stream) {
     if constexpr (FMT == 3) {
         // NVFP4: the 128 x 256 tile with LDS-staged scales (K a multiple of 512)
-        static_assert(!SWIGLU, "NVFP4 has no fused epilogue here");
-        return launch_tile<TileLargeMxKA, FMT, false, true>(p, stream, kBandMx);
+        return launch_tile<TileLargeMxKA, FMT, SWIGLU, true>(p, stream, kBandMx);
     } else {
         // Average rows per non-empty group decides the regime; the optional host
         // hint (largest group) can only move a problem to the larger tile.
@@ -782,6 +806,8 @@ GemmArgs make_args(const GemmProblem& p, int BM, int BN, int mband, int per_cu, 
     a.ntiles_n = (int)((p.N + BN - 1) / BN);
     a.mband = mband > 0 ? mband : 1;
     a.es = p.es;
+    a.rs = static_cast<const uint16_t*>(p.rs);
+    a.ysf = p.ysf;
     // Upper bound on M tiles: each non-empty group adds at most one partial tile.
     const int64_t groups_nonempty = p.G < p.T ? p.G : p.T;
     const int64_t mtiles_bound = p.T / BM + groups_nonempty;
@@ -804,7 +830,7 @@ hipError_t launch_grouped_gemm(const GemmProblem& p, hipStream_t stream) {
         case 2:
             return swiglu ? launch_fmt<2, true>(p, stream) : launch_fmt<2, false>(p, stream);
         case 3:
-            return swiglu ? hipErrorInvalidValue : launch_fmt<3, false>(p, stream);
+            return swiglu ? launch_fmt<3, true>(p, stream) : launch_fmt<3, false>(p, stream);
         default:
             return hipErrorInvalidValue;
     }

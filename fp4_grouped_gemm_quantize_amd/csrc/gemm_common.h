@@ -36,6 +36,8 @@ struct GemmArgs {
     int mband;          // tile order within a group: bands of mband M tiles, N walked within a band
                         // (1: M tiles outer; >= the group's M tiles: N tiles outer)
     const float* es;    // NVFP4: per-expert epilogue scale (fp32 [E]); unused otherwise
+    const uint16_t* rs; // NVFP4 fused: optional bf16 scale per routed row (nullptr: 1)
+    const float* ysf;   // NVFP4 fused: per-expert encode-side tensor scale of y (fp32 [E])
 };
 
 // FMT: 0 = FP8 rowwise, 1 = MXFP8, 2 = MXFP4, 3 = NVFP4.

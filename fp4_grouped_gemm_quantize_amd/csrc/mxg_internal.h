@@ -26,6 +26,10 @@ hipError_t launch_combine(const void* y, int64_t T, int64_t H, const int32_t* ro
 hipError_t launch_silu_quantize(const void* h, void* yq, void* ys, const uint32_t* off, int G, int64_t T,
                                 int64_t I, hipStream_t stream);
 
+// NVFP4 requant of y = bf16(silu(g) u): rows of group g use y_scales_sf[ids[g]].
+hipError_t launch_silu_quantize_nvfp4(const void* h, void* yq, void* ys, const float* y_sf, const uint32_t* off,
+                                      const int32_t* ids, int G, int E, int64_t T, int64_t I, hipStream_t stream);
+
 // Grouped GEMM; when yq != nullptr the SwiGLU + MXFP4 requant epilogue runs
 // (N = 2I) and c is not written.
 struct GemmProblem {
@@ -45,7 +49,9 @@ struct GemmProblem {
     int64_t N;
     int64_t K;
     int64_t max_rows_hint;
-    const float* es;  // NVFP4 (fmt 3): per-expert epilogue scale, fp32 [E]
+    const float* es;   // NVFP4 (fmt 3): per-expert epilogue scale, fp32 [E]
+    const void* rs;    // NVFP4 fused: optional bf16 row scales [T]
+    const float* ysf;  // NVFP4 fused: per-expert encode-side tensor scale of y, fp32 [E]
 };
 
 hipError_t launch_grouped_gemm(const GemmProblem& p, hipStream_t stream);

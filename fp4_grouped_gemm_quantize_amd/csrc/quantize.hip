@@ -287,6 +287,48 @@ __global__ __launch_bounds__(kThreads) void silu_quantize_kernel(const uint16_t*
     }
 }
 
+// SwiGLU + NVFP4 requant: as above, with lane pairs forming 16-output blocks
+// and the row's group supplying the expert's tensor scale of y.
+__global__ __launch_bounds__(kThreads) void silu_quantize_nv_kernel(const uint16_t* __restrict__ h,
+                                                                    uint8_t* __restrict__ yq,
+                                                                    uint8_t* __restrict__ ys,
+                                                                    const uint32_t* __restrict__ off, int G,
+                                                                    int64_t T, int64_t I, NvScales nv) {
+    __shared__ uint32_t s_off[kMaxGroups + 1];
+    load_offsets(s_off, off, G);
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t nw = (int64_t)gridDim.x * kWavesPerBlock;
+    const int64_t nunits = I / 8;  // even: I is a multiple of 16
+    for (int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave; t < T; t += nw) {
+        const int g = wave_row_group(s_off, nv.ids, G, nv.E, T, t);
+        if (g < 0) continue;
+        const float sf = nv.sf[nv.ids[g]];
+        const uint4* hr = reinterpret_cast<const uint4*>(h + t * 2 * I);
+        uint8_t* qrow = yq + t * (I / 2);
+        uint8_t* srow = ys + t * (I / 16);
+        for (int64_t base = 0; base < nunits; base += kWave) {
+            const int64_t idx = base + lane;
+            uint4 v0 = make_uint4(0, 0, 0, 0), v1 = make_uint4(0, 0, 0, 0);
+            if (idx < nunits) {
+                v0 = hr[2 * idx];
+                v1 = hr[2 * idx + 1];
+            }
+            float gu[16];
+            unpack8(v0, gu);
+            unpack8(v1, gu + 8);
+            float y[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) y[i] = bf16_to_f32(f32_to_bf16(silu_mul(gu[2 * i], gu[2 * i + 1])));
+            uint32_t sc;
+            const uint32_t packed = nv_encode8(y, sf, sc);
+            if (idx < nunits) {
+                *reinterpret_cast<uint32_t*>(qrow + idx * 4) = packed;
+                if ((lane & 1) == 0) srow[idx >> 1] = (uint8_t)sc;
+            }
+        }
+    }
+}
+
 // Persistent grid: as many blocks as can be resident, at most one wave per row.
 template <class Kern>
 int64_t persistent_grid(Kern kernel, int64_t T) {
@@ -359,6 +401,14 @@ hipError_t launch_silu_quantize(const void* h, void* yq, void* ys, const uint32_
     hipLaunchKernelGGL(silu_quantize_kernel, dim3((unsigned)persistent_grid(silu_quantize_kernel, T)), dim3(kThreads),
                        0, stream, static_cast<const uint16_t*>(h), static_cast<uint8_t*>(yq), static_cast<uint8_t*>(ys),
                        off, G, T, I);
+    return hipGetLastError();
+}
+
+hipError_t launch_silu_quantize_nvfp4(const void* h, void* yq, void* ys, const float* y_sf, const uint32_t* off,
+                                      const int32_t* ids, int G, int E, int64_t T, int64_t I, hipStream_t stream) {
+    hipLaunchKernelGGL(silu_quantize_nv_kernel, dim3((unsigned)persistent_grid(silu_quantize_nv_kernel, T)),
+                       dim3(kThreads), 0, stream, static_cast<const uint16_t*>(h), static_cast<uint8_t*>(yq),
+                       static_cast<uint8_t*>(ys), off, G, T, I, NvScales{ids, y_sf, E});
     return hipGetLastError();
 }
 

@@ -17,6 +17,9 @@
  *                             scale, e2m1 codes) under a per-expert tensor scale
  *   mx_grouped_matmul_nvfp4   ragged grouped GEMM of NVFP4 operands with a
  *                             per-expert epilogue scale, BF16 output
+ *   mx_grouped_matmul_swiglu_nvfp4  NVFP4 gate/up grouped GEMM fused with SwiGLU
+ *                             and an NVFP4 requant of the activation
+ *   mx_silu_quantize_nvfp4    its unfused second half
  *   mx_moe_combine            after the down-projection: each token's row is the
  *                             router-weighted sum of its routed rows
  *
@@ -203,6 +206,61 @@ mxg_status mx_grouped_matmul_nvfp4(const void* a_q, const void* a_scales, const 
                                    const int32_t* expert_ids, int32_t num_groups, int32_t num_experts,
                                    int64_t total_rows, int64_t N, int64_t K, int64_t max_rows_per_group_hint,
                                    hipStream_t stream);
+
+/*
+ * mx_grouped_matmul_swiglu_nvfp4 -- NVFP4 gate/up grouped GEMM + SwiGLU +
+ * NVFP4 requant, fused.
+ * (NvMxf4f8Strategy, grouped_matmul_swiglu(): expert_scales -- per-expert
+ *  epilogue scaling factors; input_scales -- the raw per-expert SiLU-output
+ *  scale, which the strategy inverts before the kernel uses it; a_row_scales
+ *  -- an optional BF16 scale per hidden row applied with the expert scale
+ *  before the SwiGLU, NVFP4 only; prepare_swiglu_operands(): the inversion.
+ *  The arithmetic is not given; reading:)
+ *
+ *   g_j, u_j = bf16( acc * fl32(expert_scales[e] * a_row_scales[t]) ) for
+ *              columns 2j, 2j+1 of the NVFP4 GEMM against W[e] (rows
+ *              interleaved gate, up), acc its fp32 sum;
+ *   y_j      = bf16( g_j / (1 + e^-g_j) * u_j ), fp32;
+ *   (y_q, y_scales) = the NVFP4 quantization of y along j (blocks of 16)
+ *              under sf = y_tensor_scales[e], exactly as
+ *              mx_grouped_quantize_nvfp4 quantizes a row.
+ *
+ *   a_q, a_scales, w_q [E, 2I, K/2], w_scales [E, 2I, K/16], expert_scales
+ *              as mx_grouped_matmul_nvfp4.
+ *   a_row_scales_bf16  bf16 [total_rows] or NULL (all 1).
+ *   y_tensor_scales    fp32 [num_experts], encode side (1 / input_scale).
+ *   y_q [total_rows, I/2] u8; y_scales [total_rows, I/16] u8 E4M3.
+ * Without row scales the result equals mx_grouped_matmul_nvfp4 followed by
+ * mx_silu_quantize_nvfp4, byte for byte.
+ *
+ * Errors: as mx_grouped_matmul_nvfp4; NOT_SUPPORTED also for I % 32 != 0.
+ */
+mxg_status mx_grouped_matmul_swiglu_nvfp4(const void* a_q, const void* a_scales, const void* w_q,
+                                          const void* w_scales, const float* expert_scales,
+                                          const void* a_row_scales_bf16, const float* y_tensor_scales, void* y_q,
+                                          void* y_scales, const uint32_t* row_offsets, const int32_t* expert_ids,
+                                          int32_t num_groups, int32_t num_experts, int64_t total_rows, int64_t I,
+                                          int64_t K, int64_t max_rows_per_group_hint, hipStream_t stream);
+
+/*
+ * mx_silu_quantize_nvfp4 -- SwiGLU + NVFP4 requant of a BF16 gate/up tensor.
+ * (NvMxf4f8Strategy, fused_silu_quantize(input_scales): the gated activation,
+ *  then quantization, with the inverted per-expert scale.)
+ *
+ *   h_bf16    [total_rows, 2I] bf16, column 2j = gate_j, 2j+1 = up_j.
+ *   y_tensor_scales  fp32 [num_experts], encode side; rows of group g use
+ *             y_tensor_scales[expert_ids[g]]; a group whose id lies outside
+ *             [0, num_experts) is skipped.
+ *   y_q [total_rows, I/2] u8; y_scales [total_rows, I/16] u8 E4M3; only
+ *             covered rows are written.
+ *
+ * Errors: INVALID_VALUE for a null pointer, I <= 0, negative sizes,
+ * num_experts <= 0, misalignment; NOT_SUPPORTED for I % 16 != 0 or
+ * num_groups > MXG_MAX_GROUPS.
+ */
+mxg_status mx_silu_quantize_nvfp4(const void* h_bf16, void* y_q, void* y_scales, const float* y_tensor_scales,
+                                  const uint32_t* row_offsets, const int32_t* expert_ids, int32_t num_groups,
+                                  int32_t num_experts, int64_t total_rows, int64_t I, hipStream_t stream);
 
 /*
  * mx_grouped_matmul_swiglu -- fused gate/up grouped GEMM + SwiGLU + MXFP4 requant.

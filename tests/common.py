@@ -102,7 +102,8 @@ _SILU_ARGMIN = -1.2784645427610738  # where silu(z) = z / (1 + e^-z) is smallest
 
 
 def _silu(z):
-    return z / (1.0 + np.exp(-z))
+    with np.errstate(over="ignore"):  # exp(-z) = inf for very negative z: the limit -0 is right
+        return z / (1.0 + np.exp(-z))
 
 
 def _silu_range(lo, hi):

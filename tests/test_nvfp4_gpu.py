@@ -208,3 +208,186 @@ def test_nvfp4_gemm_full_size_sampled_rows():
     ref = oracle.gemm_rows_nvfp4(a, sa, b, sb, es, r.row_offsets, r.expert_ids, w.N, w.K, rows)
     worst, exact = check_gemm_rows(c[rows], ref, "full size")
     print(f"full size: {rows.size} rows, max |err|/tol = {worst:.3g}, bf16-exact = {exact:.4f}")
+
+
+# ----------------------------------------------------------------------------- SwiGLU + NVFP4 requant
+from common import _silu_range, gemm_tolerance  # noqa: E402
+
+E2M1_TAB = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6, -0.0, -0.5, -1, -1.5, -2, -3, -4, -6], np.float64)
+
+
+def fragile_mask(y64, rel=2.0**-20):
+    return oracle.bf16_round_array(y64 * (1 - rel)) != oracle.bf16_round_array(y64 * (1 + rel))
+
+
+def nibbles(q):
+    return np.stack([q & 0xF, q >> 4], axis=-1).reshape(q.shape[0], -1)
+
+
+def check_requant_exact(yq, ys, yq_ref, ys_ref, y64):
+    """Bit-exact except in blocks holding an element whose fp64 y lies within
+    2^-20 (relative) of a bf16 rounding boundary (the GPU evaluates silu in fp32)."""
+    n, I = y64.shape
+    frag_blk = fragile_mask(y64).reshape(n, I // 16, 16).any(axis=2)
+    assert np.array_equal(ys[~frag_blk], ys_ref[~frag_blk]), "block scales differ in non-fragile blocks"
+    strict = np.repeat(~frag_blk & (ys == ys_ref), 16, axis=1)
+    assert np.array_equal(nibbles(yq)[strict], nibbles(yq_ref)[strict]), "codes differ in non-fragile blocks"
+    return float(frag_blk.mean())
+
+
+def check_nv_swiglu_interval(yq, ys, gu_exact, gu_bound, sf_rows):
+    """The fused result must be reachable from SOME gate/up pair inside the GEMM
+    tolerance: its E4M3 block scale must come from an amax in the block's
+    interval, and each code must be the rounding of some y in the element's
+    interval under that scale (the encode steps are monotone)."""
+    tol = gemm_tolerance(gu_exact, gu_bound)
+    lo = oracle.bf16_value_array(oracle.bf16_round_array(gu_exact - tol))
+    hi = oracle.bf16_value_array(oracle.bf16_round_array(gu_exact + tol))
+    s_lo, s_hi = _silu_range(lo[:, 0::2], hi[:, 0::2])
+    u_lo, u_hi = lo[:, 1::2], hi[:, 1::2]
+    corners = np.stack([s_lo * u_lo, s_lo * u_hi, s_hi * u_lo, s_hi * u_hi])
+    c_min, c_max = corners.min(axis=0), corners.max(axis=0)
+    c_min = c_min - np.abs(c_min) * 2.0**-20
+    c_max = c_max + np.abs(c_max) * 2.0**-20
+    y_lo = oracle.bf16_value_array(oracle.bf16_round_array(c_min))
+    y_hi = oracle.bf16_value_array(oracle.bf16_round_array(c_max))
+    n, I = y_lo.shape
+    amag_hi = np.maximum(np.abs(y_lo), np.abs(y_hi)).reshape(n, I // 16, 16).max(axis=2)
+    amag_lo = np.where((y_lo <= 0) & (y_hi >= 0), 0.0,
+                       np.minimum(np.abs(y_lo), np.abs(y_hi))).reshape(n, I // 16, 16).max(axis=2)
+    sf = np.asarray(sf_rows, np.float32)[:, None]
+
+    def scale_code(amag):
+        u = (amag.astype(np.float32) / np.float32(6.0)) * sf
+        return oracle.e4m3_encode_array(np.minimum(u, np.float32(448.0)).astype(np.float64)).astype(np.int64)
+
+    c_lo_s, c_hi_s = scale_code(amag_lo), scale_code(amag_hi)
+    sc = ys.astype(np.int64)
+    bad = (sc < c_lo_s) | (sc > c_hi_s)
+    if bad.any():
+        i, b = np.argwhere(bad)[0]
+        raise AssertionError(f"scale outside interval at row {i} block {b}: gpu {sc[i, b]:#x} "
+                             f"allowed [{c_lo_s[i, b]:#x}, {c_hi_s[i, b]:#x}]")
+    sval = oracle.e4m3_value_array(ys.astype(np.uint8)).astype(np.float32)
+    r = np.where(sval == 0, np.float32(0), sf / np.where(sval == 0, np.float32(1), sval)).astype(np.float32)
+    rr = np.repeat(r, 16, axis=1)
+    e_lo = E2M1_TAB[oracle.e2m1_encode_array((y_lo.astype(np.float32) * rr).astype(np.float64))]
+    e_hi = E2M1_TAB[oracle.e2m1_encode_array((y_hi.astype(np.float32) * rr).astype(np.float64))]
+    val = E2M1_TAB[nibbles(yq)]
+    bad = (val < np.minimum(e_lo, e_hi)) | (val > np.maximum(e_lo, e_hi))
+    if bad.any():
+        i, j = np.argwhere(bad)[0]
+        raise AssertionError(f"code outside interval at row {i} output {j}: gpu {val[i, j]} "
+                             f"allowed [{e_lo[i, j]}, {e_hi[i, j]}]")
+
+
+@pytest.mark.parametrize("I,T", [(16, 17), (1024, 96), (80, 300)])
+def test_silu_quantize_nvfp4_matches_oracle(I, T):
+    rng = np.random.default_rng(I + T)
+    vals = rng.standard_normal((T, 2 * I)) * np.exp(rng.uniform(-6, 4, (T, 1)))
+    vals[0, :8] = [0.0, 5.0, -0.0, 3.0, 1.0, 2.0, -20.0, 4.0]
+    h = oracle.bf16_round_array(vals)
+    # groups: [0, 3) expert 1, an empty one, [3, T-8) with an out-of-range id (skipped),
+    # [T-8, T-4) expert 0; the last 4 rows are uncovered
+    off = np.array([0, 3, 3, T - 8, T - 4], np.uint32)
+    ids = np.array([1, 0, 5, 0], np.int32)
+    sfy = np.array([0.5, 300.0], np.float32)
+    yq_ref, ys_ref, y64 = oracle.silu_requant_nvfp4(h, off, ids, sfy, np.full((T, I // 2), 0xA5, np.uint8),
+                                                    np.full((T, I // 16), 0x5A, np.uint8), want_y64=True)
+    hg = to_gpu(h.view(np.int16)).view(torch.bfloat16)
+    yq = torch.full((T, I // 2), 0xA5, dtype=torch.uint8, device="cuda")
+    ys = torch.full((T, I // 16), 0x5A, dtype=torch.uint8, device="cuda")
+    mxg.mx_silu_quantize_nvfp4(hg, yq, ys, to_gpu(sfy), offsets_gpu(off), to_gpu(ids))
+    yq, ys = yq.cpu().numpy(), ys.cpu().numpy()
+    cov = np.zeros(T, bool)
+    cov[0:3] = True
+    cov[T - 8:T - 4] = True
+    assert np.all(yq[~cov] == 0xA5) and np.all(ys[~cov] == 0x5A)
+    frac = check_requant_exact(yq[cov], ys[cov], yq_ref[cov], ys_ref[cov], y64[cov])
+    print(f"fragile block fraction {frac:.2e}")
+
+
+def nv_swiglu_inputs(w, seed, quantized=True):
+    r, a, sa, b, sb, es = nv_gemm_inputs(w, seed, quantized)
+    sfy = np.random.default_rng(seed + 7).uniform(0.5, 500.0, size=w.E).astype(np.float32)
+    return r, a, sa, b, sb, es, sfy
+
+
+def run_nv_fused(r, a, sa, b, sb, es, sfy, rs=None, hint=0):
+    T, I = a.shape[0], b.shape[1] // 2
+    yq = torch.full((T, I // 2), 0xA5, dtype=torch.uint8, device="cuda")
+    ys = torch.full((T, I // 16), 0x5A, dtype=torch.uint8, device="cuda")
+    rs_g = None if rs is None else to_gpu(rs.view(np.int16)).view(torch.bfloat16)
+    mxg.mx_grouped_matmul_swiglu_nvfp4(to_gpu(a), to_gpu(sa), to_gpu(b), to_gpu(sb), to_gpu(es), to_gpu(sfy), yq, ys,
+                                       offsets_gpu(r.row_offsets), to_gpu(r.expert_ids.astype(np.int32)), rs_g, hint)
+    torch.cuda.synchronize()
+    return yq.cpu().numpy(), ys.cpu().numpy()
+
+
+def run_nv_chained(r, a, sa, b, sb, es, sfy):
+    T, N = a.shape[0], b.shape[1]
+    c = torch.zeros((T, N), dtype=torch.bfloat16, device="cuda")
+    off, ids = offsets_gpu(r.row_offsets), to_gpu(r.expert_ids.astype(np.int32))
+    mxg.mx_grouped_matmul_nvfp4(to_gpu(a), to_gpu(sa), to_gpu(b), to_gpu(sb), to_gpu(es), c, off, ids)
+    yq = torch.full((T, N // 4), 0xA5, dtype=torch.uint8, device="cuda")
+    ys = torch.full((T, N // 32), 0x5A, dtype=torch.uint8, device="cuda")
+    mxg.mx_silu_quantize_nvfp4(c, yq, ys, to_gpu(sfy), off, ids)
+    torch.cuda.synchronize()
+    return yq.cpu().numpy(), ys.cpu().numpy()
+
+
+NV_FUSED = {
+    "k512": W.WORKLOADS[5].scaled(tokens=96, E=8, masked=1, top_k=4, N=320, K=512),
+    "k1024_tall": W.WORKLOADS[5].scaled(tokens=512, E=4, masked=0, top_k=2, N=256, K=1024),
+}
+
+
+@pytest.mark.parametrize("name", list(NV_FUSED))
+def test_nvfp4_fused_equals_chained_and_oracle(name):
+    w = NV_FUSED[name]
+    r, a, sa, b, sb, es, sfy = nv_swiglu_inputs(w, seed=31)
+    yq, ys = run_nv_fused(r, a, sa, b, sb, es, sfy)
+    yq2, ys2 = run_nv_chained(r, a, sa, b, sb, es, sfy)
+    assert np.array_equal(yq, yq2) and np.array_equal(ys, ys2), "fused and chained NVFP4 paths differ"
+    rows = np.arange(a.shape[0])
+    ref = oracle.gemm_swiglu_rows_nvfp4(a, sa, b, sb, es, None, sfy, r.row_offsets, r.expert_ids, w.N // 2, w.K, rows)
+    cov = ref["group"] >= 0
+    assert np.all(yq[~cov] == 0xA5) and np.all(ys[~cov] == 0x5A)
+    sf_rows = sfy[r.expert_ids[ref["group"][cov]]]
+    check_nv_swiglu_interval(yq[cov], ys[cov], ref["gu_exact"][cov], ref["gu_bound"][cov], sf_rows)
+    same = np.mean(ys[cov] == ref["ys"][cov])
+    print(f"{name}: scale bytes equal to the oracle's {same:.4f}")
+    assert same > 0.95
+
+
+def test_nvfp4_fused_with_row_scales_vs_oracle():
+    w = NV_FUSED["k512"]
+    r, a, sa, b, sb, es, sfy = nv_swiglu_inputs(w, seed=37)
+    rs = oracle.bf16_round_array(np.random.default_rng(3).uniform(0.25, 4.0, a.shape[0]))
+    yq, ys = run_nv_fused(r, a, sa, b, sb, es, sfy, rs=rs)
+    rows = np.arange(a.shape[0])
+    ref = oracle.gemm_swiglu_rows_nvfp4(a, sa, b, sb, es, rs, sfy, r.row_offsets, r.expert_ids, w.N // 2, w.K, rows)
+    cov = ref["group"] >= 0
+    check_nv_swiglu_interval(yq[cov], ys[cov], ref["gu_exact"][cov], ref["gu_bound"][cov],
+                             sfy[r.expert_ids[ref["group"][cov]]])
+    assert np.mean(ys[cov] == ref["ys"][cov]) > 0.95
+
+
+def test_nvfp4_fused_full_size_sampled_rows():
+    """The mxfp4_swiglu routing and shape (32,768 rows, I = 2048, K = 7168) in
+    NVFP4, seeded random operands: fused == chained on every row, and sampled
+    rows inside the oracle's intervals."""
+    w = W.WORKLOADS[5]
+    r, a, sa, b, sb, es, sfy = nv_swiglu_inputs(w, seed=41, quantized=False)
+    yq, ys = run_nv_fused(r, a, sa, b, sb, es, sfy, hint=int(r.counts.max()))
+    yq2, ys2 = run_nv_chained(r, a, sa, b, sb, es, sfy)
+    assert np.array_equal(yq, yq2) and np.array_equal(ys, ys2), "fused and chained NVFP4 paths differ"
+    rng = np.random.default_rng(42)
+    rows = []
+    for g in range(len(r.expert_ids)):
+        lo, hi = int(r.row_offsets[g]), int(r.row_offsets[g + 1])
+        if hi > lo:
+            rows += [lo, hi - 1]
+    rows = np.unique(np.array(rows + list(rng.integers(0, a.shape[0], 16))))
+    ref = oracle.gemm_swiglu_rows_nvfp4(a, sa, b, sb, es, None, sfy, r.row_offsets, r.expert_ids, w.N // 2, w.K, rows)
+    check_nv_swiglu_interval(yq[rows], ys[rows], ref["gu_exact"], ref["gu_bound"], sfy[r.expert_ids[ref["group"]]])
