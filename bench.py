@@ -360,28 +360,43 @@ def main():
         def nv_gemm():
             mxg.mx_grouped_matmul_nvfp4(an, san, bn, sbn, esn, cn, off, ids, hint)
 
+        # fused: SwiGLU + NVFP4 requant of y under a per-expert scale (input choice)
+        sfy = torch.full((E,), 400.0, dtype=torch.float32, device="cuda")
+        yqn = torch.empty((T, N // 4), dtype=torch.uint8, device="cuda")
+        ysn = torch.empty((T, N // 32), dtype=torch.uint8, device="cuda")
+
+        def nv_fused():
+            mxg.mx_grouped_matmul_swiglu_nvfp4(an, san, bn, sbn, esn, sfy, yqn, ysn, off, ids, None, hint)
+
         for _ in range(args.warmup):
             nv_quant()
             nv_gemm()
-        nq_ms, ng_ms = [], []
+            nv_fused()
+        ed.append(torch.cuda.Event(enable_timing=True))
+        nq_ms, ng_ms, nf_ms = [], [], []
         for _ in range(args.steps):
             ed[0].record(stream)
             nv_quant()
             ed[1].record(stream)
             nv_gemm()
             ed[2].record(stream)
+            nv_fused()
+            ed[3].record(stream)
             torch.cuda.synchronize()
             nq_ms.append(ed[0].elapsed_time(ed[1]))
             ng_ms.append(ed[1].elapsed_time(ed[2]))
-        nq_avg, ng_avg = float(np.mean(nq_ms)), float(np.mean(ng_ms))
+            nf_ms.append(ed[2].elapsed_time(ed[3]))
+        nq_avg, ng_avg, nf_avg = float(np.mean(nq_ms)), float(np.mean(ng_ms)), float(np.mean(nf_ms))
         nq_bytes = T * K * 2 + T * (K // 2 + K // 16)
         ng_flops = 2.0 * T * N * K
         out["kernels"].update({"nvfp4_quantize_ms": round(nq_avg, 4),
                                "nvfp4_quantize_GBps": round(nq_bytes / (nq_avg * 1e-3) / 1e9, 1),
                                "nvfp4_gemm_ms": round(ng_avg, 4),
                                "nvfp4_gemm_TFLOPs": round(ng_flops / (ng_avg * 1e-3) / 1e12, 1),
-                               "nvfp4_gemm_frac_f16_peak": round(ng_flops / (ng_avg * 1e-3) / 2.5e15, 4)})
-        del bn, sbn, an, san, cn
+                               "nvfp4_gemm_frac_f16_peak": round(ng_flops / (ng_avg * 1e-3) / 2.5e15, 4),
+                               "nvfp4_fused_ms": round(nf_avg, 4),
+                               "nvfp4_fused_TFLOPs": round(ng_flops / (nf_avg * 1e-3) / 1e12, 1)})
+        del bn, sbn, an, san, cn, yqn, ysn
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, r, x, args.cpu_seconds)
     print(json.dumps(out), flush=True)
