@@ -109,6 +109,11 @@ def lib() -> ctypes.CDLL:
         L.mxo_gemm_swiglu_rows_nvfp4.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I64, _I64, _I64,
                                                  _P, _I64, _P, _P, _P, _P, _P]
         L.mxo_gemm_swiglu_rows_nvfp4.restype = ctypes.c_int
+        L.mxo_quantize_padded.argtypes = [ctypes.c_int, _P, _P, _P, _P, _I64, _P, _I32, _I64, _I64]
+        L.mxo_quantize_padded.restype = ctypes.c_int
+        L.mxo_gemm_rows_padded.argtypes = [ctypes.c_int, _P, _P, _P, _I64, _P, _P, _P, _P, _I32, _I32, _I64, _I64,
+                                           _I64, _P, _I64, _P, _P, _P, _P]
+        L.mxo_gemm_rows_padded.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -448,3 +453,52 @@ def gemm_swiglu_rows_nvfp4(a, a_scale, w, w_scale, expert_scales, row_scales_bf1
     if rc != 0:
         raise ValueError("oracle gemm_swiglu_nvfp4: invalid arguments")
     return {"yq": yq, "ys": ys, "gu_exact": gu_exact, "gu_bound": gu_bound, "group": group}
+
+
+# ---------------------------------------------------------------- padded MX scale layouts
+def quantize_padded(fmt: int, x_bf16, offsets, scales_offsets, scale_rows: int, q=None, scales=None):
+    """MX grouped quantize with the scales of group g's row t in row
+    scales_offsets[g] + (t - offsets[g]) of a [scale_rows, K/32] tensor; a row whose
+    scale row is at or past scale_rows is left untouched.  Returns (q, scales)."""
+    x = _c(x_bf16, np.uint16)
+    T, K = x.shape
+    off = _c(offsets, np.uint32)
+    soff = _c(scales_offsets, np.uint32).ravel()
+    qcols = K // 2 if fmt == MXFP4 else K
+    if q is None:
+        q = np.zeros((T, qcols), np.uint8)
+    if scales is None:
+        scales = np.zeros((scale_rows, K // 32), np.uint8)
+    assert soff.size >= off.size - 1 and scales.shape == (scale_rows, K // 32)
+    rc = lib().mxo_quantize_padded(fmt, _ptr(x), _ptr(q), _ptr(scales), _ptr(soff), scale_rows, _ptr(off),
+                                   off.size - 1, T, K)
+    if rc != 0:
+        raise ValueError("oracle quantize_padded: invalid arguments")
+    return q, scales
+
+
+def gemm_rows_padded(fmt: int, a, a_scale, a_scales_offsets, b, b_scale, offsets, expert_ids, N: int, K: int, rows,
+                     want_exact: bool = True):
+    """MX grouped GEMM rows with A's scales in a padded layout ([S, K/32], group g's
+    rows from row a_scales_offsets[g]); same return dict as gemm_rows."""
+    a = _c(a, np.uint8)
+    b = _c(b, np.uint8)
+    a_scale = _c(a_scale, np.uint8)
+    b_scale = _c(b_scale, np.uint8)
+    asoff = _c(a_scales_offsets, np.uint32).ravel()
+    T = a.shape[0]
+    E = b.shape[0]
+    off = _c(offsets, np.uint32)
+    ids = _c(expert_ids, np.int32)
+    r = _c(rows, np.int64).ravel()
+    n = r.size
+    out = np.zeros((n, N), np.uint16)
+    exact = np.zeros((n, N), np.float64) if want_exact else None
+    bound = np.zeros((n, N), np.float64) if want_exact else None
+    group = np.zeros((n,), np.int32)
+    rc = lib().mxo_gemm_rows_padded(fmt, _ptr(a), _ptr(a_scale), _ptr(asoff), a_scale.shape[0], _ptr(b),
+                                    _ptr(b_scale), _ptr(off), _ptr(ids), off.size - 1, E, T, N, K, _ptr(r), n,
+                                    _ptr(out), _ptr(exact), _ptr(bound), _ptr(group))
+    if rc != 0:
+        raise ValueError("oracle gemm_rows_padded: invalid arguments")
+    return {"out": out, "exact": exact, "bound": bound, "group": group}

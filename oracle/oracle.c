@@ -672,6 +672,77 @@ int mxo_gemm_swiglu_rows_nvfp4(const uint8_t* a, const uint8_t* a_scale, const u
 }
 
 /* ------------------------------------------------------------------------- */
+/* Padded / slot-strided MX scale layouts (grouped_quantize_dynamic_scaled_fp4_
+ * async_kernel: scales_offsets, the per-expert offsets into the scale tensor,
+ * found with row_offsets by binary search; NvMxf4f8Strategy grouped_quantize()
+ * "padded scale alignment", scales_offset; Struct_ep_dispatch_mxfp4: the
+ * fixed-stride slot layout [n_local_experts * max_padded_M, K_SCALES]).
+ * Reading: routed row t of group g keeps its K/32 scale bytes in row
+ * soff[g] + (t - row_offsets[g]) of a scale tensor of S rows (the slot layout
+ * is soff[g] = expert_ids[g] * max_padded_M); a row whose scale row lies at or
+ * past S is left untouched (codes included); scale rows nothing maps to are
+ * never written.  MX formats only (fmt 1, 2).                               */
+int mxo_quantize_padded(int fmt, const uint16_t* x, uint8_t* q, uint8_t* scales, const uint32_t* soff, int64_t S,
+                        const uint32_t* off, int32_t G, int64_t T, int64_t K) {
+    if (!x || !q || !scales || !soff || !off || G < 0 || T < 0 || S < 0 || K <= 0 || (K % 32) != 0) return MXO_EINVAL;
+    if (fmt != 1 && fmt != 2) return MXO_EINVAL;
+    const int elem = fmt == 2 ? MXO_E2M1 : MXO_E4M3;
+    const int64_t row_bytes = fmt == 2 ? K / 2 : K;
+    for (int32_t g = 0; g < G; ++g) {
+        int64_t lo, hi;
+        group_range(off, g, T, &lo, &hi);
+        if (lo > hi) continue;
+#pragma omp parallel for schedule(dynamic, 16)
+        for (int64_t t = lo; t < hi; ++t) {
+            const int64_t srow = (int64_t)soff[g] + (t - lo);
+            if (srow >= S) continue;
+            quantize_row_mx(elem, x + t * K, K, q + t * row_bytes, scales + srow * (K / 32));
+        }
+    }
+    return MXO_OK;
+}
+
+/* Grouped GEMM rows with A's scales in such a layout: the dense A scales are
+ * gathered row by row through the map above, then mxo_gemm_rows runs; a row
+ * whose scale row lies at or past Sa is reported uncovered (group -1).     */
+int mxo_gemm_rows_padded(int fmt, const uint8_t* a, const uint8_t* a_scale, const uint32_t* asoff, int64_t Sa,
+                         const uint8_t* b, const uint8_t* b_scale, const uint32_t* off, const int32_t* ids, int32_t G,
+                         int32_t E, int64_t T, int64_t N, int64_t K, const int64_t* rows, int64_t nrows, uint16_t* out,
+                         double* exact, double* bound, int32_t* group) {
+    if (!a_scale || !asoff || Sa < 0 || (fmt != 1 && fmt != 2) || K <= 0 || (K % 32) != 0 || T < 0 || G < 0)
+        return MXO_EINVAL;
+    const int64_t nblk = K / 32;
+    uint8_t* dense = (uint8_t*)calloc((size_t)(T > 0 ? T : 1) * (size_t)nblk, 1);
+    int32_t* grp = (int32_t*)malloc(sizeof(int32_t) * (size_t)(nrows > 0 ? nrows : 1));
+    if (!dense || !grp) {
+        free(dense);
+        free(grp);
+        return MXO_EINVAL;
+    }
+    for (int64_t i = 0; i < nrows; ++i) {
+        const int64_t t = rows[i];
+        const int32_t g = (t >= 0 && t < T) ? group_of_row(off, ids, G, E, T, t) : -1;
+        grp[i] = g;
+        if (g < 0) continue;
+        int64_t lo, hi;
+        group_range(off, g, T, &lo, &hi);
+        const int64_t srow = (int64_t)asoff[g] + (t - lo);
+        if (srow >= Sa) {
+            grp[i] = -1;
+            continue;
+        }
+        memcpy(dense + t * nblk, a_scale + srow * nblk, (size_t)nblk);
+    }
+    int rc = mxo_gemm_rows(fmt, a, dense, b, b_scale, off, ids, G, E, T, N, K, rows, nrows, out, exact, bound, group);
+    if (rc == MXO_OK && group)
+        for (int64_t i = 0; i < nrows; ++i)
+            if (grp[i] < 0) group[i] = -1;
+    free(grp);
+    free(dense);
+    return rc;
+}
+
+/* ------------------------------------------------------------------------- */
 /* Array forms of the scalar codecs, for exhaustive checks.                    */
 void mxo_e4m3_encode_array(const double* v, uint8_t* out, int64_t n) {
     for (int64_t i = 0; i < n; ++i) out[i] = mxo_e4m3_encode(v[i]);
