@@ -32,7 +32,8 @@ LIB_PATH = os.path.join(_PKG, "libmxg.so")
 
 EXPORTED = ("mx_grouped_quantize", "mx_grouped_quantize_gather", "mx_grouped_matmul", "mx_grouped_matmul_swiglu",
             "mx_silu_quantize", "mx_moe_combine", "mx_grouped_quantize_nvfp4", "mx_grouped_matmul_nvfp4",
-            "mx_grouped_matmul_swiglu_nvfp4", "mx_silu_quantize_nvfp4", "mxg_status_string")
+            "mx_grouped_matmul_swiglu_nvfp4", "mx_silu_quantize_nvfp4", "mx_grouped_quantize_padded",
+            "mx_grouped_matmul_padded", "mx_grouped_matmul_swiglu_padded", "mxg_status_string")
 
 
 class MxgError(RuntimeError):
@@ -69,9 +70,15 @@ def lib() -> ctypes.CDLL:
         L.mx_grouped_matmul_swiglu_nvfp4.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I64,
                                                      _I64, _I64, _I64, _P]
         L.mx_silu_quantize_nvfp4.argtypes = [_P, _P, _P, _P, _P, _P, _I32, _I32, _I64, _I64, _P]
+        L.mx_grouped_quantize_padded.argtypes = [ctypes.c_int, _P, _P, _P, _P, _I64, _P, _I32, _I64, _I64, _P]
+        L.mx_grouped_matmul_padded.argtypes = [ctypes.c_int, _P, _P, _P, _I64, _P, _P, _P, _P, _P, _I32, _I32,
+                                               _I64, _I64, _I64, _I64, _P]
+        L.mx_grouped_matmul_swiglu_padded.argtypes = [ctypes.c_int, _P, _P, _P, _I64, _P, _P, _P, _P, _P, _P, _I32,
+                                                      _I32, _I64, _I64, _I64, _I64, _P]
         for name in ("mx_grouped_quantize", "mx_grouped_quantize_gather", "mx_grouped_matmul",
                      "mx_grouped_matmul_swiglu", "mx_silu_quantize", "mx_moe_combine", "mx_grouped_quantize_nvfp4",
-                     "mx_grouped_matmul_nvfp4", "mx_grouped_matmul_swiglu_nvfp4", "mx_silu_quantize_nvfp4"):
+                     "mx_grouped_matmul_nvfp4", "mx_grouped_matmul_swiglu_nvfp4", "mx_silu_quantize_nvfp4",
+                     "mx_grouped_quantize_padded", "mx_grouped_matmul_padded", "mx_grouped_matmul_swiglu_padded"):
             getattr(L, name).restype = ctypes.c_int
         L.mxg_status_string.argtypes = [ctypes.c_int]
         L.mxg_status_string.restype = ctypes.c_char_p
@@ -256,6 +263,78 @@ def mx_silu_quantize_nvfp4(h, y_q, y_scales, y_tensor_scales, row_offsets, exper
     _check(lib().mx_silu_quantize_nvfp4(_ptr(h), _ptr(y_q), _ptr(y_scales), _ptr(y_tensor_scales), _ptr(row_offsets),
                                         _ptr(expert_ids), G, y_tensor_scales.numel(), T, I, _stream(h)),
            "mx_silu_quantize_nvfp4")
+
+
+def mx_grouped_quantize_padded(fmt: int, x, q, scales, scales_offsets, row_offsets) -> None:
+    """MX grouped quantize of bf16 x [T, K] with group g's scales from row
+    scales_offsets[g] of scales [S, K/32] (rows mapped past S are left untouched)."""
+    _expect(x, "x", _BF16)
+    T, K = x.shape
+    dev = x.device
+    qcols = K // 2 if fmt == MXFP4 else K
+    _expect(q, "q", _U8, (T, qcols), dev)
+    _expect(scales, "scales", _U8, None, dev)
+    if scales.dim() != 2 or scales.shape[1] != K // 32:
+        raise ValueError("scales must be [scale_rows, K/32]")
+    _expect(scales_offsets, "scales_offsets", _U32, None, dev)
+    _expect(row_offsets, "row_offsets", _U32, None, dev)
+    G = row_offsets.numel() - 1
+    if scales_offsets.numel() < G:
+        raise ValueError("scales_offsets needs one entry per group")
+    _check(lib().mx_grouped_quantize_padded(fmt, _ptr(x), _ptr(q), _ptr(scales), _ptr(scales_offsets),
+                                            scales.shape[0], _ptr(row_offsets), G, T, K, _stream(x)),
+           "mx_grouped_quantize_padded")
+
+
+def mx_grouped_matmul_padded(fmt: int, a_q, a_scales, a_scales_offsets, b_q, b_scales, c, row_offsets, expert_ids,
+                             max_rows_per_group_hint: int = 0) -> None:
+    """MX grouped GEMM with A's scales [S, K/32] in the padded layout."""
+    _expect(a_q, "a_q", _U8)
+    dev = a_q.device
+    T = a_q.shape[0]
+    E, N = b_q.shape[0], b_q.shape[1]
+    K = a_q.shape[1] * (2 if fmt == MXFP4 else 1)
+    _expect(b_q, "b_q", _U8, (E, N, a_q.shape[1]), dev)
+    _expect(a_scales, "a_scales", _U8, None, dev)
+    if a_scales.dim() != 2 or a_scales.shape[1] != K // 32:
+        raise ValueError("a_scales must be [scale_rows, K/32]")
+    _expect(b_scales, "b_scales", _U8, (E, N, K // 32), dev)
+    _expect(c, "c", _BF16, (T, N), dev)
+    _expect(a_scales_offsets, "a_scales_offsets", _U32, None, dev)
+    _expect(row_offsets, "row_offsets", _U32, None, dev)
+    G = row_offsets.numel() - 1
+    _expect(expert_ids, "expert_ids", _I32T, (G,), dev)
+    _check(lib().mx_grouped_matmul_padded(fmt, _ptr(a_q), _ptr(a_scales), _ptr(a_scales_offsets), a_scales.shape[0],
+                                          _ptr(b_q), _ptr(b_scales), _ptr(c), _ptr(row_offsets), _ptr(expert_ids), G,
+                                          E, T, N, K, int(max_rows_per_group_hint), _stream(a_q)),
+           "mx_grouped_matmul_padded")
+
+
+def mx_grouped_matmul_swiglu_padded(fmt: int, a_q, a_scales, a_scales_offsets, w_q, w_scales, y_q, y_scales,
+                                    row_offsets, expert_ids, max_rows_per_group_hint: int = 0) -> None:
+    """Fused MX gate/up GEMM + SwiGLU + MXFP4 requant with A's scales in the padded layout."""
+    _expect(a_q, "a_q", _U8)
+    dev = a_q.device
+    T = a_q.shape[0]
+    E, N2 = w_q.shape[0], w_q.shape[1]
+    I = N2 // 2
+    K = a_q.shape[1] * (2 if fmt == MXFP4 else 1)
+    _expect(w_q, "w_q", _U8, (E, N2, a_q.shape[1]), dev)
+    _expect(a_scales, "a_scales", _U8, None, dev)
+    if a_scales.dim() != 2 or a_scales.shape[1] != K // 32:
+        raise ValueError("a_scales must be [scale_rows, K/32]")
+    _expect(w_scales, "w_scales", _U8, (E, N2, K // 32), dev)
+    _expect(y_q, "y_q", _U8, (T, I // 2), dev)
+    _expect(y_scales, "y_scales", _U8, (T, I // 32), dev)
+    _expect(a_scales_offsets, "a_scales_offsets", _U32, None, dev)
+    _expect(row_offsets, "row_offsets", _U32, None, dev)
+    G = row_offsets.numel() - 1
+    _expect(expert_ids, "expert_ids", _I32T, (G,), dev)
+    _check(lib().mx_grouped_matmul_swiglu_padded(fmt, _ptr(a_q), _ptr(a_scales), _ptr(a_scales_offsets),
+                                                 a_scales.shape[0], _ptr(w_q), _ptr(w_scales), _ptr(y_q),
+                                                 _ptr(y_scales), _ptr(row_offsets), _ptr(expert_ids), G, E, T, I, K,
+                                                 int(max_rows_per_group_hint), _stream(a_q)),
+           "mx_grouped_matmul_swiglu_padded")
 
 
 def mx_grouped_matmul(fmt: int, a_q, a_scales, b_q, b_scales, c, row_offsets, expert_ids,

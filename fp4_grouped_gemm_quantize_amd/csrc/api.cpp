@@ -80,6 +80,21 @@ mxg_status mx_grouped_quantize_nvfp4(const void* x_bf16, void* q, void* scales, 
                                                num_experts, total_rows, K, stream));
 }
 
+mxg_status mx_grouped_quantize_padded(mxg_format fmt, const void* x_bf16, void* q, void* scales,
+                                      const uint32_t* scales_offsets, int64_t scale_rows,
+                                      const uint32_t* row_offsets, int32_t num_groups, int64_t total_rows, int64_t K,
+                                      hipStream_t stream) {
+    if (!valid_fmt(fmt)) return MXG_ERROR_INVALID_VALUE;
+    if (K <= 0 || total_rows < 0 || num_groups < 0 || scale_rows < 0) return MXG_ERROR_INVALID_VALUE;
+    if (fmt == MXG_FP8_E4M3_ROWWISE || K % 32 != 0 || num_groups > MXG_MAX_GROUPS) return MXG_ERROR_NOT_SUPPORTED;
+    if (total_rows == 0 || num_groups == 0) return MXG_SUCCESS;  // nothing is read or written
+    if (!x_bf16 || !q || !scales || !scales_offsets || !row_offsets) return MXG_ERROR_INVALID_VALUE;
+    if (!aligned(x_bf16, 16) || !aligned(q, 16) || !aligned(scales_offsets, 4) || !aligned(row_offsets, 4))
+        return MXG_ERROR_INVALID_VALUE;
+    return from_hip(mxg::launch_quantize_padded((int)fmt, x_bf16, q, scales, scales_offsets, scale_rows, row_offsets,
+                                                num_groups, total_rows, K, stream));
+}
+
 mxg_status mx_moe_combine(const void* y_bf16, int64_t total_rows, int64_t H, const int32_t* row_of_slot,
                           const float* weights, int64_t num_tokens, int32_t top_k, void* out_bf16,
                           hipStream_t stream) {
@@ -141,6 +156,57 @@ mxg_status mx_grouped_matmul_nvfp4(const void* a_q, const void* a_scales, const 
         return MXG_ERROR_INVALID_VALUE;
     mxg::GemmProblem p{3, a_q, a_scales, b_q, b_scales, c_bf16, nullptr, nullptr, row_offsets, expert_ids,
                        num_groups, num_experts, total_rows, N, K, max_rows_per_group_hint, expert_scales};
+    return from_hip(mxg::launch_grouped_gemm(p, stream));
+}
+
+// Padded A scales: the MX GEMM / fused GEMM with a_scales in the layout of
+// mx_grouped_quantize_padded.
+static mxg_status check_padded(mxg_format fmt, const uint32_t* a_scales_offsets, int64_t a_scale_rows,
+                               const void* a_scales) {
+    if (a_scale_rows < 0) return MXG_ERROR_INVALID_VALUE;
+    if (fmt == MXG_FP8_E4M3_ROWWISE) return MXG_ERROR_NOT_SUPPORTED;
+    if (!a_scales_offsets || !aligned(a_scales_offsets, 4) || !aligned(a_scales, 16)) return MXG_ERROR_INVALID_VALUE;
+    return MXG_SUCCESS;
+}
+
+mxg_status mx_grouped_matmul_padded(mxg_format fmt, const void* a_q, const void* a_scales,
+                                    const uint32_t* a_scales_offsets, int64_t a_scale_rows, const void* b_q,
+                                    const void* b_scales, void* c_bf16, const uint32_t* row_offsets,
+                                    const int32_t* expert_ids, int32_t num_groups, int32_t num_experts,
+                                    int64_t total_rows, int64_t N, int64_t K, int64_t max_rows_per_group_hint,
+                                    hipStream_t stream) {
+    mxg_status st = check_gemm_common(fmt, a_q, a_scales, b_q, b_scales, row_offsets, expert_ids, num_groups,
+                                      num_experts, total_rows, N, K);
+    if (st != MXG_SUCCESS) return st;
+    if (a_scale_rows < 0) return MXG_ERROR_INVALID_VALUE;
+    if (fmt == MXG_FP8_E4M3_ROWWISE) return MXG_ERROR_NOT_SUPPORTED;
+    if (total_rows == 0 || num_groups == 0) return MXG_SUCCESS;
+    if ((st = check_padded(fmt, a_scales_offsets, a_scale_rows, a_scales)) != MXG_SUCCESS) return st;
+    if (!c_bf16 || !aligned(c_bf16, 16)) return MXG_ERROR_INVALID_VALUE;
+    mxg::GemmProblem p{(int)fmt, a_q, a_scales, b_q, b_scales, c_bf16, nullptr, nullptr, row_offsets, expert_ids,
+                       num_groups, num_experts, total_rows, N, K, max_rows_per_group_hint, nullptr, nullptr, nullptr,
+                       a_scales_offsets, a_scale_rows};
+    return from_hip(mxg::launch_grouped_gemm(p, stream));
+}
+
+mxg_status mx_grouped_matmul_swiglu_padded(mxg_format fmt, const void* a_q, const void* a_scales,
+                                           const uint32_t* a_scales_offsets, int64_t a_scale_rows, const void* w_q,
+                                           const void* w_scales, void* y_q, void* y_scales,
+                                           const uint32_t* row_offsets, const int32_t* expert_ids,
+                                           int32_t num_groups, int32_t num_experts, int64_t total_rows, int64_t I,
+                                           int64_t K, int64_t max_rows_per_group_hint, hipStream_t stream) {
+    if (I <= 0) return MXG_ERROR_INVALID_VALUE;
+    mxg_status st = check_gemm_common(fmt, a_q, a_scales, w_q, w_scales, row_offsets, expert_ids, num_groups,
+                                      num_experts, total_rows, 2 * I, K);
+    if (st != MXG_SUCCESS) return st;
+    if (a_scale_rows < 0) return MXG_ERROR_INVALID_VALUE;
+    if (fmt == MXG_FP8_E4M3_ROWWISE || I % 32 != 0) return MXG_ERROR_NOT_SUPPORTED;
+    if (total_rows == 0 || num_groups == 0) return MXG_SUCCESS;
+    if ((st = check_padded(fmt, a_scales_offsets, a_scale_rows, a_scales)) != MXG_SUCCESS) return st;
+    if (!y_q || !y_scales || !aligned(y_q, 16)) return MXG_ERROR_INVALID_VALUE;
+    mxg::GemmProblem p{(int)fmt, a_q, a_scales, w_q, w_scales, nullptr, y_q, y_scales, row_offsets, expert_ids,
+                       num_groups, num_experts, total_rows, 2 * I, K, max_rows_per_group_hint, nullptr, nullptr,
+                       nullptr, a_scales_offsets, a_scale_rows};
     return from_hip(mxg::launch_grouped_gemm(p, stream));
 }
 

@@ -404,8 +404,16 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
                 *reinterpret_cast<uint4*>(slot + kAStage + (wave + NW * j) * 1024 + lane * 16) = tb[j];
         };
 
-        // ---- MX scale words of this lane's rows / columns, one stage ahead
-        const uint8_t* sa_base = static_cast<const uint8_t*>(args.as) + m0 * nblk;
+        // ---- MX scale words of this lane's rows / columns, one stage ahead.
+        // A padded A-scale layout moves the tile's first scale row (a tile
+        // never spans groups); a tile whose scale rows would run past the
+        // tensor is skipped (its outputs are left untouched).
+        int64_t sa_row0 = m0;
+        if (F::kMX && args.asoff) {
+            sa_row0 = (int64_t)args.asoff[tc.g] + (m0 - tc.glo);
+            if (sa_row0 + rows_in > args.as_rows) continue;  // uniform; before any LDS use
+        }
+        const uint8_t* sa_base = static_cast<const uint8_t*>(args.as) + sa_row0 * nblk;
         const uint8_t* sb_base = static_cast<const uint8_t*>(args.bs) + ((int64_t)e * args.N + n0) * nblk;
         uint32_t sa_off[TM], sb_off[TN];
         uint32_t wa[TM][kWords], wb[TN][kWords];
@@ -808,6 +816,8 @@ GemmArgs make_args(const GemmProblem& p, int BM, int BN, int mband, int per_cu, 
     a.es = p.es;
     a.rs = static_cast<const uint16_t*>(p.rs);
     a.ysf = p.ysf;
+    a.asoff = p.asoff;
+    a.as_rows = p.as_rows;
     // Upper bound on M tiles: each non-empty group adds at most one partial tile.
     const int64_t groups_nonempty = p.G < p.T ? p.G : p.T;
     const int64_t mtiles_bound = p.T / BM + groups_nonempty;

@@ -38,6 +38,8 @@ struct GemmArgs {
     const float* es;    // NVFP4: per-expert epilogue scale (fp32 [E]); unused otherwise
     const uint16_t* rs; // NVFP4 fused: optional bf16 scale per routed row (nullptr: 1)
     const float* ysf;   // NVFP4 fused: per-expert encode-side tensor scale of y (fp32 [E])
+    const uint32_t* asoff;  // padded MX A scales: group g's rows start at scale row asoff[g] (nullptr: dense)
+    int64_t as_rows;        // rows of the padded A scale tensor
 };
 
 // FMT: 0 = FP8 rowwise, 1 = MXFP8, 2 = MXFP4, 3 = NVFP4.
@@ -164,6 +166,8 @@ __device__ __forceinline__ void build_tile_prefix(const GemmArgs& args, uint32_t
 }
 
 struct TileCoord {
+    int g;           // group
+    int64_t glo;     // the group's first row
     int e;           // expert
     int64_t m0;      // first row of the tile
     int64_t m_end;   // one past its last real row
@@ -212,6 +216,8 @@ __device__ __forceinline__ TileCoord locate_tile(const GemmArgs& args, const uin
     const int nt = r / gm;
     const GroupRange gr = group_range(args.off, args.ids, g, args.T, args.E);
     TileCoord t;
+    t.g = g;
+    t.glo = gr.lo;
     t.e = args.ids[g];
     t.m0 = gr.lo + (int64_t)mt * BM;
     t.m_end = t.m0 + BM < gr.hi ? t.m0 + BM : gr.hi;

@@ -214,7 +214,8 @@ __device__ __forceinline__ uint32_t nv_encode8(const float* f, float sf, uint32_
 }
 
 // The group covering row t whose expert id lies in [0, E) (the lowest such
-// group), or -1.  Wave-cooperative, result wave-uniform; offsets from LDS.
+// group; with ids == nullptr any covering group), or -1.  Wave-cooperative,
+// result wave-uniform; offsets from LDS.
 __device__ __forceinline__ int wave_row_group(const uint32_t* s_off, const int32_t* ids, int G, int E, int64_t T,
                                               int64_t t) {
     const int lane = threadIdx.x & (kWave - 1);
@@ -226,8 +227,12 @@ __device__ __forceinline__ int wave_row_group(const uint32_t* s_off, const int32
             lo = lo < T ? lo : T;
             hi = hi < T ? hi : T;
             if (t >= lo && t < hi) {
-                const int e = ids[g];
-                hit = e >= 0 && e < E;
+                if (ids) {
+                    const int e = ids[g];
+                    hit = e >= 0 && e < E;
+                } else {
+                    hit = true;
+                }
             }
         }
         const uint64_t m = __ballot(hit);

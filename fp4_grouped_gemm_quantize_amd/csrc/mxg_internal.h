@@ -14,6 +14,11 @@ hipError_t launch_quantize_gather(int fmt, const void* x, int64_t nsrc, const in
                                   void* q, void* scales, const uint32_t* off, int G, int64_t T, int64_t K,
                                   hipStream_t stream);
 
+// MX (fmt 1, 2) with group g's scales from row scales_offsets[g] of a [scale_rows, K/32] tensor.
+hipError_t launch_quantize_padded(int fmt, const void* x, void* q, void* scales, const uint32_t* scales_offsets,
+                                  int64_t scale_rows, const uint32_t* off, int G, int64_t T, int64_t K,
+                                  hipStream_t stream);
+
 // NVFP4: rows of group g use tensor_scales[ids[g]]; groups with an id outside [0, E) are skipped.
 hipError_t launch_quantize_nvfp4(const void* x, void* q, void* scales, const float* tensor_scales,
                                   const uint32_t* off, const int32_t* ids, int G, int E, int64_t T, int64_t K,
@@ -52,6 +57,8 @@ struct GemmProblem {
     const float* es;   // NVFP4 (fmt 3): per-expert epilogue scale, fp32 [E]
     const void* rs;    // NVFP4 fused: optional bf16 row scales [T]
     const float* ysf;  // NVFP4 fused: per-expert encode-side tensor scale of y, fp32 [E]
+    const uint32_t* asoff;  // padded A scales: group g's rows from row asoff[g] (nullptr: dense)
+    int64_t as_rows;        // rows of that scale tensor
 };
 
 hipError_t launch_grouped_gemm(const GemmProblem& p, hipStream_t stream);

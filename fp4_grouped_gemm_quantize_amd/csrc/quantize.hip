@@ -54,6 +54,25 @@ struct NvScales {
     int E;
 };
 
+// Padded MX scale layout (grouped_quantize_dynamic_scaled_fp4_async_kernel:
+// scales_offsets): the scales of group g's row t go to row soff[g] + (t -
+// row_offsets[g]) of a scale tensor of S rows; a row mapped at or past S is
+// skipped.  soff == nullptr: the dense layout (scale row t).
+struct Pad {
+    const uint32_t* soff;
+    int64_t S;
+};
+
+// Scale row of row t under the layout, or -1 when the row is not written.
+__device__ __forceinline__ int64_t scale_row(const Pad& pd, const uint32_t* s_off, int G, int64_t T, int64_t t) {
+    if (!pd.soff) return wave_row_covered(s_off, G, T, t) ? t : -1;
+    const int g = wave_row_group(s_off, nullptr, G, 0, T, t);
+    if (g < 0) return -1;
+    const int64_t lo = (int64_t)s_off[g] < T ? (int64_t)s_off[g] : T;
+    const int64_t r = (int64_t)pd.soff[g] + (t - lo);
+    return r < pd.S ? r : -1;
+}
+
 template <bool GATHER>
 __device__ __forceinline__ int64_t source_row(const Gather& g, int64_t t) {
     if constexpr (!GATHER) {
@@ -74,7 +93,8 @@ template <int FMT, int NC, bool GATHER>
 __global__ __launch_bounds__(kThreads) void quantize_rows_kernel(const uint16_t* __restrict__ x,
                                                                  uint8_t* __restrict__ q, void* __restrict__ scales,
                                                                  const uint32_t* __restrict__ off, int G,
-                                                                 int64_t T, int64_t K, Gather ga, NvScales nv) {
+                                                                 int64_t T, int64_t K, Gather ga, NvScales nv,
+                                                                 Pad pd) {
     __shared__ uint32_t s_off[kMaxGroups + 1];
     load_offsets(s_off, off, G);
     const int lane = threadIdx.x & (kWave - 1);
@@ -120,8 +140,11 @@ __global__ __launch_bounds__(kThreads) void quantize_rows_kernel(const uint16_t*
                     }
                 }
             }
-        } else if (sr >= 0 && wave_row_covered(s_off, G, T, t)) {
-            if constexpr (FMT == 0) {
+        } else if (sr >= 0) {
+            const int64_t srix = scale_row(pd, s_off, G, T, t);  // -1: the row is not written
+            if (srix < 0) {
+                // skipped (uncovered, or no scale row in the padded layout)
+            } else if constexpr (FMT == 0) {
                 // bf16 magnitudes order like their bit patterns with the sign cleared
                 uint32_t amax_bits = 0;
 #pragma unroll
@@ -154,7 +177,7 @@ __global__ __launch_bounds__(kThreads) void quantize_rows_kernel(const uint16_t*
             } else {
                 constexpr bool FP4 = FMT == 2;
                 uint8_t* qrow = q + t * (FP4 ? K / 2 : K);
-                uint8_t* srow = static_cast<uint8_t*>(scales) + t * (K / 32);
+                uint8_t* srow = static_cast<uint8_t*>(scales) + srix * (K / 32);
 #pragma unroll
                 for (int c = 0; c < NC; ++c) {
                     const int idx = c * kWave + lane;
@@ -180,7 +203,8 @@ template <int FMT, bool GATHER>
 __global__ __launch_bounds__(kThreads) void quantize_long_kernel(const uint16_t* __restrict__ x,
                                                                  uint8_t* __restrict__ q, void* __restrict__ scales,
                                                                  const uint32_t* __restrict__ off, int G,
-                                                                 int64_t T, int64_t K, Gather ga, NvScales nv) {
+                                                                 int64_t T, int64_t K, Gather ga, NvScales nv,
+                                                                 Pad pd) {
     __shared__ uint32_t s_off[kMaxGroups + 1];
     load_offsets(s_off, off, G);
     const int lane = threadIdx.x & (kWave - 1);
@@ -209,7 +233,8 @@ __global__ __launch_bounds__(kThreads) void quantize_long_kernel(const uint16_t*
             }
             continue;
         }
-        if (!wave_row_covered(s_off, G, T, t)) continue;
+        const int64_t srix = scale_row(pd, s_off, G, T, t);
+        if (srix < 0) continue;
         if constexpr (FMT == 0) {
             uint32_t amax_bits = 0;
             for (int64_t idx = lane; idx < nvec; idx += kWave) {
@@ -235,7 +260,7 @@ __global__ __launch_bounds__(kThreads) void quantize_long_kernel(const uint16_t*
         } else {
             constexpr bool FP4 = FMT == 2;
             uint8_t* qrow = q + t * (FP4 ? K / 2 : K);
-            uint8_t* srow = static_cast<uint8_t*>(scales) + t * (K / 32);
+            uint8_t* srow = static_cast<uint8_t*>(scales) + srix * (K / 32);
             // whole 512-element chunks per iteration keep every lane in the loop
             for (int64_t base = 0; base < nvec; base += kWave) {
                 const int64_t idx = base + lane;
@@ -344,25 +369,27 @@ int64_t persistent_grid(Kern kernel, int64_t T) {
 
 template <class Kern>
 hipError_t launch_persistent(Kern kernel, const uint16_t* x, uint8_t* q, void* s, const uint32_t* off, int G,
-                             int64_t T, int64_t K, const Gather& ga, const NvScales& nv, hipStream_t stream) {
+                             int64_t T, int64_t K, const Gather& ga, const NvScales& nv, const Pad& pd,
+                             hipStream_t stream) {
     hipLaunchKernelGGL(kernel, dim3((unsigned)persistent_grid(kernel, T)), dim3(kThreads), 0, stream, x, q, s, off,
-                       G, T, K, ga, nv);
+                       G, T, K, ga, nv, pd);
     return hipGetLastError();
 }
 
 template <int FMT, bool GATHER>
 hipError_t launch_fmt(const uint16_t* x, uint8_t* q, void* s, const uint32_t* off, int G, int64_t T, int64_t K,
-                      const Gather& ga, hipStream_t stream, const NvScales& nv = NvScales{nullptr, nullptr, 0}) {
+                      const Gather& ga, hipStream_t stream, const NvScales& nv = NvScales{nullptr, nullptr, 0},
+                      const Pad& pd = Pad{nullptr, 0}) {
     const int64_t nc = (K + kChunk - 1) / kChunk;
-    if (nc <= 1) return launch_persistent(quantize_rows_kernel<FMT, 1, GATHER>, x, q, s, off, G, T, K, ga, nv, stream);
-    if (nc <= 2) return launch_persistent(quantize_rows_kernel<FMT, 2, GATHER>, x, q, s, off, G, T, K, ga, nv, stream);
-    if (nc <= 4) return launch_persistent(quantize_rows_kernel<FMT, 4, GATHER>, x, q, s, off, G, T, K, ga, nv, stream);
-    if (nc <= 8) return launch_persistent(quantize_rows_kernel<FMT, 8, GATHER>, x, q, s, off, G, T, K, ga, nv, stream);
+    if (nc <= 1) return launch_persistent(quantize_rows_kernel<FMT, 1, GATHER>, x, q, s, off, G, T, K, ga, nv, pd, stream);
+    if (nc <= 2) return launch_persistent(quantize_rows_kernel<FMT, 2, GATHER>, x, q, s, off, G, T, K, ga, nv, pd, stream);
+    if (nc <= 4) return launch_persistent(quantize_rows_kernel<FMT, 4, GATHER>, x, q, s, off, G, T, K, ga, nv, pd, stream);
+    if (nc <= 8) return launch_persistent(quantize_rows_kernel<FMT, 8, GATHER>, x, q, s, off, G, T, K, ga, nv, pd, stream);
     if (nc <= 14)
-        return launch_persistent(quantize_rows_kernel<FMT, 14, GATHER>, x, q, s, off, G, T, K, ga, nv, stream);
+        return launch_persistent(quantize_rows_kernel<FMT, 14, GATHER>, x, q, s, off, G, T, K, ga, nv, pd, stream);
     if (nc <= 16)
-        return launch_persistent(quantize_rows_kernel<FMT, 16, GATHER>, x, q, s, off, G, T, K, ga, nv, stream);
-    return launch_persistent(quantize_long_kernel<FMT, GATHER>, x, q, s, off, G, T, K, ga, nv, stream);
+        return launch_persistent(quantize_rows_kernel<FMT, 16, GATHER>, x, q, s, off, G, T, K, ga, nv, pd, stream);
+    return launch_persistent(quantize_long_kernel<FMT, GATHER>, x, q, s, off, G, T, K, ga, nv, pd, stream);
 }
 
 template <bool GATHER>
@@ -387,6 +414,18 @@ hipError_t launch_quantize_gather(int fmt, const void* x, int64_t nsrc, const in
                                   void* q, void* scales, const uint32_t* off, int G, int64_t T, int64_t K,
                                   hipStream_t stream) {
     return launch_any<true>(fmt, x, q, scales, off, G, T, K, Gather{indices, divisor, nsrc}, stream);
+}
+
+hipError_t launch_quantize_padded(int fmt, const void* x, void* q, void* scales, const uint32_t* scales_offsets,
+                                  int64_t scale_rows, const uint32_t* off, int G, int64_t T, int64_t K,
+                                  hipStream_t stream) {
+    const uint16_t* xb = static_cast<const uint16_t*>(x);
+    uint8_t* qb = static_cast<uint8_t*>(q);
+    const Gather ga{nullptr, 1, T};
+    const NvScales nv{nullptr, nullptr, 0};
+    const Pad pd{scales_offsets, scale_rows};
+    if (fmt == 1) return launch_fmt<1, false>(xb, qb, scales, off, G, T, K, ga, stream, nv, pd);
+    return launch_fmt<2, false>(xb, qb, scales, off, G, T, K, ga, stream, nv, pd);
 }
 
 hipError_t launch_quantize_nvfp4(const void* x, void* q, void* scales, const float* tensor_scales,

@@ -20,6 +20,10 @@
  *   mx_grouped_matmul_swiglu_nvfp4  NVFP4 gate/up grouped GEMM fused with SwiGLU
  *                             and an NVFP4 requant of the activation
  *   mx_silu_quantize_nvfp4    its unfused second half
+ *   mx_grouped_quantize_padded, mx_grouped_matmul_padded,
+ *   mx_grouped_matmul_swiglu_padded
+ *                             MX quantize / GEMM / fused GEMM with the activation
+ *                             scales in a padded or expert-slot layout
  *   mx_moe_combine            after the down-projection: each token's row is the
  *                             router-weighted sum of its routed rows
  *
@@ -337,6 +341,54 @@ mxg_status mx_silu_quantize(const void* h_bf16, void* y_q, void* y_scales, const
 mxg_status mx_grouped_quantize_nvfp4(const void* x_bf16, void* q, void* scales, const float* tensor_scales,
                                      const uint32_t* row_offsets, const int32_t* expert_ids, int32_t num_groups,
                                      int32_t num_experts, int64_t total_rows, int64_t K, hipStream_t stream);
+
+/*
+ * mx_grouped_quantize_padded, mx_grouped_matmul_padded,
+ * mx_grouped_matmul_swiglu_padded -- the MX entry points with the activation
+ * block scales in a padded / slot-strided layout.
+ * (grouped_quantize_dynamic_scaled_fp4_async_kernel: scales_offsets, the
+ *  per-expert offsets into the scale tensor, found with row_offsets by
+ *  binary search; NvMxf4f8Strategy, grouped_quantize(): "padded scale
+ *  alignment", scales_offset, and a_scales_max_padded_m of grouped_matmul();
+ *  Struct_ep_dispatch_mxfp4: the slot layout [n_local_experts *
+ *  max_padded_M, K_SCALES] with slot stride max_padded_M * K_SCALES.  The
+ *  pages give no formula; reading:)
+ *
+ * Routed row t of group g keeps its K/32 E8M0 scale bytes in row
+ *   scales_offsets[g] + (t - row_offsets[g])
+ * of a scale tensor [scale_rows, K/32] u8 (the slot layout is scales_offsets[g]
+ * = expert_ids[g] * max_padded_M, scale_rows = n_local_experts *
+ * max_padded_M).  scales_offsets is uint32 [num_groups] (device).  The quantize
+ * writes the codes of row t as mx_grouped_quantize does and its scales into
+ * that row; a row whose scale row lies at or past scale_rows is left
+ * untouched (codes too); scale rows nothing maps to (the padding) are never
+ * written.  The GEMMs read A's scales through the same map (weights keep the
+ * dense layout); a tile whose rows' scale rows would run past scale_rows is
+ * skipped and its output rows are left untouched.  Results are otherwise
+ * identical to the dense entry points.  Other arguments, layouts and errors as
+ * mx_grouped_quantize / mx_grouped_matmul / mx_grouped_matmul_swiglu;
+ * NOT_SUPPORTED also for MXG_FP8_E4M3_ROWWISE (its scale is per row, not per
+ * block); INVALID_VALUE also for scale_rows < 0, a null or misaligned
+ * scales_offsets (4 bytes), or a_scales not on 16 bytes.
+ */
+mxg_status mx_grouped_quantize_padded(mxg_format fmt, const void* x_bf16, void* q, void* scales,
+                                      const uint32_t* scales_offsets, int64_t scale_rows,
+                                      const uint32_t* row_offsets, int32_t num_groups, int64_t total_rows, int64_t K,
+                                      hipStream_t stream);
+
+mxg_status mx_grouped_matmul_padded(mxg_format fmt, const void* a_q, const void* a_scales,
+                                    const uint32_t* a_scales_offsets, int64_t a_scale_rows, const void* b_q,
+                                    const void* b_scales, void* c_bf16, const uint32_t* row_offsets,
+                                    const int32_t* expert_ids, int32_t num_groups, int32_t num_experts,
+                                    int64_t total_rows, int64_t N, int64_t K, int64_t max_rows_per_group_hint,
+                                    hipStream_t stream);
+
+mxg_status mx_grouped_matmul_swiglu_padded(mxg_format fmt, const void* a_q, const void* a_scales,
+                                           const uint32_t* a_scales_offsets, int64_t a_scale_rows, const void* w_q,
+                                           const void* w_scales, void* y_q, void* y_scales,
+                                           const uint32_t* row_offsets, const int32_t* expert_ids,
+                                           int32_t num_groups, int32_t num_experts, int64_t total_rows, int64_t I,
+                                           int64_t K, int64_t max_rows_per_group_hint, hipStream_t stream);
 
 /*
  * mx_moe_combine -- the MoE combine after the down-projection (itself
