@@ -145,3 +145,92 @@ def test_binding_rejects_cpu_tensors():
     x = torch.zeros((4, 64), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         mxg.quantize(0, x, torch.tensor([0, 4], dtype=torch.int32))
+
+
+# Every call below fails validation (or is a no-op with no rows / no groups):
+# the fake pointers are never handed to a kernel.
+def nq(x=FAKE, qq=FAKE, s=FAKE, sf=FAKE, off=FAKE, ids=FAKE, G=1, E=2, T=4, K=64):
+    return mxg.lib().mx_grouped_quantize_nvfp4(x, qq, s, sf, off, ids, G, E, T, K, None)
+
+
+def test_quantize_nvfp4_argument_errors():
+    for kw in [dict(x=None), dict(qq=None), dict(s=None), dict(sf=None), dict(off=None), dict(ids=None), dict(E=0),
+               dict(K=0), dict(T=-1), dict(G=-1), dict(x=FAKE_ODD), dict(sf=FAKE_ODD)]:
+        assert nq(**kw) == mxg.ERROR_INVALID_VALUE, kw
+    assert nq(K=24) == mxg.ERROR_NOT_SUPPORTED
+    assert nq(G=1025) == mxg.ERROR_NOT_SUPPORTED
+    assert nq(T=0) == mxg.SUCCESS
+    assert nq(G=0) == mxg.SUCCESS
+
+
+def nm(a=FAKE, sa=FAKE, b=FAKE, sb=FAKE, es=FAKE, c=FAKE, off=FAKE, ids=FAKE, G=1, E=1, T=4, N=32, K=512):
+    return mxg.lib().mx_grouped_matmul_nvfp4(a, sa, b, sb, es, c, off, ids, G, E, T, N, K, 0, None)
+
+
+def test_matmul_nvfp4_argument_errors():
+    for kw in [dict(a=None), dict(sa=None), dict(b=None), dict(sb=None), dict(es=None), dict(c=None),
+               dict(off=None), dict(ids=None), dict(K=0), dict(N=0), dict(E=0), dict(T=-1), dict(G=-1),
+               dict(a=FAKE_ODD), dict(sa=FAKE_ODD), dict(es=FAKE_ODD), dict(c=FAKE_ODD)]:
+        assert nm(**kw) == mxg.ERROR_INVALID_VALUE, kw
+    assert nm(K=256) == mxg.ERROR_NOT_SUPPORTED
+    assert nm(G=2000) == mxg.ERROR_NOT_SUPPORTED
+    assert nm(T=0) == mxg.SUCCESS
+
+
+def ns(a=FAKE, sa=FAKE, w=FAKE, ws=FAKE, es=FAKE, rs=None, ysf=FAKE, yq=FAKE, ys=FAKE, off=FAKE, ids=FAKE, G=1, E=1,
+       T=4, I=64, K=512):
+    return mxg.lib().mx_grouped_matmul_swiglu_nvfp4(a, sa, w, ws, es, rs, ysf, yq, ys, off, ids, G, E, T, I, K, 0,
+                                                    None)
+
+
+def test_swiglu_nvfp4_argument_errors():
+    for kw in [dict(a=None), dict(es=None), dict(ysf=None), dict(yq=None), dict(ys=None), dict(I=0), dict(E=0),
+               dict(rs=FAKE_ODD), dict(yq=FAKE_ODD), dict(ysf=FAKE_ODD)]:
+        assert ns(**kw) == mxg.ERROR_INVALID_VALUE, kw
+    assert ns(I=48) == mxg.ERROR_NOT_SUPPORTED
+    assert ns(K=1000) == mxg.ERROR_NOT_SUPPORTED
+    assert ns(T=0) == mxg.SUCCESS
+
+
+def nsq(h=FAKE, yq=FAKE, ys=FAKE, ysf=FAKE, off=FAKE, ids=FAKE, G=1, E=1, T=4, I=64):
+    return mxg.lib().mx_silu_quantize_nvfp4(h, yq, ys, ysf, off, ids, G, E, T, I, None)
+
+
+def test_silu_quantize_nvfp4_argument_errors():
+    for kw in [dict(h=None), dict(yq=None), dict(ys=None), dict(ysf=None), dict(off=None), dict(ids=None),
+               dict(I=0), dict(E=0), dict(h=FAKE_ODD)]:
+        assert nsq(**kw) == mxg.ERROR_INVALID_VALUE, kw
+    assert nsq(I=24) == mxg.ERROR_NOT_SUPPORTED
+    assert nsq(T=0) == mxg.SUCCESS
+
+
+def qp(fmt=2, x=FAKE, qq=FAKE, s=FAKE, soff=FAKE, S=16, off=FAKE, G=1, T=4, K=64):
+    return mxg.lib().mx_grouped_quantize_padded(fmt, x, qq, s, soff, S, off, G, T, K, None)
+
+
+def mp(fmt=2, a=FAKE, sa=FAKE, asoff=FAKE, S=16, b=FAKE, sb=FAKE, c=FAKE, off=FAKE, ids=FAKE, G=1, E=1, T=4, N=32,
+       K=64):
+    return mxg.lib().mx_grouped_matmul_padded(fmt, a, sa, asoff, S, b, sb, c, off, ids, G, E, T, N, K, 0, None)
+
+
+def sp(fmt=2, a=FAKE, sa=FAKE, asoff=FAKE, S=16, w=FAKE, ws=FAKE, yq=FAKE, ys=FAKE, off=FAKE, ids=FAKE, G=1, E=1,
+       T=4, I=64, K=64):
+    return mxg.lib().mx_grouped_matmul_swiglu_padded(fmt, a, sa, asoff, S, w, ws, yq, ys, off, ids, G, E, T, I, K, 0,
+                                                     None)
+
+
+def test_padded_argument_errors():
+    for kw in [dict(x=None), dict(soff=None), dict(S=-1), dict(fmt=5), dict(soff=FAKE_ODD)]:
+        assert qp(**kw) == mxg.ERROR_INVALID_VALUE, kw
+    assert qp(fmt=0) == mxg.ERROR_NOT_SUPPORTED
+    assert qp(K=48) == mxg.ERROR_NOT_SUPPORTED
+    assert qp(T=0) == mxg.SUCCESS
+    for kw in [dict(asoff=None), dict(S=-1), dict(sa=FAKE_ODD), dict(c=None), dict(fmt=5), dict(asoff=FAKE_ODD)]:
+        assert mp(**kw) == mxg.ERROR_INVALID_VALUE, kw
+    assert mp(fmt=0) == mxg.ERROR_NOT_SUPPORTED
+    assert mp(T=0) == mxg.SUCCESS
+    for kw in [dict(asoff=None), dict(S=-1), dict(yq=None), dict(I=0)]:
+        assert sp(**kw) == mxg.ERROR_INVALID_VALUE, kw
+    assert sp(fmt=0) == mxg.ERROR_NOT_SUPPORTED
+    assert sp(I=48) == mxg.ERROR_NOT_SUPPORTED
+    assert sp(T=0) == mxg.SUCCESS
