@@ -55,10 +55,16 @@ using namespace gemm;
 namespace {
 
 // BM x BN output tile, WGM x WGN waves, SLOTS stages of LDS ring (2: one stage
-// in flight while one is consumed; 3: two in flight).
-template <int BM_, int BN_, int WGM_, int WGN_, int SLOTS_ = 3, int MINB_ = 1>
+// in flight while one is consumed; 3: two in flight).  STREAM_B: the weight
+// operand is loaded with the nontemporal cache policy -- for the small
+// weight-streaming tile, where each weight panel is read by the few M tiles
+// of its expert at about the same time and then never again (measured on
+// the decode-shaped workload: 157-164 -> 141-146 us; the large tiles, whose
+// weight panels are re-read from L2, were slower with it).
+template <int BM_, int BN_, int WGM_, int WGN_, int SLOTS_ = 3, int MINB_ = 1, bool STREAM_B_ = false>
 struct Tile {
     static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_, kMinBlocks = MINB_, kSlots = SLOTS_;
+    static constexpr bool kStreamB = STREAM_B_;
     // Fragment buffers per wave: with one wave per SIMD the fragments of step
     // s+1 are read while step s computes (2); with two waves per SIMD the
     // other wave covers the LDS latency and the registers go to accumulators.
@@ -277,6 +283,10 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
     constexpr int kStage = kAStage + kBStage;
     constexpr int A_J = BM / 8 / NW, B_J = BN / 8 / NW;  // 1 KiB load instructions per wave per stage
     constexpr int kWords = F::kWords;                    // scale words per row per stage
+    // cache policy of the weight loads (a named constant: written as a
+    // conditional expression inside the builtin call, hipcc dropped the
+    // kernels' host launch stubs without an error)
+    constexpr int kBPolicy = TL::kStreamB ? kCpolNT : 0;
     // MX scales through LDS: every kSclStages stages the workgroup loads the
     // next 32 scale bytes (32 blocks) of each of its BM + BN rows with direct
     // loads (an instruction covers 32 rows, two lanes per row), into one of
@@ -376,7 +386,7 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
             for (int j = 0; j < B_J; ++j)
                 __builtin_amdgcn_global_load_lds(
                     (gptr_t)(bk + (kLeanOffsets ? op_off(rb, j, cols_in) : opaque(b_off[j]))),
-                    (lptr_t)(slot + kAStage + (wave + NW * j) * 1024), 16, 0, 0);
+                    (lptr_t)(slot + kAStage + (wave + NW * j) * 1024), 16, 0, kBPolicy);
         };
         // The partial last stage: VGPR loads with the K tail zero-filled.
         uint4 ta[A_J], tb[B_J];
@@ -624,8 +634,8 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
                     const int row = q / kPieces, pc = q % kPieces;
                     const int64_t grow = m0 + row, gcol = n0 + pc * 8;
                     if (grow < m_end && gcol < n_end)
-                        *reinterpret_cast<uint4*>(args.c + grow * args.N + gcol) =
-                            *reinterpret_cast<const uint4*>(srow(row) + pc * 8);
+                        store_stream16(args.c + grow * args.N + gcol,
+                                       *reinterpret_cast<const uint4*>(srow(row) + pc * 8));
                 }
             } else {
 #pragma unroll
@@ -745,7 +755,7 @@ using TileLargeFp8 = Tile<256, 256, 2, 4, 2>;
 using TileLargeMx = Tile<128, 256, 2, 2, 3>;
 using TileLargeMxKA = Tile<128, 256, 2, 2, 2>;
 using TileLargeMxKA8 = Tile<256, 256, 2, 4, 2>;
-using TileSmall = Tile<32, 128, 1, 4, 3>;
+using TileSmall = Tile<32, 128, 1, 4, 3, 1, true>;
 constexpr int kBandLarge = 4, kBandMx = 8, kBandNOuter = 1 << 30;
 constexpr int64_t kTallRows = 384;
 

@@ -129,6 +129,10 @@ __device__ __forceinline__ void stage_barrier() {
 typedef const void __attribute__((address_space(1)))* gptr_t;
 typedef void __attribute__((address_space(3)))* lptr_t;
 
+// Cache-policy operand of the direct global -> LDS load: the nontemporal bit
+// (the line is marked to be replaced first; data still comes through L2).
+constexpr int kCpolNT = 2;
+
 // ---------------------------------------------------------------------------
 // Ragged tile map.  Each workgroup turns row_offsets into a prefix over the
 // per-group M-tile counts (in LDS; groups that are empty, inverted or carry an

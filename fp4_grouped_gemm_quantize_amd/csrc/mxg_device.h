@@ -121,6 +121,32 @@ __device__ __forceinline__ bool wave_row_covered(const uint32_t* s_off, int G, i
     return __any(hit);
 }
 
+// 16 bytes of a stream that is read once, loaded with the nontemporal hint.
+// Measured on MI355X: the grouped quantize of 537 MB of BF16 rows runs ~17 %
+// faster than with ordinary loads (FP8 rowwise 155 -> 129 us, MXFP4 133 ->
+// 115 us, same bytes out).  Nontemporal stores of the codes gave nothing on
+// top; the gathered quantize (token rows shared by several slots), the
+// SwiGLU requant and the combine were as fast or faster with ordinary loads
+// and keep them.
+__device__ __forceinline__ uint4 load_stream16(const void* p) {
+    typedef unsigned u4v __attribute__((ext_vector_type(4)));
+    const u4v t = __builtin_nontemporal_load(static_cast<const u4v*>(p));
+    return make_uint4(t.x, t.y, t.z, t.w);
+}
+
+// 16 bytes written with the nontemporal hint (an output nothing in the same
+// kernel reads back).  The GEMM's BF16 output pieces use it: ~1 % faster on
+// the ragged FP8 and MXFP8 GEMMs, same bytes.
+__device__ __forceinline__ void store_stream16(void* p, const uint4& v) {
+    typedef unsigned u4v __attribute__((ext_vector_type(4)));
+    u4v t;
+    t.x = v.x;
+    t.y = v.y;
+    t.z = v.z;
+    t.w = v.w;
+    __builtin_nontemporal_store(t, static_cast<u4v*>(p));
+}
+
 // Unpack a 16-byte vector of 8 bf16 into fp32.
 __device__ __forceinline__ void unpack8(const uint4& v, float* f) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};

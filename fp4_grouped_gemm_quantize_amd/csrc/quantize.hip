@@ -101,14 +101,17 @@ __global__ __launch_bounds__(kThreads) void quantize_rows_kernel(const uint16_t*
     const int64_t nw = (int64_t)gridDim.x * kWavesPerBlock;
     const int nvec = (int)(K / kVecElems);
 
-    // source row sr of x (-1: none; the registers are then left as they are)
+    // source row sr of x (-1: none; the registers are then left as they are).
+    // Rows are streamed once (nontemporal); gathered source rows are shared
+    // by the slots of a token and keep ordinary loads.
     auto load_row = [&](int64_t sr, uint4 (&v)[NC]) {
         if (sr < 0) return;
         const uint4* xr = reinterpret_cast<const uint4*>(x + sr * K);
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
             const int idx = c * kWave + lane;
-            v[c] = idx < nvec ? xr[idx] : make_uint4(0, 0, 0, 0);
+            if (idx < nvec) v[c] = GATHER ? xr[idx] : load_stream16(xr + idx);
+            else v[c] = make_uint4(0, 0, 0, 0);
         }
     };
 
@@ -223,7 +226,7 @@ __global__ __launch_bounds__(kThreads) void quantize_long_kernel(const uint16_t*
             for (int64_t base = 0; base < nvec; base += kWave) {
                 const int64_t idx = base + lane;
                 float f[8];
-                unpack8(idx < nvec ? xr[idx] : make_uint4(0, 0, 0, 0), f);
+                unpack8(idx < nvec ? load_stream16(xr + idx) : make_uint4(0, 0, 0, 0), f);
                 uint32_t sc;
                 const uint32_t packed = nv_encode8(f, sf, sc);
                 if (idx < nvec) {
@@ -251,7 +254,7 @@ __global__ __launch_bounds__(kThreads) void quantize_long_kernel(const uint16_t*
             uint8_t* qr = q + t * K;
             for (int64_t idx = lane; idx < nvec; idx += kWave) {
                 float f[8];
-                unpack8(xr[idx], f);
+                unpack8(load_stream16(xr + idx), f);
                 if (amax != 0.0f)
                     for (int i = 0; i < 8; ++i) f[i] = div_by_scale(f[i], inv);
                 *reinterpret_cast<uint2*>(qr + idx * 8) = pack8_e4m3(f);
@@ -265,7 +268,7 @@ __global__ __launch_bounds__(kThreads) void quantize_long_kernel(const uint16_t*
             for (int64_t base = 0; base < nvec; base += kWave) {
                 const int64_t idx = base + lane;
                 float f[8];
-                unpack8(idx < nvec ? xr[idx] : make_uint4(0, 0, 0, 0), f);
+                unpack8(idx < nvec ? load_stream16(xr + idx) : make_uint4(0, 0, 0, 0), f);
                 uint2 packed;
                 const int X = mx_encode8<FP4>(f, packed);
                 if (idx < nvec) mx_store8<FP4>(packed, X, qrow, srow, idx, lane);
