@@ -86,49 +86,75 @@ __device__ __forceinline__ int64_t source_row(const Gather& g, int64_t t) {
 }
 
 // ---------------------------------------------------------------------------
-// FP8 rowwise and MX, rows of K <= NC * 512 held in registers.
+// Work units held in registers: a wave owns one unit at a time.  FP8 rowwise:
+// a unit is a whole row (K <= NC * 512), since its scale needs the row's
+// maximum.  MX and NVFP4 blocks are independent along K, so a row is split
+// into nseg segments of NC * 512 elements (the last one may be shorter) and
+// each segment is a unit: long rows then need no more than 8 chunks of
+// registers per buffer, which keeps 4 waves per SIMD resident (measured: K =
+// 7168 as one 14-chunk unit reached 63 % of HBM bandwidth, at 2 waves per
+// SIMD).
 // FMT: 0 = FP8 rowwise (scale = amax / 448, code = e4m3(x / scale)),
 //      1 = MXFP8, 2 = MXFP4, 3 = NVFP4.
 template <int FMT, int NC, bool GATHER>
 __global__ __launch_bounds__(kThreads) void quantize_rows_kernel(const uint16_t* __restrict__ x,
                                                                  uint8_t* __restrict__ q, void* __restrict__ scales,
                                                                  const uint32_t* __restrict__ off, int G,
-                                                                 int64_t T, int64_t K, Gather ga, NvScales nv,
-                                                                 Pad pd) {
+                                                                 int64_t T, int64_t K, int nseg, Gather ga,
+                                                                 NvScales nv, Pad pd) {
     __shared__ uint32_t s_off[kMaxGroups + 1];
     load_offsets(s_off, off, G);
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t nw = (int64_t)gridDim.x * kWavesPerBlock;
-    const int nvec = (int)(K / kVecElems);
+    constexpr int64_t kSegElems = (int64_t)NC * kChunk;
+    const int64_t units = T * nseg;
 
-    // source row sr of x (-1: none; the registers are then left as they are).
-    // Rows are streamed once (nontemporal); gathered source rows are shared
-    // by the slots of a token and keep ordinary loads.
-    auto load_row = [&](int64_t sr, uint4 (&v)[NC]) {
-        if (sr < 0) return;
-        const uint4* xr = reinterpret_cast<const uint4*>(x + sr * K);
+    // Unit u: row t = u / nseg, elements [e0, e0 + 8 * nvec).
+    struct Unit {
+        int64_t t, e0, sr;  // sr: source row of x (-1: none)
+        int nvec;           // 16-byte vectors in the unit
+    };
+    auto unit = [&](int64_t u) {
+        Unit w{0, 0, -1, 0};
+        if (u >= units) return w;
+        w.t = nseg == 1 ? u : u / nseg;
+        w.e0 = (u - w.t * nseg) * kSegElems;
+        const int64_t left = K - w.e0;
+        w.nvec = (int)((left < kSegElems ? left : kSegElems) / kVecElems);
+        w.sr = source_row<GATHER>(ga, w.t);
+        return w;
+    };
+    // the unit's elements into v (sr < 0: the registers are left as they
+    // are).  Rows are streamed once (nontemporal); gathered source rows are
+    // shared by the slots of a token and keep ordinary loads.
+    auto load_unit = [&](const Unit& w, uint4 (&v)[NC]) {
+        if (w.sr < 0) return;
+        const uint4* xr = reinterpret_cast<const uint4*>(x + w.sr * K + w.e0);
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
             const int idx = c * kWave + lane;
-            if (idx < nvec) v[c] = GATHER ? xr[idx] : load_stream16(xr + idx);
+            if (idx < w.nvec) v[c] = GATHER ? xr[idx] : load_stream16(xr + idx);
             else v[c] = make_uint4(0, 0, 0, 0);
         }
     };
 
     uint4 v[NC], vn[NC];
-    int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
-    int64_t sr = t < T ? source_row<GATHER>(ga, t) : -1;
-    load_row(sr, v);
-    for (; t < T; t += nw) {
-        const int64_t tn = t + nw;
-        const int64_t srn = tn < T ? source_row<GATHER>(ga, tn) : -1;
-        load_row(srn, vn);
+    // the unit bookkeeping is wave-uniform: scalar registers
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    int64_t u = (int64_t)blockIdx.x * kWavesPerBlock + wave;
+    Unit cu = unit(u);
+    load_unit(cu, v);
+    for (; u < units; u += nw) {
+        const Unit nu = unit(u + nw);
+        load_unit(nu, vn);
+        const int64_t t = cu.t;
+        const int nvec = cu.nvec;
         if constexpr (FMT == 3) {
-            const int g = sr >= 0 ? wave_row_group(s_off, nv.ids, G, nv.E, T, t) : -1;
+            const int g = cu.sr >= 0 ? wave_row_group(s_off, nv.ids, G, nv.E, T, t) : -1;
             if (g >= 0) {
                 const float sf = nv.sf[nv.ids[g]];
-                uint8_t* qrow = q + t * (K / 2);
-                uint8_t* srow = static_cast<uint8_t*>(scales) + t * (K / 16);
+                uint8_t* qrow = q + t * (K / 2) + cu.e0 / 2;
+                uint8_t* srow = static_cast<uint8_t*>(scales) + t * (K / 16) + cu.e0 / 16;
 #pragma unroll
                 for (int c = 0; c < NC; ++c) {
                     const int idx = c * kWave + lane;
@@ -143,7 +169,7 @@ __global__ __launch_bounds__(kThreads) void quantize_rows_kernel(const uint16_t*
                     }
                 }
             }
-        } else if (sr >= 0) {
+        } else if (cu.sr >= 0) {
             const int64_t srix = scale_row(pd, s_off, G, T, t);  // -1: the row is not written
             if (srix < 0) {
                 // skipped (uncovered, or no scale row in the padded layout)
@@ -179,8 +205,8 @@ __global__ __launch_bounds__(kThreads) void quantize_rows_kernel(const uint16_t*
                 if (lane == 0) static_cast<float*>(scales)[t] = amax == 0.0f ? 0.0f : scale;
             } else {
                 constexpr bool FP4 = FMT == 2;
-                uint8_t* qrow = q + t * (FP4 ? K / 2 : K);
-                uint8_t* srow = static_cast<uint8_t*>(scales) + srix * (K / 32);
+                uint8_t* qrow = q + t * (FP4 ? K / 2 : K) + (FP4 ? cu.e0 / 2 : cu.e0);
+                uint8_t* srow = static_cast<uint8_t*>(scales) + srix * (K / 32) + cu.e0 / 32;
 #pragma unroll
                 for (int c = 0; c < NC; ++c) {
                     const int idx = c * kWave + lane;
@@ -196,18 +222,18 @@ __global__ __launch_bounds__(kThreads) void quantize_rows_kernel(const uint16_t*
         }
 #pragma unroll
         for (int c = 0; c < NC; ++c) v[c] = vn[c];
-        sr = srn;
+        cu = nu;
     }
 }
 
-// Rows longer than the register budget: rowwise reads the row twice (the
-// second pass from cache); MX streams 512-element chunks.
-template <int FMT, bool GATHER>
+// FP8 rowwise rows longer than the register budget: the row is read twice,
+// the amax pass and then the encode pass (from cache).  (MX and NVFP4 rows of
+// any length are split into register-sized segments above.)
+template <bool GATHER>
 __global__ __launch_bounds__(kThreads) void quantize_long_kernel(const uint16_t* __restrict__ x,
                                                                  uint8_t* __restrict__ q, void* __restrict__ scales,
                                                                  const uint32_t* __restrict__ off, int G,
-                                                                 int64_t T, int64_t K, Gather ga, NvScales nv,
-                                                                 Pad pd) {
+                                                                 int64_t T, int64_t K, Gather ga, Pad pd) {
     __shared__ uint32_t s_off[kMaxGroups + 1];
     load_offsets(s_off, off, G);
     const int lane = threadIdx.x & (kWave - 1);
@@ -217,63 +243,28 @@ __global__ __launch_bounds__(kThreads) void quantize_long_kernel(const uint16_t*
         const int64_t sr = source_row<GATHER>(ga, t);
         if (sr < 0) continue;
         const uint4* xr = reinterpret_cast<const uint4*>(x + sr * K);
-        if constexpr (FMT == 3) {
-            const int g = wave_row_group(s_off, nv.ids, G, nv.E, T, t);
-            if (g < 0) continue;
-            const float sf = nv.sf[nv.ids[g]];
-            uint8_t* qrow = q + t * (K / 2);
-            uint8_t* srow = static_cast<uint8_t*>(scales) + t * (K / 16);
-            for (int64_t base = 0; base < nvec; base += kWave) {
-                const int64_t idx = base + lane;
-                float f[8];
-                unpack8(idx < nvec ? load_stream16(xr + idx) : make_uint4(0, 0, 0, 0), f);
-                uint32_t sc;
-                const uint32_t packed = nv_encode8(f, sf, sc);
-                if (idx < nvec) {
-                    *reinterpret_cast<uint32_t*>(qrow + idx * 4) = packed;
-                    if ((lane & 1) == 0) srow[idx >> 1] = (uint8_t)sc;
-                }
-            }
-            continue;
-        }
-        const int64_t srix = scale_row(pd, s_off, G, T, t);
-        if (srix < 0) continue;
-        if constexpr (FMT == 0) {
-            uint32_t amax_bits = 0;
-            for (int64_t idx = lane; idx < nvec; idx += kWave) {
-                const uint4 v = xr[idx];
-                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-                for (int i = 0; i < 4; ++i) {
-                    amax_bits = max(amax_bits, w[i] & 0x7fffu);
-                    amax_bits = max(amax_bits, (w[i] >> 16) & 0x7fffu);
-                }
-            }
-            const float amax = wave_max(bf16_to_f32(amax_bits));
-            const float scale = amax / 448.0f;
-            const double inv = amax == 0.0f ? 0.0 : 1.0 / (double)scale;
-            uint8_t* qr = q + t * K;
-            for (int64_t idx = lane; idx < nvec; idx += kWave) {
-                float f[8];
-                unpack8(load_stream16(xr + idx), f);
-                if (amax != 0.0f)
-                    for (int i = 0; i < 8; ++i) f[i] = div_by_scale(f[i], inv);
-                *reinterpret_cast<uint2*>(qr + idx * 8) = pack8_e4m3(f);
-            }
-            if (lane == 0) static_cast<float*>(scales)[t] = amax == 0.0f ? 0.0f : scale;
-        } else {
-            constexpr bool FP4 = FMT == 2;
-            uint8_t* qrow = q + t * (FP4 ? K / 2 : K);
-            uint8_t* srow = static_cast<uint8_t*>(scales) + srix * (K / 32);
-            // whole 512-element chunks per iteration keep every lane in the loop
-            for (int64_t base = 0; base < nvec; base += kWave) {
-                const int64_t idx = base + lane;
-                float f[8];
-                unpack8(idx < nvec ? load_stream16(xr + idx) : make_uint4(0, 0, 0, 0), f);
-                uint2 packed;
-                const int X = mx_encode8<FP4>(f, packed);
-                if (idx < nvec) mx_store8<FP4>(packed, X, qrow, srow, idx, lane);
+        if (scale_row(pd, s_off, G, T, t) < 0) continue;
+        uint32_t amax_bits = 0;
+        for (int64_t idx = lane; idx < nvec; idx += kWave) {
+            const uint4 v = xr[idx];
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+            for (int i = 0; i < 4; ++i) {
+                amax_bits = max(amax_bits, w[i] & 0x7fffu);
+                amax_bits = max(amax_bits, (w[i] >> 16) & 0x7fffu);
             }
         }
+        const float amax = wave_max(bf16_to_f32(amax_bits));
+        const float scale = amax / 448.0f;
+        const double inv = amax == 0.0f ? 0.0 : 1.0 / (double)scale;
+        uint8_t* qr = q + t * K;
+        for (int64_t idx = lane; idx < nvec; idx += kWave) {
+            float f[8];
+            unpack8(load_stream16(xr + idx), f);
+            if (amax != 0.0f)
+                for (int i = 0; i < 8; ++i) f[i] = div_by_scale(f[i], inv);
+            *reinterpret_cast<uint2*>(qr + idx * 8) = pack8_e4m3(f);
+        }
+        if (lane == 0) static_cast<float*>(scales)[t] = amax == 0.0f ? 0.0f : scale;
     }
 }
 
@@ -357,25 +348,30 @@ __global__ __launch_bounds__(kThreads) void silu_quantize_nv_kernel(const uint16
     }
 }
 
-// Persistent grid: as many blocks as can be resident, at most one wave per row.
+// Persistent grid: as many blocks as can be resident, at most one wave per
+// work unit (row, or row segment).
 template <class Kern>
-int64_t persistent_grid(Kern kernel, int64_t T) {
+int64_t persistent_grid(Kern kernel, int64_t units) {
     int dev = 0, cus = 0, occ = 0;
     int64_t cap = 2048;
     if (hipGetDevice(&dev) == hipSuccess &&
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, kThreads, 0) == hipSuccess && cus > 0)
         cap = (int64_t)cus * (occ > 0 ? occ : 1);
-    const int64_t need = (T + kWavesPerBlock - 1) / kWavesPerBlock;
+    const int64_t need = (units + kWavesPerBlock - 1) / kWavesPerBlock;
     return need < cap ? need : cap;
 }
 
-template <class Kern>
-hipError_t launch_persistent(Kern kernel, const uint16_t* x, uint8_t* q, void* s, const uint32_t* off, int G,
-                             int64_t T, int64_t K, const Gather& ga, const NvScales& nv, const Pad& pd,
-                             hipStream_t stream) {
-    hipLaunchKernelGGL(kernel, dim3((unsigned)persistent_grid(kernel, T)), dim3(kThreads), 0, stream, x, q, s, off,
-                       G, T, K, ga, nv, pd);
+// The register-resident kernel with NC chunks per unit: whole rows for FP8
+// rowwise (K <= NC * 512), segments of NC * 512 elements for the block formats.
+template <int FMT, int NC, bool GATHER>
+hipError_t launch_rows(const uint16_t* x, uint8_t* q, void* s, const uint32_t* off, int G, int64_t T, int64_t K,
+                       const Gather& ga, const NvScales& nv, const Pad& pd, hipStream_t stream) {
+    constexpr int64_t kSeg = (int64_t)NC * kChunk;
+    const int64_t nseg = FMT == 0 ? 1 : (K + kSeg - 1) / kSeg;
+    auto kernel = quantize_rows_kernel<FMT, NC, GATHER>;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)persistent_grid(kernel, T * nseg)), dim3(kThreads), 0, stream, x, q, s,
+                       off, G, T, K, (int)nseg, ga, nv, pd);
     return hipGetLastError();
 }
 
@@ -383,16 +379,28 @@ template <int FMT, bool GATHER>
 hipError_t launch_fmt(const uint16_t* x, uint8_t* q, void* s, const uint32_t* off, int G, int64_t T, int64_t K,
                       const Gather& ga, hipStream_t stream, const NvScales& nv = NvScales{nullptr, nullptr, 0},
                       const Pad& pd = Pad{nullptr, 0}) {
-    const int64_t nc = (K + kChunk - 1) / kChunk;
-    if (nc <= 1) return launch_persistent(quantize_rows_kernel<FMT, 1, GATHER>, x, q, s, off, G, T, K, ga, nv, pd, stream);
-    if (nc <= 2) return launch_persistent(quantize_rows_kernel<FMT, 2, GATHER>, x, q, s, off, G, T, K, ga, nv, pd, stream);
-    if (nc <= 4) return launch_persistent(quantize_rows_kernel<FMT, 4, GATHER>, x, q, s, off, G, T, K, ga, nv, pd, stream);
-    if (nc <= 8) return launch_persistent(quantize_rows_kernel<FMT, 8, GATHER>, x, q, s, off, G, T, K, ga, nv, pd, stream);
-    if (nc <= 14)
-        return launch_persistent(quantize_rows_kernel<FMT, 14, GATHER>, x, q, s, off, G, T, K, ga, nv, pd, stream);
-    if (nc <= 16)
-        return launch_persistent(quantize_rows_kernel<FMT, 16, GATHER>, x, q, s, off, G, T, K, ga, nv, pd, stream);
-    return launch_persistent(quantize_long_kernel<FMT, GATHER>, x, q, s, off, G, T, K, ga, nv, pd, stream);
+    const int64_t nc = (K + kChunk - 1) / kChunk;  // 512-element chunks per row
+    if constexpr (FMT != 0) {
+        // block formats: the fewest segments of at most 8 chunks, evened out
+        const int64_t nseg = (nc + 7) / 8;
+        const int64_t per = (nc + nseg - 1) / nseg;
+        if (per <= 1) return launch_rows<FMT, 1, GATHER>(x, q, s, off, G, T, K, ga, nv, pd, stream);
+        if (per <= 2) return launch_rows<FMT, 2, GATHER>(x, q, s, off, G, T, K, ga, nv, pd, stream);
+        if (per <= 4) return launch_rows<FMT, 4, GATHER>(x, q, s, off, G, T, K, ga, nv, pd, stream);
+        if (per <= 7) return launch_rows<FMT, 7, GATHER>(x, q, s, off, G, T, K, ga, nv, pd, stream);
+        return launch_rows<FMT, 8, GATHER>(x, q, s, off, G, T, K, ga, nv, pd, stream);
+    } else {
+        if (nc <= 1) return launch_rows<FMT, 1, GATHER>(x, q, s, off, G, T, K, ga, nv, pd, stream);
+        if (nc <= 2) return launch_rows<FMT, 2, GATHER>(x, q, s, off, G, T, K, ga, nv, pd, stream);
+        if (nc <= 4) return launch_rows<FMT, 4, GATHER>(x, q, s, off, G, T, K, ga, nv, pd, stream);
+        if (nc <= 8) return launch_rows<FMT, 8, GATHER>(x, q, s, off, G, T, K, ga, nv, pd, stream);
+        if (nc <= 14) return launch_rows<FMT, 14, GATHER>(x, q, s, off, G, T, K, ga, nv, pd, stream);
+        if (nc <= 16) return launch_rows<FMT, 16, GATHER>(x, q, s, off, G, T, K, ga, nv, pd, stream);
+        auto kernel = quantize_long_kernel<GATHER>;
+        hipLaunchKernelGGL(kernel, dim3((unsigned)persistent_grid(kernel, T)), dim3(kThreads), 0, stream, x, q, s, off,
+                           G, T, K, ga, pd);
+        return hipGetLastError();
+    }
 }
 
 template <bool GATHER>
