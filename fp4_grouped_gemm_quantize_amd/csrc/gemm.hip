@@ -312,6 +312,10 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
     __shared__ __attribute__((aligned(16))) uint8_t s_scl1[kLdsScales ? kSclRows * kSclBytes : 16];
     __shared__ uint32_t s_pre[kMaxGroups + 1];
     __shared__ uint32_t s_wave[NW];
+    // FP8 rowwise: the tile's per-row activation scales, loaded at the start
+    // of the tile (the loads land behind the K loop) so that the epilogue
+    // reads them from LDS instead of issuing a global load per output row.
+    __shared__ float s_ascale[F::kMX ? 1 : BM];
 
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -337,6 +341,11 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
         // the last column (partial M tiles, half tiles of a split round)
         // skips its matrix-core work; the loads stay shared.
         const bool wave_live = wm * WTM < rows_in && wn * WTN < cols_in;  // wave-uniform
+        if constexpr (!F::kMX) {
+            // rows past the group's end take the last real row's scale (never stored)
+            const float* as = static_cast<const float*>(args.as);
+            for (int i = tid; i < BM; i += NT) s_ascale[i] = as[m0 + (i < rows_in ? i : rows_in - 1)];
+        }
 
         // ---- operand sources: tile base (uniform) + 32-bit per-lane offsets;
         // load j of a wave covers rows r0 + 8 NW j .. +7 x 8 chunks (1 KiB of
@@ -602,8 +611,7 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
                 float v = acc[i][j][r];
                 if constexpr (F::kNV) v = v * es_e;
                 if constexpr (!F::kMX) {
-                    const int64_t row = m0 + wm * WTM + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                    v = v * static_cast<const float*>(args.as)[row < m_end ? row : m_end - 1];
+                    v = v * s_ascale[wm * WTM + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3)];
                     v = v * sbv;
                 }
                 return (uint16_t)f32_to_bf16(v);
