@@ -312,10 +312,13 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
     __shared__ __attribute__((aligned(16))) uint8_t s_scl1[kLdsScales ? kSclRows * kSclBytes : 16];
     __shared__ uint32_t s_pre[kMaxGroups + 1];
     __shared__ uint32_t s_wave[NW];
-    // FP8 rowwise: the tile's per-row activation scales, loaded at the start
-    // of the tile (the loads land behind the K loop) so that the epilogue
-    // reads them from LDS instead of issuing a global load per output row.
-    __shared__ float s_ascale[F::kMX ? 1 : BM];
+    // The tile's per-row epilogue factor -- FP8 rowwise: a_scale of the row;
+    // NVFP4: the expert scale times, fused with a row scale, the row's scale
+    // -- loaded at the start of the tile (the loads land behind the K loop) so
+    // that the epilogue reads it from LDS instead of issuing global loads
+    // after the K loop.
+    constexpr bool kRowFactor = !F::kMX || F::kNV;
+    __shared__ float s_rowf[kRowFactor ? BM : 1];
 
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -341,10 +344,15 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
         // the last column (partial M tiles, half tiles of a split round)
         // skips its matrix-core work; the loads stay shared.
         const bool wave_live = wm * WTM < rows_in && wn * WTN < cols_in;  // wave-uniform
+        // (rows past the group's end take the last real row's factor; never stored)
         if constexpr (!F::kMX) {
-            // rows past the group's end take the last real row's scale (never stored)
             const float* as = static_cast<const float*>(args.as);
-            for (int i = tid; i < BM; i += NT) s_ascale[i] = as[m0 + (i < rows_in ? i : rows_in - 1)];
+            for (int i = tid; i < BM; i += NT) s_rowf[i] = as[m0 + (i < rows_in ? i : rows_in - 1)];
+        } else if constexpr (F::kNV) {
+            const float es_e = args.es[e];
+            for (int i = tid; i < BM; i += NT)
+                s_rowf[i] = SWIGLU && args.rs ? es_e * bf16_to_f32(args.rs[m0 + (i < rows_in ? i : rows_in - 1)])
+                                              : es_e;
         }
 
         // ---- operand sources: tile base (uniform) + 32-bit per-lane offsets;
@@ -606,14 +614,10 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
         if constexpr (!SWIGLU) {
             // out = bf16((acc * a_scale[row]) * b_scale[col]) for FP8 rowwise,
             // bf16(acc * expert_scale[e]) for NVFP4
-            const float es_e = F::kNV ? args.es[e] : 1.0f;
             auto value = [&](int i, int j, int r, float sbv) {
                 float v = acc[i][j][r];
-                if constexpr (F::kNV) v = v * es_e;
-                if constexpr (!F::kMX) {
-                    v = v * s_ascale[wm * WTM + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3)];
-                    v = v * sbv;
-                }
+                if constexpr (kRowFactor) v = v * s_rowf[wm * WTM + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3)];
+                if constexpr (!F::kMX) v = v * sbv;
                 return (uint16_t)f32_to_bf16(v);
             };
             auto b_scale = [&](int j) {
@@ -666,7 +670,6 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
             // (NVFP4: gate/up = bf16(acc * fl32(expert_scale * row_scale)),
             // requant to NVFP4 blocks of 16 under y's tensor scale.)
             static_assert(BN % 64 == 0, "fused tile must hold whole 32-output blocks");
-            const float es_e = F::kNV ? args.es[e] : 1.0f;
 #pragma unroll
             for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -676,14 +679,7 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
                     for (int r = 0; r < 16; ++r) {
                         const int row = wm * WTM + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
                         float v = acc[i][j][r];
-                        if constexpr (F::kNV) {
-                            float f = es_e;
-                            if (args.rs) {
-                                const int64_t grow = m0 + row < m_end ? m0 + row : m_end - 1;
-                                f = es_e * bf16_to_f32(args.rs[grow]);
-                            }
-                            v = v * f;
-                        }
+                        if constexpr (F::kNV) v = v * s_rowf[row];
                         srow(row)[col] = (uint16_t)f32_to_bf16(v);
                     }
                 }
