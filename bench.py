@@ -36,15 +36,40 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "ragged MoE grouped GEMM TFLOP/s + % FP8/MXFP4 MFMA peak; quantize GB/s"
 
 
+# Measured on MI355X: after the GPU goes from idle to this load, the clock
+# dips for roughly the first 30-40 ms (prefill GEMM 515 us at step 2, 665 us
+# at step 6, back to ~505 us by step 40; the quantize likewise 131 -> 142 ->
+# 130 us), so the default warm-up runs for longer than that.
+WARMUP_SECONDS = 0.1
+
+
+def warm_up(step, count):
+    """Untimed warm-up: `count` steps, or, with count None, batches of 10
+    steps until WARMUP_SECONDS of wall time have passed.  Returns the steps run."""
+    import torch
+
+    if count is not None:
+        for _ in range(count):
+            step()
+        torch.cuda.synchronize()
+        return count
+    n, t0 = 0, time.perf_counter()
+    while True:
+        for _ in range(10):
+            step()
+        n += 10
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= WARMUP_SECONDS:
+            return n
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
-    # Measured on MI355X: after the GPU goes from idle to this load, the clock
-    # dips for roughly the first 40 steps of the prefill workload (GEMM 515 us
-    # at step 2, 665 us at step 6, back to ~505 us by step 40, quantize likewise
-    # 131 -> 142 -> 130 us), so the default warm-up runs past that transient.
-    p.add_argument("--warmup", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=None,
+                   help="untimed warm-up steps (default: whole batches of 10 steps until at least "
+                        f"{WARMUP_SECONDS:g} s have passed; the JSON line reports the count)")
     p.add_argument("--workload", type=int, default=3, help="1..5 (default: 3, prefill FP8 rowwise)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU baseline")
@@ -199,10 +224,11 @@ def main():
         else:
             mxg.mx_grouped_matmul(fmt, a, sa, b, sb, c, off, ids, hint)
 
-    for _ in range(args.warmup):
+    def step():
         quant()
         gemm()
-    torch.cuda.synchronize()
+
+    warmup = warm_up(step, args.warmup)
 
     stream = torch.cuda.current_stream()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
@@ -243,7 +269,7 @@ def main():
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": warmup,
         "ms_per_step": round(step_ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -274,8 +300,7 @@ def main():
         def quant_gather():
             mxg.mx_grouped_quantize_gather(fmt, xs, idx, w.top_k, a, sa, off, ids)
 
-        for _ in range(args.warmup):
-            quant_gather()
+        warm_up(quant_gather, args.warmup)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(args.steps):
@@ -309,9 +334,7 @@ def main():
         def combine():
             mxg.mx_moe_combine(yd, ros, wts, comb)
 
-        for _ in range(args.warmup):
-            down()
-            combine()
+        warm_up(lambda: (down(), combine()), args.warmup)
         ed = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
         d_ms, c_ms = [], []
         for _ in range(args.steps):
@@ -372,10 +395,7 @@ def main():
         def nv_fused():
             mxg.mx_grouped_matmul_swiglu_nvfp4(an, san, bn, sbn, esn, sfy, yqn, ysn, off, ids, None, hint)
 
-        for _ in range(args.warmup):
-            nv_quant()
-            nv_gemm()
-            nv_fused()
+        warm_up(lambda: (nv_quant(), nv_gemm(), nv_fused()), args.warmup)
         ed.append(torch.cuda.Event(enable_timing=True))
         nq_ms, ng_ms, nf_ms = [], [], []
         for _ in range(args.steps):
