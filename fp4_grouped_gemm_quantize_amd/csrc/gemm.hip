@@ -747,18 +747,21 @@ hipError_t launch_tile(const GemmProblem& p, hipStream_t stream, int mband) {
 // Tile shapes and tile orders, chosen by measurement on MI355X (ragged
 // workloads of the benchmark): FP8 rowwise with many rows per group ->
 // 256 x 256 with eight waves (fewest operand bytes per FLOP; two ring slots
-// fit 160 KiB of LDS) in bands of 4 M tiles; MX formats -> 128 x 256 with
-// four waves in bands of 8 M tiles, or, with at least 384 rows per group on
-// average, the eight-wave 256 x 256 tile with 16-byte scale chunks
-// (measured: 5-16 % faster at 512-1024 rows per group for N = 1536 .. 7168;
-// at ~256 rows per group its partial M tiles cost more than it saves);
-// few rows per group (decode-like, weight streaming) -> 32 x 128 tiles, many
-// of them, walked N-outer so the M tiles of an expert share each weight panel
-// in L2.
+// fit 160 KiB of LDS) in bands of 4 M tiles; MX formats with K a multiple of
+// 1024 (LDS-staged scales) -> with at least 384 rows per group on average
+// the eight-wave 256 x 256 tile with 16-byte scale chunks, else the
+// eight-wave 192 x 256 tile in bands of 8 M tiles (at 170-270 rows per group
+// it streams ~13 % fewer operand rows than 128 x 256 and pads far less than
+// 256 x 256: MXFP8 and fused MXFP4 8-17 % faster than 128 x 256; at 512 rows
+// per group 256 x 256 stays 3-4 % ahead); other MX shapes -> 128 x 256 with
+// four waves and three slots; few rows per group (decode-like, weight
+// streaming) -> 32 x 128 tiles, many of them, walked N-outer so the M tiles
+// of an expert share each weight panel in L2.
 using TileLargeFp8 = Tile<256, 256, 2, 4, 2>;
 using TileLargeMx = Tile<128, 256, 2, 2, 3>;
 using TileLargeMxKA = Tile<128, 256, 2, 2, 2>;
 using TileLargeMxKA8 = Tile<256, 256, 2, 4, 2>;
+using TileMx192 = Tile<192, 256, 2, 4, 2>;
 using TileSmall = Tile<32, 128, 1, 4, 3, 1, true>;
 constexpr int kBandLarge = 4, kBandMx = 8, kBandNOuter = 1 << 30;
 constexpr int64_t kTallRows = 384;
@@ -783,7 +786,7 @@ hipError_t launch_fmt(const GemmProblem& p, hipStream_t stream) {
             } else {
                 if (ka && avg_rows >= kTallRows)
                     return launch_tile<TileLargeMxKA8, FMT, SWIGLU, true>(p, stream, kBandLarge);
-                return ka ? launch_tile<TileLargeMxKA, FMT, SWIGLU, true>(p, stream, kBandMx)
+                return ka ? launch_tile<TileMx192, FMT, SWIGLU, true>(p, stream, kBandMx)
                           : launch_tile<TileLargeMx, FMT, SWIGLU, false>(p, stream, kBandMx);
             }
         }

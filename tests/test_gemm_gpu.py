@@ -56,8 +56,9 @@ SMALL = {
 
 # The row-count hint selects the tile shape: 0 lets small reduced problems use
 # the decode-regime tile, a large hint forces the prefill-regime tile (FP8:
-# 256 x 256 with eight waves; MX: 128 x 256), so both code paths see every
-# case, including partial M / N tiles and K tails.
+# 256 x 256 with eight waves; MX: 192 x 256 with eight waves when K is a
+# multiple of 1024, else 128 x 256), so both code paths see every case,
+# including partial M / N tiles and K tails.
 HINTS = [0, 1 << 20]
 
 

@@ -71,7 +71,7 @@ def padded_case(case: GemmCase, round_to=128):
 
 
 PAD_CASES = {
-    # the 128x256 tile with LDS scales, the eight-wave 256x256 MX tile, per-lane scale loads (K % 1024 != 0)
+    # the 192x256 tile with LDS scales, the eight-wave 256x256 MX tile, per-lane scale loads (K % 1024 != 0)
     "mxfp4_k1024": W.WORKLOADS[5].scaled(tokens=96, E=8, masked=1, top_k=4, N=320, K=1024, swiglu=False),
     "mxfp8_tall": W.WORKLOADS[4].scaled(rows=4096, E=8, N=288, K=1024),
     "mxfp4_k608": W.WORKLOADS[5].scaled(tokens=64, E=6, masked=1, top_k=4, N=256, K=608, swiglu=False),
