@@ -755,14 +755,18 @@ hipError_t launch_tile(const GemmProblem& p, hipStream_t stream, int mband) {
 // 256 x 256: MXFP8 and fused MXFP4 8-17 % faster than 128 x 256; at 512 rows
 // per group 256 x 256 stays 3-4 % ahead); other MX shapes -> 128 x 256 with
 // four waves and three slots; few rows per group (decode-like, weight
-// streaming) -> 32 x 128 tiles, many of them, walked N-outer so the M tiles
-// of an expert share each weight panel in L2.
+// streaming) -> 32-row tiles, many of them, walked N-outer so the M tiles of
+// an expert share each weight panel in L2: FP8 rowwise 32 x 256 with two
+// slots (decode workload 140 -> 136 us against 32 x 128 with three; 32 x 512,
+// three slots, or 32 x 64 / 32 x 128 with two were slower), MX 32 x 128 with
+// three slots.
 using TileLargeFp8 = Tile<256, 256, 2, 4, 2>;
 using TileLargeMx = Tile<128, 256, 2, 2, 3>;
 using TileLargeMxKA = Tile<128, 256, 2, 2, 2>;
 using TileLargeMxKA8 = Tile<256, 256, 2, 4, 2>;
 using TileMx192 = Tile<192, 256, 2, 4, 2>;
 using TileSmall = Tile<32, 128, 1, 4, 3, 1, true>;
+using TileSmallFp8 = Tile<32, 256, 1, 4, 2, 1, true>;
 constexpr int kBandLarge = 4, kBandMx = 8, kBandNOuter = 1 << 30;
 constexpr int64_t kTallRows = 384;
 
@@ -790,7 +794,8 @@ hipError_t launch_fmt(const GemmProblem& p, hipStream_t stream) {
                           : launch_tile<TileLargeMx, FMT, SWIGLU, false>(p, stream, kBandMx);
             }
         }
-        return launch_tile<TileSmall, FMT, SWIGLU, false>(p, stream, kBandNOuter);
+        if constexpr (FMT == 0) return launch_tile<TileSmallFp8, FMT, SWIGLU, false>(p, stream, kBandNOuter);
+        else return launch_tile<TileSmall, FMT, SWIGLU, false>(p, stream, kBandNOuter);
     }
 }
 
