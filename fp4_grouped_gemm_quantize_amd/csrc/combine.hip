@@ -24,6 +24,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWavesPerBlock = kThreads / kWave;
+constexpr int kGather = 8;  // slot rows loaded together per lane
 
 __global__ __launch_bounds__(kThreads) void combine_kernel(const uint16_t* __restrict__ y, int64_t T, int64_t H,
                                                            const int32_t* __restrict__ row_of_slot,
@@ -48,16 +49,30 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const uint16_t* __res
                 wk = wt[kk];
             }
             const int kn = top_k - k0 < kWave ? top_k - k0 : kWave;
-            for (int j = 0; j < kn; ++j) {
-                const int32_t rj = __shfl(r, j, kWave);
-                const float wj = __shfl(wk, j, kWave);
-                if (rj < 0 || (int64_t)rj >= T) continue;  // wave-uniform: a dropped slot
-                if (on) {
-                    const uint4 v = *reinterpret_cast<const uint4*>(y + (int64_t)rj * H + u * 8);
-                    float f[8];
-                    unpack8(v, f);
+            // slots in groups of kGather: all their row loads are issued
+            // before any is accumulated (one load at a time left each wave
+            // waiting out the memory latency per slot); the accumulation
+            // order stays slot 0, 1, ...
+            for (int j0 = 0; j0 < kn; j0 += kGather) {
+                uint4 v[kGather];
+                float wj[kGather];
+                bool use[kGather];
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) acc[i] = fmaf(wj, f[i], acc[i]);
+                for (int q = 0; q < kGather; ++q) {
+                    const int j = j0 + q < kn ? j0 + q : 0;  // uniform
+                    const int32_t rj = __shfl(r, j, kWave);
+                    wj[q] = __shfl(wk, j, kWave);
+                    use[q] = j0 + q < kn && rj >= 0 && (int64_t)rj < T;  // wave-uniform: a dropped slot
+                    v[q] = use[q] && on ? *reinterpret_cast<const uint4*>(y + (int64_t)rj * H + u * 8)
+                                        : make_uint4(0, 0, 0, 0);
+                }
+#pragma unroll
+                for (int q = 0; q < kGather; ++q) {
+                    if (!use[q] || !on) continue;
+                    float f[8];
+                    unpack8(v[q], f);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) acc[i] = fmaf(wj[q], f[i], acc[i]);
                 }
             }
         }
