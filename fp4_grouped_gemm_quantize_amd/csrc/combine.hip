@@ -78,10 +78,10 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const uint16_t* __res
         }
         if (on) {
             uint4 o;
-            o.x = f32_to_bf16(acc[0]) | (f32_to_bf16(acc[1]) << 16);
-            o.y = f32_to_bf16(acc[2]) | (f32_to_bf16(acc[3]) << 16);
-            o.z = f32_to_bf16(acc[4]) | (f32_to_bf16(acc[5]) << 16);
-            o.w = f32_to_bf16(acc[6]) | (f32_to_bf16(acc[7]) << 16);
+            o.x = f32x2_to_bf16x2(acc[0], acc[1]);
+            o.y = f32x2_to_bf16x2(acc[2], acc[3]);
+            o.z = f32x2_to_bf16x2(acc[4], acc[5]);
+            o.w = f32x2_to_bf16x2(acc[6], acc[7]);
             *reinterpret_cast<uint4*>(out + t * H + u * 8) = o;
         }
     }

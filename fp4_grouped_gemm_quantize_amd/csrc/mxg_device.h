@@ -13,14 +13,31 @@ constexpr int kMaxGroups = 1024;
 
 // ---------------------------------------------------------------------------
 // bf16 <-> fp32.  bf16 is the upper half of binary32; fp32 -> bf16 rounds to
-// nearest, ties to even (overflow goes to infinity as IEEE rounding does).
+// nearest, ties to even (overflow goes to infinity as IEEE rounding does, a
+// NaN keeps its upper half with the quiet bit set).  The conversion is the
+// hardware packed convert (v_cvt_pk_bf16_f32), checked on gfx950 against the
+// integer form of that rounding -- u += 0x7fff + ((u >> 16) & 1), keep the
+// upper half; NaN: (u >> 16) | 0x40 -- for all 2^32 fp32 inputs, bit for bit.
+// One instruction instead of five; the GEMM epilogues and the SwiGLU requant
+// round every output through it.
+typedef float mxg_f2v __attribute__((ext_vector_type(2)));
+typedef __bf16 mxg_b2v __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
+// lo in bits 0..15, hi in bits 16..31
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float lo, float hi) {
+    const mxg_b2v b = __builtin_convertvector((mxg_f2v){lo, hi}, mxg_b2v);
+    uint32_t r;
+    __builtin_memcpy(&r, &b, 4);
+    return r;
+}
+
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;  // quiet NaN
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
+    const __bf16 b = (__bf16)f;
+    uint16_t r;
+    __builtin_memcpy(&r, &b, 2);
+    return r;
 }
 
 // ---------------------------------------------------------------------------
