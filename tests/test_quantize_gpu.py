@@ -62,9 +62,11 @@ def test_quantize_matches_oracle(fmt, case):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
-@pytest.mark.parametrize("K", [32, 96, 544, 1056, 8192, 8224, 12288])
+@pytest.mark.parametrize("K", [32, 96, 544, 1056, 2080, 7168, 8192, 8224, 12288])
 def test_quantize_row_lengths(fmt, K):
-    """Tails of the 512-element wave vector, the register-resident limit and the long-row path."""
+    """Tails of the 512-element wave vector, the register-resident limit, the long-row path and
+    (block formats) K segments: 2080 and 7168 are one and two segments with a partial last chunk
+    / whole chunks."""
     rng = np.random.default_rng(K + fmt)
     T = 37
     vals = rng.standard_normal((T, K)) * np.exp(rng.uniform(-20, 20, (T, 1)))
