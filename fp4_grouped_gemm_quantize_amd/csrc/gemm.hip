@@ -338,7 +338,8 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
         const TileCoord tc = locate_item<BM, BN>(args, s_pre, ws, W);
         if (tc.cols_in <= 0) continue;  // the empty second half of a last, narrow tile (uniform)
         const int e = tc.e;
-        const int64_t m0 = tc.m0, m_end = tc.m_end, n0 = tc.n0, n_end = tc.n_end;
+        const int64_t m0 = tc.m0, n0 = tc.n0, n_end = tc.n_end;
+        int64_t m_end = tc.m_end;  // one past the last row stored (a padded scale layout can lower it)
         const int rows_in = tc.rows_in, cols_in = tc.cols_in;
         // A wave whose sub-tile lies wholly past the group's last row or past
         // the last column (partial M tiles, half tiles of a split round)
@@ -433,12 +434,20 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
 
         // ---- MX scale words of this lane's rows / columns, one stage ahead.
         // A padded A-scale layout moves the tile's first scale row (a tile
-        // never spans groups); a tile whose scale rows would run past the
-        // tensor is skipped (its outputs are left untouched).
+        // never spans groups).  Rows whose scale row lies at or past the end
+        // of the scale tensor are not stored (their outputs are left
+        // untouched); their scale reads are clamped to the last row that
+        // exists, as rows past a group's end are.
         int64_t sa_row0 = m0;
+        int rows_sc = rows_in;  // rows of the tile whose scale rows exist
         if (F::kMX && args.asoff) {
             sa_row0 = (int64_t)args.asoff[tc.g] + (m0 - tc.glo);
-            if (sa_row0 + rows_in > args.as_rows) continue;  // uniform; before any LDS use
+            const int64_t avail = args.as_rows - sa_row0;
+            if (avail <= 0) continue;  // uniform; nothing to store
+            if (avail < rows_in) {
+                rows_sc = (int)avail;
+                m_end = m0 + avail;
+            }
         }
         const uint8_t* sa_base = static_cast<const uint8_t*>(args.as) + sa_row0 * nblk;
         const uint8_t* sb_base = static_cast<const uint8_t*>(args.bs) + ((int64_t)e * args.N + n0) * nblk;
@@ -448,7 +457,7 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
 #pragma unroll
             for (int i = 0; i < TM; ++i) {
                 const int r = wm * WTM + i * 32 + r32;
-                sa_off[i] = (uint32_t)((r < rows_in ? r : rows_in - 1) * nblk);
+                sa_off[i] = (uint32_t)((r < rows_sc ? r : rows_sc - 1) * nblk);
             }
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
@@ -472,7 +481,7 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
                 const int r = q * kSclRowsPerLoad + lane / (kSclBytes / 16);
                 const bool in_a = q * kSclRowsPerLoad < BM;  // wave-uniform
                 scl_base[k] = in_a ? sa_base : sb_base;
-                scl_off[k] = (in_a ? (uint32_t)((r < rows_in ? r : rows_in - 1) * nblk)
+                scl_off[k] = (in_a ? (uint32_t)((r < rows_sc ? r : rows_sc - 1) * nblk)
                                    : (uint32_t)((r - BM < cols_in ? r - BM : cols_in - 1) * nblk)) +
                              16 * (lane % (kSclBytes / 16));
             }

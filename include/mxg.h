@@ -363,8 +363,9 @@ mxg_status mx_grouped_quantize_nvfp4(const void* x_bf16, void* q, void* scales, 
  * that row; a row whose scale row lies at or past scale_rows is left
  * untouched (codes too); scale rows nothing maps to (the padding) are never
  * written.  The GEMMs read A's scales through the same map (weights keep the
- * dense layout); a tile whose rows' scale rows would run past scale_rows is
- * skipped and its output rows are left untouched.  Results are otherwise
+ * dense layout); a row whose scale row lies at or past scale_rows is not
+ * computed and its output row is left untouched, whatever tile shape is
+ * chosen.  Results are otherwise
  * identical to the dense entry points.  Other arguments, layouts and errors as
  * mx_grouped_quantize / mx_grouped_matmul / mx_grouped_matmul_swiglu;
  * NOT_SUPPORTED also for MXG_FP8_E4M3_ROWWISE (its scale is per row, not per

@@ -119,6 +119,66 @@ def test_padded_gemm_skips_tiles_past_the_scale_tensor():
     check_gemm_rows(out[:int(case.off[-2])][cov], {k: v[cov] for k, v in ref.items() if k != "group"}, "skip")
 
 
+def cut_mid_group(case: GemmCase, round_to=128):
+    """A slot layout whose scale tensor ends inside the largest group, part
+    way into one of its M tiles: rows before the cut are computed, the rest
+    of that group and every group whose slot starts later are not."""
+    soff, sp = padded_case(case, round_to)
+    counts = np.diff(case.off.astype(np.int64))
+    g = int(np.argmax(counts))
+    assert counts[g] > 40
+    S = int(soff[g]) + int(counts[g]) // 2 + 5
+    return soff, np.ascontiguousarray(sp[:S]), S
+
+
+@pytest.mark.parametrize("name", list(PAD_CASES))
+@pytest.mark.parametrize("hint", [0, 1 << 20])
+def test_padded_gemm_scale_tensor_ends_mid_group(name, hint):
+    case = GemmCase(PAD_CASES[name])
+    soff, sp, S = cut_mid_group(case)
+    inp = case.gpu_inputs()
+    T, N = case.T, case.w.N
+    c = torch.full((T, N), SENT_BF16, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    mxg.mx_grouped_matmul_padded(case.fmt, inp["a_q"], to_gpu(sp), to_gpu(soff), inp["b_q"], inp["b_scales"], c,
+                                 inp["row_offsets"], inp["expert_ids"], hint)
+    torch.cuda.synchronize()
+    out = c.view(torch.int16).cpu().numpy().view(np.uint16)
+    ref = oracle.gemm_rows_padded(case.fmt, case.a, sp, soff, case.b, case.sb, case.off, case.ids, N, case.w.K,
+                                  np.arange(T))
+    cov = ref["group"] >= 0
+    assert 0 < cov.sum() < T
+    assert np.all(out[~cov] == SENT_BF16), "rows without scale rows were written"
+    check_gemm_rows(out[cov], {k: v[cov] for k, v in ref.items() if k != "group"}, f"{name} hint={hint}")
+
+
+@pytest.mark.parametrize("hint", [0, 1 << 20])
+def test_padded_fused_swiglu_scale_tensor_ends_mid_group(hint):
+    w = W.WORKLOADS[5].scaled(tokens=256, E=8, masked=1, top_k=4, N=256, K=1024)
+    case = GemmCase(w)
+    soff, sp, S = cut_mid_group(case, round_to=64)
+    soff_full, sp_full = padded_case(case, round_to=64)
+    inp = case.gpu_inputs()
+    T, I = case.T, w.N // 2
+    ys = [(torch.full((T, I // 2), 0xA5, dtype=torch.uint8, device="cuda"),
+           torch.full((T, I // 32), 0x5A, dtype=torch.uint8, device="cuda")) for _ in range(2)]
+    mxg.mx_grouped_matmul_swiglu_padded(case.fmt, inp["a_q"], to_gpu(sp_full), to_gpu(soff_full), inp["b_q"],
+                                        inp["b_scales"], ys[0][0], ys[0][1], inp["row_offsets"], inp["expert_ids"],
+                                        hint)
+    mxg.mx_grouped_matmul_swiglu_padded(case.fmt, inp["a_q"], to_gpu(sp), to_gpu(soff), inp["b_q"],
+                                        inp["b_scales"], ys[1][0], ys[1][1], inp["row_offsets"], inp["expert_ids"],
+                                        hint)
+    torch.cuda.synchronize()
+    ref = oracle.gemm_rows_padded(case.fmt, case.a, sp, soff, case.b, case.sb, case.off, case.ids, w.N, w.K,
+                                  np.arange(T))
+    cov = ref["group"] >= 0
+    assert 0 < cov.sum() < T
+    full = [y.cpu().numpy() for y in ys[0]]
+    cut = [y.cpu().numpy() for y in ys[1]]
+    for f, c_ in zip(full, cut):
+        assert np.array_equal(f[cov], c_[cov]), "rows with scale rows differ from the uncut layout"
+    assert np.all(cut[0][~cov] == 0xA5) and np.all(cut[1][~cov] == 0x5A), "rows without scale rows were written"
+
+
 def test_padded_fused_swiglu_equals_dense():
     w = W.WORKLOADS[5].scaled(tokens=256, E=8, masked=1, top_k=4, N=256, K=1024)
     case = GemmCase(w)
