@@ -25,12 +25,15 @@
 //    2- or 3-slot LDS ring filled by direct global->LDS loads
 //    (global_load_lds_dwordx4: each lane's 16 bytes land at LDS base + 16 *
 //    lane, no VGPR staging), issued one or two stages ahead of the matrix
-//    cores.  The 16-byte chunks of a row are XOR-swizzled (chunk c of row r
-//    sits at slot c ^ ((r >> 1) & 7)) so the 16-byte fragment reads of 16
+//    cores.  The large FP8 rowwise tile instead streams 64-byte stages
+//    through four slots, so two stages stay in flight across each barrier
+//    (a 128-byte two-slot ring drains to none at every barrier; measured 1-5 %
+//    faster on the prefill shapes).  The 16-byte chunks of a row are
+//    XOR-swizzled (see swz_chunk) so the 16-byte fragment reads of 16
 //    consecutive rows hit distinct bank groups; the swizzle is realised by
 //    choosing which global chunk each lane fetches.  A stage that runs past
-//    the end of K (only the last one, when K bytes are not a multiple of 128)
-//    goes through VGPRs so its tail can be zero-filled.
+//    the end of K (only the last one, when K bytes are not a multiple of the
+//    stage) goes through VGPRs so its tail can be zero-filled.
 //  * MX scales: when K is a multiple of 1024 the workgroup stages 32 (or, for
 //    the 256 x 256 tile, 16) scale bytes of each of its rows through two LDS
 //    buffers with direct loads, one chunk per 32 (16) blocks, and each lane
@@ -55,26 +58,34 @@ using namespace gemm;
 namespace {
 
 // BM x BN output tile, WGM x WGN waves, SLOTS stages of LDS ring (2: one stage
-// in flight while one is consumed; 3: two in flight).  STREAM_B: the weight
+// in flight while one is consumed; 3: two; 4: three), SB K bytes per row per
+// stage (128, or 64 for FP8 rowwise: half the LDS per stage, so a 256 x 256
+// tile fits four slots and keeps loads in flight across its barriers).
+// STREAM_B: the weight
 // operand is loaded with the nontemporal cache policy -- for the small
 // weight-streaming tile, where each weight panel is read by the few M tiles
 // of its expert at about the same time and then never again (measured on
 // the decode-shaped workload: 157-164 -> 141-146 us; the large tiles, whose
 // weight panels are re-read from L2, were slower with it).
-template <int BM_, int BN_, int WGM_, int WGN_, int SLOTS_ = 3, int MINB_ = 1, bool STREAM_B_ = false>
+template <int BM_, int BN_, int WGM_, int WGN_, int SLOTS_ = 3, int MINB_ = 1, bool STREAM_B_ = false, int SB_ = 128>
 struct Tile {
     static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_, kMinBlocks = MINB_, kSlots = SLOTS_;
+    static constexpr int kSB = SB_;
+    // direct-to-LDS loads: 16 bytes per lane, kLPR lanes per stage row, so one
+    // wave instruction (1 KiB) covers kRPI rows
+    static constexpr int kLPR = SB_ / 16, kRPI = 64 / kLPR;
     static constexpr bool kStreamB = STREAM_B_;
     // Fragment buffers per wave: with one wave per SIMD the fragments of step
     // s+1 are read while step s computes (2); with two waves per SIMD the
     // other wave covers the LDS latency and the registers go to accumulators.
-    static_assert(SLOTS_ == 2 || SLOTS_ == 3, "2- or 3-slot LDS ring");
+    static_assert(SLOTS_ >= 2 && SLOTS_ <= 4, "2- to 4-slot LDS ring");
+    static_assert(SB_ == 128 || SB_ == 64, "stage rows of 128 or 64 bytes");
     static constexpr int kWaves = WGM * WGN, kThreads = kWave * kWaves;
     static constexpr int WTM = BM / WGM, WTN = BN / WGN;
     static constexpr int TM = WTM / 32, TN = WTN / 32;
     static constexpr int kFragBufs = kWaves >= 8 ? 1 : 2;
     static_assert(TM >= 1 && TN >= 1, "wave tile below one 32x32 accumulator");
-    static_assert(BM % (8 * kWaves) == 0 && BN % (8 * kWaves) == 0, "loader: whole 8-row groups per wave");
+    static_assert(BM % (kRPI * kWaves) == 0 && BN % (kRPI * kWaves) == 0, "loader: whole row groups per wave");
 };
 
 // One fragment of a 64-deep K step, read from LDS: A row block i (from sa)
@@ -82,11 +93,11 @@ struct Tile {
 template <class TL, int FMT>
 __device__ __forceinline__ v8i load_frag(const uint8_t* __restrict__ base, int s, int row, int h) {
     if constexpr (Fmt<FMT>::kFP4) {
-        const uint4 x = *reinterpret_cast<const uint4*>(base + swz(row, 2 * s + h));
+        const uint4 x = *reinterpret_cast<const uint4*>(base + swz<TL::kSB>(row, 2 * s + h));
         return v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
     } else {
-        const uint4 x0 = *reinterpret_cast<const uint4*>(base + swz(row, 4 * s + h));
-        const uint4 x1 = *reinterpret_cast<const uint4*>(base + swz(row, 4 * s + 2 + h));
+        const uint4 x0 = *reinterpret_cast<const uint4*>(base + swz<TL::kSB>(row, 4 * s + h));
+        const uint4 x1 = *reinterpret_cast<const uint4*>(base + swz<TL::kSB>(row, 4 * s + 2 + h));
         return v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
     }
 }
@@ -163,14 +174,14 @@ __device__ __forceinline__ void mma_stage_nv(const uint8_t* __restrict__ sa, con
         h2v ma[TM][2], mb[TN][2];
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
-            ra[i] = *reinterpret_cast<const uint4*>(sa + swz(wm * TL::WTM + i * 32 + r32, 2 * s + h));
+            ra[i] = *reinterpret_cast<const uint4*>(sa + swz<128>(wm * TL::WTM + i * 32 + r32, 2 * s + h));
             const uint32_t w = wa[i][s] >> (16 * h);  // bytes 0, 1: this lane's two blocks
             nv_split_scale(w & 0xffu, pa[i][0], ma[i][0]);
             nv_split_scale((w >> 8) & 0xffu, pa[i][1], ma[i][1]);
         }
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-            rb[j] = *reinterpret_cast<const uint4*>(sb + swz(wn * TL::WTN + j * 32 + r32, 2 * s + h));
+            rb[j] = *reinterpret_cast<const uint4*>(sb + swz<128>(wn * TL::WTN + j * 32 + r32, 2 * s + h));
             const uint32_t w = wb[j][s] >> (16 * h);
             nv_split_scale(w & 0xffu, pb[j][0], mb[j][0]);
             nv_split_scale((w >> 8) & 0xffu, pb[j][1], mb[j][1]);
@@ -214,6 +225,7 @@ __device__ __forceinline__ void mma_stage(const uint8_t* __restrict__ sa, const 
         return;
     }
     constexpr int TM = TL::TM, TN = TL::TN, kW = F::kWords;
+    constexpr int kSteps = TL::kSB / (F::kFP4 ? 32 : 64);  // 64-deep K steps per stage
     uint32_t wa[TM][kW], wb[TN][kW];
     if constexpr (F::kMX) {
 #pragma unroll
@@ -232,12 +244,12 @@ __device__ __forceinline__ void mma_stage(const uint8_t* __restrict__ sa, const 
 #pragma unroll
     for (int j = 0; j < TN; ++j) bf[0][j] = load_frag<TL, FMT>(sb, 0, brow(j), h);
 #pragma unroll
-    for (int s = 0; s < F::kSteps; ++s) {
+    for (int s = 0; s < kSteps; ++s) {
         const int c = s & 1, n = c ^ 1;
         if constexpr (TL::kFragBufs == 1) {
 #pragma unroll
             for (int i = 0; i < TM; ++i) mma_row<TL, FMT>(i, s, af[i], bf[c], wa, wb, acc);
-            if (s + 1 < F::kSteps) {
+            if (s + 1 < kSteps) {
 #pragma unroll
                 for (int i = 0; i < TM; ++i) af[i] = load_frag<TL, FMT>(sa, s + 1, arow(i), h);
 #pragma unroll
@@ -248,7 +260,7 @@ __device__ __forceinline__ void mma_stage(const uint8_t* __restrict__ sa, const 
 #pragma unroll
             for (int i = 0; i < TM; ++i) {
                 mma_row<TL, FMT>(i, s, af[i], bf[c], wa, wb, acc);
-                if (s + 1 < F::kSteps) {
+                if (s + 1 < kSteps) {
                     af[i] = load_frag<TL, FMT>(sa, s + 1, arow(i), h);
 #pragma unroll
                     for (int k = 0; k < kBPerRow; ++k)
@@ -256,7 +268,7 @@ __device__ __forceinline__ void mma_stage(const uint8_t* __restrict__ sa, const 
                             bf[n][i * kBPerRow + k] = load_frag<TL, FMT>(sb, s + 1, brow(i * kBPerRow + k), h);
                 }
             }
-            if (s + 1 < F::kSteps) {
+            if (s + 1 < kSteps) {
                 // interleave: one matrix-core op, then a share of the next step's LDS reads
                 constexpr int kMfma = TM * TN;
                 constexpr int kReads = (TM + TN) * (F::kFP4 ? 1 : 2);
@@ -279,9 +291,11 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
     using F = Fmt<FMT>;
     constexpr int BM = TL::BM, BN = TL::BN, NW = TL::kWaves, NT = TL::kThreads;
     constexpr int WTM = TL::WTM, WTN = TL::WTN, TM = TL::TM, TN = TL::TN;
-    constexpr int kAStage = BM * kStageBytes, kBStage = BN * kStageBytes;
+    constexpr int SB = TL::kSB, kLPR = TL::kLPR, kRPI = TL::kRPI;
+    static_assert(SB == kStageBytes || (!F::kMX && KA), "64-byte stages: FP8 rowwise with whole stages only");
+    constexpr int kAStage = BM * SB, kBStage = BN * SB;
     constexpr int kStage = kAStage + kBStage;
-    constexpr int A_J = BM / 8 / NW, B_J = BN / 8 / NW;  // 1 KiB load instructions per wave per stage
+    constexpr int A_J = BM / kRPI / NW, B_J = BN / kRPI / NW;  // 1 KiB load instructions per wave per stage
     constexpr int kWords = F::kWords;                    // scale words per row per stage
     // cache policy of the weight loads (a named constant: written as a
     // conditional expression inside the builtin call, hipcc dropped the
@@ -308,6 +322,7 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
     __shared__ __attribute__((aligned(16))) uint8_t s_ring0[kStage];
     __shared__ __attribute__((aligned(16))) uint8_t s_ring1[kStage];
     __shared__ __attribute__((aligned(16))) uint8_t s_ring2[kSlots > 2 ? kStage : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t s_ring3[kSlots > 3 ? kStage : 16];
     __shared__ __attribute__((aligned(16))) uint8_t s_scl0[kLdsScales ? kSclRows * kSclBytes : 16];
     __shared__ __attribute__((aligned(16))) uint8_t s_scl1[kLdsScales ? kSclRows * kSclBytes : 16];
     __shared__ uint32_t s_pre[kMaxGroups + 1];
@@ -329,8 +344,8 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
     build_tile_prefix<NT, BM>(args, s_pre, s_wave);
     const int64_t total_tiles = (int64_t)s_pre[G] * args.ntiles_n;
     const int64_t row_bytes = args.row_bytes;
-    const int nkt = (int)((row_bytes + kStageBytes - 1) / kStageBytes);
-    const bool k_tail = !KA && (row_bytes % kStageBytes) != 0;  // the last stage is partial
+    const int nkt = (int)((row_bytes + SB - 1) / SB);
+    const bool k_tail = !KA && (row_bytes % SB) != 0;  // the last stage is partial
     const int64_t nblk = args.K / F::kBlockElems;  // scale bytes per row
 
     const WorkSplit ws = work_split(total_tiles, gridDim.x);
@@ -357,10 +372,11 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
         }
 
         // ---- operand sources: tile base (uniform) + 32-bit per-lane offsets;
-        // load j of a wave covers rows r0 + 8 NW j .. +7 x 8 chunks (1 KiB of
-        // the slot).  Rows past the group / columns past N re-read the last
+        // load j of a wave covers rows r0 + kRPI NW j .. + kRPI - 1, kLPR
+        // chunks each (1 KiB of the slot).  Rows past the group / columns past N re-read the last
         // real one.  With an even wave count the swizzled chunk of a lane is
-        // the same for every j.  The offsets are held in registers (one per
+        // the same for every j (the swizzle reads row bits the step
+        // kRPI NW j leaves alone).  The offsets are held in registers (one per
         // load) through the K loop, except in the eight-wave MX kernel, which
         // runs out of registers (spills in the K loop stall it on the
         // prefetch): there they are recomputed per stage from two registers.
@@ -368,11 +384,11 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
         constexpr bool kLeanOffsets = F::kMX && NW >= 8;
         const uint8_t* a_base = args.a + m0 * row_bytes;
         const uint8_t* b_base = args.b + ((int64_t)e * args.N + n0) * row_bytes;
-        const int r0 = wave * 8 + (lane >> 3);
-        const uint32_t chunk16 = (uint32_t)swz_chunk(r0, lane & 7) << 4;
+        const int r0 = wave * kRPI + lane / kLPR;
+        const uint32_t chunk16 = (uint32_t)swz_chunk<SB>(r0, lane % kLPR) << 4;
         const uint32_t rb32 = (uint32_t)row_bytes;
         auto op_off = [&](int rbase, int j, int live) {
-            const int r = rbase + 8 * NW * j;
+            const int r = rbase + kRPI * NW * j;
             return (uint32_t)(r < live ? r : live - 1) * rb32 + chunk16;
         };
         uint32_t a_off[A_J], b_off[B_J];
@@ -392,8 +408,8 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
             return v;
         };
         auto issue_stage = [&](int kt, uint8_t* slot) {
-            const uint8_t* ak = a_base + (int64_t)kt * kStageBytes;
-            const uint8_t* bk = b_base + (int64_t)kt * kStageBytes;
+            const uint8_t* ak = a_base + (int64_t)kt * SB;
+            const uint8_t* bk = b_base + (int64_t)kt * SB;
             const int rb = kLeanOffsets ? (int)opaque((uint32_t)r0) : r0;
 #pragma unroll
             for (int j = 0; j < A_J; ++j)
@@ -409,18 +425,18 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
         // The partial last stage: VGPR loads with the K tail zero-filled.
         uint4 ta[A_J], tb[B_J];
         auto load_tail = [&](int kt) {
-            const int64_t kb = (int64_t)kt * kStageBytes;
-            const int c_lo = lane & 7;  // physical chunk; the logical one depends on the row
+            const int64_t kb = (int64_t)kt * SB;
+            const int c_lo = lane % kLPR;  // physical chunk; the logical one depends on the row
 #pragma unroll
             for (int j = 0; j < A_J; ++j) {
-                const int r = (wave + NW * j) * 8 + (lane >> 3);
-                const bool in = kb + swz_chunk(r, c_lo) * 16 < row_bytes;
+                const int r = (wave + NW * j) * kRPI + lane / kLPR;
+                const bool in = kb + swz_chunk<SB>(r, c_lo) * 16 < row_bytes;
                 ta[j] = in ? *reinterpret_cast<const uint4*>(a_base + kb + op_off(r0, j, rows_in)) : make_uint4(0, 0, 0, 0);
             }
 #pragma unroll
             for (int j = 0; j < B_J; ++j) {
-                const int r = (wave + NW * j) * 8 + (lane >> 3);
-                const bool in = kb + swz_chunk(r, c_lo) * 16 < row_bytes;
+                const int r = (wave + NW * j) * kRPI + lane / kLPR;
+                const bool in = kb + swz_chunk<SB>(r, c_lo) * 16 < row_bytes;
                 tb[j] = in ? *reinterpret_cast<const uint4*>(b_base + kb + op_off(r0, j, cols_in)) : make_uint4(0, 0, 0, 0);
             }
         };
@@ -533,12 +549,33 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
                 issue_stage(kt, slot);
             }
         };
-        put_stage(0, s_ring0);
-        if (kSlots > 2 && nkt > 1) put_stage(1, s_ring1);
-        if constexpr (kLdsScales) issue_scales(0, s_scl0);
-        else if constexpr (F::kMX) load_scales(0, wa, wb);
-        wait_vmem<0>();
-        __syncthreads();
+        constexpr int L = A_J + B_J;  // direct loads per wave per stage
+        // wait until this wave's loads of the stage needed next have landed,
+        // leaving those of the `later` stages issued after it in flight (the
+        // loads land in issue order), then the workgroup barrier
+        auto barrier_leaving = [&](int later) {
+            if (later >= 2) stage_barrier<2 * L>();
+            else if (later == 1) stage_barrier<L>();
+            else stage_barrier<0>();
+        };
+        if constexpr (kSlots == 4) {
+            static_assert(KA, "four slots: whole stages only");
+            // The previous tile's output stores share the vector-memory counter
+            // with these loads and may complete out of order with them; let
+            // them finish first so the counted waits see only this tile's stages.
+            wait_vmem<0>();
+            issue_stage(0, s_ring0);
+            if (nkt > 1) issue_stage(1, s_ring1);
+            if (nkt > 2) issue_stage(2, s_ring2);
+            barrier_leaving(nkt - 1 < 2 ? nkt - 1 : 2);
+        } else {
+            put_stage(0, s_ring0);
+            if (kSlots > 2 && nkt > 1) put_stage(1, s_ring1);
+            if constexpr (kLdsScales) issue_scales(0, s_scl0);
+            else if constexpr (F::kMX) load_scales(0, wa, wb);
+            wait_vmem<0>();
+            __syncthreads();
+        }
 
         // One stage: the matrix cores consume `cur` (stage kt) while stage
         // kt + kSlots - 1 streams into `pf` (and, with three slots, stage kt+1,
@@ -568,9 +605,16 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
                     }
                 }
             // stage kt+1 (and its scales) must have landed; with three slots
-            // stage kt+2's direct loads, the most recent ones, may stay in flight
-            if (D == 2 && pf_on && !pf_tail) stage_barrier<A_J + B_J>();
-            else stage_barrier<0>();
+            // stage kt+2's direct loads, the most recent ones, may stay in
+            // flight, with four slots those of kt+2 and kt+3
+            if constexpr (D == 3) {
+                const int later = nkt - 2 - kt;
+                barrier_leaving(later < 2 ? (later > 0 ? later : 0) : 2);
+            } else if (D == 2 && pf_on && !pf_tail) {
+                stage_barrier<L>();
+            } else {
+                stage_barrier<0>();
+            }
         };
         // With LDS scales: the stage also reads its scale words from `scur`
         // (position pos of the chunk) and, in a chunk's last stage, starts the
@@ -597,6 +641,13 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
                                   (u / kSclStages) % 2 ? s_scl1 : s_scl0, (u / kSclStages) % 2 ? s_scl0 : s_scl1,
                                   u % kSclStages);
             }
+        } else if constexpr (kSlots == 4) {
+            for (int kt = 0; kt < nkt; kt += 4) {
+                stage(kt, s_ring0, s_ring3);
+                if (kt + 1 < nkt) stage(kt + 1, s_ring1, s_ring0);
+                if (kt + 2 < nkt) stage(kt + 2, s_ring2, s_ring1);
+                if (kt + 3 < nkt) stage(kt + 3, s_ring3, s_ring2);
+            }
         } else if constexpr (kSlots == 3) {
             for (int kt = 0; kt < nkt; kt += 3) {
                 stage(kt, s_ring0, s_ring2);
@@ -617,7 +668,8 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
         constexpr int kRowsPerSlot = kStage / (BN * 2);
         static_assert(kSlots * kRowsPerSlot >= BM, "staging tile must fit the LDS ring");
         auto srow = [&](int row) -> uint16_t* {
-            uint8_t* base = row < kRowsPerSlot ? s_ring0 : row < 2 * kRowsPerSlot ? s_ring1 : s_ring2;
+            uint8_t* base = row < kRowsPerSlot ? s_ring0 : row < 2 * kRowsPerSlot ? s_ring1
+                          : row < 3 * kRowsPerSlot ? s_ring2 : s_ring3;
             return reinterpret_cast<uint16_t*>(base + (row % kRowsPerSlot) * BN * 2);
         };
         if constexpr (!SWIGLU) {
@@ -755,8 +807,9 @@ hipError_t launch_tile(const GemmProblem& p, hipStream_t stream, int mband) {
 
 // Tile shapes and tile orders, chosen by measurement on MI355X (ragged
 // workloads of the benchmark): FP8 rowwise with many rows per group ->
-// 256 x 256 with eight waves (fewest operand bytes per FLOP; two ring slots
-// fit 160 KiB of LDS) in bands of 4 M tiles; MX formats with K a multiple of
+// 256 x 256 with eight waves (fewest operand bytes per FLOP that fit the
+// register file; 64-byte stages in four slots when K is a multiple of 64,
+// else 128-byte stages in two) in bands of 4 M tiles; MX formats with K a multiple of
 // 1024 (LDS-staged scales) -> with at least 384 rows per group on average
 // the eight-wave 256 x 256 tile with 16-byte scale chunks, else the
 // eight-wave 192 x 256 tile in bands of 8 M tiles (at 170-270 rows per group
@@ -769,7 +822,8 @@ hipError_t launch_tile(const GemmProblem& p, hipStream_t stream, int mband) {
 // slots (decode workload 140 -> 136 us against 32 x 128 with three; 32 x 512,
 // three slots, or 32 x 64 / 32 x 128 with two were slower), MX 32 x 128 with
 // three slots.
-using TileLargeFp8 = Tile<256, 256, 2, 4, 2>;
+using TileLargeFp8 = Tile<256, 256, 2, 4, 4, 1, false, 64>;   // whole 64-byte stages
+using TileLargeFp8Tail = Tile<256, 256, 2, 4, 2>;              // K bytes not a multiple of 128
 using TileLargeMx = Tile<128, 256, 2, 2, 3>;
 using TileLargeMxKA = Tile<128, 256, 2, 2, 2>;
 using TileLargeMxKA8 = Tile<256, 256, 2, 4, 2>;
@@ -790,13 +844,14 @@ hipError_t launch_fmt(const GemmProblem& p, hipStream_t stream) {
         const int64_t groups = p.G < p.T ? p.G : p.T;
         const int64_t avg_rows = groups > 0 ? p.T / groups : p.T;
         const int64_t rows = p.max_rows_hint > avg_rows ? (avg_rows + p.max_rows_hint) / 2 : avg_rows;
-        // whole stages; for MX also whole 32-byte scale chunks (LDS-staged scales)
-        const bool ka = FMT == 0 ? p.K % kStageBytes == 0 : p.K % 1024 == 0;
         if (rows >= 128) {
             if constexpr (FMT == 0) {
-                return ka ? launch_tile<TileLargeFp8, FMT, SWIGLU, true>(p, stream, kBandLarge)
-                          : launch_tile<TileLargeFp8, FMT, SWIGLU, false>(p, stream, kBandLarge);
+                // whole 64-byte stages: the four-slot pipeline
+                return p.K % 64 == 0 ? launch_tile<TileLargeFp8, FMT, SWIGLU, true>(p, stream, kBandLarge)
+                                     : launch_tile<TileLargeFp8Tail, FMT, SWIGLU, false>(p, stream, kBandLarge);
             } else {
+                // whole 128-byte stages and whole 32-byte scale chunks (LDS-staged scales)
+                const bool ka = p.K % 1024 == 0;
                 if (ka && avg_rows >= kTallRows)
                     return launch_tile<TileLargeMxKA8, FMT, SWIGLU, true>(p, stream, kBandLarge);
                 return ka ? launch_tile<TileMx192, FMT, SWIGLU, true>(p, stream, kBandMx)

@@ -13,7 +13,7 @@ namespace gemm {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-constexpr int kStageBytes = 128;  // K bytes per row per stage
+constexpr int kStageBytes = 128;  // K bytes per row per stage (block formats; FP8 rowwise may use 64)
 constexpr int kNumXcd = 8;
 
 struct GemmArgs {
@@ -48,19 +48,30 @@ struct Fmt {
     static constexpr bool kMX = FMT != 0;          // block scales (E8M0, or E4M3 for NVFP4)
     static constexpr bool kNV = FMT == 3;          // 16-element blocks, E4M3 scales, f16 matrix cores
     static constexpr bool kFP4 = FMT == 2 || FMT == 3;
-    static constexpr int kSteps = kFP4 ? 4 : 2;    // 64-deep K steps per stage
     static constexpr int kBlockElems = kNV ? 16 : 32;
-    static constexpr int kBlocks = (kFP4 ? 256 : 128) / kBlockElems;  // scale blocks (bytes) per stage
+    static constexpr int kBlocks = (kFP4 ? 256 : 128) / kBlockElems;  // scale blocks (bytes) per 128-byte stage
     static constexpr int kWords = kBlocks / 4;     // scale words per row per stage
     static constexpr int kTypeCode = kFP4 ? 4 : 0;  // cbsz / blgp: 0 = e4m3, 4 = e2m1
 };
 
-// LDS byte offset of 16-byte chunk `chunk` of stage row `row`.  A row is 128
-// bytes (32 of the 64 four-byte banks), so even and odd rows fall in opposite
-// bank halves; XOR-ing the chunk with bits 1..3 of the row gives the 16 rows a
-// 16-lane slice of a fragment read touches 16 distinct 4-bank groups.
-__device__ __forceinline__ int swz_chunk(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
-__device__ __forceinline__ int swz(int row, int chunk) { return row * kStageBytes + (swz_chunk(row, chunk) << 4); }
+// LDS byte offset of 16-byte chunk `chunk` of stage row `row`, for stage rows
+// of SB bytes (K bytes per row per stage: 128 or 64).  A ds_read_b128 serves
+// 16 lanes at a time across the 64 four-byte banks (16 four-bank groups), and
+// a fragment read's 16-lane slice reads one chunk of 16 consecutive rows.
+//  * SB = 128: a row covers 8 groups, so even and odd rows fall in opposite
+//    halves; XOR-ing the chunk with bits 1..3 of the row spreads the 16 rows
+//    over 16 distinct groups.
+//  * SB = 64: a row covers 4 groups, so rows r, r + 4, r + 8, r + 12 start in
+//    the same group; XOR-ing the chunk with bits 2..3 of the row separates them.
+template <int SB>
+__device__ __forceinline__ int swz_chunk(int row, int chunk) {
+    static_assert(SB == 128 || SB == 64, "stage rows of 128 or 64 bytes");
+    return SB == 128 ? chunk ^ ((row >> 1) & 7) : chunk ^ ((row >> 2) & 3);
+}
+template <int SB>
+__device__ __forceinline__ int swz(int row, int chunk) {
+    return row * SB + (swz_chunk<SB>(row, chunk) << 4);
+}
 
 // Bijective remap so that the workgroups the dispatcher sends to one XCD
 // (b, b + 8, b + 16, ...) get consecutive logical indices.

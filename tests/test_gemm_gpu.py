@@ -40,6 +40,11 @@ SMALL = {
     "tiny_fp8": W.WORKLOADS[1],
     "decode_fp8": W.WORKLOADS[2].scaled(tokens=32, N=320, K=1056),
     "prefill_fp8": W.WORKLOADS[3].scaled(tokens=160, E=16, N=384, K=1024),
+    # FP8 rowwise 64-byte stages: an odd stage count, and one to three stages
+    # (the four-slot pipeline's prologue and drain)
+    "prefill_fp8_k960": W.WORKLOADS[3].scaled(tokens=160, E=16, N=384, K=960),
+    "fp8_k64": W.WORKLOADS[3].scaled(tokens=96, E=8, top_k=3, N=256, K=64),
+    "fp8_k192": W.WORKLOADS[3].scaled(tokens=96, E=8, top_k=3, N=256, K=192),
     "mxfp8": W.WORKLOADS[4].scaled(rows=700, E=8, N=288, K=608),
     "mxfp4": W.WORKLOADS[5].scaled(tokens=96, E=16, N=256, K=1344),
     "mxfp4_ktail": W.WORKLOADS[5].scaled(tokens=40, E=6, masked=1, top_k=4, N=192, K=800, swiglu=False),
@@ -56,7 +61,8 @@ SMALL = {
 
 # The row-count hint selects the tile shape: 0 lets small reduced problems use
 # the decode-regime tile, a large hint forces the prefill-regime tile (FP8:
-# 256 x 256 with eight waves; MX: 192 x 256 with eight waves when K is a
+# 256 x 256 with eight waves, 64-byte stages in four slots when K is a
+# multiple of 64, else 128-byte stages in two; MX: 192 x 256 with eight waves when K is a
 # multiple of 1024, else 128 x 256), so both code paths see every case,
 # including partial M / N tiles and K tails.
 HINTS = [0, 1 << 20]
