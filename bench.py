@@ -2,6 +2,7 @@
 """Benchmark of the ragged MoE expert path on one MI355X.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload 3] [--no-cpu-baseline]
+                    [--settle-seconds 0.2]
 
 A step is one pass of the path over the workload's routed batch: the grouped
 dynamic quantize of the bf16 activations, then the grouped GEMM (with its
@@ -15,6 +16,14 @@ on.  `value` is GEMM FLOP per step / step time (TFLOP/s).  The roofline object
 describes the GEMM kernel from HIP events recorded around each launch inside
 the timed region; the CPU baseline times the oracle on a bounded sample.
 Prints ONE JSON line.
+
+Before the warm-up steps the GPU runs the step for a fixed wall time (the
+clock settle, reported as `clock_settle_s`): after idle the MI355X clock
+overshoots and dips for the first ~30 ms of matrix-core load, and a handful
+of warm-up steps would time that transient rather than the kernels.  Working sets that the 256 MB last-level cache could hold
+(the quantize of the smaller workloads) are rotated over several copies.
+The engine clock the timed steps ran at is measured by the library's clock
+probe on a side stream (`gpu_clock`).
 """
 from __future__ import annotations
 
@@ -39,8 +48,82 @@ METRIC = "ragged MoE grouped GEMM TFLOP/s + % FP8/MXFP4 MFMA peak; quantize GB/s
 # Measured on MI355X: after the GPU goes from idle to this load, the clock
 # dips for roughly the first 30-40 ms (prefill GEMM 515 us at step 2, 665 us
 # at step 6, back to ~505 us by step 40; the quantize likewise 131 -> 142 ->
-# 130 us), so the default warm-up runs for longer than that.
+# 130 us), so the default warm-up runs for longer than that, and a fixed
+# clock settle runs before any warm-up.
 WARMUP_SECONDS = 0.1
+SETTLE_SECONDS = 0.2
+# rotate inputs over copies until the rotated working set exceeds this (the
+# MI355X last-level cache holds 256 MB)
+ROTATE_BYTES = 512 << 20
+MAX_COPIES = 32
+
+
+def settle(step, seconds):
+    """Run `step` in batches of 10 for `seconds` of wall time (untimed)."""
+    import torch
+
+    if seconds <= 0:
+        return 0
+    n, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            step()
+        n += 10
+        torch.cuda.synchronize()
+    return n
+
+
+class ClockProbe:
+    """The library's shader-clock probe, run on a stream of its own while the
+    timed steps are repeated (untimed) right after the timed region: one wave
+    counts engine-clock ticks against the GPU's constant 100 MHz counter,
+    which gives the average clock the steps run at.  (Not during the timed
+    steps themselves: the probe's wave takes register space on one compute
+    unit, which then cannot host a workgroup of the persistent GEMM.)"""
+
+    def __init__(self, enabled=True):
+        self.enabled = enabled
+        self.out = None
+        self.window_us = 0
+
+    def start(self, window_us):
+        import torch
+
+        import fp4_grouped_gemm_quantize_amd as mxg
+        if not self.enabled:
+            return
+        self.window_us = int(max(1, min(window_us, 10_000_000)))
+        self.out = torch.zeros(2, dtype=torch.int64, device="cuda")
+        self.stream = torch.cuda.Stream()  # default priority
+        mxg.clock_probe(self.window_us, self.out, stream=self.stream)
+
+    def result(self):
+        if self.out is None:
+            return {"error": "not measured (--no-clock)"}
+        c, r = (int(v) for v in self.out.cpu())
+        if r <= 0:
+            return {"error": "probe did not run"}
+        return {"mhz": round(100.0 * c / r, 1), "window_us": round(r / 100.0, 1),
+                "source": "shader-clock probe (s_memtime vs the 100 MHz counter) on a side stream while the "
+                          "timed steps were repeated untimed"}
+
+
+def cpu_info():
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"cpu_model": model, "nproc": os.cpu_count(), "affinity": len(os.sched_getaffinity(0))}
+
+
+def stats_ms(values):
+    import numpy as np
+    v = np.asarray(values, dtype=np.float64)
+    return {"mean": round(float(v.mean()), 4), "median": round(float(np.median(v)), 4), "min": round(float(v.min()), 4)}
 
 
 def warm_up(step, count):
@@ -72,6 +155,9 @@ def parse():
                         f"{WARMUP_SECONDS:g} s have passed; the JSON line reports the count)")
     p.add_argument("--workload", type=int, default=3, help="1..5 (default: 3, prefill FP8 rowwise)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-clock", action="store_true", help="do not measure the engine clock during the timed steps")
+    p.add_argument("--settle-seconds", type=float, default=SETTLE_SECONDS,
+                   help="untimed clock settle before the warm-up steps (wall seconds of steps; 0 disables)")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU baseline")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="before the workload, run torch.bitwise_not over this many MiB of int32 three times: a "
@@ -205,9 +291,16 @@ def main():
     off = torch.from_numpy(r.row_offsets.view(np.int32)).cuda()
     ids = torch.from_numpy(r.expert_ids).cuda()
     qcols = K // 2 if fmt == mxg.MXFP4 else K
-    a = torch.empty((T, qcols), dtype=torch.uint8, device="cuda")
-    sa = torch.empty((T,), dtype=torch.float32, device="cuda") if fmt == 0 else \
-        torch.empty((T, K // 32), dtype=torch.uint8, device="cuda")
+    # Copies of the activations and of the quantized rows the step cycles
+    # through, so that a working set the last-level cache could hold is not
+    # served from it on the next step (one copy when it is large enough).
+    q_bytes = T * K * 2 + T * qcols + (T * 4 if fmt == 0 else T * (K // 32))
+    copies = int(min(MAX_COPIES, max(1, -(-ROTATE_BYTES // max(q_bytes, 1)))))
+    xs_rot = [x] + [x.clone() for _ in range(copies - 1)]
+    a_rot = [torch.empty((T, qcols), dtype=torch.uint8, device="cuda") for _ in range(copies)]
+    sa_rot = [torch.empty((T,), dtype=torch.float32, device="cuda") if fmt == 0 else
+              torch.empty((T, K // 32), dtype=torch.uint8, device="cuda") for _ in range(copies)]
+    a, sa = a_rot[0], sa_rot[0]
     if w.swiglu:
         yq = torch.empty((T, N // 4), dtype=torch.uint8, device="cuda")
         ys = torch.empty((T, N // 64), dtype=torch.uint8, device="cuda")
@@ -215,20 +308,30 @@ def main():
         c = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
     hint = int(r.counts.max())
 
+    cur = [0]
+
     def quant():
-        mxg.mx_grouped_quantize(fmt, x, a, sa, off, ids)
+        i = cur[0]
+        mxg.mx_grouped_quantize(fmt, xs_rot[i], a_rot[i], sa_rot[i], off, ids)
 
     def gemm():
+        i = cur[0]
         if w.swiglu:
-            mxg.mx_grouped_matmul_swiglu(fmt, a, sa, b, sb, yq, ys, off, ids, hint)
+            mxg.mx_grouped_matmul_swiglu(fmt, a_rot[i], sa_rot[i], b, sb, yq, ys, off, ids, hint)
         else:
-            mxg.mx_grouped_matmul(fmt, a, sa, b, sb, c, off, ids, hint)
+            mxg.mx_grouped_matmul(fmt, a_rot[i], sa_rot[i], b, sb, c, off, ids, hint)
 
     def step():
         quant()
         gemm()
+        cur[0] = (cur[0] + 1) % copies
 
+    settled = settle(step, args.settle_seconds)
+    tw = time.perf_counter()
     warmup = warm_up(step, args.warmup)
+    tw = time.perf_counter() - tw
+    # expected length of the timed region, for the clock probe's window
+    step_s = tw / warmup if warmup else (args.settle_seconds / settled if settled else 1e-3)
 
     stream = torch.cuda.current_stream()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
@@ -240,14 +343,20 @@ def main():
         ev[s][1].record(stream)
         gemm()
         ev[s][2].record(stream)
+        cur[0] = (cur[0] + 1) % copies
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # the engine clock under the same load: the steps again, untimed, beside the probe
+    clock = ClockProbe(enabled=not args.no_clock)
+    clock.start(0.8 * args.steps * step_s * 1e6)
+    for s in range(args.steps):
+        step()
+    torch.cuda.synchronize()
 
     q_ms = [ev[s][0].elapsed_time(ev[s][1]) for s in range(args.steps)]
     g_ms = [ev[s][1].elapsed_time(ev[s][2]) for s in range(args.steps)]
     step_ms = wall * 1e3 / args.steps
     flops = 2.0 * T * N * K
-    q_bytes = T * K * 2 + a.numel() + sa.numel() * sa.element_size()
     g_bytes = algorithmic_gemm_bytes(w, r.counts, K, N, T, fmt)
     g_avg = float(np.mean(g_ms))
     q_avg = float(np.mean(q_ms))
@@ -270,6 +379,8 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": warmup,
+        "clock_settle_s": args.settle_seconds,
+        "clock_settle_steps": settled,
         "ms_per_step": round(step_ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -287,7 +398,10 @@ def main():
             "gemm_frac_mfma_peak": round(g_tflops / peak, 4),
             "gemm_GBps_algorithmic": round(g_bytes / (g_avg * 1e-3) / 1e9, 1),
             "gemm_flop": flops, "gemm_algorithmic_bytes": g_bytes, "quantize_bytes": q_bytes,
+            "quantize_ms_stats": stats_ms(q_ms), "gemm_ms_stats": stats_ms(g_ms),
+            "input_copies": copies,
         },
+        "gpu_clock": clock.result(),
         "roofline": roof,
     }
     if r.token_of_row is not None:
@@ -423,6 +537,7 @@ def main():
         del bn, sbn, an, san, cn, yqn, ysn
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, r, x, args.cpu_seconds)
+        out["cpu_baseline"].update(cpu_info())
     print(json.dumps(out), flush=True)
 
 

@@ -33,7 +33,7 @@ LIB_PATH = os.path.join(_PKG, "libmxg.so")
 EXPORTED = ("mx_grouped_quantize", "mx_grouped_quantize_gather", "mx_grouped_matmul", "mx_grouped_matmul_swiglu",
             "mx_silu_quantize", "mx_moe_combine", "mx_grouped_quantize_nvfp4", "mx_grouped_matmul_nvfp4",
             "mx_grouped_matmul_swiglu_nvfp4", "mx_silu_quantize_nvfp4", "mx_grouped_quantize_padded",
-            "mx_grouped_matmul_padded", "mx_grouped_matmul_swiglu_padded", "mxg_status_string")
+            "mx_grouped_matmul_padded", "mx_grouped_matmul_swiglu_padded", "mxg_clock_probe", "mxg_status_string")
 
 
 class MxgError(RuntimeError):
@@ -80,6 +80,8 @@ def lib() -> ctypes.CDLL:
                      "mx_grouped_matmul_nvfp4", "mx_grouped_matmul_swiglu_nvfp4", "mx_silu_quantize_nvfp4",
                      "mx_grouped_quantize_padded", "mx_grouped_matmul_padded", "mx_grouped_matmul_swiglu_padded"):
             getattr(L, name).restype = ctypes.c_int
+        L.mxg_clock_probe.argtypes = [_P, _I64, _P]
+        L.mxg_clock_probe.restype = ctypes.c_int
         L.mxg_status_string.argtypes = [ctypes.c_int]
         L.mxg_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -502,3 +504,13 @@ def quantize_weights_nvfp4(w, tensor_scales):
     ids = torch.arange(E, dtype=torch.int32, device=w.device)
     q, s = quantize_nvfp4(w.reshape(E * N, K), off, ids, tensor_scales)
     return q.reshape(E, N, K // 2), s.reshape(E, N, K // 16)
+
+
+def clock_probe(window_us: int, out: torch.Tensor, stream=None) -> None:
+    """Enqueue the shader-clock probe (one wave sleeping window_us of the GPU's
+    100 MHz counter) on `stream` (default: the current stream); afterwards
+    out[0] / out[1] * 100 MHz is the average engine clock over the window.
+    out: int64 [2] on the GPU."""
+    _expect(out, "out", (torch.int64,), shape=(2,))
+    s = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream(out)
+    _check(lib().mxg_clock_probe(_ptr(out), int(window_us), s), "mxg_clock_probe")

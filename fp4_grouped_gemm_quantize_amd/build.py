@@ -19,7 +19,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmxg.so")
-SOURCES = ["api.cpp", "quantize.hip", "gemm.hip", "combine.hip"]
+SOURCES = ["api.cpp", "quantize.hip", "gemm.hip", "combine.hip", "clock.hip"]
 ARCH = os.environ.get("MXG_OFFLOAD_ARCH", "gfx950")
 
 COMMON = [

@@ -18,6 +18,12 @@ bool valid_fmt(int fmt) { return fmt == MXG_FP8_E4M3_ROWWISE || fmt == MXG_MXFP8
 
 extern "C" {
 
+mxg_status mxg_clock_probe(unsigned long long* out, int64_t window_us, hipStream_t stream) {
+    if (!out || !aligned(out, 8)) return MXG_ERROR_INVALID_VALUE;
+    if (window_us <= 0 || window_us > MXG_CLOCK_PROBE_MAX_US) return MXG_ERROR_INVALID_VALUE;
+    return from_hip(mxg::launch_clock_probe(out, (unsigned long long)window_us * 100ull, stream));
+}
+
 const char* mxg_status_string(mxg_status status) {
     switch (status) {
         case MXG_SUCCESS:

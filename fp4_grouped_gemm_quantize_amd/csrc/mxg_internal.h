@@ -63,4 +63,7 @@ struct GemmProblem {
 
 hipError_t launch_grouped_gemm(const GemmProblem& p, hipStream_t stream);
 
+// One wave: out[0] = shader-clock ticks, out[1] = 100 MHz ticks (>= ticks) of one sleep window.
+hipError_t launch_clock_probe(unsigned long long* out, unsigned long long ticks, hipStream_t stream);
+
 }  // namespace mxg

@@ -26,6 +26,7 @@
  *                             scales in a padded or expert-slot layout
  *   mx_moe_combine            after the down-projection: each token's row is the
  *                             router-weighted sum of its routed rows
+ *   mxg_clock_probe           measurement aid: the engine clock over a window
  *
  * Conventions shared by every entry point
  *   - Every tensor pointer is a DEVICE pointer owned by the caller; the library
@@ -421,6 +422,20 @@ mxg_status mx_grouped_matmul_swiglu_padded(mxg_format fmt, const void* a_q, cons
 mxg_status mx_moe_combine(const void* y_bf16, int64_t total_rows, int64_t H, const int32_t* row_of_slot,
                           const float* weights, int64_t num_tokens, int32_t top_k, void* out_bf16,
                           hipStream_t stream);
+
+/*
+ * mxg_clock_probe -- a measurement aid, not part of the path: one wave on
+ * `stream` sleeps for window_us microseconds of the GPU's constant 100 MHz
+ * counter and counts the shader clock meanwhile.  On completion
+ *   out[0] = shader-clock ticks, out[1] = 100 MHz ticks of the window,
+ * so the average engine clock is 100 MHz * out[0] / out[1].  Enqueued on a
+ * stream of its own beside other work, it measures the clock that work runs
+ * at (it holds one wave slot of one compute unit).  out: device uint64 [2],
+ * 8-byte aligned.  INVALID_VALUE for a null or misaligned out, or window_us
+ * outside [1, MXG_CLOCK_PROBE_MAX_US].
+ */
+#define MXG_CLOCK_PROBE_MAX_US 10000000
+mxg_status mxg_clock_probe(unsigned long long* out, int64_t window_us, hipStream_t stream);
 
 /* Static, human-readable name of a status code. */
 const char* mxg_status_string(mxg_status status);

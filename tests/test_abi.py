@@ -12,7 +12,12 @@ import fp4_grouped_gemm_quantize_amd as mxg
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "mxg.h")
 
-pytestmark = pytest.mark.skipif(not os.path.exists(mxg.LIB_PATH), reason="libmxg.so not built")
+
+
+def test_library_is_built():
+    """The boundary tests need the built library; a missing one is a failure
+    (build it with `python -m fp4_grouped_gemm_quantize_amd.build`), never a skip."""
+    assert os.path.exists(mxg.LIB_PATH), f"libmxg.so not built at {mxg.LIB_PATH}"
 
 
 def declared_functions():
@@ -234,3 +239,11 @@ def test_padded_argument_errors():
     assert sp(fmt=0) == mxg.ERROR_NOT_SUPPORTED
     assert sp(I=48) == mxg.ERROR_NOT_SUPPORTED
     assert sp(T=0) == mxg.SUCCESS
+
+
+def test_clock_probe_argument_errors():
+    L = mxg.lib()
+    assert L.mxg_clock_probe(None, 100, None) == mxg.ERROR_INVALID_VALUE
+    assert L.mxg_clock_probe(P(0x10004), 100, None) == mxg.ERROR_INVALID_VALUE  # not on 8 bytes
+    assert L.mxg_clock_probe(FAKE, 0, None) == mxg.ERROR_INVALID_VALUE
+    assert L.mxg_clock_probe(FAKE, 10_000_001, None) == mxg.ERROR_INVALID_VALUE

@@ -67,3 +67,32 @@ def test_fused_algorithmic_bytes_skip_empty_experts():
     b = active * 2 * I * (K // 2 + K // 32)
     y = T * (I // 2 + I // 32)
     assert bench.algorithmic_gemm_bytes(w, np.asarray(r.counts), K, w.N, T, w.fmt) == a + b + y
+
+
+def test_clock_settle_runs_whole_batches_for_the_set_time(monkeypatch):
+    import torch
+
+    monkeypatch.setattr(torch.cuda, "synchronize", lambda: None)
+    calls = []
+
+    def step():
+        calls.append(1)
+        time.sleep(0.001)
+
+    t0 = time.perf_counter()
+    n = bench.settle(step, 0.05)
+    assert time.perf_counter() - t0 >= 0.05 and n == len(calls) and n % 10 == 0
+    assert bench.settle(step, 0) == 0
+
+
+def test_clock_probe_disabled_reports_why():
+    c = bench.ClockProbe(enabled=False)
+    c.start(1000)
+    assert "error" in c.result()
+
+
+def test_report_helpers():
+    s = bench.stats_ms([1.0, 2.0, 3.0, 10.0])
+    assert s == {"mean": 4.0, "median": 2.5, "min": 1.0}
+    info = bench.cpu_info()
+    assert info["nproc"] >= 1 and info["affinity"] >= 1 and "cpu_model" in info
