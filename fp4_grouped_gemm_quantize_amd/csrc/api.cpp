@@ -128,6 +128,9 @@ static mxg_status check_gemm_common(mxg_format fmt, const void* a_q, const void*
         return MXG_ERROR_INVALID_VALUE;
     if (fmt == MXG_FP8_E4M3_ROWWISE && (!aligned(a_scales, 4) || !aligned(b_scales, 4)))
         return MXG_ERROR_INVALID_VALUE;
+    // block scales: 16-byte direct-to-LDS chunks when K is a multiple of 1024
+    if (fmt != MXG_FP8_E4M3_ROWWISE && (!aligned(a_scales, 16) || !aligned(b_scales, 16)))
+        return MXG_ERROR_INVALID_VALUE;
     return MXG_SUCCESS;
 }
 

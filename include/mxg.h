@@ -170,8 +170,10 @@ mxg_status mx_grouped_quantize_gather(mxg_format fmt, const void* x_bf16, int64_
  *             max_num_tokens_per_expert).
  *
  * Errors: INVALID_VALUE for null pointers, a bad fmt, K/N/num_experts <= 0,
- * total_rows/num_groups < 0, misalignment; NOT_SUPPORTED for K % 32 != 0 or
- * num_groups > MXG_MAX_GROUPS.
+ * total_rows/num_groups < 0, misalignment (codes and c on 16 bytes; rowwise
+ * fp32 scales on 4; MX scale tensors on 16, since they are streamed in
+ * 16-byte pieces); NOT_SUPPORTED for K % 32 != 0 or num_groups >
+ * MXG_MAX_GROUPS.  The same pointer rules hold for mx_grouped_matmul_swiglu.
  */
 mxg_status mx_grouped_matmul(mxg_format fmt, const void* a_q, const void* a_scales, const void* b_q,
                              const void* b_scales, void* c_bf16, const uint32_t* row_offsets,
@@ -181,9 +183,9 @@ mxg_status mx_grouped_matmul(mxg_format fmt, const void* a_q, const void* a_scal
 
 /*
  * mx_grouped_matmul_nvfp4 -- ragged grouped GEMM of NVFP4 operands.
- * (NvMxf4f8Strategy, grouped_matmul(): block-scaled grouped matmul with
- *  per-expert scales -- expert_scales, the per-expert matmul-epilogue scaling
- *  factors; is_nvfp4.  The arithmetic is not given on the pages; reading:)
+ * (NvMxf4f8Strategy, grouped_matmul(), description and Args expert_scales;
+ *  is_nvfp4.  The pages name one scale per expert, applied after the
+ *  product, and give no arithmetic; reading:)
  *
  *   out[t, n] = bf16( expert_scales[e] * sum_b sa[t, b] * sb[e, n, b] *
  *                     sum_{k in block b} qa[t, k] * qb[e, n, k] )
@@ -215,12 +217,13 @@ mxg_status mx_grouped_matmul_nvfp4(const void* a_q, const void* a_scales, const 
 /*
  * mx_grouped_matmul_swiglu_nvfp4 -- NVFP4 gate/up grouped GEMM + SwiGLU +
  * NVFP4 requant, fused.
- * (NvMxf4f8Strategy, grouped_matmul_swiglu(): expert_scales -- per-expert
- *  epilogue scaling factors; input_scales -- the raw per-expert SiLU-output
- *  scale, which the strategy inverts before the kernel uses it; a_row_scales
- *  -- an optional BF16 scale per hidden row applied with the expert scale
- *  before the SwiGLU, NVFP4 only; prepare_swiglu_operands(): the inversion.
- *  The arithmetic is not given; reading:)
+ * (NvMxf4f8Strategy, grouped_matmul_swiglu(), Args expert_scales,
+ *  input_scales and a_row_scales; prepare_swiglu_operands(), Returns.  In
+ *  short: one epilogue factor per expert; one output-side scale per expert,
+ *  which the caller hands over already inverted; and, for this format, an
+ *  optional BF16 factor per routed row that multiplies in together with the
+ *  expert factor, ahead of the activation.  The arithmetic is not given;
+ *  reading:)
  *
  *   g_j, u_j = bf16( acc * fl32(expert_scales[e] * a_row_scales[t]) ) for
  *              columns 2j, 2j+1 of the NVFP4 GEMM against W[e] (rows

@@ -586,9 +586,10 @@ int mxo_gemm_rows_nvfp4(const uint8_t* a, const uint8_t* a_scale, const uint8_t*
     return MXO_OK;
 }
 
-/* NVFP4 gated activation + requant (NvMxf4f8Strategy fused_silu_quantize()
- * and grouped_matmul_swiglu() with input_scales, the raw per-expert SiLU-output
- * scale that the strategy inverts before use; a_row_scales).  Readings: sf_y
+/* NVFP4 gated activation + requant (NvMxf4f8Strategy, fused_silu_quantize();
+ * grouped_matmul_swiglu(), Args input_scales and a_row_scales: one output-side
+ * scale per expert, inverted by the strategy before the kernel sees it, and
+ * an optional factor per routed row).  Readings: sf_y
  * below is that inverted (encode-side) scale; y_j = bf16(silu(g_j) u_j) as in
  * silu_requant_row, quantized to NVFP4 along j in blocks of 16 exactly as
  * quantize_row_nvfp4 does for a row of bf16 values.                        */
@@ -627,7 +628,8 @@ int mxo_silu_requant_nvfp4(const uint16_t* h, uint8_t* yq, uint8_t* ys, const fl
 
 /* Fused NVFP4 gate/up GEMM + SwiGLU + NVFP4 requant on a list of rows: the
  * NVFP4 GEMM (expert scale included), times the optional bf16 row scale
- * rs[t] (reading: "applied with the expert scale before the SwiGLU"), each
+ * rs[t] (reading: it multiplies in with the expert scale, ahead of the
+ * activation; grouped_matmul_swiglu(), Args a_row_scales), each
  * output rounded to bf16, then silu_requant_row_nvfp4 with sf_y[e].
  * gu_exact / gu_bound include the row scale.                                */
 int mxo_gemm_swiglu_rows_nvfp4(const uint8_t* a, const uint8_t* a_scale, const uint8_t* w, const uint8_t* w_scale,

@@ -137,6 +137,25 @@ def test_swiglu_argument_errors():
     assert sw(T=0) == mxg.SUCCESS
 
 
+FAKE_4 = P(0x10004)  # on 4 bytes, not on 16
+
+
+def test_mx_scale_tensors_must_be_16_byte_aligned():
+    """MX block-scale tensors are streamed in 16-byte pieces: a scale pointer
+    off 16 bytes is refused by every MX GEMM entry point (every call here is
+    refused before a launch)."""
+    for fmt in (1, 2):
+        assert mm(fmt=fmt, sa=FAKE_4) == mxg.ERROR_INVALID_VALUE
+        assert mm(fmt=fmt, sb=FAKE_4) == mxg.ERROR_INVALID_VALUE
+    assert sw(sa=FAKE_4) == mxg.ERROR_INVALID_VALUE
+    assert sw(sw_=FAKE_4) == mxg.ERROR_INVALID_VALUE
+    L = mxg.lib()
+    for sa, sb in ((FAKE_4, FAKE), (FAKE, FAKE_4)):
+        assert L.mx_grouped_matmul_padded(2, FAKE, sa, FAKE, 8, FAKE, sb, FAKE, FAKE, FAKE, 1, 1, 4, 32, 64, 0,
+                                          None) == mxg.ERROR_INVALID_VALUE
+    assert mm(fmt=0, sa=FAKE_ODD) == mxg.ERROR_INVALID_VALUE  # rowwise fp32 scales: 4 bytes
+
+
 def test_silu_quantize_argument_errors():
     f = mxg.lib().mx_silu_quantize
     assert f(None, FAKE, FAKE, FAKE, 1, 4, 64, None) == mxg.ERROR_INVALID_VALUE
