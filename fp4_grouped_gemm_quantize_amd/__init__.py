@@ -33,7 +33,8 @@ LIB_PATH = os.path.join(_PKG, "libmxg.so")
 EXPORTED = ("mx_grouped_quantize", "mx_grouped_quantize_gather", "mx_grouped_matmul", "mx_grouped_matmul_swiglu",
             "mx_silu_quantize", "mx_moe_combine", "mx_grouped_quantize_nvfp4", "mx_grouped_matmul_nvfp4",
             "mx_grouped_matmul_swiglu_nvfp4", "mx_silu_quantize_nvfp4", "mx_grouped_quantize_padded",
-            "mx_grouped_matmul_padded", "mx_grouped_matmul_swiglu_padded", "mxg_clock_probe", "mxg_status_string")
+            "mx_grouped_matmul_padded", "mx_grouped_matmul_swiglu_padded", "mxg_clock_probe",
+            "mxg_validation_message", "mxg_routing_violation", "mxg_status_string")
 
 
 class MxgError(RuntimeError):
@@ -80,6 +81,10 @@ def lib() -> ctypes.CDLL:
                      "mx_grouped_matmul_nvfp4", "mx_grouped_matmul_swiglu_nvfp4", "mx_silu_quantize_nvfp4",
                      "mx_grouped_quantize_padded", "mx_grouped_matmul_padded", "mx_grouped_matmul_swiglu_padded"):
             getattr(L, name).restype = ctypes.c_int
+        L.mxg_validation_message.argtypes = []
+        L.mxg_validation_message.restype = ctypes.c_char_p
+        L.mxg_routing_violation.argtypes = [_P, _P, _I32, _I32, _I64, ctypes.c_char_p, _I64]
+        L.mxg_routing_violation.restype = ctypes.c_int
         L.mxg_clock_probe.argtypes = [_P, _I64, _P]
         L.mxg_clock_probe.restype = ctypes.c_int
         L.mxg_status_string.argtypes = [ctypes.c_int]
@@ -514,3 +519,22 @@ def clock_probe(window_us: int, out: torch.Tensor, stream=None) -> None:
     _expect(out, "out", (torch.int64,), shape=(2,))
     s = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream(out)
     _check(lib().mxg_clock_probe(_ptr(out), int(window_us), s), "mxg_clock_probe")
+
+
+def validation_message() -> str:
+    """Under MXG_VALIDATE: the first routing violation of this thread's last refused call."""
+    return lib().mxg_validation_message().decode()
+
+
+def routing_violation(row_offsets, expert_ids=None, num_experts: int = 0, total_rows: int = 0):
+    """The MXG_VALIDATE check on host (numpy) arrays: None if the routing is
+    well formed, else a description of the first violation."""
+    import numpy as np
+    off = np.ascontiguousarray(row_offsets, dtype=np.uint32)
+    ids = None if expert_ids is None else np.ascontiguousarray(expert_ids, dtype=np.int32)
+    msg = ctypes.create_string_buffer(192)
+    rc = lib().mxg_routing_violation(off.ctypes.data, None if ids is None else ids.ctypes.data, off.size - 1,
+                                     num_experts, total_rows, msg, len(msg))
+    if rc < 0:
+        raise ValueError("mxg_routing_violation: invalid arguments")
+    return msg.value.decode() if rc else None

@@ -5,6 +5,11 @@
 #include "mxg_internal.h"
 
 #include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <vector>
 
 namespace {
 
@@ -14,6 +19,68 @@ mxg_status from_hip(hipError_t e) { return e == hipSuccess ? MXG_SUCCESS : MXG_E
 
 bool valid_fmt(int fmt) { return fmt == MXG_FP8_E4M3_ROWWISE || fmt == MXG_MXFP8_E4M3 || fmt == MXG_MXFP4_E2M1; }
 
+// ---- MXG_VALIDATE: the optional check of the routing metadata (a debug mode).
+thread_local char t_validation_msg[192] = "";
+
+bool validation_on() {
+    const char* v = getenv("MXG_VALIDATE");
+    return v != nullptr && v[0] != '\0' && strcmp(v, "0") != 0;
+}
+
+// First violation in host copies of row_offsets [G + 1] and (if E > 0)
+// expert_ids [G], written to `msg`; false if the routing is well formed.
+bool find_violation(const uint32_t* off, const int32_t* ids, int64_t G, int64_t E, int64_t T, char* msg,
+                    size_t len) {
+    for (int64_t g = 0; g <= G; ++g) {
+        if ((int64_t)off[g] > T) {
+            snprintf(msg, len, "row_offsets[%lld] = %u exceeds total_rows = %lld", (long long)g, off[g],
+                     (long long)T);
+            return true;
+        }
+        if (g > 0 && off[g] < off[g - 1]) {
+            snprintf(msg, len, "row_offsets[%lld] = %u is below row_offsets[%lld] = %u", (long long)g, off[g],
+                     (long long)(g - 1), off[g - 1]);
+            return true;
+        }
+    }
+    if (ids != nullptr && E > 0)
+        for (int64_t g = 0; g < G; ++g)
+            if (ids[g] < 0 || ids[g] >= E) {
+                snprintf(msg, len, "expert_ids[%lld] = %d lies outside [0, %lld)", (long long)g, ids[g],
+                         (long long)E);
+                return true;
+            }
+    return false;
+}
+
+// With MXG_VALIDATE set: copy the routing metadata to the host (synchronising
+// `stream`) and refuse malformed routing before anything is launched.
+// ids / E: the expert ids are checked when the entry point takes num_experts.
+mxg_status check_routing(const uint32_t* off, const int32_t* ids, int64_t G, int64_t E, int64_t T,
+                         hipStream_t stream) {
+    if (!validation_on()) return MXG_SUCCESS;
+    t_validation_msg[0] = '\0';
+    std::vector<uint32_t> h_off((size_t)G + 1);
+    std::vector<int32_t> h_ids(ids != nullptr && E > 0 ? (size_t)G : 0);
+    if (hipMemcpyAsync(h_off.data(), off, sizeof(uint32_t) * h_off.size(), hipMemcpyDeviceToHost, stream) !=
+        hipSuccess)
+        return MXG_ERROR_LAUNCH;
+    if (!h_ids.empty() && hipMemcpyAsync(h_ids.data(), ids, sizeof(int32_t) * h_ids.size(), hipMemcpyDeviceToHost,
+                                         stream) != hipSuccess)
+        return MXG_ERROR_LAUNCH;
+    if (hipStreamSynchronize(stream) != hipSuccess) return MXG_ERROR_LAUNCH;
+    if (find_violation(h_off.data(), h_ids.empty() ? nullptr : h_ids.data(), G, E, T, t_validation_msg,
+                       sizeof t_validation_msg))
+        return MXG_ERROR_INVALID_VALUE;
+    return MXG_SUCCESS;
+}
+
+mxg_status launch_gemm_checked(const mxg::GemmProblem& p, hipStream_t stream) {
+    const mxg_status st = check_routing(p.off, p.ids, p.G, p.E, p.T, stream);
+    if (st != MXG_SUCCESS) return st;
+    return from_hip(mxg::launch_grouped_gemm(p, stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -22,6 +89,18 @@ mxg_status mxg_clock_probe(unsigned long long* out, int64_t window_us, hipStream
     if (!out || !aligned(out, 8)) return MXG_ERROR_INVALID_VALUE;
     if (window_us <= 0 || window_us > MXG_CLOCK_PROBE_MAX_US) return MXG_ERROR_INVALID_VALUE;
     return from_hip(mxg::launch_clock_probe(out, (unsigned long long)window_us * 100ull, stream));
+}
+
+const char* mxg_validation_message(void) { return t_validation_msg; }
+
+int mxg_routing_violation(const uint32_t* row_offsets_host, const int32_t* expert_ids_host, int32_t num_groups,
+                          int32_t num_experts, int64_t total_rows, char* msg, int64_t msg_len) {
+    if (!row_offsets_host || num_groups < 0 || total_rows < 0) return -1;
+    char local[192];
+    const bool bad = find_violation(row_offsets_host, expert_ids_host, num_groups, num_experts, total_rows, local,
+                                    sizeof local);
+    if (msg != nullptr && msg_len > 0) snprintf(msg, (size_t)msg_len, "%s", bad ? local : "");
+    return bad ? 1 : 0;
 }
 
 const char* mxg_status_string(mxg_status status) {
@@ -50,6 +129,7 @@ mxg_status mx_grouped_quantize(mxg_format fmt, const void* x_bf16, void* q, void
     if (!aligned(x_bf16, 16) || !aligned(q, 16) || (fmt == MXG_FP8_E4M3_ROWWISE && !aligned(scales, 4)) ||
         !aligned(row_offsets, 4))
         return MXG_ERROR_INVALID_VALUE;
+    if (mxg_status st = check_routing(row_offsets, nullptr, num_groups, 0, total_rows, stream)) return st;
     return from_hip(mxg::launch_quantize((int)fmt, x_bf16, q, scales, row_offsets, num_groups, total_rows, K,
                                          stream));
 }
@@ -68,6 +148,7 @@ mxg_status mx_grouped_quantize_gather(mxg_format fmt, const void* x_bf16, int64_
     if (!aligned(x_bf16, 16) || !aligned(q, 16) || (fmt == MXG_FP8_E4M3_ROWWISE && !aligned(scales, 4)) ||
         !aligned(row_offsets, 4) || !aligned(indices, 4))
         return MXG_ERROR_INVALID_VALUE;
+    if (mxg_status st = check_routing(row_offsets, nullptr, num_groups, 0, total_rows, stream)) return st;
     return from_hip(mxg::launch_quantize_gather((int)fmt, x_bf16, num_src_rows, indices, indices_divisor, q, scales,
                                                 row_offsets, num_groups, total_rows, K, stream));
 }
@@ -82,6 +163,7 @@ mxg_status mx_grouped_quantize_nvfp4(const void* x_bf16, void* q, void* scales, 
     if (!aligned(x_bf16, 16) || !aligned(q, 16) || !aligned(tensor_scales, 4) || !aligned(row_offsets, 4) ||
         !aligned(expert_ids, 4))
         return MXG_ERROR_INVALID_VALUE;
+    if (mxg_status st = check_routing(row_offsets, expert_ids, num_groups, num_experts, total_rows, stream)) return st;
     return from_hip(mxg::launch_quantize_nvfp4(x_bf16, q, scales, tensor_scales, row_offsets, expert_ids, num_groups,
                                                num_experts, total_rows, K, stream));
 }
@@ -97,6 +179,7 @@ mxg_status mx_grouped_quantize_padded(mxg_format fmt, const void* x_bf16, void* 
     if (!x_bf16 || !q || !scales || !scales_offsets || !row_offsets) return MXG_ERROR_INVALID_VALUE;
     if (!aligned(x_bf16, 16) || !aligned(q, 16) || !aligned(scales_offsets, 4) || !aligned(row_offsets, 4))
         return MXG_ERROR_INVALID_VALUE;
+    if (mxg_status st = check_routing(row_offsets, nullptr, num_groups, 0, total_rows, stream)) return st;
     return from_hip(mxg::launch_quantize_padded((int)fmt, x_bf16, q, scales, scales_offsets, scale_rows, row_offsets,
                                                 num_groups, total_rows, K, stream));
 }
@@ -146,7 +229,7 @@ mxg_status mx_grouped_matmul(mxg_format fmt, const void* a_q, const void* a_scal
     if (!c_bf16 || !aligned(c_bf16, 16)) return MXG_ERROR_INVALID_VALUE;
     mxg::GemmProblem p{(int)fmt, a_q, a_scales, b_q, b_scales, c_bf16, nullptr, nullptr, row_offsets, expert_ids,
                        num_groups, num_experts, total_rows, N, K, max_rows_per_group_hint};
-    return from_hip(mxg::launch_grouped_gemm(p, stream));
+    return launch_gemm_checked(p, stream);
 }
 
 mxg_status mx_grouped_matmul_nvfp4(const void* a_q, const void* a_scales, const void* b_q, const void* b_scales,
@@ -165,7 +248,7 @@ mxg_status mx_grouped_matmul_nvfp4(const void* a_q, const void* a_scales, const 
         return MXG_ERROR_INVALID_VALUE;
     mxg::GemmProblem p{3, a_q, a_scales, b_q, b_scales, c_bf16, nullptr, nullptr, row_offsets, expert_ids,
                        num_groups, num_experts, total_rows, N, K, max_rows_per_group_hint, expert_scales};
-    return from_hip(mxg::launch_grouped_gemm(p, stream));
+    return launch_gemm_checked(p, stream);
 }
 
 // Padded A scales: the MX GEMM / fused GEMM with a_scales in the layout of
@@ -195,7 +278,7 @@ mxg_status mx_grouped_matmul_padded(mxg_format fmt, const void* a_q, const void*
     mxg::GemmProblem p{(int)fmt, a_q, a_scales, b_q, b_scales, c_bf16, nullptr, nullptr, row_offsets, expert_ids,
                        num_groups, num_experts, total_rows, N, K, max_rows_per_group_hint, nullptr, nullptr, nullptr,
                        a_scales_offsets, a_scale_rows};
-    return from_hip(mxg::launch_grouped_gemm(p, stream));
+    return launch_gemm_checked(p, stream);
 }
 
 mxg_status mx_grouped_matmul_swiglu_padded(mxg_format fmt, const void* a_q, const void* a_scales,
@@ -216,7 +299,7 @@ mxg_status mx_grouped_matmul_swiglu_padded(mxg_format fmt, const void* a_q, cons
     mxg::GemmProblem p{(int)fmt, a_q, a_scales, w_q, w_scales, nullptr, y_q, y_scales, row_offsets, expert_ids,
                        num_groups, num_experts, total_rows, 2 * I, K, max_rows_per_group_hint, nullptr, nullptr,
                        nullptr, a_scales_offsets, a_scale_rows};
-    return from_hip(mxg::launch_grouped_gemm(p, stream));
+    return launch_gemm_checked(p, stream);
 }
 
 mxg_status mx_grouped_matmul_swiglu_nvfp4(const void* a_q, const void* a_scales, const void* w_q,
@@ -239,7 +322,7 @@ mxg_status mx_grouped_matmul_swiglu_nvfp4(const void* a_q, const void* a_scales,
     mxg::GemmProblem p{3, a_q, a_scales, w_q, w_scales, nullptr, y_q, y_scales, row_offsets, expert_ids,
                        num_groups, num_experts, total_rows, 2 * I, K, max_rows_per_group_hint, expert_scales,
                        a_row_scales_bf16, y_tensor_scales};
-    return from_hip(mxg::launch_grouped_gemm(p, stream));
+    return launch_gemm_checked(p, stream);
 }
 
 mxg_status mx_silu_quantize_nvfp4(const void* h_bf16, void* y_q, void* y_scales, const float* y_tensor_scales,
@@ -253,6 +336,7 @@ mxg_status mx_silu_quantize_nvfp4(const void* h_bf16, void* y_q, void* y_scales,
     if (!aligned(h_bf16, 16) || !aligned(y_q, 16) || !aligned(y_tensor_scales, 4) || !aligned(row_offsets, 4) ||
         !aligned(expert_ids, 4))
         return MXG_ERROR_INVALID_VALUE;
+    if (mxg_status st = check_routing(row_offsets, expert_ids, num_groups, num_experts, total_rows, stream)) return st;
     return from_hip(mxg::launch_silu_quantize_nvfp4(h_bf16, y_q, y_scales, y_tensor_scales, row_offsets, expert_ids,
                                                     num_groups, num_experts, total_rows, I, stream));
 }
@@ -271,7 +355,7 @@ mxg_status mx_grouped_matmul_swiglu(mxg_format fmt, const void* a_q, const void*
     if (!y_q || !y_scales || !aligned(y_q, 16)) return MXG_ERROR_INVALID_VALUE;
     mxg::GemmProblem p{(int)fmt, a_q, a_scales, w_q, w_scales, nullptr, y_q, y_scales, row_offsets, expert_ids,
                        num_groups, num_experts, total_rows, 2 * I, K, max_rows_per_group_hint};
-    return from_hip(mxg::launch_grouped_gemm(p, stream));
+    return launch_gemm_checked(p, stream);
 }
 
 mxg_status mx_silu_quantize(const void* h_bf16, void* y_q, void* y_scales, const uint32_t* row_offsets,
@@ -281,6 +365,7 @@ mxg_status mx_silu_quantize(const void* h_bf16, void* y_q, void* y_scales, const
     if (total_rows == 0 || num_groups == 0) return MXG_SUCCESS;
     if (!h_bf16 || !y_q || !y_scales || !row_offsets) return MXG_ERROR_INVALID_VALUE;
     if (!aligned(h_bf16, 16) || !aligned(y_q, 16) || !aligned(row_offsets, 4)) return MXG_ERROR_INVALID_VALUE;
+    if (mxg_status st = check_routing(row_offsets, nullptr, num_groups, 0, total_rows, stream)) return st;
     return from_hip(mxg::launch_silu_quantize(h_bf16, y_q, y_scales, row_offsets, num_groups, total_rows, I, stream));
 }
 

@@ -27,6 +27,8 @@
  *   mx_moe_combine            after the down-projection: each token's row is the
  *                             router-weighted sum of its routed rows
  *   mxg_clock_probe           measurement aid: the engine clock over a window
+ *   mxg_validation_message, mxg_routing_violation
+ *                             the MXG_VALIDATE debug check of routing metadata
  *
  * Conventions shared by every entry point
  *   - Every tensor pointer is a DEVICE pointer owned by the caller; the library
@@ -55,6 +57,16 @@
  *     an error).  MXG_ERROR_LAUNCH reports a failed kernel launch.  With
  *     total_rows == 0 or num_groups == 0 a call (after its enum and size
  *     checks) is a no-op that examines no pointer.
+ *   - Debug mode: with the environment variable MXG_VALIDATE set (to anything
+ *     but "" or "0"), every entry point that takes row_offsets first copies
+ *     row_offsets (and, where it takes num_experts, expert_ids) to the host,
+ *     synchronising `stream`, and returns MXG_ERROR_INVALID_VALUE without
+ *     launching anything if an offset exceeds total_rows, an offset is below
+ *     the one before it, or an expert id lies outside [0, num_experts);
+ *     mxg_validation_message() then names the first violation.  (The
+ *     malformed-routing convention of NvMxf4f8Strategy,
+ *     prepare_swiglu_operands(), Raises: refuse instead of proceeding.)
+ *     Without it, malformed routing is handled as described above.
  */
 #ifndef MXG_H
 #define MXG_H
@@ -439,6 +451,22 @@ mxg_status mx_moe_combine(const void* y_bf16, int64_t total_rows, int64_t H, con
  */
 #define MXG_CLOCK_PROBE_MAX_US 10000000
 mxg_status mxg_clock_probe(unsigned long long* out, int64_t window_us, hipStream_t stream);
+
+/*
+ * mxg_validation_message -- under MXG_VALIDATE, the first violation found by
+ * the calling thread's last refused call ("" if its last validated call
+ * passed).  Valid until that thread's next validated call.
+ *
+ * mxg_routing_violation -- the same check on host arrays: row_offsets_host
+ * [num_groups + 1]; expert_ids_host [num_groups] or NULL (ids not checked,
+ * nor when num_experts <= 0).  Returns 1 and writes a description into msg
+ * (msg_len bytes, NUL-terminated; msg may be NULL) for malformed routing, 0
+ * for well-formed routing (msg gets ""), -1 for a NULL row_offsets_host or a
+ * negative num_groups / total_rows.  Host memory only; no GPU is touched.
+ */
+const char* mxg_validation_message(void);
+int mxg_routing_violation(const uint32_t* row_offsets_host, const int32_t* expert_ids_host, int32_t num_groups,
+                          int32_t num_experts, int64_t total_rows, char* msg, int64_t msg_len);
 
 /* Static, human-readable name of a status code. */
 const char* mxg_status_string(mxg_status status);

@@ -266,3 +266,20 @@ def test_clock_probe_argument_errors():
     assert L.mxg_clock_probe(P(0x10004), 100, None) == mxg.ERROR_INVALID_VALUE  # not on 8 bytes
     assert L.mxg_clock_probe(FAKE, 0, None) == mxg.ERROR_INVALID_VALUE
     assert L.mxg_clock_probe(FAKE, 10_000_001, None) == mxg.ERROR_INVALID_VALUE
+
+
+def test_routing_check_on_host_arrays():
+    """The MXG_VALIDATE rule, on host arrays (no GPU): offsets non-decreasing
+    and within total_rows, expert ids inside [0, num_experts) when checked."""
+    v = mxg.routing_violation
+    assert v([0, 3, 5, 9], [0, 1, 2], 3, 9) is None
+    assert v([0, 0, 0, 0], [2, 2, 2], 3, 9) is None            # empty groups, repeated experts
+    assert v([0], None, 0, 0) is None                          # no groups
+    assert "below" in v([0, 3, 2, 9], [0, 1, 2], 3, 9)
+    assert "exceeds total_rows" in v([0, 3, 5, 10], [0, 1, 2], 3, 9)
+    assert "exceeds total_rows" in v([11, 11, 11, 11], None, 0, 9)
+    assert "expert_ids[1] = 3" in v([0, 3, 5, 9], [0, 3, 2], 3, 9)
+    assert "expert_ids[0] = -1" in v([0, 3, 5, 9], [-1, 0, 0], 3, 9)
+    assert v([0, 3, 5, 9], [0, 3, 2], 0, 9) is None            # ids not checked without num_experts
+    assert mxg.lib().mxg_routing_violation(None, None, 1, 1, 4, None, 0) == -1
+    assert mxg.lib().mxg_routing_violation(FAKE, None, -1, 1, 4, None, 0) == -1
