@@ -198,3 +198,40 @@ class GemmCase:
     def oracle_rows(self, rows, N=None):
         N = N if N is not None else self.w.N
         return oracle.gemm_rows(self.fmt, self.a, self.sa, self.b, self.sb, self.off, self.ids, N, self.w.K, rows)
+
+
+# ---------------------------------------------------------------- guard bytes
+GUARD_BYTES = 256
+GUARD_PATTERN = 0x5C
+
+
+class Guarded:
+    """A GPU output tensor placed inside a larger allocation with
+    GUARD_BYTES of a known pattern before and after it, so a write past
+    either end of the tensor is caught (`check()`).  The tensor itself starts
+    on a 256-byte boundary, like a fresh allocation, and is contiguous."""
+
+    def __init__(self, init: np.ndarray):
+        init = np.ascontiguousarray(init)
+        self.nbytes = init.nbytes
+        self.buf = torch.full((self.nbytes + 2 * GUARD_BYTES,), GUARD_PATTERN, dtype=torch.uint8, device="cuda")
+        inner = self.buf[GUARD_BYTES:GUARD_BYTES + self.nbytes]
+        inner.copy_(torch.from_numpy(init.view(np.uint8).reshape(-1)).cuda())
+        self.dtype = init.dtype
+        self.shape = init.shape
+
+    def view(self, torch_dtype=None) -> torch.Tensor:
+        inner = self.buf[GUARD_BYTES:GUARD_BYTES + self.nbytes]
+        tdt = {np.dtype(np.uint8): torch.uint8, np.dtype(np.int16): torch.int16, np.dtype(np.uint16): torch.int16,
+               np.dtype(np.float32): torch.float32, np.dtype(np.int32): torch.int32}[self.dtype]
+        t = inner.view(tdt).view(self.shape)
+        return t.view(torch_dtype) if torch_dtype is not None else t
+
+    def check(self, label: str = "") -> None:
+        head = self.buf[:GUARD_BYTES].cpu().numpy()
+        tail = self.buf[GUARD_BYTES + self.nbytes:].cpu().numpy()
+        assert np.all(head == GUARD_PATTERN), f"{label}: bytes before the output were written"
+        assert np.all(tail == GUARD_PATTERN), f"{label}: bytes after the output were written"
+
+    def numpy(self) -> np.ndarray:
+        return self.buf[GUARD_BYTES:GUARD_BYTES + self.nbytes].cpu().numpy().view(self.dtype).reshape(self.shape)

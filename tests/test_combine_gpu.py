@@ -9,7 +9,7 @@ import torch
 import fp4_grouped_gemm_quantize_amd as mxg
 import oracle
 import workloads as W
-from common import to_gpu
+from common import Guarded, to_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -33,8 +33,11 @@ def check_combine(out_bits: np.ndarray, ref: dict, top_k: int):
 
 def run(y_bits, ros, w, ntok):
     y = to_gpu(y_bits.view(np.int16)).view(torch.bfloat16)
-    out = torch.full((ntok, y_bits.shape[1]), 0x7FA5, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    g = Guarded(np.full((ntok, y_bits.shape[1]), 0x7FA5, np.uint16))
+    out = g.view(torch.bfloat16)
     mxg.mx_moe_combine(y, to_gpu(ros.astype(np.int32)), to_gpu(w.astype(np.float32)), out)
+    torch.cuda.synchronize()
+    g.check("combine out")
     torch.cuda.synchronize()
     return out.view(torch.int16).cpu().numpy().view(np.uint16)
 

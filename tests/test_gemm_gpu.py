@@ -8,7 +8,7 @@ import torch
 import fp4_grouped_gemm_quantize_amd as mxg
 import oracle
 import workloads as W
-from common import GemmCase, check_gemm_rows, sample_rows
+from common import Guarded, GemmCase, check_gemm_rows, sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -18,10 +18,11 @@ SENT_BF16 = 0x7FA5  # a NaN pattern no result can produce
 def run_gemm(case: GemmCase, N=None, hint=0):
     inp = case.gpu_inputs()
     N = N if N is not None else case.w.N
-    c = torch.full((case.T, N), SENT_BF16, dtype=torch.int16, device="cuda").view(torch.bfloat16)
-    mxg.mx_grouped_matmul(case.fmt, c=c, max_rows_per_group_hint=hint, **inp)
+    g = Guarded(np.full((case.T, N), SENT_BF16, np.uint16))
+    mxg.mx_grouped_matmul(case.fmt, c=g.view(torch.bfloat16), max_rows_per_group_hint=hint, **inp)
     torch.cuda.synchronize()
-    return c.view(torch.int16).cpu().numpy().view(np.uint16)
+    g.check(f"c, hint {hint}")
+    return g.numpy()
 
 
 def check_all_rows(case: GemmCase, c: np.ndarray, label: str):

@@ -8,7 +8,7 @@ import torch
 import fp4_grouped_gemm_quantize_amd as mxg
 import oracle
 import workloads as W
-from common import bits, offsets_gpu, sentinel_like, to_gpu
+from common import Guarded, bits, offsets_gpu, sentinel_like, to_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -148,11 +148,12 @@ def nv_gemm_inputs(w, seed, quantized=True):
 
 def run_nv_gemm(r, a, sa, b, sb, es, hint=0):
     T, N = a.shape[0], b.shape[1]
-    c = torch.full((T, N), SENT_BF16, dtype=torch.int16, device="cuda").view(torch.bfloat16)
-    mxg.mx_grouped_matmul_nvfp4(to_gpu(a), to_gpu(sa), to_gpu(b), to_gpu(sb), to_gpu(es), c,
+    g = Guarded(np.full((T, N), SENT_BF16, np.uint16))
+    mxg.mx_grouped_matmul_nvfp4(to_gpu(a), to_gpu(sa), to_gpu(b), to_gpu(sb), to_gpu(es), g.view(torch.bfloat16),
                                 offsets_gpu(r.row_offsets), to_gpu(r.expert_ids.astype(np.int32)), hint)
     torch.cuda.synchronize()
-    return c.view(torch.int16).cpu().numpy().view(np.uint16)
+    g.check("NVFP4 c")
+    return g.numpy()
 
 
 NV_SMALL = {
@@ -315,13 +316,16 @@ def nv_swiglu_inputs(w, seed, quantized=True):
 
 def run_nv_fused(r, a, sa, b, sb, es, sfy, rs=None, hint=0):
     T, I = a.shape[0], b.shape[1] // 2
-    yq = torch.full((T, I // 2), 0xA5, dtype=torch.uint8, device="cuda")
-    ys = torch.full((T, I // 16), 0x5A, dtype=torch.uint8, device="cuda")
+    gq = Guarded(np.full((T, I // 2), 0xA5, np.uint8))
+    gs = Guarded(np.full((T, I // 16), 0x5A, np.uint8))
     rs_g = None if rs is None else to_gpu(rs.view(np.int16)).view(torch.bfloat16)
-    mxg.mx_grouped_matmul_swiglu_nvfp4(to_gpu(a), to_gpu(sa), to_gpu(b), to_gpu(sb), to_gpu(es), to_gpu(sfy), yq, ys,
-                                       offsets_gpu(r.row_offsets), to_gpu(r.expert_ids.astype(np.int32)), rs_g, hint)
+    mxg.mx_grouped_matmul_swiglu_nvfp4(to_gpu(a), to_gpu(sa), to_gpu(b), to_gpu(sb), to_gpu(es), to_gpu(sfy),
+                                       gq.view(), gs.view(), offsets_gpu(r.row_offsets),
+                                       to_gpu(r.expert_ids.astype(np.int32)), rs_g, hint)
     torch.cuda.synchronize()
-    return yq.cpu().numpy(), ys.cpu().numpy()
+    gq.check("NVFP4 fused codes")
+    gs.check("NVFP4 fused scales")
+    return gq.numpy(), gs.numpy()
 
 
 def run_nv_chained(r, a, sa, b, sb, es, sfy):

@@ -7,7 +7,7 @@ import torch
 import fp4_grouped_gemm_quantize_amd as mxg
 import oracle
 import workloads as W
-from common import SENTINEL, bits, offsets_gpu, oracle_quantize_weights, sentinel_like, to_gpu
+from common import Guarded, SENTINEL, bits, offsets_gpu, oracle_quantize_weights, sentinel_like, to_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -24,11 +24,13 @@ def run_both(fmt, x_bits: np.ndarray, off: np.ndarray):
         s0 = sentinel_like((T, K // 32), value=0x5A)
     q_ref, s_ref = oracle.quantize(fmt, x_bits, off, sentinel_like((T, qcols)), s0.copy())
     x = to_gpu(x_bits.view(np.int16)).view(torch.bfloat16)
-    q = to_gpu(sentinel_like((T, qcols)))
-    s = to_gpu(s0.copy())
-    mxg.mx_grouped_quantize(fmt, x, q, s, offsets_gpu(off))
+    q = Guarded(sentinel_like((T, qcols)))
+    s = Guarded(s0.copy())
+    mxg.mx_grouped_quantize(fmt, x, q.view(), s.view(), offsets_gpu(off))
     torch.cuda.synchronize()
-    return (q.cpu().numpy(), s.cpu().numpy()), (q_ref, s_ref)
+    q.check("codes")
+    s.check("scales")
+    return (q.numpy(), s.numpy()), (q_ref, s_ref)
 
 
 def assert_same(gpu, ref, label):

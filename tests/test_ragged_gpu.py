@@ -8,7 +8,7 @@ import torch
 
 import fp4_grouped_gemm_quantize_amd as mxg
 import oracle
-from common import check_gemm_rows, ids_gpu, offsets_gpu, to_gpu
+from common import Guarded, check_gemm_rows, ids_gpu, offsets_gpu, to_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -31,11 +31,12 @@ def run_case(fmt, a, sa, b, sb, off, ids, N, K):
     T = a.shape[0]
     outs = []
     for hint in (0, 1 << 20):
-        c = torch.full((T, N), SENT, dtype=torch.int16, device="cuda").view(torch.bfloat16)
-        mxg.mx_grouped_matmul(fmt, to_gpu(a), to_gpu(sa), to_gpu(b), to_gpu(sb), c, offsets_gpu(off), ids_gpu(ids),
-                              hint)
+        g = Guarded(np.full((T, N), SENT, np.uint16))
+        mxg.mx_grouped_matmul(fmt, to_gpu(a), to_gpu(sa), to_gpu(b), to_gpu(sb), g.view(torch.bfloat16),
+                              offsets_gpu(off), ids_gpu(ids), hint)
         torch.cuda.synchronize()
-        outs.append(c.view(torch.int16).cpu().numpy().view(np.uint16))
+        g.check(f"fmt {fmt} hint {hint}")
+        outs.append(g.numpy())
     assert np.array_equal(outs[0], outs[1]), "tile regimes disagree"
     c = outs[0]
     ref = oracle.gemm_rows(fmt, a, sa, b, sb, off, ids, N, K, np.arange(T))

@@ -16,7 +16,7 @@ import torch
 import fp4_grouped_gemm_quantize_amd as mxg
 import oracle
 import workloads as W
-from common import GemmCase, check_swiglu_interval, offsets_gpu, sample_rows, to_gpu
+from common import Guarded, GemmCase, check_swiglu_interval, offsets_gpu, sample_rows, to_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -76,8 +76,9 @@ FUSED = {
 def run_fused_and_chained(case: GemmCase, hint: int = 0):
     inp = case.gpu_inputs()
     T, I = case.T, case.w.N // 2
-    yq = torch.full((T, I // 2), 0xA5, dtype=torch.uint8, device="cuda")
-    ys = torch.full((T, I // 32), 0x5A, dtype=torch.uint8, device="cuda")
+    gq = Guarded(np.full((T, I // 2), 0xA5, np.uint8))
+    gs = Guarded(np.full((T, I // 32), 0x5A, np.uint8))
+    yq, ys = gq.view(), gs.view()
     mxg.mx_grouped_matmul_swiglu(case.fmt, inp["a_q"], inp["a_scales"], inp["b_q"], inp["b_scales"], yq, ys,
                                  inp["row_offsets"], inp["expert_ids"], hint)
     c = torch.zeros((T, 2 * I), dtype=torch.bfloat16, device="cuda")
@@ -86,6 +87,8 @@ def run_fused_and_chained(case: GemmCase, hint: int = 0):
     ys2 = torch.full((T, I // 32), 0x5A, dtype=torch.uint8, device="cuda")
     mxg.mx_silu_quantize(c, yq2, ys2, inp["row_offsets"])
     torch.cuda.synchronize()
+    gq.check("fused codes")
+    gs.check("fused scales")
     return (yq.cpu().numpy(), ys.cpu().numpy()), (yq2.cpu().numpy(), ys2.cpu().numpy())
 
 
