@@ -89,6 +89,8 @@ def lib() -> ctypes.CDLL:
         L.mxo_quantize.restype = ctypes.c_int
         L.mxo_quantize_gather.argtypes = [ctypes.c_int, _P, _I64, _P, _I32, _P, _P, _P, _I32, _I64, _I64]
         L.mxo_quantize_gather.restype = ctypes.c_int
+        L.mxo_quantize_scatter.argtypes = [ctypes.c_int, _P, _I64, _P, _I32, _P, _P, _P, _I32, _I64, _I64]
+        L.mxo_quantize_scatter.restype = ctypes.c_int
         L.mxo_combine.argtypes = [_P, _I64, _I64, _P, _P, _I64, _I32, _P, _P, _P]
         L.mxo_combine.restype = ctypes.c_int
         L.mxo_gemm_rows.argtypes = [ctypes.c_int, _P, _P, _P, _P, _P, _P, _I32, _I32, _I64, _I64, _I64,
@@ -243,6 +245,31 @@ def quantize_gather(fmt: int, x_src, indices, divisor: int, offsets, q=None, sca
                                    off.size - 1, T, K)
     if rc != 0:
         raise ValueError("oracle quantize_gather: invalid arguments")
+    return q, scales
+
+
+def quantize_scatter(fmt: int, x_tokens, row_of_slot, total_rows: int, offsets, q=None, scales=None):
+    """Token-major grouped quantize: token row s (x_tokens bf16 bits [S, K]) is
+    quantized once and its result goes to every routed row row_of_slot[s*top_k + k]
+    (int32 [S * top_k]) that lies in [0, total_rows) and is covered by a group.
+    Returns (q, scales) [total_rows, ...]; every other row keeps its contents."""
+    x = _c(x_tokens, np.uint16)
+    S, K = x.shape
+    ros = _c(row_of_slot, np.int32)
+    assert S > 0 and ros.size % S == 0
+    top_k = ros.size // S
+    T = int(total_rows)
+    off = _c(offsets, np.uint32)
+    qcols = K // 2 if fmt == MXFP4 else K
+    if q is None:
+        q = np.zeros((T, qcols), np.uint8)
+    if scales is None:
+        scales = np.zeros((T,), np.float32) if fmt == FP8_ROWWISE else np.zeros((T, K // 32), np.uint8)
+    assert q.shape == (T, qcols) and q.dtype == np.uint8
+    rc = lib().mxo_quantize_scatter(fmt, _ptr(x), S, _ptr(ros), top_k, _ptr(q), _ptr(scales), _ptr(off),
+                                    off.size - 1, T, K)
+    if rc != 0:
+        raise ValueError("oracle quantize_scatter: invalid arguments")
     return q, scales
 
 

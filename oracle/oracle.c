@@ -340,6 +340,50 @@ int mxo_quantize_gather(int fmt, const uint16_t* x, int64_t nsrc, const int32_t*
     return MXO_OK;
 }
 
+/* Token-major form of the gathered quantize (NvMxf4f8Strategy,
+ * grouped_quantize(), Args indices and indices_divisor, read through the
+ * inverse slot map the combine uses).  For token s < ntok and slot k < top_k,
+ * routed row r = ros[s * top_k + k] receives the quantization of token row s
+ * when r lies in [0, T) and a group covers it; every other row of q and
+ * scales is left as it was.  A routed row is a copy of its token's row, so
+ * each token row is quantized once here and its result copied to the rows.  */
+int mxo_quantize_scatter(int fmt, const uint16_t* x, int64_t ntok, const int32_t* ros, int32_t top_k, uint8_t* q,
+                         void* scales, const uint32_t* off, int32_t G, int64_t T, int64_t K) {
+    if (!q || !scales || !off || !ros || G < 0 || T < 0 || ntok < 0 || top_k < 1 || K <= 0 || (K % 32) != 0)
+        return MXO_EINVAL;
+    if (ntok > 0 && !x) return MXO_EINVAL;
+    if (fmt < 0 || fmt > 2) return MXO_EINVAL;
+    const int64_t qcols = fmt == 2 ? K / 2 : K;
+    int failed = 0;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t s = 0; s < ntok; ++s) {
+        uint8_t* qt = (uint8_t*)malloc((size_t)qcols);
+        const uint16_t* xr = x + s * K;
+        uint8_t* sblk = (uint8_t*)malloc((size_t)(K / 32 > 4 ? K / 32 : 4));
+        if (!qt || !sblk) {
+            free(qt);
+            free(sblk);
+#pragma omp atomic write
+            failed = 1;
+            continue;
+        }
+        float sf = 0.0f;
+        if (fmt == 0) quantize_row_fp8(xr, K, qt, &sf);
+        else quantize_row_mx(fmt == 1 ? MXO_E4M3 : MXO_E2M1, xr, K, qt, sblk);
+        for (int32_t k = 0; k < top_k; ++k) {
+            const int32_t r = ros[s * top_k + k];
+            if (r < 0 || (int64_t)r >= T) continue;
+            if (group_of_row(off, NULL, G, 0, T, r) == -1) continue;  /* not covered */
+            memcpy(q + (int64_t)r * qcols, qt, (size_t)qcols);
+            if (fmt == 0) ((float*)scales)[r] = sf;
+            else memcpy((uint8_t*)scales + (int64_t)r * (K / 32), sblk, (size_t)(K / 32));
+        }
+        free(sblk);
+        free(qt);
+    }
+    return failed ? MXO_EINVAL : MXO_OK;
+}
+
 /* ------------------------------------------------------------------------- */
 /* Grouped GEMM on a list of rows (grouped_matmul_rowwise_dynamic_scaled_fp8,
  * description; NvMxf4f8Strategy grouped_matmul()).  For each listed row t the

@@ -252,3 +252,49 @@ def test_quantize_gather_skips_rows_without_a_source(fmt):
             qr, sr = oracle.quantize(fmt, x[src:src + 1], np.array([0, 1], np.uint32))
             assert np.array_equal(q[t], qr[0]) and np.array_equal(np.atleast_1d(s[t]).view(np.uint8),
                                                                   np.atleast_1d(sr[0]).view(np.uint8))
+
+
+@pytest.mark.parametrize("fmt", [0, 1, 2])
+def test_quantize_scatter_equals_quantize_of_the_routed_rows(fmt):
+    """Token-major form: routed rows named through the inverse slot map get
+    exactly the quantization of their token row, as if the routed rows had
+    been materialised and quantized (every slot of every token routed once)."""
+    rng = np.random.default_rng(70 + fmt)
+    S, top_k, K = 19, 4, 96
+    x = oracle.bf16_round_array(rng.standard_normal((S, K)) * np.exp(rng.uniform(-6, 6, (S, 1))))
+    slots = rng.permutation(S * top_k).astype(np.int32)   # routed row t serves slot slots[t]
+    T = slots.size
+    ros = np.empty(T, np.int32)
+    ros[slots] = np.arange(T, dtype=np.int32)              # the inverse map
+    off = np.array([0, 20, 20, 51, T], np.uint32)
+    q, s = oracle.quantize_scatter(fmt, x, ros, T, off)
+    qr, sr = oracle.quantize(fmt, x[slots // top_k], off)
+    assert np.array_equal(q, qr) and np.array_equal(s.view(np.uint8), sr.view(np.uint8))
+    qg, sg = oracle.quantize_gather(fmt, x, slots, top_k, off)
+    assert np.array_equal(q, qg) and np.array_equal(s.view(np.uint8), sg.view(np.uint8))
+
+
+@pytest.mark.parametrize("fmt", [0, 1, 2])
+def test_quantize_scatter_leaves_dropped_and_uncovered_rows(fmt):
+    rng = np.random.default_rng(80 + fmt)
+    S, top_k, K, T = 6, 2, 64, 14
+    x = oracle.bf16_round_array(rng.standard_normal((S, K)))
+    ros = np.array([0, 13, -1, 5, 20, 7, 3, 2**31 - 1, 9, 11, 12, -5], np.int32)
+    off = np.array([2, 5, 3, 7, 12], np.uint32)         # rows 2..11 covered (g1 inverted, g2 overlaps g0)
+    qcols = K // 2 if fmt == 2 else K
+    q0 = np.full((T, qcols), 0xA5, np.uint8)
+    s0 = np.full((T,), -3.0, np.float32) if fmt == 0 else np.full((T, K // 32), 0x5A, np.uint8)
+    q, s = oracle.quantize_scatter(fmt, x, ros, T, off, q0.copy(), s0.copy())
+    written = {}
+    for i, r in enumerate(ros):
+        if 2 <= r < 12:
+            written[int(r)] = i // top_k
+    for r in range(T):
+        if r in written:
+            qr, sr = oracle.quantize(fmt, x[written[r]:written[r] + 1], np.array([0, 1], np.uint32))
+            assert np.array_equal(q[r], qr[0]) and np.array_equal(np.atleast_1d(s[r]).view(np.uint8),
+                                                                  np.atleast_1d(sr[0]).view(np.uint8)), r
+        else:
+            assert np.all(q[r] == 0xA5) and np.array_equal(np.atleast_1d(s[r]).view(np.uint8),
+                                                           np.atleast_1d(s0[r]).view(np.uint8)), r
+    assert set(written) == {3, 5, 7, 9, 11}
