@@ -426,7 +426,27 @@ def main():
         out["kernels"].update({"quantize_gather_ms": round(qg_avg, 4),
                                "quantize_gather_GBps": round(qg_bytes / (qg_avg * 1e-3) / 1e9, 1),
                                "quantize_gather_bytes": qg_bytes})
-        del xs, idx
+        # the token-major form: each token row read once, stored to its routed rows
+        # through the inverse slot map; algorithmic bytes: token rows once,
+        # codes, scales and the slot map
+        ros = torch.from_numpy(W.rows_of_slots(r, w.top_k, xs.shape[0])).cuda()
+
+        def quant_scatter():
+            mxg.mx_grouped_quantize_scatter(fmt, xs, ros, a, sa, off, ids)
+
+        warm_up(quant_scatter, args.warmup)
+        e0.record(stream)
+        for _ in range(args.steps):
+            quant_scatter()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        qs_avg = e0.elapsed_time(e1) / args.steps
+        qs_bytes = xs.numel() * 2 + a.numel() + sa.numel() * sa.element_size() + ros.numel() * 4
+        out["kernels"].update({"quantize_scatter_ms": round(qs_avg, 4),
+                               "quantize_scatter_GBps": round(qs_bytes / (qs_avg * 1e-3) / 1e9, 1),
+                               "quantize_scatter_frac_hbm": round(qs_bytes / (qs_avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                               "quantize_scatter_bytes": qs_bytes})
+        del xs, idx, ros
     if w.swiglu and r.token_of_row is not None:
         # the rest of the expert FFN, timed on its own: the down-projection
         # (MX grouped GEMM with K = I on the fused output, weights [E, H, I])

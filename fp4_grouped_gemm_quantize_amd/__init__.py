@@ -30,7 +30,7 @@ MAX_GROUPS = 1024
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmxg.so")
 
-EXPORTED = ("mx_grouped_quantize", "mx_grouped_quantize_gather", "mx_grouped_matmul", "mx_grouped_matmul_swiglu",
+EXPORTED = ("mx_grouped_quantize", "mx_grouped_quantize_gather", "mx_grouped_quantize_scatter", "mx_grouped_matmul", "mx_grouped_matmul_swiglu",
             "mx_silu_quantize", "mx_moe_combine", "mx_grouped_quantize_nvfp4", "mx_grouped_matmul_nvfp4",
             "mx_grouped_matmul_swiglu_nvfp4", "mx_silu_quantize_nvfp4", "mx_grouped_quantize_padded",
             "mx_grouped_matmul_padded", "mx_grouped_matmul_swiglu_padded", "mxg_clock_probe",
@@ -60,6 +60,8 @@ def lib() -> ctypes.CDLL:
         L.mx_grouped_quantize.argtypes = [ctypes.c_int, _P, _P, _P, _P, _P, _I32, _I64, _I64, _P]
         L.mx_grouped_quantize_gather.argtypes = [ctypes.c_int, _P, _I64, _P, _I32, _P, _P, _P, _P, _I32, _I64, _I64,
                                                  _P]
+        L.mx_grouped_quantize_scatter.argtypes = [ctypes.c_int, _P, _I64, _P, _I32, _P, _P, _P, _P, _I32, _I64,
+                                                  _I64, _P]
         L.mx_grouped_matmul.argtypes = [ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I64, _I64, _I64,
                                         _I64, _P]
         L.mx_grouped_matmul_swiglu.argtypes = [ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I64,
@@ -76,7 +78,7 @@ def lib() -> ctypes.CDLL:
                                                _I64, _I64, _I64, _I64, _P]
         L.mx_grouped_matmul_swiglu_padded.argtypes = [ctypes.c_int, _P, _P, _P, _I64, _P, _P, _P, _P, _P, _P, _I32,
                                                       _I32, _I64, _I64, _I64, _I64, _P]
-        for name in ("mx_grouped_quantize", "mx_grouped_quantize_gather", "mx_grouped_matmul",
+        for name in ("mx_grouped_quantize", "mx_grouped_quantize_gather", "mx_grouped_quantize_scatter", "mx_grouped_matmul",
                      "mx_grouped_matmul_swiglu", "mx_silu_quantize", "mx_moe_combine", "mx_grouped_quantize_nvfp4",
                      "mx_grouped_matmul_nvfp4", "mx_grouped_matmul_swiglu_nvfp4", "mx_silu_quantize_nvfp4",
                      "mx_grouped_quantize_padded", "mx_grouped_matmul_padded", "mx_grouped_matmul_swiglu_padded"):
@@ -181,6 +183,38 @@ def mx_grouped_quantize_gather(fmt: int, x_src, indices, indices_divisor: int, q
     _check(lib().mx_grouped_quantize_gather(fmt, _ptr(x_src), S, _ptr(indices), int(indices_divisor), _ptr(q),
                                             _ptr(scales), _ptr(row_offsets), _ptr(expert_ids), G, T, K,
                                             _stream(x_src)), "mx_grouped_quantize_gather")
+
+
+def mx_grouped_quantize_scatter(fmt: int, x_tokens, row_of_slot, q, scales, row_offsets, expert_ids=None) -> None:
+    """Token-major grouped quantize: each token row of x_tokens [S, K] bf16 is quantized
+    once into every routed row row_of_slot[s*top_k + k] (int32 [S * top_k]) of
+    q / scales [T, ...] that lies in [0, T) and is covered by a group."""
+    _expect(x_tokens, "x_tokens", _BF16)
+    if x_tokens.dim() != 2:
+        raise ValueError("x_tokens must be [num_tokens, K]")
+    S, K = x_tokens.shape
+    dev = x_tokens.device
+    _expect(row_of_slot, "row_of_slot", _I32T, None, dev)
+    if S == 0 or row_of_slot.dim() != 1 or row_of_slot.numel() % S != 0:
+        if S != 0:
+            raise ValueError("row_of_slot must hold num_tokens * top_k entries")
+    top_k = row_of_slot.numel() // S if S else 1
+    if q.dim() != 2:
+        raise ValueError("q must be [total_rows, K or K/2]")
+    T = q.shape[0]
+    qcols = K // 2 if fmt == MXFP4 else K
+    _expect(q, "q", _U8, (T, qcols), dev)
+    if fmt == FP8_ROWWISE:
+        _expect(scales, "scales", _F32, (T,), dev)
+    else:
+        _expect(scales, "scales", _U8, (T, K // 32), dev)
+    _expect(row_offsets, "row_offsets", _U32, None, dev)
+    G = row_offsets.numel() - 1
+    if expert_ids is not None:
+        _expect(expert_ids, "expert_ids", _I32T, (G,), dev)
+    _check(lib().mx_grouped_quantize_scatter(fmt, _ptr(x_tokens), S, _ptr(row_of_slot), top_k, _ptr(q),
+                                             _ptr(scales), _ptr(row_offsets), _ptr(expert_ids), G, T, K,
+                                             _stream(x_tokens)), "mx_grouped_quantize_scatter")
 
 
 def mx_grouped_quantize_nvfp4(x, q, scales, tensor_scales, row_offsets, expert_ids) -> None:

@@ -153,6 +153,26 @@ mxg_status mx_grouped_quantize_gather(mxg_format fmt, const void* x_bf16, int64_
                                                 row_offsets, num_groups, total_rows, K, stream));
 }
 
+mxg_status mx_grouped_quantize_scatter(mxg_format fmt, const void* x_tokens, int64_t num_tokens,
+                                       const int32_t* row_of_slot, int32_t top_k, void* q, void* scales,
+                                       const uint32_t* row_offsets, const int32_t* expert_ids, int32_t num_groups,
+                                       int64_t total_rows, int64_t K, hipStream_t stream) {
+    (void)expert_ids;  // not read, as in mx_grouped_quantize
+    if (!valid_fmt(fmt)) return MXG_ERROR_INVALID_VALUE;
+    if (K <= 0 || total_rows < 0 || num_groups < 0 || num_tokens < 0 || top_k < 1) return MXG_ERROR_INVALID_VALUE;
+    if (K % 32 != 0 || num_groups > MXG_MAX_GROUPS || top_k > 64) return MXG_ERROR_NOT_SUPPORTED;
+    if (fmt == MXG_FP8_E4M3_ROWWISE && K > 8192) return MXG_ERROR_NOT_SUPPORTED;
+    if (num_tokens > INT32_MAX / top_k) return MXG_ERROR_NOT_SUPPORTED;
+    if (total_rows == 0 || num_groups == 0 || num_tokens == 0) return MXG_SUCCESS;  // nothing is read or written
+    if (!x_tokens || !row_of_slot || !q || !scales || !row_offsets) return MXG_ERROR_INVALID_VALUE;
+    if (!aligned(x_tokens, 16) || !aligned(q, 16) || (fmt == MXG_FP8_E4M3_ROWWISE && !aligned(scales, 4)) ||
+        !aligned(row_offsets, 4) || !aligned(row_of_slot, 4))
+        return MXG_ERROR_INVALID_VALUE;
+    if (mxg_status st = check_routing(row_offsets, nullptr, num_groups, 0, total_rows, stream)) return st;
+    return from_hip(mxg::launch_quantize_scatter((int)fmt, x_tokens, num_tokens, row_of_slot, top_k, q, scales,
+                                                 row_offsets, num_groups, total_rows, K, stream));
+}
+
 mxg_status mx_grouped_quantize_nvfp4(const void* x_bf16, void* q, void* scales, const float* tensor_scales,
                                      const uint32_t* row_offsets, const int32_t* expert_ids, int32_t num_groups,
                                      int32_t num_experts, int64_t total_rows, int64_t K, hipStream_t stream) {

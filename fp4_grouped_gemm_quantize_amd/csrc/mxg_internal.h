@@ -14,6 +14,12 @@ hipError_t launch_quantize_gather(int fmt, const void* x, int64_t nsrc, const in
                                   void* q, void* scales, const uint32_t* off, int G, int64_t T, int64_t K,
                                   hipStream_t stream);
 
+// Token-major form: token row s (of ntok) is quantized once into every routed row
+// row_of_slot[s * top_k + k] in [0, T) that a group covers (top_k <= 64; FP8 rowwise K <= 8192).
+hipError_t launch_quantize_scatter(int fmt, const void* x, int64_t ntok, const int32_t* row_of_slot, int top_k,
+                                   void* q, void* scales, const uint32_t* off, int G, int64_t T, int64_t K,
+                                   hipStream_t stream);
+
 // MX (fmt 1, 2) with group g's scales from row scales_offsets[g] of a [scale_rows, K/32] tensor.
 hipError_t launch_quantize_padded(int fmt, const void* x, void* q, void* scales, const uint32_t* scales_offsets,
                                   int64_t scale_rows, const uint32_t* off, int G, int64_t T, int64_t K,

@@ -63,6 +63,17 @@ struct Pad {
     int64_t S;
 };
 
+// Token-major input (the gathered quantize read through the inverse slot map
+// that the combine takes): unit rows are the ntok token rows of x; token s is
+// encoded once and its codes and scales go to every routed row
+// ros[s * top_k + k] that lies in [0, T) and is covered by a group (a routed
+// row is a copy of its token's row).  top_k <= 64: lane k holds slot k.
+struct Scatter {
+    const int32_t* ros;
+    int top_k;
+    int64_t ntok;
+};
+
 // Scale row of row t under the layout, or -1 when the row is not written.
 __device__ __forceinline__ int64_t scale_row(const Pad& pd, const uint32_t* s_off, int G, int64_t T, int64_t t) {
     if (!pd.soff) return wave_row_covered(s_off, G, T, t) ? t : -1;
@@ -96,18 +107,19 @@ __device__ __forceinline__ int64_t source_row(const Gather& g, int64_t t) {
 // SIMD).
 // FMT: 0 = FP8 rowwise (scale = amax / 448, code = e4m3(x / scale)),
 //      1 = MXFP8, 2 = MXFP4, 3 = NVFP4.
-template <int FMT, int NC, bool GATHER>
+template <int FMT, int NC, bool GATHER, bool SCATTER>
 __global__ __launch_bounds__(kThreads) void quantize_rows_kernel(const uint16_t* __restrict__ x,
                                                                  uint8_t* __restrict__ q, void* __restrict__ scales,
                                                                  const uint32_t* __restrict__ off, int G,
                                                                  int64_t T, int64_t K, int nseg, Gather ga,
-                                                                 NvScales nv, Pad pd) {
+                                                                 NvScales nv, Pad pd, Scatter sc) {
+    static_assert(!(GATHER && SCATTER) && (!SCATTER || FMT <= 2), "scatter: FP8 rowwise / MX, no gather");
     __shared__ uint32_t s_off[kMaxGroups + 1];
     load_offsets(s_off, off, G);
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t nw = (int64_t)gridDim.x * kWavesPerBlock;
     constexpr int64_t kSegElems = (int64_t)NC * kChunk;
-    const int64_t units = T * nseg;
+    const int64_t units = (SCATTER ? sc.ntok : T) * nseg;  // unit rows: tokens when scattering
 
     // Unit u: row t = u / nseg, elements [e0, e0 + 8 * nvec).
     struct Unit {
@@ -121,7 +133,7 @@ __global__ __launch_bounds__(kThreads) void quantize_rows_kernel(const uint16_t*
         w.e0 = (u - w.t * nseg) * kSegElems;
         const int64_t left = K - w.e0;
         w.nvec = (int)((left < kSegElems ? left : kSegElems) / kVecElems);
-        w.sr = source_row<GATHER>(ga, w.t);
+        w.sr = SCATTER ? w.t : source_row<GATHER>(ga, w.t);
         return w;
     };
     // the unit's elements into v (sr < 0: the registers are left as they
@@ -149,7 +161,72 @@ __global__ __launch_bounds__(kThreads) void quantize_rows_kernel(const uint16_t*
         load_unit(nu, vn);
         const int64_t t = cu.t;
         const int nvec = cu.nvec;
-        if constexpr (FMT == 3) {
+        if constexpr (SCATTER) {
+            // lane k < top_k holds the routed row of the token's slot k
+            const int32_t my_row = lane < sc.top_k ? sc.ros[t * sc.top_k + lane] : -1;
+            auto dest = [&](int k) {  // wave-uniform: the routed row of slot k, or -1
+                const int32_t r = __builtin_amdgcn_readlane(my_row, k);
+                return (r >= 0 && (int64_t)r < T && wave_row_covered(s_off, G, T, r)) ? (int64_t)r : (int64_t)-1;
+            };
+            if constexpr (FMT == 0) {
+                uint32_t amax_bits = 0;
+#pragma unroll
+                for (int c = 0; c < NC; ++c) {
+                    const uint32_t w[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        amax_bits = max(amax_bits, w[i] & 0x7fffu);
+                        amax_bits = max(amax_bits, (w[i] >> 16) & 0x7fffu);
+                    }
+                }
+                const float amax = wave_max(bf16_to_f32(amax_bits));
+                const float scale = amax / 448.0f;  // IEEE binary32 division
+                const double inv = amax == 0.0f ? 0.0 : 1.0 / (double)scale;
+                uint2 pk[NC];
+#pragma unroll
+                for (int c = 0; c < NC; ++c) {
+                    float f[8];
+                    unpack8(v[c], f);
+                    if (amax != 0.0f) {
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) f[i] = div_by_scale(f[i], inv);
+                    }
+                    pk[c] = pack8_e4m3(f);
+                }
+                for (int k = 0; k < sc.top_k; ++k) {
+                    const int64_t r = dest(k);
+                    if (r < 0) continue;
+                    uint8_t* qr = q + r * K;
+#pragma unroll
+                    for (int c = 0; c < NC; ++c) {
+                        const int idx = c * kWave + lane;
+                        if (idx < nvec) *reinterpret_cast<uint2*>(qr + (int64_t)idx * 8) = pk[c];
+                    }
+                    if (lane == 0) static_cast<float*>(scales)[r] = amax == 0.0f ? 0.0f : scale;
+                }
+            } else {
+                constexpr bool FP4 = FMT == 2;
+                uint2 pk[NC];
+                int xs[NC];
+#pragma unroll
+                for (int c = 0; c < NC; ++c) {
+                    float f[8];
+                    unpack8(v[c], f);
+                    xs[c] = mx_encode8<FP4>(f, pk[c]);
+                }
+                for (int k = 0; k < sc.top_k; ++k) {
+                    const int64_t r = dest(k);
+                    if (r < 0) continue;
+                    uint8_t* qrow = q + r * (FP4 ? K / 2 : K) + (FP4 ? cu.e0 / 2 : cu.e0);
+                    uint8_t* srow = static_cast<uint8_t*>(scales) + r * (K / 32) + cu.e0 / 32;
+#pragma unroll
+                    for (int c = 0; c < NC; ++c) {
+                        const int idx = c * kWave + lane;
+                        if (idx < nvec) mx_store8<FP4>(pk[c], xs[c], qrow, srow, idx, lane);
+                    }
+                }
+            }
+        } else if constexpr (FMT == 3) {
             const int g = cu.sr >= 0 ? wave_row_group(s_off, nv.ids, G, nv.E, T, t) : -1;
             if (g >= 0) {
                 const float sf = nv.sf[nv.ids[g]];
@@ -364,42 +441,47 @@ int64_t persistent_grid(Kern kernel, int64_t units) {
 
 // The register-resident kernel with NC chunks per unit: whole rows for FP8
 // rowwise (K <= NC * 512), segments of NC * 512 elements for the block formats.
-template <int FMT, int NC, bool GATHER>
+template <int FMT, int NC, bool GATHER, bool SCATTER>
 hipError_t launch_rows(const uint16_t* x, uint8_t* q, void* s, const uint32_t* off, int G, int64_t T, int64_t K,
-                       const Gather& ga, const NvScales& nv, const Pad& pd, hipStream_t stream) {
+                       const Gather& ga, const NvScales& nv, const Pad& pd, const Scatter& sc, hipStream_t stream) {
     constexpr int64_t kSeg = (int64_t)NC * kChunk;
     const int64_t nseg = FMT == 0 ? 1 : (K + kSeg - 1) / kSeg;
-    auto kernel = quantize_rows_kernel<FMT, NC, GATHER>;
-    hipLaunchKernelGGL(kernel, dim3((unsigned)persistent_grid(kernel, T * nseg)), dim3(kThreads), 0, stream, x, q, s,
-                       off, G, T, K, (int)nseg, ga, nv, pd);
+    auto kernel = quantize_rows_kernel<FMT, NC, GATHER, SCATTER>;
+    const int64_t rows = SCATTER ? sc.ntok : T;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)persistent_grid(kernel, rows * nseg)), dim3(kThreads), 0, stream, x, q,
+                       s, off, G, T, K, (int)nseg, ga, nv, pd, sc);
     return hipGetLastError();
 }
 
-template <int FMT, bool GATHER>
+template <int FMT, bool GATHER, bool SCATTER = false>
 hipError_t launch_fmt(const uint16_t* x, uint8_t* q, void* s, const uint32_t* off, int G, int64_t T, int64_t K,
                       const Gather& ga, hipStream_t stream, const NvScales& nv = NvScales{nullptr, nullptr, 0},
-                      const Pad& pd = Pad{nullptr, 0}) {
+                      const Pad& pd = Pad{nullptr, 0}, const Scatter& sc = Scatter{nullptr, 0, 0}) {
     const int64_t nc = (K + kChunk - 1) / kChunk;  // 512-element chunks per row
     if constexpr (FMT != 0) {
         // block formats: the fewest segments of at most 8 chunks, evened out
         const int64_t nseg = (nc + 7) / 8;
         const int64_t per = (nc + nseg - 1) / nseg;
-        if (per <= 1) return launch_rows<FMT, 1, GATHER>(x, q, s, off, G, T, K, ga, nv, pd, stream);
-        if (per <= 2) return launch_rows<FMT, 2, GATHER>(x, q, s, off, G, T, K, ga, nv, pd, stream);
-        if (per <= 4) return launch_rows<FMT, 4, GATHER>(x, q, s, off, G, T, K, ga, nv, pd, stream);
-        if (per <= 7) return launch_rows<FMT, 7, GATHER>(x, q, s, off, G, T, K, ga, nv, pd, stream);
-        return launch_rows<FMT, 8, GATHER>(x, q, s, off, G, T, K, ga, nv, pd, stream);
+        if (per <= 1) return launch_rows<FMT, 1, GATHER, SCATTER>(x, q, s, off, G, T, K, ga, nv, pd, sc, stream);
+        if (per <= 2) return launch_rows<FMT, 2, GATHER, SCATTER>(x, q, s, off, G, T, K, ga, nv, pd, sc, stream);
+        if (per <= 4) return launch_rows<FMT, 4, GATHER, SCATTER>(x, q, s, off, G, T, K, ga, nv, pd, sc, stream);
+        if (per <= 7) return launch_rows<FMT, 7, GATHER, SCATTER>(x, q, s, off, G, T, K, ga, nv, pd, sc, stream);
+        return launch_rows<FMT, 8, GATHER, SCATTER>(x, q, s, off, G, T, K, ga, nv, pd, sc, stream);
     } else {
-        if (nc <= 1) return launch_rows<FMT, 1, GATHER>(x, q, s, off, G, T, K, ga, nv, pd, stream);
-        if (nc <= 2) return launch_rows<FMT, 2, GATHER>(x, q, s, off, G, T, K, ga, nv, pd, stream);
-        if (nc <= 4) return launch_rows<FMT, 4, GATHER>(x, q, s, off, G, T, K, ga, nv, pd, stream);
-        if (nc <= 8) return launch_rows<FMT, 8, GATHER>(x, q, s, off, G, T, K, ga, nv, pd, stream);
-        if (nc <= 14) return launch_rows<FMT, 14, GATHER>(x, q, s, off, G, T, K, ga, nv, pd, stream);
-        if (nc <= 16) return launch_rows<FMT, 16, GATHER>(x, q, s, off, G, T, K, ga, nv, pd, stream);
-        auto kernel = quantize_long_kernel<GATHER>;
-        hipLaunchKernelGGL(kernel, dim3((unsigned)persistent_grid(kernel, T)), dim3(kThreads), 0, stream, x, q, s, off,
-                           G, T, K, ga, pd);
-        return hipGetLastError();
+        if (nc <= 1) return launch_rows<FMT, 1, GATHER, SCATTER>(x, q, s, off, G, T, K, ga, nv, pd, sc, stream);
+        if (nc <= 2) return launch_rows<FMT, 2, GATHER, SCATTER>(x, q, s, off, G, T, K, ga, nv, pd, sc, stream);
+        if (nc <= 4) return launch_rows<FMT, 4, GATHER, SCATTER>(x, q, s, off, G, T, K, ga, nv, pd, sc, stream);
+        if (nc <= 8) return launch_rows<FMT, 8, GATHER, SCATTER>(x, q, s, off, G, T, K, ga, nv, pd, sc, stream);
+        if (nc <= 14) return launch_rows<FMT, 14, GATHER, SCATTER>(x, q, s, off, G, T, K, ga, nv, pd, sc, stream);
+        if (nc <= 16) return launch_rows<FMT, 16, GATHER, SCATTER>(x, q, s, off, G, T, K, ga, nv, pd, sc, stream);
+        if constexpr (SCATTER) {
+            return hipErrorInvalidValue;  // token rows past 8192 elements (refused by the C ABI before this)
+        } else {
+            auto kernel = quantize_long_kernel<GATHER>;
+            hipLaunchKernelGGL(kernel, dim3((unsigned)persistent_grid(kernel, T)), dim3(kThreads), 0, stream, x, q, s,
+                               off, G, T, K, ga, pd);
+            return hipGetLastError();
+        }
     }
 }
 
@@ -425,6 +507,20 @@ hipError_t launch_quantize_gather(int fmt, const void* x, int64_t nsrc, const in
                                   void* q, void* scales, const uint32_t* off, int G, int64_t T, int64_t K,
                                   hipStream_t stream) {
     return launch_any<true>(fmt, x, q, scales, off, G, T, K, Gather{indices, divisor, nsrc}, stream);
+}
+
+hipError_t launch_quantize_scatter(int fmt, const void* x, int64_t ntok, const int32_t* row_of_slot, int top_k,
+                                   void* q, void* scales, const uint32_t* off, int G, int64_t T, int64_t K,
+                                   hipStream_t stream) {
+    const uint16_t* xb = static_cast<const uint16_t*>(x);
+    uint8_t* qb = static_cast<uint8_t*>(q);
+    const Gather ga{nullptr, 1, ntok};
+    const NvScales nv{nullptr, nullptr, 0};
+    const Pad pd{nullptr, 0};
+    const Scatter sc{row_of_slot, top_k, ntok};
+    if (fmt == 0) return launch_fmt<0, false, true>(xb, qb, scales, off, G, T, K, ga, stream, nv, pd, sc);
+    if (fmt == 1) return launch_fmt<1, false, true>(xb, qb, scales, off, G, T, K, ga, stream, nv, pd, sc);
+    return launch_fmt<2, false, true>(xb, qb, scales, off, G, T, K, ga, stream, nv, pd, sc);
 }
 
 hipError_t launch_quantize_padded(int fmt, const void* x, void* q, void* scales, const uint32_t* scales_offsets,

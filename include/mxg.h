@@ -24,6 +24,8 @@
  *   mx_grouped_matmul_swiglu_padded
  *                             MX quantize / GEMM / fused GEMM with the activation
  *                             scales in a padded or expert-slot layout
+ *   mx_grouped_quantize_scatter  the same in token-major form: each token row
+ *                             is read once and stored to its routed rows
  *   mx_moe_combine            after the down-projection: each token's row is the
  *                             router-weighted sum of its routed rows
  *   mxg_clock_probe           measurement aid: the engine clock over a window
@@ -154,6 +156,39 @@ mxg_status mx_grouped_quantize_gather(mxg_format fmt, const void* x_bf16, int64_
                                       const int32_t* indices, int32_t indices_divisor, void* q, void* scales,
                                       const uint32_t* row_offsets, const int32_t* expert_ids, int32_t num_groups,
                                       int64_t total_rows, int64_t K, hipStream_t stream);
+
+/*
+ * mx_grouped_quantize_scatter -- the gathered quantize in token-major form:
+ * each token row is read and quantized once and its result is stored to every
+ * routed row that token feeds, through the inverse slot map (the row_of_slot
+ * table mx_moe_combine takes).  A routed row is a copy of its token's row, so
+ * the results equal mx_grouped_quantize_gather's for the same routing while
+ * the token rows are read once instead of once per slot.
+ * (NvMxf4f8Strategy, grouped_quantize(), Args indices and indices_divisor,
+ *  with the reading given at mx_grouped_quantize_gather.)
+ *
+ *   x_tokens     [num_tokens, K] bf16 token rows.
+ *   row_of_slot  int32 [num_tokens * top_k], device: the routed row of slot
+ *                (token s, k).  Slots naming a row outside [0, total_rows)
+ *                or a row no group covers are dropped.  A routed row named
+ *                by several slots receives one of their results.
+ *   top_k        slots per token, 1 .. 64.
+ *   q, scales, row_offsets, expert_ids, num_groups, total_rows, K, stream:
+ *                as in mx_grouped_quantize; routed rows no slot names are
+ *                left untouched.
+ *
+ * Errors: INVALID_VALUE for a bad fmt, K <= 0, total_rows / num_groups /
+ * num_tokens < 0, top_k < 1, a null pointer (x_tokens, row_of_slot, q,
+ * scales, row_offsets) or misalignment (x_tokens and q on 16 bytes, fp32
+ * scales, row_offsets and row_of_slot on 4); NOT_SUPPORTED for K % 32 != 0,
+ * num_groups > MXG_MAX_GROUPS, top_k > 64, FP8 rowwise rows longer than 8192
+ * elements, or num_tokens * top_k > INT32_MAX.  total_rows, num_groups or
+ * num_tokens of 0 is a no-op.
+ */
+mxg_status mx_grouped_quantize_scatter(mxg_format fmt, const void* x_tokens, int64_t num_tokens,
+                                       const int32_t* row_of_slot, int32_t top_k, void* q, void* scales,
+                                       const uint32_t* row_offsets, const int32_t* expert_ids, int32_t num_groups,
+                                       int64_t total_rows, int64_t K, hipStream_t stream);
 
 /*
  * mx_grouped_matmul -- ragged grouped GEMM with BF16 output.

@@ -70,7 +70,17 @@ int main() {
         CALL(MXG_SUCCESS, false, mx_grouped_quantize(f, nullptr, nullptr, nullptr, nullptr, nullptr, G, 0, K, nullptr));
         CALL(MXG_SUCCESS, true, mx_grouped_quantize_gather(f, x, T, ids, 1, q, s, off, ids, G, T, K, nullptr));
         CALL(MXG_ERROR_INVALID_VALUE, false, mx_grouped_quantize_gather(f, x, T, ids, 0, q, s, off, ids, G, T, K, nullptr));
+        CALL(MXG_SUCCESS, true, mx_grouped_quantize_scatter(f, x, 2, ids, 2, q, s, off, ids, G, T, K, nullptr));
+        EXPECT(strcmp(g_stub.last, "quantize_scatter") == 0);
+        CALL(MXG_ERROR_INVALID_VALUE, false, mx_grouped_quantize_scatter(f, x, 2, ids, 0, q, s, off, ids, G, T, K, nullptr));
+        CALL(MXG_ERROR_NOT_SUPPORTED, false, mx_grouped_quantize_scatter(f, x, 2, ids, 65, q, s, off, ids, G, T, K, nullptr));
+        CALL(MXG_ERROR_INVALID_VALUE, false, mx_grouped_quantize_scatter(f, x, 2, nullptr, 2, q, s, off, ids, G, T, K, nullptr));
+        CALL(MXG_SUCCESS, false, mx_grouped_quantize_scatter(f, nullptr, 0, nullptr, 2, q, s, off, ids, G, T, K, nullptr));
+        CALL(MXG_ERROR_NOT_SUPPORTED, false,
+             mx_grouped_quantize_scatter(f, x, (int64_t)INT32_MAX, ids, 2, q, s, off, ids, G, T, K, nullptr));
     }
+    CALL(MXG_ERROR_NOT_SUPPORTED, false, mx_grouped_quantize_scatter(F8, x, 2, ids, 2, q, s, off, ids, G, T, 8224, nullptr));
+    CALL(MXG_SUCCESS, true, mx_grouped_quantize_scatter(MX4, x, 2, ids, 2, q, s, off, ids, G, T, 8224, nullptr));
     CALL(MXG_ERROR_INVALID_VALUE, false, mx_grouped_quantize((mxg_format)7, x, q, s, off, ids, G, T, K, nullptr));
     CALL(MXG_ERROR_INVALID_VALUE, false, mx_grouped_quantize(F8, x, q, s, off, ids, -1, T, K, nullptr));
     CALL(MXG_ERROR_NOT_SUPPORTED, false, mx_grouped_quantize(F8, x, q, s, off, ids, MXG_MAX_GROUPS + 1, T, K, nullptr));

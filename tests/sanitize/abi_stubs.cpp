@@ -25,6 +25,10 @@ hipError_t launch_quantize_gather(int, const void*, int64_t, const int32_t*, int
                                   int, int64_t, int64_t, hipStream_t) {
     return record("quantize_gather");
 }
+hipError_t launch_quantize_scatter(int, const void*, int64_t, const int32_t*, int, void*, void*, const uint32_t*, int,
+                                   int64_t, int64_t, hipStream_t) {
+    return record("quantize_scatter");
+}
 hipError_t launch_quantize_padded(int, const void*, void*, void*, const uint32_t*, int64_t, const uint32_t*, int,
                                   int64_t, int64_t, hipStream_t) {
     return record("quantize_padded");

@@ -283,3 +283,20 @@ def test_routing_check_on_host_arrays():
     assert v([0, 3, 5, 9], [0, 3, 2], 0, 9) is None            # ids not checked without num_experts
     assert mxg.lib().mxg_routing_violation(None, None, 1, 1, 4, None, 0) == -1
     assert mxg.lib().mxg_routing_violation(FAKE, None, -1, 1, 4, None, 0) == -1
+
+
+def test_quantize_scatter_argument_errors():
+    f = mxg.lib().mx_grouped_quantize_scatter
+
+    def sc(fmt=0, x=FAKE, ntok=4, ros=FAKE, top_k=2, qq=FAKE, s=FAKE, off=FAKE, G=1, T=8, K=64):
+        return f(fmt, x, ntok, ros, top_k, qq, s, off, None, G, T, K, None)
+
+    for kw in [dict(x=None), dict(ros=None), dict(qq=None), dict(s=None), dict(off=None), dict(fmt=5),
+               dict(K=0), dict(T=-1), dict(ntok=-1), dict(top_k=0), dict(G=-1), dict(x=FAKE_ODD),
+               dict(ros=FAKE_ODD)]:
+        assert sc(**kw) == mxg.ERROR_INVALID_VALUE, kw
+    assert sc(top_k=65) == mxg.ERROR_NOT_SUPPORTED
+    assert sc(K=48) == mxg.ERROR_NOT_SUPPORTED
+    assert sc(fmt=0, K=8192 + 32) == mxg.ERROR_NOT_SUPPORTED
+    assert sc(G=2000) == mxg.ERROR_NOT_SUPPORTED
+    assert sc(ntok=0) == mxg.SUCCESS and sc(T=0) == mxg.SUCCESS and sc(G=0) == mxg.SUCCESS

@@ -202,3 +202,72 @@ def test_quantize_gather_full_size_prefill():
     q_ref, s_ref = oracle.quantize_gather(w.fmt, xs, sub_idx, w.top_k, np.array([0, rows.size], np.uint32))
     assert np.array_equal(q.cpu().numpy()[rows], q_ref)
     assert np.array_equal(s.cpu().numpy()[rows].view(np.uint8), s_ref.view(np.uint8))
+
+
+# ---------------------------------------------------------------- token-major (scatter) quantize
+def run_scatter_both(fmt, x_tok_bits: np.ndarray, ros: np.ndarray, T: int, off: np.ndarray):
+    S, K = x_tok_bits.shape
+    qcols = K // 2 if fmt == mxg.MXFP4 else K
+    s0 = np.full((T,), -3.0, np.float32) if fmt == mxg.FP8_ROWWISE else sentinel_like((T, K // 32), value=0x5A)
+    q_ref, s_ref = oracle.quantize_scatter(fmt, x_tok_bits, ros, T, off, sentinel_like((T, qcols)), s0.copy())
+    x = to_gpu(x_tok_bits.view(np.int16)).view(torch.bfloat16)
+    q = Guarded(sentinel_like((T, qcols)))
+    s = Guarded(s0.copy())
+    mxg.mx_grouped_quantize_scatter(fmt, x, to_gpu(ros.astype(np.int32)), q.view(), s.view(), offsets_gpu(off))
+    torch.cuda.synchronize()
+    q.check("scatter codes")
+    s.check("scatter scales")
+    return (q.numpy(), s.numpy()), (q_ref, s_ref)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("case", ["prefill", "mxfp4"])
+def test_quantize_scatter_matches_oracle_and_gather(fmt, case):
+    """Token rows quantized once and stored to their routed rows through the
+    inverse slot map: bit-exact with the oracle, and equal to the gathered
+    form on the same routing."""
+    widx, kw = CASES[case]
+    w = W.WORKLOADS[widx].scaled(**kw)
+    r = W.routing(w)
+    xs = bits(W.source_activations(w, r))
+    ros = W.rows_of_slots(r, w.top_k, xs.shape[0])
+    gpu, ref = run_scatter_both(fmt, xs, ros, r.total_rows, r.row_offsets)
+    assert_same(gpu, ref, f"scatter {case} fmt={fmt}")
+    g_gpu, _ = run_gather_both(fmt, xs, W.slot_indices(r, w.top_k), w.top_k, r.row_offsets)
+    assert_same(gpu, g_gpu, f"scatter == gather {case} fmt={fmt}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("K", [32, 1056, 7168])
+def test_quantize_scatter_edge_slots(fmt, K):
+    """Dropped slots (negative, past the rows), rows no group covers and rows
+    no slot names are left untouched; top_k of 1 and 64."""
+    rng = np.random.default_rng(K + 10 * fmt)
+    for S, top_k in ((23, 3), (3, 64), (40, 1)):
+        T = 70
+        xs = oracle.bf16_round_array(rng.standard_normal((S, K)) * np.exp(rng.uniform(-3, 3, (S, 1))))
+        ros = rng.permutation(max(T, S * top_k))[:S * top_k].astype(np.int32)   # some >= T (dropped)
+        ros[rng.integers(0, S * top_k, 3)] = -2
+        off = np.array([2, 20, 20, 64], np.uint32)  # rows 0-1 and 64.. uncovered
+        gpu, ref = run_scatter_both(fmt, xs, ros, T, off)
+        assert_same(gpu, ref, f"scatter edges K={K} fmt={fmt} S={S} top_k={top_k}")
+
+
+@pytest.mark.parametrize("widx", [3, 5])
+def test_quantize_scatter_full_size(widx):
+    """The prefill (FP8 rowwise) and fused (MXFP4) workloads at full size, in
+    the benchmark's launch configuration: every routed row bit-exact."""
+    w = W.WORKLOADS[widx]
+    r = W.routing(w)
+    xs_gpu = W.source_activations(w, r, device="cuda")
+    xs = bits(xs_gpu)
+    ros = W.rows_of_slots(r, w.top_k, xs.shape[0])
+    T, K = r.total_rows, w.K
+    qcols = K // 2 if w.fmt == mxg.MXFP4 else K
+    q = torch.zeros((T, qcols), dtype=torch.uint8, device="cuda")
+    s = torch.zeros((T,), dtype=torch.float32, device="cuda") if w.fmt == 0 else \
+        torch.zeros((T, K // 32), dtype=torch.uint8, device="cuda")
+    mxg.mx_grouped_quantize_scatter(w.fmt, xs_gpu, to_gpu(ros), q, s, offsets_gpu(r.row_offsets))
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle.quantize_scatter(w.fmt, xs, ros, T, r.row_offsets)
+    assert_same((q.cpu().numpy(), s.cpu().numpy()), (q_ref, s_ref), f"scatter workload {widx}")
