@@ -91,6 +91,8 @@ def lib() -> ctypes.CDLL:
         L.mxo_quantize_gather.restype = ctypes.c_int
         L.mxo_quantize_scatter.argtypes = [ctypes.c_int, _P, _I64, _P, _I32, _P, _P, _P, _I32, _I64, _I64]
         L.mxo_quantize_scatter.restype = ctypes.c_int
+        L.mxo_quantize_nvfp4_padded.argtypes = [_P, _P, _P, _P, _P, _I64, _P, _P, _I32, _I32, _I64, _I64]
+        L.mxo_quantize_nvfp4_padded.restype = ctypes.c_int
         L.mxo_combine.argtypes = [_P, _I64, _I64, _P, _P, _I64, _I32, _P, _P, _P]
         L.mxo_combine.restype = ctypes.c_int
         L.mxo_gemm_rows.argtypes = [ctypes.c_int, _P, _P, _P, _P, _P, _P, _I32, _I32, _I64, _I64, _I64,
@@ -503,6 +505,29 @@ def quantize_padded(fmt: int, x_bf16, offsets, scales_offsets, scale_rows: int, 
         raise ValueError("oracle quantize_padded: invalid arguments")
     return q, scales
 
+
+
+def quantize_nvfp4_padded(x_bf16, offsets, expert_ids, tensor_scales, scales_offsets, scale_rows: int, q=None,
+                          scales=None):
+    """NVFP4 grouped quantize (as quantize_nvfp4) with the E4M3 scales of group g's row t
+    in row scales_offsets[g] + (t - offsets[g]) of a [scale_rows, K/16] tensor; a row whose
+    scale row is at or past scale_rows is left untouched.  Returns (q, scales)."""
+    x = _c(x_bf16, np.uint16)
+    T, K = x.shape
+    off = _c(offsets, np.uint32)
+    ids = _c(expert_ids, np.int32)
+    sf = _c(tensor_scales, np.float32)
+    soff = _c(scales_offsets, np.uint32).ravel()
+    if q is None:
+        q = np.zeros((T, K // 2), np.uint8)
+    if scales is None:
+        scales = np.zeros((scale_rows, K // 16), np.uint8)
+    assert soff.size >= off.size - 1 and scales.shape == (scale_rows, K // 16)
+    rc = lib().mxo_quantize_nvfp4_padded(_ptr(x), _ptr(q), _ptr(scales), _ptr(sf), _ptr(soff), scale_rows,
+                                         _ptr(off), _ptr(ids), off.size - 1, sf.size, T, K)
+    if rc != 0:
+        raise ValueError("oracle quantize_nvfp4_padded: invalid arguments")
+    return q, scales
 
 def gemm_rows_padded(fmt: int, a, a_scale, a_scales_offsets, b, b_scale, offsets, expert_ids, N: int, K: int, rows,
                      want_exact: bool = True):

@@ -748,6 +748,33 @@ int mxo_quantize_padded(int fmt, const uint16_t* x, uint8_t* q, uint8_t* scales,
     return MXO_OK;
 }
 
+/* NVFP4 in the same padded / slot-strided layout (the scales_offsets argument
+ * of grouped_quantize_dynamic_scaled_fp4_async_kernel covers NVFP4 as well):
+ * routed row t of taken group g (expert id in [0, E)) is quantized as in
+ * mxo_quantize_nvfp4 with tensor scale sf[ids[g]], its K/16 E4M3 scale bytes
+ * going to row soff[g] + (t - row_offsets[g]) of a [S, K/16] tensor; a row
+ * whose scale row lies at or past S is left untouched (codes included).    */
+int mxo_quantize_nvfp4_padded(const uint16_t* x, uint8_t* q, uint8_t* scales, const float* sf,
+                              const uint32_t* soff, int64_t S, const uint32_t* off, const int32_t* ids, int32_t G,
+                              int32_t E, int64_t T, int64_t K) {
+    if (!x || !q || !scales || !sf || !soff || !off || !ids || G < 0 || E <= 0 || T < 0 || S < 0 || K <= 0 ||
+        (K % 16) != 0)
+        return MXO_EINVAL;
+    for (int32_t g = 0; g < G; ++g) {
+        int64_t lo, hi;
+        group_range(off, g, T, &lo, &hi);
+        if (lo > hi || ids[g] < 0 || ids[g] >= E) continue;
+        const float f = sf[ids[g]];
+#pragma omp parallel for schedule(dynamic, 16)
+        for (int64_t t = lo; t < hi; ++t) {
+            const int64_t srow = (int64_t)soff[g] + (t - lo);
+            if (srow >= S) continue;
+            quantize_row_nvfp4(x + t * K, K, f, q + t * (K / 2), scales + srow * (K / 16));
+        }
+    }
+    return MXO_OK;
+}
+
 /* Grouped GEMM rows with A's scales in such a layout: the dense A scales are
  * gathered row by row through the map above, then mxo_gemm_rows runs; a row
  * whose scale row lies at or past Sa is reported uncovered (group -1).     */

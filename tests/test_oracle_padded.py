@@ -81,3 +81,55 @@ def test_gemm_with_moved_scales_is_unchanged(fmt):
     assert np.array_equal(dense["group"], padded["group"])
     cov = dense["group"] >= 0
     assert np.array_equal(dense["exact"][cov], padded["exact"][cov])
+
+
+def nv_case():
+    w, r, x = case()
+    sf = np.linspace(50.0, 2688.0, w.E).astype(np.float32)
+    return w, r, x, sf
+
+
+def test_nvfp4_identity_offsets_are_the_dense_layout():
+    w, r, x, sf = nv_case()
+    T = x.shape[0]
+    qd, sd = oracle.quantize_nvfp4(x, r.row_offsets, r.expert_ids, sf)
+    qp, sp = oracle.quantize_nvfp4_padded(x, r.row_offsets, r.expert_ids, sf, r.row_offsets[:-1], T)
+    cov = np.zeros(T, bool)
+    for g in range(len(r.expert_ids)):
+        cov[r.row_offsets[g]:r.row_offsets[g + 1]] = True
+    assert np.array_equal(qd[cov], qp[cov]) and np.array_equal(sd[cov], sp[cov])
+
+
+def test_nvfp4_slot_layout_moves_scale_rows_and_cuts_at_the_end():
+    """NVFP4 scales (16-element blocks) in the expert-slot layout: codes as the
+    dense quantize, each group's scale rows moved to its slot, padding rows
+    never written; with the tensor cut inside a slot, the rows past the cut
+    are left untouched, codes included."""
+    w, r, x, sf = nv_case()
+    T, K = x.shape
+    counts = np.diff(r.row_offsets.astype(np.int64))
+    mpad = int(-(-counts.max() // 64) * 64)
+    soff = (r.expert_ids.astype(np.int64) * mpad).astype(np.uint32)
+    S = int(w.E * mpad)
+    qd, sd = oracle.quantize_nvfp4(x, r.row_offsets, r.expert_ids, sf)
+    qp, sp = oracle.quantize_nvfp4_padded(x, r.row_offsets, r.expert_ids, sf, soff, S,
+                                          scales=np.full((S, K // 16), 0x5A, np.uint8))
+    written = np.zeros(S, bool)
+    for g in range(len(r.expert_ids)):
+        lo, hi = int(r.row_offsets[g]), int(r.row_offsets[g + 1])
+        assert np.array_equal(qp[lo:hi], qd[lo:hi])
+        assert np.array_equal(sp[soff[g]:soff[g] + hi - lo], sd[lo:hi])
+        written[soff[g]:soff[g] + hi - lo] = True
+    assert np.all(sp[~written] == 0x5A)
+    g = int(np.argmax(counts))
+    cut = int(soff[g]) + int(counts[g]) // 2
+    q0 = np.full((T, K // 2), 0xA5, np.uint8)
+    qc, sc = oracle.quantize_nvfp4_padded(x, r.row_offsets, r.expert_ids, sf, soff, cut, q0.copy(),
+                                          np.full((cut, K // 16), 0x5A, np.uint8))
+    for gg in range(len(r.expert_ids)):
+        lo, hi = int(r.row_offsets[gg]), int(r.row_offsets[gg + 1])
+        for t in range(lo, hi):
+            if int(soff[gg]) + t - lo < cut:
+                assert np.array_equal(qc[t], qd[t]) and np.array_equal(sc[int(soff[gg]) + t - lo], sd[t])
+            else:
+                assert np.all(qc[t] == 0xA5)
