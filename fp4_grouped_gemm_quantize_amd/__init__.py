@@ -33,7 +33,8 @@ LIB_PATH = os.path.join(_PKG, "libmxg.so")
 EXPORTED = ("mx_grouped_quantize", "mx_grouped_quantize_gather", "mx_grouped_quantize_scatter", "mx_grouped_matmul", "mx_grouped_matmul_swiglu",
             "mx_silu_quantize", "mx_moe_combine", "mx_grouped_quantize_nvfp4", "mx_grouped_matmul_nvfp4",
             "mx_grouped_matmul_swiglu_nvfp4", "mx_silu_quantize_nvfp4", "mx_grouped_quantize_padded",
-            "mx_grouped_matmul_padded", "mx_grouped_matmul_swiglu_padded", "mxg_clock_probe",
+            "mx_grouped_matmul_padded", "mx_grouped_matmul_swiglu_padded",
+            "mx_grouped_quantize_nvfp4_padded", "mx_grouped_matmul_nvfp4_padded", "mxg_clock_probe",
             "mxg_validation_message", "mxg_routing_violation", "mxg_status_string")
 
 
@@ -83,6 +84,11 @@ def lib() -> ctypes.CDLL:
                      "mx_grouped_matmul_nvfp4", "mx_grouped_matmul_swiglu_nvfp4", "mx_silu_quantize_nvfp4",
                      "mx_grouped_quantize_padded", "mx_grouped_matmul_padded", "mx_grouped_matmul_swiglu_padded"):
             getattr(L, name).restype = ctypes.c_int
+        L.mx_grouped_quantize_nvfp4_padded.argtypes = [_P, _P, _P, _P, _P, _I64, _P, _P, _I32, _I32, _I64, _I64, _P]
+        L.mx_grouped_matmul_nvfp4_padded.argtypes = [_P, _P, _P, _I64, _P, _P, _P, _P, _P, _P, _I32, _I32, _I64,
+                                                     _I64, _I64, _I64, _P]
+        L.mx_grouped_quantize_nvfp4_padded.restype = ctypes.c_int
+        L.mx_grouped_matmul_nvfp4_padded.restype = ctypes.c_int
         L.mxg_validation_message.argtypes = []
         L.mxg_validation_message.restype = ctypes.c_char_p
         L.mxg_routing_violation.argtypes = [_P, _P, _I32, _I32, _I64, ctypes.c_char_p, _I64]
@@ -572,3 +578,50 @@ def routing_violation(row_offsets, expert_ids=None, num_experts: int = 0, total_
     if rc < 0:
         raise ValueError("mxg_routing_violation: invalid arguments")
     return msg.value.decode() if rc else None
+
+
+def mx_grouped_quantize_nvfp4_padded(x, q, scales, tensor_scales, scales_offsets, row_offsets, expert_ids) -> None:
+    """NVFP4 grouped quantize of bf16 x [T, K] into q u8 [T, K/2] with the E4M3 scales of
+    group g's row t in row scales_offsets[g] + (t - row_offsets[g]) of scales u8 [S, K/16]."""
+    _expect(x, "x", _BF16)
+    T, K = x.shape
+    dev = x.device
+    _expect(q, "q", _U8, (T, K // 2), dev)
+    _expect(scales, "scales", _U8, None, dev)
+    if scales.dim() != 2 or scales.shape[1] != K // 16:
+        raise ValueError("scales must be [scale_rows, K/16]")
+    _expect(tensor_scales, "tensor_scales", _F32, None, dev)
+    _expect(row_offsets, "row_offsets", _U32, None, dev)
+    G = row_offsets.numel() - 1
+    _expect(expert_ids, "expert_ids", _I32T, (G,), dev)
+    _expect(scales_offsets, "scales_offsets", _U32, (G,), dev)
+    _check(lib().mx_grouped_quantize_nvfp4_padded(_ptr(x), _ptr(q), _ptr(scales), _ptr(tensor_scales),
+                                                  _ptr(scales_offsets), scales.shape[0], _ptr(row_offsets),
+                                                  _ptr(expert_ids), G, tensor_scales.numel(), T, K, _stream(x)),
+           "mx_grouped_quantize_nvfp4_padded")
+
+
+def mx_grouped_matmul_nvfp4_padded(a_q, a_scales, a_scales_offsets, b_q, b_scales, expert_scales, c, row_offsets,
+                                   expert_ids, max_rows_per_group_hint: int = 0) -> None:
+    """NVFP4 grouped GEMM with A's E4M3 scales in the padded layout (a_scales u8 [S, K/16])."""
+    _expect(a_q, "a_q", _U8)
+    T, K2 = a_q.shape
+    K = 2 * K2
+    dev = a_q.device
+    _expect(a_scales, "a_scales", _U8, None, dev)
+    if a_scales.dim() != 2 or a_scales.shape[1] != K // 16:
+        raise ValueError("a_scales must be [scale_rows, K/16]")
+    _expect(b_q, "b_q", _U8, None, dev)
+    E, N, _ = b_q.shape
+    _expect(b_scales, "b_scales", _U8, (E, N, K // 16), dev)
+    _expect(expert_scales, "expert_scales", _F32, (E,), dev)
+    _expect(c, "c", _BF16, (T, N), dev)
+    _expect(row_offsets, "row_offsets", _U32, None, dev)
+    G = row_offsets.numel() - 1
+    _expect(expert_ids, "expert_ids", _I32T, (G,), dev)
+    _expect(a_scales_offsets, "a_scales_offsets", _U32, (G,), dev)
+    _check(lib().mx_grouped_matmul_nvfp4_padded(_ptr(a_q), _ptr(a_scales), _ptr(a_scales_offsets), a_scales.shape[0],
+                                                _ptr(b_q), _ptr(b_scales), _ptr(expert_scales), _ptr(c),
+                                                _ptr(row_offsets), _ptr(expert_ids), G, E, T, N, K,
+                                                int(max_rows_per_group_hint), _stream(a_q)),
+           "mx_grouped_matmul_nvfp4_padded")

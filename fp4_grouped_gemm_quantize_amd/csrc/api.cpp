@@ -204,6 +204,26 @@ mxg_status mx_grouped_quantize_padded(mxg_format fmt, const void* x_bf16, void* 
                                                 num_groups, total_rows, K, stream));
 }
 
+mxg_status mx_grouped_quantize_nvfp4_padded(const void* x_bf16, void* q, void* scales, const float* tensor_scales,
+                                            const uint32_t* scales_offsets, int64_t scale_rows,
+                                            const uint32_t* row_offsets, const int32_t* expert_ids,
+                                            int32_t num_groups, int32_t num_experts, int64_t total_rows, int64_t K,
+                                            hipStream_t stream) {
+    if (K <= 0 || total_rows < 0 || num_groups < 0 || num_experts <= 0 || scale_rows < 0)
+        return MXG_ERROR_INVALID_VALUE;
+    if (K % 16 != 0 || num_groups > MXG_MAX_GROUPS) return MXG_ERROR_NOT_SUPPORTED;
+    if (total_rows == 0 || num_groups == 0) return MXG_SUCCESS;  // nothing is read or written
+    if (!x_bf16 || !q || !scales || !tensor_scales || !scales_offsets || !row_offsets || !expert_ids)
+        return MXG_ERROR_INVALID_VALUE;
+    if (!aligned(x_bf16, 16) || !aligned(q, 16) || !aligned(tensor_scales, 4) || !aligned(scales_offsets, 4) ||
+        !aligned(row_offsets, 4) || !aligned(expert_ids, 4))
+        return MXG_ERROR_INVALID_VALUE;
+    if (mxg_status st = check_routing(row_offsets, expert_ids, num_groups, num_experts, total_rows, stream)) return st;
+    return from_hip(mxg::launch_quantize_nvfp4_padded(x_bf16, q, scales, tensor_scales, scales_offsets, scale_rows,
+                                                      row_offsets, expert_ids, num_groups, num_experts, total_rows,
+                                                      K, stream));
+}
+
 mxg_status mx_moe_combine(const void* y_bf16, int64_t total_rows, int64_t H, const int32_t* row_of_slot,
                           const float* weights, int64_t num_tokens, int32_t top_k, void* out_bf16,
                           hipStream_t stream) {
@@ -268,6 +288,30 @@ mxg_status mx_grouped_matmul_nvfp4(const void* a_q, const void* a_scales, const 
         return MXG_ERROR_INVALID_VALUE;
     mxg::GemmProblem p{3, a_q, a_scales, b_q, b_scales, c_bf16, nullptr, nullptr, row_offsets, expert_ids,
                        num_groups, num_experts, total_rows, N, K, max_rows_per_group_hint, expert_scales};
+    return launch_gemm_checked(p, stream);
+}
+
+mxg_status mx_grouped_matmul_nvfp4_padded(const void* a_q, const void* a_scales, const uint32_t* a_scales_offsets,
+                                          int64_t a_scale_rows, const void* b_q, const void* b_scales,
+                                          const float* expert_scales, void* c_bf16, const uint32_t* row_offsets,
+                                          const int32_t* expert_ids, int32_t num_groups, int32_t num_experts,
+                                          int64_t total_rows, int64_t N, int64_t K, int64_t max_rows_per_group_hint,
+                                          hipStream_t stream) {
+    if (K <= 0 || N <= 0 || num_experts <= 0 || total_rows < 0 || num_groups < 0 || a_scale_rows < 0)
+        return MXG_ERROR_INVALID_VALUE;
+    if (K % 512 != 0 || num_groups > MXG_MAX_GROUPS) return MXG_ERROR_NOT_SUPPORTED;
+    if (N > INT32_MAX / 2 || total_rows > INT32_MAX) return MXG_ERROR_NOT_SUPPORTED;
+    if (total_rows == 0 || num_groups == 0) return MXG_SUCCESS;  // nothing is read or written
+    if (!a_q || !a_scales || !a_scales_offsets || !b_q || !b_scales || !expert_scales || !c_bf16 || !row_offsets ||
+        !expert_ids)
+        return MXG_ERROR_INVALID_VALUE;
+    if (!aligned(a_q, 16) || !aligned(b_q, 16) || !aligned(a_scales, 16) || !aligned(b_scales, 16) ||
+        !aligned(c_bf16, 16) || !aligned(expert_scales, 4) || !aligned(a_scales_offsets, 4) ||
+        !aligned(row_offsets, 4) || !aligned(expert_ids, 4))
+        return MXG_ERROR_INVALID_VALUE;
+    mxg::GemmProblem p{3, a_q, a_scales, b_q, b_scales, c_bf16, nullptr, nullptr, row_offsets, expert_ids,
+                       num_groups, num_experts, total_rows, N, K, max_rows_per_group_hint, expert_scales, nullptr,
+                       nullptr, a_scales_offsets, a_scale_rows};
     return launch_gemm_checked(p, stream);
 }
 

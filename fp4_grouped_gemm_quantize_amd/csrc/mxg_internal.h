@@ -30,6 +30,11 @@ hipError_t launch_quantize_nvfp4(const void* x, void* q, void* scales, const flo
                                   const uint32_t* off, const int32_t* ids, int G, int E, int64_t T, int64_t K,
                                   hipStream_t stream);
 
+// NVFP4 with group g's E4M3 scales from row scales_offsets[g] of a [scale_rows, K/16] tensor.
+hipError_t launch_quantize_nvfp4_padded(const void* x, void* q, void* scales, const float* tensor_scales,
+                                        const uint32_t* scales_offsets, int64_t scale_rows, const uint32_t* off,
+                                        const int32_t* ids, int G, int E, int64_t T, int64_t K, hipStream_t stream);
+
 // out[t, :] = bf16(sum_k weights[t*top_k + k] * y[row_of_slot[t*top_k + k], :]).
 hipError_t launch_combine(const void* y, int64_t T, int64_t H, const int32_t* row_of_slot, const float* weights,
                           int64_t ntok, int top_k, void* out, hipStream_t stream);

@@ -228,10 +228,17 @@ __global__ __launch_bounds__(kThreads) void quantize_rows_kernel(const uint16_t*
             }
         } else if constexpr (FMT == 3) {
             const int g = cu.sr >= 0 ? wave_row_group(s_off, nv.ids, G, nv.E, T, t) : -1;
-            if (g >= 0) {
+            // scale row: t, or in a padded layout the group's slot row (-1: past the tensor)
+            int64_t srix = g >= 0 ? t : -1;
+            if (g >= 0 && pd.soff) {
+                const int64_t lo = (int64_t)s_off[g] < T ? (int64_t)s_off[g] : T;
+                srix = (int64_t)pd.soff[g] + (t - lo);
+                if (srix >= pd.S) srix = -1;
+            }
+            if (srix >= 0) {
                 const float sf = nv.sf[nv.ids[g]];
                 uint8_t* qrow = q + t * (K / 2) + cu.e0 / 2;
-                uint8_t* srow = static_cast<uint8_t*>(scales) + t * (K / 16) + cu.e0 / 16;
+                uint8_t* srow = static_cast<uint8_t*>(scales) + srix * (K / 16) + cu.e0 / 16;
 #pragma unroll
                 for (int c = 0; c < NC; ++c) {
                     const int idx = c * kWave + lane;
@@ -540,6 +547,14 @@ hipError_t launch_quantize_nvfp4(const void* x, void* q, void* scales, const flo
                                   hipStream_t stream) {
     return launch_fmt<3, false>(static_cast<const uint16_t*>(x), static_cast<uint8_t*>(q), scales, off, G, T, K,
                                 Gather{nullptr, 1, T}, stream, NvScales{ids, tensor_scales, E});
+}
+
+hipError_t launch_quantize_nvfp4_padded(const void* x, void* q, void* scales, const float* tensor_scales,
+                                        const uint32_t* scales_offsets, int64_t scale_rows, const uint32_t* off,
+                                        const int32_t* ids, int G, int E, int64_t T, int64_t K, hipStream_t stream) {
+    return launch_fmt<3, false>(static_cast<const uint16_t*>(x), static_cast<uint8_t*>(q), scales, off, G, T, K,
+                                Gather{nullptr, 1, T}, stream, NvScales{ids, tensor_scales, E},
+                                Pad{scales_offsets, scale_rows});
 }
 
 hipError_t launch_silu_quantize(const void* h, void* yq, void* ys, const uint32_t* off, int G, int64_t T,

@@ -21,9 +21,11 @@
  *                             and an NVFP4 requant of the activation
  *   mx_silu_quantize_nvfp4    its unfused second half
  *   mx_grouped_quantize_padded, mx_grouped_matmul_padded,
- *   mx_grouped_matmul_swiglu_padded
- *                             MX quantize / GEMM / fused GEMM with the activation
- *                             scales in a padded or expert-slot layout
+ *   mx_grouped_matmul_swiglu_padded, mx_grouped_quantize_nvfp4_padded,
+ *   mx_grouped_matmul_nvfp4_padded
+ *                             MX / NVFP4 quantize, GEMM (and MX fused GEMM) with
+ *                             the activation scales in a padded or expert-slot
+ *                             layout
  *   mx_grouped_quantize_scatter  the same in token-major form: each token row
  *                             is read once and stored to its routed rows
  *   mx_moe_combine            after the down-projection: each token's row is the
@@ -441,6 +443,33 @@ mxg_status mx_grouped_matmul_swiglu_padded(mxg_format fmt, const void* a_q, cons
                                            const uint32_t* row_offsets, const int32_t* expert_ids,
                                            int32_t num_groups, int32_t num_experts, int64_t total_rows, int64_t I,
                                            int64_t K, int64_t max_rows_per_group_hint, hipStream_t stream);
+
+/*
+ * mx_grouped_quantize_nvfp4_padded, mx_grouped_matmul_nvfp4_padded -- the
+ * NVFP4 quantize and grouped GEMM with the activation block scales in the
+ * padded / slot-strided layout above (the offsets-into-the-scale-tensor
+ * argument of grouped_quantize_dynamic_scaled_fp4_async_kernel covers NVFP4
+ * as well as the MX formats).  Routed row t of group g keeps its K/16 E4M3
+ * scale bytes in row scales_offsets[g] + (t - row_offsets[g]) of a
+ * [scale_rows, K/16] u8 tensor; the rest as for MX: the quantize leaves a
+ * row whose scale row lies at or past scale_rows untouched (codes too) and
+ * never writes padding rows; the GEMM reads A's scales through the map and
+ * leaves such rows of c untouched.  Other arguments, layouts and errors as
+ * mx_grouped_quantize_nvfp4 / mx_grouped_matmul_nvfp4, plus INVALID_VALUE
+ * for scale_rows < 0 or a null or misaligned scales_offsets (4 bytes); the
+ * GEMM's a_scales must be on 16 bytes.
+ */
+mxg_status mx_grouped_quantize_nvfp4_padded(const void* x_bf16, void* q, void* scales, const float* tensor_scales,
+                                            const uint32_t* scales_offsets, int64_t scale_rows,
+                                            const uint32_t* row_offsets, const int32_t* expert_ids,
+                                            int32_t num_groups, int32_t num_experts, int64_t total_rows, int64_t K,
+                                            hipStream_t stream);
+mxg_status mx_grouped_matmul_nvfp4_padded(const void* a_q, const void* a_scales, const uint32_t* a_scales_offsets,
+                                          int64_t a_scale_rows, const void* b_q, const void* b_scales,
+                                          const float* expert_scales, void* c_bf16, const uint32_t* row_offsets,
+                                          const int32_t* expert_ids, int32_t num_groups, int32_t num_experts,
+                                          int64_t total_rows, int64_t N, int64_t K, int64_t max_rows_per_group_hint,
+                                          hipStream_t stream);
 
 /*
  * mx_moe_combine -- the MoE combine after the down-projection (itself

@@ -91,6 +91,10 @@ int main() {
     CALL(MXG_SUCCESS, true, mx_grouped_quantize_nvfp4(x, q, s, sfd, off, ids, G, E, T, K, nullptr));
     CALL(MXG_ERROR_NOT_SUPPORTED, false, mx_grouped_quantize_nvfp4(x, q, s, sfd, off, ids, G, E, T, 24, nullptr));
     CALL(MXG_SUCCESS, true, mx_grouped_quantize_padded(MX4, x, q, s, off, 100, off, G, T, K, nullptr));
+    CALL(MXG_SUCCESS, true, mx_grouped_quantize_nvfp4_padded(x, q, s, sfd, off, 100, off, ids, G, E, T, K, nullptr));
+    EXPECT(strcmp(g_stub.last, "quantize_nvfp4_padded") == 0);
+    CALL(MXG_ERROR_INVALID_VALUE, false,
+         mx_grouped_quantize_nvfp4_padded(x, q, s, sfd, nullptr, 100, off, ids, G, E, T, K, nullptr));
     CALL(MXG_ERROR_NOT_SUPPORTED, false, mx_grouped_quantize_padded(F8, x, q, s, off, 100, off, G, T, K, nullptr));
     CALL(MXG_ERROR_INVALID_VALUE, false, mx_grouped_quantize_padded(MX4, x, q, s, off, -1, off, G, T, K, nullptr));
 
@@ -116,6 +120,9 @@ int main() {
     CALL(MXG_SUCCESS, true,
          mx_grouped_matmul_swiglu_padded(MX4, q, s, off, 100, b, bs, c, s, off, ids, G, E, T, I, K, 0, nullptr));
     CALL(MXG_SUCCESS, true, mx_grouped_matmul_nvfp4(q, s, b, bs, sfd, c, off, ids, G, E, T, N, 512, 0, nullptr));
+    CALL(MXG_SUCCESS, true,
+         mx_grouped_matmul_nvfp4_padded(q, s, off, 100, b, bs, sfd, c, off, ids, G, E, T, N, 512, 0, nullptr));
+    EXPECT(g_stub.gemm.fmt == 3 && g_stub.gemm.asoff == off && g_stub.gemm.as_rows == 100);
     CALL(MXG_ERROR_NOT_SUPPORTED, false, mx_grouped_matmul_nvfp4(q, s, b, bs, sfd, c, off, ids, G, E, T, N, 256, 0, nullptr));
     CALL(MXG_SUCCESS, true,
          mx_grouped_matmul_swiglu_nvfp4(q, s, b, bs, sfd, nullptr, sfd, c, s, off, ids, G, E, T, I, 512, 0, nullptr));

@@ -37,6 +37,10 @@ hipError_t launch_quantize_nvfp4(const void*, void*, void*, const float*, const 
                                  int64_t, int64_t, hipStream_t) {
     return record("quantize_nvfp4");
 }
+hipError_t launch_quantize_nvfp4_padded(const void*, void*, void*, const float*, const uint32_t*, int64_t,
+                                        const uint32_t*, const int32_t*, int, int, int64_t, int64_t, hipStream_t) {
+    return record("quantize_nvfp4_padded");
+}
 hipError_t launch_combine(const void*, int64_t, int64_t, const int32_t*, const float*, int64_t, int, void*,
                           hipStream_t) {
     return record("combine");

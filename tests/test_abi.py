@@ -300,3 +300,26 @@ def test_quantize_scatter_argument_errors():
     assert sc(fmt=0, K=8192 + 32) == mxg.ERROR_NOT_SUPPORTED
     assert sc(G=2000) == mxg.ERROR_NOT_SUPPORTED
     assert sc(ntok=0) == mxg.SUCCESS and sc(T=0) == mxg.SUCCESS and sc(G=0) == mxg.SUCCESS
+
+
+def test_nvfp4_padded_argument_errors():
+    L = mxg.lib()
+
+    def nq(x=FAKE, qq=FAKE, s=FAKE, sf=FAKE, soff=FAKE, S=16, off=FAKE, ids=FAKE, G=1, E=1, T=4, K=64):
+        return L.mx_grouped_quantize_nvfp4_padded(x, qq, s, sf, soff, S, off, ids, G, E, T, K, None)
+
+    for kw in [dict(x=None), dict(soff=None), dict(sf=None), dict(ids=None), dict(S=-1), dict(E=0), dict(K=0),
+               dict(soff=FAKE_ODD), dict(x=FAKE_ODD)]:
+        assert nq(**kw) == mxg.ERROR_INVALID_VALUE, kw
+    assert nq(K=40) == mxg.ERROR_NOT_SUPPORTED
+    assert nq(T=0) == mxg.SUCCESS
+
+    def nm(a=FAKE, sa=FAKE, soff=FAKE, S=16, b=FAKE, sb=FAKE, es=FAKE, c=FAKE, off=FAKE, ids=FAKE, G=1, E=1, T=4,
+           N=32, K=512):
+        return L.mx_grouped_matmul_nvfp4_padded(a, sa, soff, S, b, sb, es, c, off, ids, G, E, T, N, K, 0, None)
+
+    for kw in [dict(a=None), dict(soff=None), dict(es=None), dict(S=-1), dict(sa=FAKE_4), dict(soff=FAKE_ODD),
+               dict(E=0)]:
+        assert nm(**kw) == mxg.ERROR_INVALID_VALUE, kw
+    assert nm(K=256) == mxg.ERROR_NOT_SUPPORTED
+    assert nm(T=0) == mxg.SUCCESS

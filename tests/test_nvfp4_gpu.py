@@ -395,3 +395,76 @@ def test_nvfp4_fused_full_size_sampled_rows():
     rows = np.unique(np.array(rows + list(rng.integers(0, a.shape[0], 16))))
     ref = oracle.gemm_swiglu_rows_nvfp4(a, sa, b, sb, es, None, sfy, r.row_offsets, r.expert_ids, w.N // 2, w.K, rows)
     check_nv_swiglu_interval(yq[rows], ys[rows], ref["gu_exact"], ref["gu_bound"], sfy[r.expert_ids[ref["group"]]])
+
+
+# ---------------------------------------------------------------- padded / slot-strided NVFP4 scales
+def nv_slot_offsets(r, round_to=64):
+    counts = np.diff(r.row_offsets.astype(np.int64))
+    mpad = int(max(1, -(-counts.max() // round_to)) * round_to)
+    return (r.expert_ids.astype(np.int64) * mpad).astype(np.uint32), mpad
+
+
+@pytest.mark.parametrize("K", [512, 7168])
+def test_quantize_nvfp4_padded_matches_oracle(K):
+    """NVFP4 scales in the expert-slot layout, bit for bit with the oracle; the
+    padding rows and, with the tensor cut inside a slot, the rows past the cut
+    (codes included) are left untouched."""
+    w = W.WORKLOADS[5].scaled(tokens=48, E=6, masked=1, top_k=4, K=K)
+    r = W.routing(w)
+    x = bits(W.activations(w, r))
+    T = x.shape[0]
+    sf = tensor_scales(x, r.row_offsets, r.expert_ids, w.E, seed=K)
+    soff, mpad = nv_slot_offsets(r)
+    counts = np.diff(r.row_offsets.astype(np.int64))
+    g = int(np.argmax(counts))
+    for S in (w.E * mpad, int(soff[g]) + int(counts[g]) // 2 + 3):
+        q_ref, s_ref = oracle.quantize_nvfp4_padded(x, r.row_offsets, r.expert_ids, sf, soff, S,
+                                                    sentinel_like((T, K // 2)), sentinel_like((S, K // 16), value=0x5A))
+        q = Guarded(sentinel_like((T, K // 2)))
+        s = Guarded(sentinel_like((S, K // 16), value=0x5A))
+        mxg.mx_grouped_quantize_nvfp4_padded(to_gpu(x.view(np.int16)).view(torch.bfloat16), q.view(), s.view(),
+                                             to_gpu(sf), to_gpu(soff), offsets_gpu(r.row_offsets),
+                                             to_gpu(r.expert_ids.astype(np.int32)))
+        torch.cuda.synchronize()
+        q.check("codes")
+        s.check("scales")
+        assert_same((q.numpy(), s.numpy()), (q_ref, s_ref), f"NVFP4 padded K={K} S={S}")
+
+
+@pytest.mark.parametrize("hint", [0, 1 << 20])
+def test_nvfp4_gemm_padded_equals_dense_and_oracle(hint):
+    """The NVFP4 GEMM reading A's scales through the slot layout equals the
+    dense-layout GEMM bit for bit; with the scale tensor cut inside a group,
+    rows without scale rows are left untouched and the rest match the oracle."""
+    w = NV_SMALL["k1024"]
+    r, a, sa, b, sb, es = nv_gemm_inputs(w, seed=23)
+    T, K, N = a.shape[0], w.K, w.N
+    soff, mpad = nv_slot_offsets(r)
+    S = w.E * mpad
+    sp = np.full((S, K // 16), 0x38, np.uint8)
+    for gg in range(len(r.expert_ids)):
+        lo, hi = int(r.row_offsets[gg]), int(r.row_offsets[gg + 1])
+        sp[soff[gg]:soff[gg] + hi - lo] = sa[lo:hi]
+    dense = run_nv_gemm(r, a, sa, b, sb, es, hint)
+    counts = np.diff(r.row_offsets.astype(np.int64))
+    g = int(np.argmax(counts))
+    cut = int(soff[g]) + int(counts[g]) // 2 + 5
+    for S_used, label in ((S, "full"), (cut, "cut")):
+        c = Guarded(np.full((T, N), SENT_BF16, np.uint16))
+        mxg.mx_grouped_matmul_nvfp4_padded(to_gpu(a), to_gpu(np.ascontiguousarray(sp[:S_used])), to_gpu(soff),
+                                           to_gpu(b), to_gpu(sb), to_gpu(es), c.view(torch.bfloat16),
+                                           offsets_gpu(r.row_offsets), to_gpu(r.expert_ids.astype(np.int32)), hint)
+        torch.cuda.synchronize()
+        c.check(f"padded c {label}")
+        out = c.numpy()
+        covered = np.zeros(T, bool)
+        for gg in range(len(r.expert_ids)):
+            lo, hi = int(r.row_offsets[gg]), int(r.row_offsets[gg + 1])
+            for t in range(lo, hi):
+                covered[t] = int(soff[gg]) + t - lo < S_used
+        if label == "full":
+            assert np.array_equal(out, dense), "padded and dense A scales gave different results"
+        else:
+            assert 0 < covered.sum() < T
+            assert np.all(out[~covered] == SENT_BF16), "rows without scale rows were written"
+            assert np.array_equal(out[covered], dense[covered])
