@@ -407,20 +407,34 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
             __asm__ volatile("" : "+v"(v));
             return v;
         };
+        // The four-slot ring issues its direct loads from inline assembly
+        // (see lds_dma16): its K loop issues no other vector-memory
+        // instruction (FP8 rowwise: no scale loads; no register spills).
+        constexpr bool kAsmDma = TL::kSlots == 4;
+        static_assert(!kAsmDma || !F::kMX, "assembly ring loads: FP8 rowwise only");
         auto issue_stage = [&](int kt, uint8_t* slot) {
             const uint8_t* ak = a_base + (int64_t)kt * SB;
             const uint8_t* bk = b_base + (int64_t)kt * SB;
             const int rb = kLeanOffsets ? (int)opaque((uint32_t)r0) : r0;
 #pragma unroll
-            for (int j = 0; j < A_J; ++j)
-                __builtin_amdgcn_global_load_lds(
-                    (gptr_t)(ak + (kLeanOffsets ? op_off(rb, j, rows_in) : opaque(a_off[j]))),
-                    (lptr_t)(slot + (wave + NW * j) * 1024), 16, 0, 0);
+            for (int j = 0; j < A_J; ++j) {
+                const uint32_t off = kLeanOffsets ? op_off(rb, j, rows_in) : opaque(a_off[j]);
+                if constexpr (kAsmDma)
+                    lds_dma16<false>(ak, off, lds_addr(slot + (wave + NW * j) * 1024));
+                else
+                    __builtin_amdgcn_global_load_lds((gptr_t)(ak + off), (lptr_t)(slot + (wave + NW * j) * 1024), 16,
+                                                     0, 0);
+            }
 #pragma unroll
-            for (int j = 0; j < B_J; ++j)
-                __builtin_amdgcn_global_load_lds(
-                    (gptr_t)(bk + (kLeanOffsets ? op_off(rb, j, cols_in) : opaque(b_off[j]))),
-                    (lptr_t)(slot + kAStage + (wave + NW * j) * 1024), 16, 0, kBPolicy);
+            for (int j = 0; j < B_J; ++j) {
+                const uint32_t off = kLeanOffsets ? op_off(rb, j, cols_in) : opaque(b_off[j]);
+                if constexpr (kAsmDma)
+                    lds_dma16<TL::kStreamB>(bk, off, lds_addr(slot + kAStage + (wave + NW * j) * 1024));
+                else
+                    __builtin_amdgcn_global_load_lds((gptr_t)(bk + off),
+                                                     (lptr_t)(slot + kAStage + (wave + NW * j) * 1024), 16, 0,
+                                                     kBPolicy);
+            }
         };
         // The partial last stage: VGPR loads with the K tail zero-filled.
         uint4 ta[A_J], tb[B_J];

@@ -140,6 +140,52 @@ __device__ __forceinline__ void stage_barrier() {
 typedef const void __attribute__((address_space(1)))* gptr_t;
 typedef void __attribute__((address_space(3)))* lptr_t;
 
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(size_t)(const void __attribute__((address_space(3)))*)p;
+}
+
+// A direct-to-LDS load, 16 bytes per lane (global_load_lds_dwordx4), issued
+// from inline assembly for the four-slot ring.  The compiler then does not
+// see an LDS write and adds no waits of its own before LDS reads (with the
+// builtin, its alias tracking of the loads in flight gave up at the ring
+// loop's head and drained them before every fourth stage); the ring's
+// counted vmcnt waits and barriers order the reads instead, so such a K
+// loop must issue no other vector-memory instruction.  base: wave-uniform
+// global address; voff: this lane's byte offset from it; lds: wave-uniform
+// LDS address of the 1 KiB the wave's 64 lanes fill (lane l at lds + 16 l).
+// M0 carries the LDS address and is restored afterwards; the s_nop gives the
+// M0 write and an SGPR operand written by a vector instruction just before
+// their wait states.  Only the saved copy of M0 is written (by a scalar
+// move, at once).
+template <bool NT>
+__device__ __forceinline__ void lds_dma16(const void* base_in, uint32_t voff, uint32_t lds_in) {
+    // the operands are wave-uniform; read them from the first lane so that
+    // they sit in scalar registers whatever the compiler can prove (the
+    // builtin returns int: each half goes through uint32_t, so the low half
+    // is not sign-extended into the high one)
+    const uint64_t b = (uint64_t)base_in;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+    const uint64_t base = ((uint64_t)hi << 32) | (uint64_t)lo;
+    const uint32_t lds = (uint32_t)__builtin_amdgcn_readfirstlane(lds_in);
+    uint32_t saved_m0;
+    if constexpr (NT)
+        __asm__ volatile(
+            "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 4\n\t"
+            "global_load_lds_dwordx4 %1, %2 nt\n\ts_mov_b32 m0, %0"
+            : "=&s"(saved_m0)
+            : "v"(voff), "s"(base), "s"(lds)
+            : "memory");
+    else
+        __asm__ volatile(
+            "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 4\n\t"
+            "global_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
+            : "=&s"(saved_m0)
+            : "v"(voff), "s"(base), "s"(lds)
+            : "memory");
+}
+
 // Cache-policy operand of the direct global -> LDS load: the nontemporal bit
 // (the line is marked to be replaced first; data still comes through L2).
 constexpr int kCpolNT = 2;
