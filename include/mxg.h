@@ -367,8 +367,8 @@ mxg_status mx_silu_quantize(const void* h_bf16, void* y_q, void* y_scales, const
  * mx_grouped_quantize_nvfp4 -- per-expert dynamic quantization of BF16 rows to
  * NVFP4.
  * (NvMxf4f8Strategy, is_nvfp4 and grouped_quantize(input_scale);
- *  grouped_quantize_dynamic_scaled_fp4_async_kernel, Args: sf_tensor, the
- *  per-expert tensor-wise scale factor.  The pages name the format and the
+ *  grouped_quantize_dynamic_scaled_fp4_async_kernel, Args: sf_tensor, one
+ *  tensor-level scale for each expert.  The pages name the format and the
  *  scale without their arithmetic; the reading taken here follows.)
  *
  *   x_bf16         [total_rows, K] bf16 input.
