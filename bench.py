@@ -31,6 +31,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -180,13 +181,24 @@ def algorithmic_gemm_bytes(w, counts, K, N, T, fmt):
     return a + b + out
 
 
+def code_text(src):
+    """Source text without comments and blank or trailing space, so that the
+    hash below follows the code only (the sources hold no comment markers
+    inside string literals)."""
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    return "\n".join(l.rstrip() for l in src.splitlines() if l.strip())
+
+
 def kernel_sources_sha():
+    """Hash of the library's code (comments excluded): the committed counter
+    summaries carry the value they were taken with."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "fp4_grouped_gemm_quantize_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
             h.update(name.encode())
-            h.update(f.read())
+            h.update(code_text(f.read()).encode())
     return h.hexdigest()
 
 

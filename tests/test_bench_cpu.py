@@ -96,3 +96,11 @@ def test_report_helpers():
     assert s == {"mean": 4.0, "median": 2.5, "min": 1.0}
     info = bench.cpu_info()
     assert info["nproc"] >= 1 and info["affinity"] >= 1 and "cpu_model" in info
+
+
+def test_kernel_hash_follows_code_not_comments():
+    a = "int f(int x) {  // the slot\n    /* two\n       lines */ return x + 1;\n}\n"
+    b = "int f(int x) {  // another note\n\n    /* changed */ return x + 1;   \n}\n"
+    c = "int f(int x) {\n    return x + 2;\n}\n"
+    assert bench.code_text(a) == bench.code_text(b) == "int f(int x) {\n     return x + 1;\n}"
+    assert bench.code_text(a) != bench.code_text(c)
