@@ -190,12 +190,17 @@ def code_text(src):
     return "\n".join(l.rstrip() for l in src.splitlines() if l.strip())
 
 
+# the sources the grouped GEMM kernel is compiled from (the kernel whose HBM
+# traffic the counter summaries record)
+GEMM_SOURCES = ("gemm.hip", "gemm_common.h", "mxg_device.h", "mxg_internal.h")
+
+
 def kernel_sources_sha():
-    """Hash of the library's code (comments excluded): the committed counter
-    summaries carry the value they were taken with."""
+    """Hash of the GEMM kernel's code (comments excluded): the committed
+    counter summaries carry the value they were taken with."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "fp4_grouped_gemm_quantize_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in GEMM_SOURCES:
         with open(os.path.join(csrc, name), encoding="utf-8") as f:
             h.update(name.encode())
             h.update(code_text(f.read()).encode())

@@ -433,15 +433,26 @@ __global__ __launch_bounds__(kThreads) void silu_quantize_nv_kernel(const uint16
 }
 
 // Persistent grid: as many blocks as can be resident, at most one wave per
-// work unit (row, or row segment).
-template <class Kern>
-int64_t persistent_grid(Kern kernel, int64_t units) {
-    int dev = 0, cus = 0, occ = 0;
+// work unit (row, or row segment).  The resident count of each kernel is
+// asked of the runtime once per device and thread rather than at every
+// launch.
+template <auto KERNEL>
+int64_t persistent_grid(int64_t units) {
+    static thread_local int cached_dev = -1;
+    static thread_local int64_t cached_cap = 0;
+    int dev = 0;
     int64_t cap = 2048;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, kThreads, 0) == hipSuccess && cus > 0)
-        cap = (int64_t)cus * (occ > 0 ? occ : 1);
+    if (hipGetDevice(&dev) == hipSuccess) {
+        if (dev != cached_dev) {
+            int cus = 0, occ = 0;
+            if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+                hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, KERNEL, kThreads, 0) == hipSuccess && cus > 0) {
+                cached_cap = (int64_t)cus * (occ > 0 ? occ : 1);
+                cached_dev = dev;
+            }
+        }
+        if (dev == cached_dev) cap = cached_cap;
+    }
     const int64_t need = (units + kWavesPerBlock - 1) / kWavesPerBlock;
     return need < cap ? need : cap;
 }
@@ -455,7 +466,8 @@ hipError_t launch_rows(const uint16_t* x, uint8_t* q, void* s, const uint32_t* o
     const int64_t nseg = FMT == 0 ? 1 : (K + kSeg - 1) / kSeg;
     auto kernel = quantize_rows_kernel<FMT, NC, GATHER, SCATTER>;
     const int64_t rows = SCATTER ? sc.ntok : T;
-    hipLaunchKernelGGL(kernel, dim3((unsigned)persistent_grid(kernel, rows * nseg)), dim3(kThreads), 0, stream, x, q,
+    const int64_t grid = persistent_grid<quantize_rows_kernel<FMT, NC, GATHER, SCATTER>>(rows * nseg);
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, x, q,
                        s, off, G, T, K, (int)nseg, ga, nv, pd, sc);
     return hipGetLastError();
 }
@@ -485,7 +497,8 @@ hipError_t launch_fmt(const uint16_t* x, uint8_t* q, void* s, const uint32_t* of
             return hipErrorInvalidValue;  // token rows past 8192 elements (refused by the C ABI before this)
         } else {
             auto kernel = quantize_long_kernel<GATHER>;
-            hipLaunchKernelGGL(kernel, dim3((unsigned)persistent_grid(kernel, T)), dim3(kThreads), 0, stream, x, q, s,
+            hipLaunchKernelGGL(kernel, dim3((unsigned)persistent_grid<quantize_long_kernel<GATHER>>(T)), dim3(kThreads),
+                               0, stream, x, q, s,
                                off, G, T, K, ga, pd);
             return hipGetLastError();
         }
@@ -559,7 +572,7 @@ hipError_t launch_quantize_nvfp4_padded(const void* x, void* q, void* scales, co
 
 hipError_t launch_silu_quantize(const void* h, void* yq, void* ys, const uint32_t* off, int G, int64_t T,
                                 int64_t I, hipStream_t stream) {
-    hipLaunchKernelGGL(silu_quantize_kernel, dim3((unsigned)persistent_grid(silu_quantize_kernel, T)), dim3(kThreads),
+    hipLaunchKernelGGL(silu_quantize_kernel, dim3((unsigned)persistent_grid<silu_quantize_kernel>(T)), dim3(kThreads),
                        0, stream, static_cast<const uint16_t*>(h), static_cast<uint8_t*>(yq), static_cast<uint8_t*>(ys),
                        off, G, T, I);
     return hipGetLastError();
@@ -567,7 +580,7 @@ hipError_t launch_silu_quantize(const void* h, void* yq, void* ys, const uint32_
 
 hipError_t launch_silu_quantize_nvfp4(const void* h, void* yq, void* ys, const float* y_sf, const uint32_t* off,
                                       const int32_t* ids, int G, int E, int64_t T, int64_t I, hipStream_t stream) {
-    hipLaunchKernelGGL(silu_quantize_nv_kernel, dim3((unsigned)persistent_grid(silu_quantize_nv_kernel, T)),
+    hipLaunchKernelGGL(silu_quantize_nv_kernel, dim3((unsigned)persistent_grid<silu_quantize_nv_kernel>(T)),
                        dim3(kThreads), 0, stream, static_cast<const uint16_t*>(h), static_cast<uint8_t*>(yq),
                        static_cast<uint8_t*>(ys), off, G, T, I, NvScales{ids, y_sf, E});
     return hipGetLastError();
