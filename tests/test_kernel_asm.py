@@ -72,7 +72,7 @@ def test_ring_loads_take_a_scalar_base_built_from_its_halves(kernels):
         for i, l in enumerate(body):
             if "global_load_lds" not in l:
                 continue
-            m = re.search(r"global_load_lds_dwordx4\s+v\d+,\s*s\[(\d+):(\d+)\]", l)
+            m = re.search(r"global_load_lds_dword(?:x4)?\s+v\d+,\s*s\[(\d+):(\d+)\]", l)
             assert m, (tile, l.strip())
             lo, hi = int(m.group(1)), int(m.group(2))
             assert hi == lo + 1
