@@ -34,7 +34,8 @@ EXPORTED = ("mx_grouped_quantize", "mx_grouped_quantize_gather", "mx_grouped_qua
             "mx_silu_quantize", "mx_moe_combine", "mx_grouped_quantize_nvfp4", "mx_grouped_matmul_nvfp4",
             "mx_grouped_matmul_swiglu_nvfp4", "mx_silu_quantize_nvfp4", "mx_grouped_quantize_padded",
             "mx_grouped_matmul_padded", "mx_grouped_matmul_swiglu_padded",
-            "mx_grouped_quantize_nvfp4_padded", "mx_grouped_matmul_nvfp4_padded", "mxg_clock_probe",
+            "mx_grouped_quantize_nvfp4_padded", "mx_grouped_matmul_nvfp4_padded", "mx_prepared_weights_bytes",
+            "mx_prepare_weights_fp8", "mx_grouped_matmul_prepared", "mxg_clock_probe",
             "mxg_validation_message", "mxg_routing_violation", "mxg_status_string")
 
 
@@ -89,6 +90,12 @@ def lib() -> ctypes.CDLL:
                                                      _I64, _I64, _I64, _P]
         L.mx_grouped_quantize_nvfp4_padded.restype = ctypes.c_int
         L.mx_grouped_matmul_nvfp4_padded.restype = ctypes.c_int
+        L.mx_prepared_weights_bytes.argtypes = [_I64, _I64, _I64]
+        L.mx_prepared_weights_bytes.restype = ctypes.c_int64
+        L.mx_prepare_weights_fp8.argtypes = [_P, _I32, _I64, _I64, _P, _P]
+        L.mx_prepare_weights_fp8.restype = ctypes.c_int
+        L.mx_grouped_matmul_prepared.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I64, _I64, _I64, _P]
+        L.mx_grouped_matmul_prepared.restype = ctypes.c_int
         L.mxg_validation_message.argtypes = []
         L.mxg_validation_message.restype = ctypes.c_char_p
         L.mxg_routing_violation.argtypes = [_P, _P, _I32, _I32, _I64, ctypes.c_char_p, _I64]
@@ -409,6 +416,54 @@ def mx_grouped_matmul(fmt: int, a_q, a_scales, b_q, b_scales, c, row_offsets, ex
                                    int(max_rows_per_group_hint), _stream(a_q)), "mx_grouped_matmul")
 
 
+def prepared_weights_bytes(num_experts: int, N: int, K: int) -> int:
+    """Bytes of FP8 rowwise weights [E, N, K] in the prepared layout (-1: not preparable)."""
+    return int(lib().mx_prepared_weights_bytes(int(num_experts), int(N), int(K)))
+
+
+def mx_prepare_weights_fp8(b_q, b_prepared) -> None:
+    """FP8 rowwise weights b_q u8 [E, N, K] (K a multiple of 64) into b_prepared, a u8
+    tensor of prepared_weights_bytes(E, N, K) bytes: the layout the prepared GEMM reads."""
+    _expect(b_q, "b_q", _U8)
+    if b_q.dim() != 3:
+        raise ValueError("b_q must be [num_experts, N, K]")
+    E, N, K = b_q.shape
+    n = prepared_weights_bytes(E, N, K)
+    if n < 0:
+        raise ValueError(f"weights [{E}, {N}, {K}] cannot be prepared (K must be a multiple of 64)")
+    _expect(b_prepared, "b_prepared", _U8, None, b_q.device)
+    if b_prepared.numel() != n or not b_prepared.is_contiguous():
+        raise ValueError(f"b_prepared must be a contiguous u8 tensor of {n} bytes")
+    _check(lib().mx_prepare_weights_fp8(_ptr(b_q), E, N, K, _ptr(b_prepared), _stream(b_q)),
+           "mx_prepare_weights_fp8")
+
+
+def mx_grouped_matmul_prepared(a_q, a_scales, b_prepared, b_scales, c, row_offsets, expert_ids) -> None:
+    """mx_grouped_matmul (FP8 rowwise) with the weights in the prepared layout; E and N
+    come from b_scales [E, N], K from a_q [T, K]."""
+    _expect(a_q, "a_q", _U8)
+    dev = a_q.device
+    T, K = a_q.shape
+    _expect(b_scales, "b_scales", _F32, None, dev)
+    if b_scales.dim() != 2:
+        raise ValueError("b_scales must be [num_experts, N]")
+    E, N = b_scales.shape
+    n = prepared_weights_bytes(E, N, K)
+    if n < 0:
+        raise ValueError(f"no prepared layout for [{E}, {N}, {K}] (K must be a multiple of 64)")
+    _expect(b_prepared, "b_prepared", _U8, None, dev)
+    if b_prepared.numel() != n or not b_prepared.is_contiguous():
+        raise ValueError(f"b_prepared must be a contiguous u8 tensor of {n} bytes")
+    _expect(a_scales, "a_scales", _F32, (T,), dev)
+    _expect(c, "c", _BF16, (T, N), dev)
+    _expect(row_offsets, "row_offsets", _U32, None, dev)
+    G = row_offsets.numel() - 1
+    _expect(expert_ids, "expert_ids", _I32T, (G,), dev)
+    _check(lib().mx_grouped_matmul_prepared(_ptr(a_q), _ptr(a_scales), _ptr(b_prepared), _ptr(b_scales), _ptr(c),
+                                            _ptr(row_offsets), _ptr(expert_ids), G, E, T, N, K, _stream(a_q)),
+           "mx_grouped_matmul_prepared")
+
+
 def mx_grouped_matmul_swiglu(fmt: int, a_q, a_scales, w_q, w_scales, y_q, y_scales, row_offsets, expert_ids,
                              max_rows_per_group_hint: int = 0) -> None:
     """Fused gate/up grouped GEMM + SwiGLU + MXFP4 requant into y_q [T, I/2], y_scales [T, I/32]."""
@@ -532,6 +587,24 @@ def quantize_weights(fmt: int, w):
     if fmt == FP8_ROWWISE:
         return q.reshape(E, N, -1), s.reshape(E, N)
     return q.reshape(E, N, -1), s.reshape(E, N, K // 32)
+
+
+def prepare_weights_fp8(b_q):
+    """Allocating form of mx_prepare_weights_fp8: returns the prepared weights (flat u8)."""
+    E, N, K = b_q.shape
+    n = prepared_weights_bytes(E, N, K)
+    if n < 0:
+        raise ValueError(f"weights [{E}, {N}, {K}] cannot be prepared (K must be a multiple of 64)")
+    out = torch.empty((n,), dtype=torch.uint8, device=b_q.device)
+    mx_prepare_weights_fp8(b_q, out)
+    return out
+
+
+def grouped_matmul_prepared(a_q, a_scales, b_prepared, b_scales, row_offsets, expert_ids):
+    T = a_q.shape[0]
+    c = torch.empty((T, b_scales.shape[1]), dtype=torch.bfloat16, device=a_q.device)
+    mx_grouped_matmul_prepared(a_q, a_scales, b_prepared, b_scales, c, row_offsets, expert_ids)
+    return c
 
 
 def quantize_nvfp4(x, row_offsets, expert_ids, tensor_scales):

@@ -272,6 +272,43 @@ mxg_status mx_grouped_matmul(mxg_format fmt, const void* a_q, const void* a_scal
     return launch_gemm_checked(p, stream);
 }
 
+// E * ceil(N / 256) * 256 * K fits in int64
+static bool prepared_size_fits(int64_t num_experts, int64_t N, int64_t K) {
+    const int64_t rows = (N + 255) / 256 * 256;
+    return rows <= INT64_MAX / num_experts && rows * num_experts <= INT64_MAX / K;
+}
+
+int64_t mx_prepared_weights_bytes(int64_t num_experts, int64_t N, int64_t K) {
+    if (num_experts <= 0 || N <= 0 || K <= 0 || K % 64 != 0) return -1;
+    if (N > INT32_MAX / 2 || K > INT32_MAX / 2 || !prepared_size_fits(num_experts, N, K)) return -1;
+    return mxg::prepared_weights_bytes(num_experts, N, K);
+}
+
+mxg_status mx_prepare_weights_fp8(const void* b_q, int32_t num_experts, int64_t N, int64_t K, void* b_prepared,
+                                  hipStream_t stream) {
+    if (num_experts <= 0 || N <= 0 || K <= 0) return MXG_ERROR_INVALID_VALUE;
+    if (K % 64 != 0 || N > INT32_MAX / 2 || K > INT32_MAX / 2 || !prepared_size_fits(num_experts, N, K))
+        return MXG_ERROR_NOT_SUPPORTED;
+    if (!b_q || !b_prepared || !aligned(b_q, 16) || !aligned(b_prepared, 16)) return MXG_ERROR_INVALID_VALUE;
+    return from_hip(mxg::launch_prepare_weights(b_q, num_experts, N, K, b_prepared, stream));
+}
+
+mxg_status mx_grouped_matmul_prepared(const void* a_q, const void* a_scales, const void* b_prepared,
+                                      const void* b_scales, void* c_bf16, const uint32_t* row_offsets,
+                                      const int32_t* expert_ids, int32_t num_groups, int32_t num_experts,
+                                      int64_t total_rows, int64_t N, int64_t K, hipStream_t stream) {
+    mxg_status st = check_gemm_common(MXG_FP8_E4M3_ROWWISE, a_q, a_scales, b_prepared, b_scales, row_offsets,
+                                      expert_ids, num_groups, num_experts, total_rows, N, K);
+    if (st != MXG_SUCCESS) return st;
+    if (K % 64 != 0) return MXG_ERROR_NOT_SUPPORTED;
+    if (total_rows == 0 || num_groups == 0) return MXG_SUCCESS;
+    if (!c_bf16 || !aligned(c_bf16, 16)) return MXG_ERROR_INVALID_VALUE;
+    mxg::GemmProblem p{0, a_q, a_scales, b_prepared, b_scales, c_bf16, nullptr, nullptr, row_offsets, expert_ids,
+                       num_groups, num_experts, total_rows, N, K, 0};
+    p.b_prepared = true;
+    return launch_gemm_checked(p, stream);
+}
+
 mxg_status mx_grouped_matmul_nvfp4(const void* a_q, const void* a_scales, const void* b_q, const void* b_scales,
                                    const float* expert_scales, void* c_bf16, const uint32_t* row_offsets,
                                    const int32_t* expert_ids, int32_t num_groups, int32_t num_experts,

@@ -71,10 +71,13 @@ namespace {
 // of its expert at about the same time and then never again (measured on
 // the decode-shaped workload: 157-164 -> 141-146 us; the large tiles, whose
 // weight panels are re-read from L2, were slower with it).
-template <int BM_, int BN_, int WGM_, int WGN_, int SLOTS_ = 3, int MINB_ = 1, bool STREAM_B_ = false, int SB_ = 128>
+// BPREP: the weights come in the prepared layout (see prepare_weights_kernel).
+template <int BM_, int BN_, int WGM_, int WGN_, int SLOTS_ = 3, int MINB_ = 1, bool STREAM_B_ = false, int SB_ = 128,
+          bool BPREP_ = false>
 struct Tile {
     static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_, kMinBlocks = MINB_, kSlots = SLOTS_;
     static constexpr int kSB = SB_;
+    static constexpr bool kBPrep = BPREP_;
     // direct-to-LDS loads: 16 bytes per lane, kLPR lanes per stage row, so one
     // wave instruction (1 KiB) covers kRPI rows
     static constexpr int kLPR = SB_ / 16, kRPI = 64 / kLPR;
@@ -387,7 +390,13 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
         static_assert(NW % 2 == 0, "per-lane chunk independent of the load index");
         constexpr bool kLeanOffsets = F::kMX && NW >= 8;
         const uint8_t* a_base = args.a + m0 * row_bytes;
-        const uint8_t* b_base = args.b + ((int64_t)e * args.N + n0) * row_bytes;
+        // Prepared weights: the tile's stage kt is the 256 x 64-byte image at
+        // ((e * ntiles_n + n0 / BN) * nkt + kt) * BN * SB (a half tile starts
+        // at its row n0 % BN of it); one load instruction reads 1 KiB of it.
+        static_assert(!TL::kBPrep || (TL::kSlots == 4 && !F::kMX && SB == 64), "prepared weights: FP8 ring");
+        const uint8_t* b_base =
+            TL::kBPrep ? args.b + ((int64_t)e * args.ntiles_n + n0 / BN) * nkt * (int64_t)(BN * SB) + (n0 % BN) * SB
+                       : args.b + ((int64_t)e * args.N + n0) * row_bytes;
         const int r0 = wave * kRPI + lane / kLPR;
         const uint32_t chunk16 = (uint32_t)swz_chunk<SB>(r0, lane % kLPR) << 4;
         const uint32_t rb32 = (uint32_t)row_bytes;
@@ -418,7 +427,7 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
         static_assert(!kAsmDma || !F::kMX, "assembly ring loads: FP8 rowwise only");
         auto issue_stage = [&](int kt, uint8_t* slot) {
             const uint8_t* ak = a_base + (int64_t)kt * SB;
-            const uint8_t* bk = b_base + (int64_t)kt * SB;
+            const uint8_t* bk = b_base + (int64_t)kt * (TL::kBPrep ? BN * SB : SB);
             const int rb = kLeanOffsets ? (int)opaque((uint32_t)r0) : r0;
 #pragma unroll
             for (int j = 0; j < A_J; ++j) {
@@ -431,7 +440,13 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
             }
 #pragma unroll
             for (int j = 0; j < B_J; ++j) {
-                const uint32_t off = kLeanOffsets ? op_off(rb, j, cols_in) : opaque(b_off[j]);
+                uint32_t off = kLeanOffsets ? op_off(rb, j, cols_in) : opaque(b_off[j]);
+                if constexpr (TL::kBPrep) {
+                    // blocks wholly past the tile's columns re-read its last real block
+                    const int q = wave + NW * j;
+                    const int qe = q * kRPI < cols_in ? q : (cols_in - 1) / kRPI;
+                    off = opaque((uint32_t)(qe * 1024 + lane * 16));
+                }
                 if constexpr (kAsmDma)
                     lds_dma16<TL::kStreamB>(bk, off, lds_addr(slot + kAStage + (wave + NW * j) * 1024));
                 else
@@ -841,6 +856,7 @@ hipError_t launch_tile(const GemmProblem& p, hipStream_t stream, int mband) {
 // three slots, or 32 x 64 / 32 x 128 with two were slower), MX 32 x 128 with
 // three slots.
 using TileLargeFp8 = Tile<256, 256, 2, 4, 4, 1, false, 64>;   // whole 64-byte stages
+using TileLargeFp8Prep = Tile<256, 256, 2, 4, 4, 1, false, 64, true>;  // the same, prepared weights
 using TileLargeFp8Tail = Tile<256, 256, 2, 4, 2>;              // K bytes not a multiple of 128
 using TileLargeMx = Tile<128, 256, 2, 2, 3>;
 using TileLargeMxKA = Tile<128, 256, 2, 2, 2>;
@@ -850,6 +866,33 @@ using TileSmall = Tile<32, 128, 1, 4, 3, 1, true>;
 using TileSmallFp8 = Tile<32, 256, 1, 4, 2, 1, true>;
 constexpr int kBandLarge = 4, kBandMx = 8, kBandNOuter = 1 << 30;
 constexpr int64_t kTallRows = 384;
+
+// Prepared weights (FP8 rowwise, K a multiple of 64): element (e, n, k) of the
+// [E, N, K] codes goes to tile nt = n / 256, stage kt = k / 64, row r = n % 256
+// of a 256 x 64-byte block -- the block the four-slot ring copies to LDS as it
+// is -- at byte r * 64 + 16 * swz_chunk<64>(r, (k % 64) / 16) + k % 16, the
+// blocks ordered (e, nt, kt); rows past N are zero.  One 16-byte piece per
+// thread.
+__global__ __launch_bounds__(256) void prepare_weights_kernel(const uint8_t* __restrict__ b, int64_t E, int64_t N,
+                                                              int64_t K, uint8_t* __restrict__ out) {
+    constexpr int BN = TileLargeFp8Prep::BN, SB = TileLargeFp8Prep::kSB;
+    const int64_t ntn = (N + BN - 1) / BN, nkt = K / SB;
+    const int64_t pieces = E * ntn * nkt * BN * (SB / 16);
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < pieces; i += (int64_t)gridDim.x * blockDim.x) {
+        const int p = (int)(i % (SB / 16));  // position of the piece in its row
+        const int64_t rowi = i / (SB / 16);
+        const int r = (int)(rowi % BN);
+        const int64_t blk = rowi / BN;  // (e * ntn + nt) * nkt + kt
+        const int64_t kt = blk % nkt, ent = blk / nkt;
+        const int64_t nt = ent % ntn, e = ent / ntn;
+        const int64_t n = nt * BN + r;
+        // the position holds the global piece whose swizzled position it is
+        const int c = swz_chunk<SB>(r, p);
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (n < N) v = *reinterpret_cast<const uint4*>(b + (e * N + n) * K + kt * SB + c * 16);
+        *reinterpret_cast<uint4*>(out + i * 16) = v;
+    }
+}
 
 template <int FMT, bool SWIGLU>
 hipError_t launch_fmt(const GemmProblem& p, hipStream_t stream) {
@@ -936,6 +979,11 @@ GemmArgs make_args(const GemmProblem& p, int BM, int BN, int mband, int per_cu, 
 
 hipError_t launch_grouped_gemm(const GemmProblem& p, hipStream_t stream) {
     const bool swiglu = p.yq != nullptr;
+    if (p.b_prepared) {
+        // the ring that reads prepared weights, whatever the rows per group
+        if (p.fmt != 0 || swiglu || p.K % TileLargeFp8Prep::kSB != 0) return hipErrorInvalidValue;
+        return launch_tile<TileLargeFp8Prep, 0, false, true>(p, stream, kBandLarge);
+    }
     switch (p.fmt) {
         case 0:
             return launch_fmt<0, false>(p, stream);
@@ -948,6 +996,24 @@ hipError_t launch_grouped_gemm(const GemmProblem& p, hipStream_t stream) {
         default:
             return hipErrorInvalidValue;
     }
+}
+
+int64_t prepared_weights_bytes(int64_t E, int64_t N, int64_t K) {
+    constexpr int BN = TileLargeFp8Prep::BN;
+    return E * ((N + BN - 1) / BN) * BN * K;
+}
+
+hipError_t launch_prepare_weights(const void* b, int64_t E, int64_t N, int64_t K, void* out, hipStream_t stream) {
+    if (K % TileLargeFp8Prep::kSB != 0) return hipErrorInvalidValue;
+    const int64_t pieces = prepared_weights_bytes(E, N, K) / 16;
+    if (pieces <= 0) return hipSuccess;
+    const int cus = gemm::device_cus();
+    int64_t blocks = (pieces + 255) / 256;
+    const int64_t cap = (int64_t)(cus > 0 ? cus : 256) * 8;
+    if (blocks > cap) blocks = cap;
+    hipLaunchKernelGGL(prepare_weights_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       static_cast<const uint8_t*>(b), E, N, K, static_cast<uint8_t*>(out));
+    return hipGetLastError();
 }
 
 }  // namespace mxg

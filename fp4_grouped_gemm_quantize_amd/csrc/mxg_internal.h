@@ -70,9 +70,15 @@ struct GemmProblem {
     const float* ysf;  // NVFP4 fused: per-expert encode-side tensor scale of y, fp32 [E]
     const uint32_t* asoff;  // padded A scales: group g's rows from row asoff[g] (nullptr: dense)
     int64_t as_rows;        // rows of that scale tensor
+    bool b_prepared;        // FP8 rowwise: b holds the prepared weights (launch_prepare_weights)
 };
 
 hipError_t launch_grouped_gemm(const GemmProblem& p, hipStream_t stream);
+
+// FP8 rowwise weights [E, N, K] (K a multiple of 64) into the layout the
+// GEMM's four-slot ring loads as it is; out holds prepared_weights_bytes(E, N, K).
+int64_t prepared_weights_bytes(int64_t E, int64_t N, int64_t K);
+hipError_t launch_prepare_weights(const void* b, int64_t E, int64_t N, int64_t K, void* out, hipStream_t stream);
 
 // One wave: out[0] = shader-clock ticks, out[1] = 100 MHz ticks (>= ticks) of one sleep window.
 hipError_t launch_clock_probe(unsigned long long* out, unsigned long long ticks, hipStream_t stream);

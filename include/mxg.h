@@ -26,6 +26,10 @@
  *                             MX / NVFP4 quantize, GEMM (and MX fused GEMM) with
  *                             the activation scales in a padded or expert-slot
  *                             layout
+ *   mx_prepare_weights_fp8, mx_prepared_weights_bytes, mx_grouped_matmul_prepared
+ *                             FP8 rowwise weights rearranged once into the
+ *                             layout the GEMM's load ring copies as it is, and
+ *                             the grouped GEMM that reads them
  *   mx_grouped_quantize_scatter  the same in token-major form: each token row
  *                             is read once and stored to its routed rows
  *   mx_moe_combine            after the down-projection: each token's row is the
@@ -229,6 +233,51 @@ mxg_status mx_grouped_matmul(mxg_format fmt, const void* a_q, const void* a_scal
                              const int32_t* expert_ids, int32_t num_groups, int32_t num_experts,
                              int64_t total_rows, int64_t N, int64_t K, int64_t max_rows_per_group_hint,
                              hipStream_t stream);
+
+/*
+ * mx_prepare_weights_fp8, mx_prepared_weights_bytes,
+ * mx_grouped_matmul_prepared -- FP8 rowwise expert weights rearranged once
+ * into the layout the GEMM's load ring copies to LDS as it is, and the grouped
+ * GEMM that reads them.  (The counterpart here of the weight preparation step
+ * of NvMxf4f8Strategy, prepare_weight_scales(), which rearranges weight
+ * scales into its kernel's layout; the arithmetic is mx_grouped_matmul's.)
+ *
+ * The ring streams each row of a 256-column weight tile 64 bytes of K at a
+ * time; in the plain [E, N, K] layout each such piece is half a 128-byte line
+ * of its own row, and the per-request cost of the load path, not its bytes,
+ * sets the GEMM's pace.  Prepared, the 256 x 64-byte block of one tile and
+ * stage is contiguous (16 KiB, rows in the order and 16-byte piece order the
+ * ring places them in LDS), so each load instruction reads whole lines.
+ *
+ * mx_prepared_weights_bytes(E, N, K): bytes of the prepared weights,
+ *   E * ceil(N / 256) * 256 * K; -1 if E, N or K <= 0 or K % 64 != 0.
+ * mx_prepare_weights_fp8(b_q, E, N, K, b_prepared, stream): b_q [E, N, K] u8
+ *   e4m3 codes (K innermost, as mx_grouped_matmul takes them); b_prepared
+ *   receives mx_prepared_weights_bytes(E, N, K) bytes: for expert e, tile
+ *   nt = n / 256 and stage s = k / 64, block (e * ceil(N / 256) + nt) *
+ *   (K / 64) + s of 256 * 64 bytes; in it row r = n % 256 at byte 64 r, the
+ *   16-byte pieces of the row permuted as the ring's LDS swizzle permutes them
+ *   (piece position p holds piece p ^ ((r >> 2) & 3)).  Rows past N are zero.
+ *   The layout is private to this library: only mx_grouped_matmul_prepared
+ *   reads it.  Asynchronous on `stream`.
+ * mx_grouped_matmul_prepared(...): mx_grouped_matmul for MXG_FP8_E4M3_ROWWISE
+ *   with b_prepared in place of b_q; every other argument as there (no tile
+ *   hint: it always runs the 256 x 256 ring).  Results are bit-identical to
+ *   mx_grouped_matmul on the weights the prepared ones came from.
+ *
+ * Errors: INVALID_VALUE for null pointers, sizes <= 0 (total_rows /
+ * num_groups < 0), misalignment (codes, prepared weights and c on 16 bytes,
+ * scales on 4); NOT_SUPPORTED for K % 64 != 0, num_groups > MXG_MAX_GROUPS,
+ * N > INT32_MAX / 2 or total_rows > INT32_MAX.  total_rows or num_groups of
+ * 0 is a no-op.
+ */
+int64_t mx_prepared_weights_bytes(int64_t num_experts, int64_t N, int64_t K);
+mxg_status mx_prepare_weights_fp8(const void* b_q, int32_t num_experts, int64_t N, int64_t K, void* b_prepared,
+                                  hipStream_t stream);
+mxg_status mx_grouped_matmul_prepared(const void* a_q, const void* a_scales, const void* b_prepared,
+                                      const void* b_scales, void* c_bf16, const uint32_t* row_offsets,
+                                      const int32_t* expert_ids, int32_t num_groups, int32_t num_experts,
+                                      int64_t total_rows, int64_t N, int64_t K, hipStream_t stream);
 
 /*
  * mx_grouped_matmul_nvfp4 -- ragged grouped GEMM of NVFP4 operands.

@@ -112,6 +112,20 @@ int main() {
     CALL(MXG_ERROR_NOT_SUPPORTED, false,
          mx_grouped_matmul(F8, q, s, b, bs, c, off, ids, G, E, (int64_t)INT32_MAX + 1, N, K, 0, nullptr));
     CALL(MXG_ERROR_INVALID_VALUE, false, mx_grouped_matmul(F8, q, s, b, bs, c, off, ids, G, 0, T, N, K, 0, nullptr));
+    CALL(MXG_SUCCESS, true, mx_grouped_matmul_prepared(q, s, b, bs, c, off, ids, G, E, T, N, K, nullptr));
+    EXPECT(g_stub.gemm.b_prepared && g_stub.gemm.fmt == 0 && g_stub.gemm.b == b);
+    CALL(MXG_ERROR_NOT_SUPPORTED, false, mx_grouped_matmul_prepared(q, s, b, bs, c, off, ids, G, E, T, N, 96, nullptr));
+    CALL(MXG_ERROR_INVALID_VALUE, false, mx_grouped_matmul_prepared(q, s, odd, bs, c, off, ids, G, E, T, N, K, nullptr));
+    CALL(MXG_SUCCESS, false, mx_grouped_matmul_prepared(q, s, b, bs, c, off, ids, G, E, 0, N, K, nullptr));
+    EXPECT(mx_prepared_weights_bytes(E, N, K) == (int64_t)E * 256 * K);
+    EXPECT(mx_prepared_weights_bytes(E, N, 96) == -1 && mx_prepared_weights_bytes(0, N, K) == -1);
+    EXPECT(mx_prepared_weights_bytes(INT32_MAX, (int64_t)INT32_MAX / 2, (int64_t)INT32_MAX / 2 / 64 * 64) == -1);
+    CALL(MXG_SUCCESS, true, mx_prepare_weights_fp8(b, E, N, K, bs, nullptr));
+    EXPECT(strcmp(g_stub.last, "prepare_weights") == 0);
+    CALL(MXG_ERROR_NOT_SUPPORTED, false, mx_prepare_weights_fp8(b, E, N, 96, bs, nullptr));
+    CALL(MXG_ERROR_INVALID_VALUE, false, mx_prepare_weights_fp8(b, E, N, K, nullptr, nullptr));
+    CALL(MXG_ERROR_INVALID_VALUE, false, mx_prepare_weights_fp8(odd, E, N, K, bs, nullptr));
+    CALL(MXG_ERROR_INVALID_VALUE, false, mx_prepare_weights_fp8(b, 0, N, K, bs, nullptr));
     CALL(MXG_SUCCESS, true, mx_grouped_matmul_swiglu(MX4, q, s, b, bs, c, s, off, ids, G, E, T, I, K, 0, nullptr));
     EXPECT(g_stub.gemm.N == 2 * I && g_stub.gemm.yq == c);
     CALL(MXG_ERROR_NOT_SUPPORTED, false, mx_grouped_matmul_swiglu(F8, q, s, b, bs, c, s, off, ids, G, E, T, I, K, 0, nullptr));

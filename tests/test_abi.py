@@ -323,3 +323,25 @@ def test_nvfp4_padded_argument_errors():
         assert nm(**kw) == mxg.ERROR_INVALID_VALUE, kw
     assert nm(K=256) == mxg.ERROR_NOT_SUPPORTED
     assert nm(T=0) == mxg.SUCCESS
+
+
+def test_prepared_weights_size_and_argument_errors():
+    L = mxg.lib()
+    assert mxg.prepared_weights_bytes(3, 96, 128) == 3 * 256 * 128  # N rounded up to whole 256-row tiles
+    assert mxg.prepared_weights_bytes(2, 1536, 4096) == 2 * 1536 * 4096
+    assert mxg.prepared_weights_bytes(3, 96, 96) == -1   # K not a multiple of 64
+    assert mxg.prepared_weights_bytes(0, 96, 128) == -1
+    assert mxg.prepared_weights_bytes((1 << 31) - 1, 1 << 29, 1 << 29) == -1  # the size would not fit in int64
+    prep = L.mx_prepare_weights_fp8
+    assert prep(None, 3, 96, 128, FAKE, None) == mxg.ERROR_INVALID_VALUE
+    assert prep(FAKE, 3, 96, 128, None, None) == mxg.ERROR_INVALID_VALUE
+    assert prep(FAKE_ODD, 3, 96, 128, FAKE, None) == mxg.ERROR_INVALID_VALUE
+    assert prep(FAKE, 0, 96, 128, FAKE, None) == mxg.ERROR_INVALID_VALUE
+    assert prep(FAKE, 3, 96, 96, FAKE, None) == mxg.ERROR_NOT_SUPPORTED
+    mm = L.mx_grouped_matmul_prepared
+    assert mm(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 3, 4, 96, 96, None) == mxg.ERROR_NOT_SUPPORTED
+    assert mm(FAKE, FAKE, FAKE_ODD, FAKE, FAKE, FAKE, FAKE, 1, 3, 4, 96, 128, None) == mxg.ERROR_INVALID_VALUE
+    assert mm(FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 1, 3, 4, 96, 128, None) == mxg.ERROR_INVALID_VALUE
+    assert mm(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 0, 4, 96, 128, None) == mxg.ERROR_INVALID_VALUE
+    # no rows: nothing is read, written or launched
+    assert mm(None, None, None, None, None, None, None, 1, 3, 0, 96, 128, None) == mxg.SUCCESS

@@ -45,6 +45,7 @@ SMALL = {
     # (the four-slot pipeline's prologue and drain)
     "prefill_fp8_k960": W.WORKLOADS[3].scaled(tokens=160, E=16, N=384, K=960),
     "fp8_k64": W.WORKLOADS[3].scaled(tokens=96, E=8, top_k=3, N=256, K=64),
+    "fp8_k128": W.WORKLOADS[3].scaled(tokens=96, E=8, top_k=3, N=256, K=128),
     "fp8_k192": W.WORKLOADS[3].scaled(tokens=96, E=8, top_k=3, N=256, K=192),
     "mxfp8": W.WORKLOADS[4].scaled(rows=700, E=8, N=288, K=608),
     "mxfp4": W.WORKLOADS[5].scaled(tokens=96, E=16, N=256, K=1344),

@@ -23,7 +23,7 @@ HIPCC = "/opt/rocm/bin/hipcc"
 
 VMEM = re.compile(r"^\s*(global_load|global_store|global_atomic|buffer_|scratch_|flat_)")
 KERNEL = re.compile(r"^(_Z\S*grouped_gemm_kernel\S*):")
-TILE = re.compile(r"TileILi(\d+)ELi(\d+)ELi(\d)ELi(\d)ELi(\d)ELi(\d)ELb(\d)ELi(\d+)EEELi(\d)ELb(\d)ELb(\d)")
+TILE = re.compile(r"TileILi(\d+)ELi(\d+)ELi(\d)ELi(\d)ELi(\d)ELi(\d)ELb(\d)ELi(\d+)(?:ELb(\d))?EEELi(\d)ELb(\d)ELb(\d)")
 
 
 @pytest.fixture(scope="module")
@@ -55,8 +55,9 @@ def four_slot(kernels):
 
 def test_four_slot_kernels_exist(kernels):
     fs = four_slot(kernels)
-    # FP8 rowwise, 256 x 256 with 64-byte stages
-    assert len(fs) == 1 and list(fs)[0][:2] == ("256", "256"), sorted(fs)
+    # FP8 rowwise, 256 x 256 with 64-byte stages: row-major and prepared weights
+    assert len(fs) == 2 and all(k[:2] == ("256", "256") for k in fs), sorted(fs)
+    assert sorted(k[8] for k in fs) == ["0", "1"], sorted(fs)
 
 
 def test_no_other_vector_memory_among_the_ring_loads(kernels):
