@@ -32,7 +32,8 @@
 //    assembly (lds_dma16), so that the only waits before its fragment reads
 //    are the ring's own counted ones (4-5 % faster than with the builtin,
 //    whose load tracking made the compiler drain the ring every fourth
-//    stage).  The 16-byte chunks of a row are
+//    stage).  The 256 x 384 tile for prepared weights streams 64-byte
+//    stages through three slots (four would fill all of LDS), the same way.  The 16-byte chunks of a row are
 //    XOR-swizzled (see swz_chunk) so the 16-byte fragment reads of 16
 //    consecutive rows hit distinct bank groups; the swizzle is realised by
 //    choosing which global chunk each lane fetches.  A stage that runs past
@@ -60,6 +61,9 @@ namespace mxg {
 using namespace gemm;
 
 namespace {
+
+// Prepared weights come in blocks of 256 columns (prepare_weights_kernel).
+constexpr int kPrepRows = 256;
 
 // BM x BN output tile, WGM x WGN waves, SLOTS stages of LDS ring (2: one stage
 // in flight while one is consumed; 3: two; 4: three), SB K bytes per row per
@@ -245,6 +249,28 @@ __device__ __forceinline__ void mma_stage(const uint8_t* __restrict__ sa, const 
     }
     auto arow = [&](int i) { return wm * TL::WTM + i * 32 + r32; };
     auto brow = [&](int j) { return wn * TL::WTN + j * 32 + r32; };
+    if constexpr (kSteps == 1 && TL::kFragBufs == 1 && TN >= 3) {
+        // One K step per stage with a wide wave tile (its accumulators leave
+        // little room): the B fragments for the whole stage, the A fragments
+        // one row block ahead of the matrix cores.  The lane's row offsets are
+        // recomputed here from an opaque copy of its row index, so that no
+        // per-slot read address is held through the K loop.
+        uint32_t rl = (uint32_t)r32;
+        __asm__ volatile("" : "+v"(rl));
+        const int ra = wm * TL::WTM + (int)rl, rbw = wn * TL::WTN + (int)rl;
+        v8i bq[TN];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) bq[j] = load_frag<TL, FMT>(sb, 0, rbw + j * 32, h);
+        v8i a_cur = load_frag<TL, FMT>(sa, 0, ra, h);
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            v8i a_nxt;
+            if (i + 1 < TM) a_nxt = load_frag<TL, FMT>(sa, 0, ra + (i + 1) * 32, h);
+            mma_row<TL, FMT>(i, 0, a_cur, bq, wa, wb, acc);
+            if (i + 1 < TM) a_cur = a_nxt;
+        }
+        return;
+    }
     v8i af[TM], bf[2][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i) af[i] = load_frag<TL, FMT>(sa, 0, arow(i), h);
@@ -357,7 +383,7 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
 
     const WorkSplit ws = work_split(total_tiles, gridDim.x);
     for (int64_t W = xcd_remap(blockIdx.x, gridDim.x); W < ws.items; W += gridDim.x) {
-        const TileCoord tc = locate_item<BM, BN>(args, s_pre, ws, W);
+        const TileCoord tc = uniform_coord(locate_item<BM, BN>(args, s_pre, ws, W));
         if (tc.cols_in <= 0) continue;  // the empty second half of a last, narrow tile (uniform)
         const int e = tc.e;
         const int64_t m0 = tc.m0, n0 = tc.n0, n_end = tc.n_end;
@@ -393,10 +419,11 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
         // Prepared weights: the tile's stage kt is the 256 x 64-byte image at
         // ((e * ntiles_n + n0 / BN) * nkt + kt) * BN * SB (a half tile starts
         // at its row n0 % BN of it); one load instruction reads 1 KiB of it.
-        static_assert(!TL::kBPrep || (TL::kSlots == 4 && !F::kMX && SB == 64), "prepared weights: FP8 ring");
-        const uint8_t* b_base =
-            TL::kBPrep ? args.b + ((int64_t)e * args.ntiles_n + n0 / BN) * nkt * (int64_t)(BN * SB) + (n0 % BN) * SB
-                       : args.b + ((int64_t)e * args.N + n0) * row_bytes;
+        static_assert(!TL::kBPrep || (!F::kMX && SB == 64), "prepared weights: FP8 64-byte-stage ring");
+        const int64_t prep_ntn = (args.N + kPrepRows - 1) / kPrepRows;
+        const uint8_t* b_base = TL::kBPrep
+                                    ? args.b + ((int64_t)e * prep_ntn + n0 / kPrepRows) * nkt * (int64_t)(kPrepRows * SB)
+                                    : args.b + ((int64_t)e * args.N + n0) * row_bytes;
         const int r0 = wave * kRPI + lane / kLPR;
         const uint32_t chunk16 = (uint32_t)swz_chunk<SB>(r0, lane % kLPR) << 4;
         const uint32_t rb32 = (uint32_t)row_bytes;
@@ -423,11 +450,11 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
         // The four-slot ring issues its direct loads from inline assembly
         // (see lds_dma16): its K loop issues no other vector-memory
         // instruction (FP8 rowwise: no scale loads; no register spills).
-        constexpr bool kAsmDma = TL::kSlots == 4;
+        constexpr bool kAsmDma = SB == 64;
         static_assert(!kAsmDma || !F::kMX, "assembly ring loads: FP8 rowwise only");
         auto issue_stage = [&](int kt, uint8_t* slot) {
             const uint8_t* ak = a_base + (int64_t)kt * SB;
-            const uint8_t* bk = b_base + (int64_t)kt * (TL::kBPrep ? BN * SB : SB);
+            const uint8_t* bk = b_base + (int64_t)kt * (TL::kBPrep ? kPrepRows * SB : SB);
             const int rb = kLeanOffsets ? (int)opaque((uint32_t)r0) : r0;
 #pragma unroll
             for (int j = 0; j < A_J; ++j) {
@@ -442,10 +469,13 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
             for (int j = 0; j < B_J; ++j) {
                 uint32_t off = kLeanOffsets ? op_off(rb, j, cols_in) : opaque(b_off[j]);
                 if constexpr (TL::kBPrep) {
-                    // blocks wholly past the tile's columns re-read its last real block
+                    // load groups wholly past the tile's columns re-read its
+                    // last real group; a group lies in one 256-column block
+                    // (n0 and kRPI are multiples of 16)
+                    // (the lane term passes through the empty asm, the rest is uniform)
                     const int q = wave + NW * j;
-                    const int qe = q * kRPI < cols_in ? q : (cols_in - 1) / kRPI;
-                    off = opaque((uint32_t)(qe * 1024 + lane * 16));
+                    const int c = (int)(n0 % kPrepRows) + (q * kRPI < cols_in ? q : (cols_in - 1) / kRPI) * kRPI;
+                    off = opaque((uint32_t)lane * 16u) + (uint32_t)((c / kPrepRows) * nkt * (kPrepRows * SB) + (c % kPrepRows) * SB);
                 }
                 if constexpr (kAsmDma)
                     lds_dma16<TL::kStreamB>(bk, off, lds_addr(slot + kAStage + (wave + NW * j) * 1024));
@@ -699,51 +729,76 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
         // slots, then written out in coalesced 16-byte pieces -- or, fused,
         // requantized from there.
         constexpr int kRowsPerSlot = kStage / (BN * 2);
-        static_assert(kSlots * kRowsPerSlot >= BM, "staging tile must fit the LDS ring");
+        // one staging pass when the whole tile fits the ring, else two (half
+        // of every wave's row blocks each)
+        constexpr int kPasses = kSlots * kRowsPerSlot >= BM ? 1 : 2;
+        static_assert(kSlots * kRowsPerSlot >= BM / kPasses, "staging pass must fit the LDS ring");
+        static_assert(!SWIGLU || kPasses == 1, "fused epilogue: whole tile staged");
         auto srow = [&](int row) -> uint16_t* {
             uint8_t* base = row < kRowsPerSlot ? s_ring0 : row < 2 * kRowsPerSlot ? s_ring1
                           : row < 3 * kRowsPerSlot ? s_ring2 : s_ring3;
             return reinterpret_cast<uint16_t*>(base + (row % kRowsPerSlot) * BN * 2);
         };
         if constexpr (!SWIGLU) {
+            // The two-pass tile takes the lane indices through the empty asm
+            // here, so that its staging addresses are computed per tile, not
+            // hoisted out of the tile loop and held through the K loop.
+            const int eh = kPasses > 1 ? (int)opaque((uint32_t)h) : h;
+            const int e32 = kPasses > 1 ? (int)opaque((uint32_t)r32) : r32;
             // out = bf16((acc * a_scale[row]) * b_scale[col]) for FP8 rowwise,
             // bf16(acc * expert_scale[e]) for NVFP4
             auto value = [&](int i, int j, int r, float sbv) {
                 float v = acc[i][j][r];
-                if constexpr (kRowFactor) v = v * s_rowf[wm * WTM + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3)];
+                if constexpr (kRowFactor) v = v * s_rowf[wm * WTM + i * 32 + 8 * (r >> 2) + 4 * eh + (r & 3)];
                 if constexpr (!F::kMX) v = v * sbv;
                 return (uint16_t)f32_to_bf16(v);
             };
             auto b_scale = [&](int j) {
-                const int64_t col = n0 + wn * WTN + j * 32 + r32;
+                const int64_t col = n0 + wn * WTN + j * 32 + e32;
                 float sbv = 1.0f;
                 if constexpr (!F::kMX)
                     if (col < n_end) sbv = static_cast<const float*>(args.bs)[(int64_t)e * args.N + col];
                 return sbv;
             };
-            if ((args.N & 7) == 0) {  // rows of c start on 16 bytes
+            // rows of c start on 16 bytes (a two-pass tile is launched only
+            // then: its accumulators leave no room for per-element stores)
+            if (kPasses > 1 || (args.N & 7) == 0) {
+                // Pass p stages row blocks [p TM/kPasses, (p+1) TM/kPasses) of
+                // every wave (one pass: all of them); staged row s is tile row
+                // (s / kHalf) WTM + p kHalf + s % kHalf (one pass: s).  The
+                // accumulators of a pass die as it is staged.
+                constexpr int kIPer = TM / kPasses, kHalf = WTM / kPasses;
+                constexpr int kPassRows = BM / kPasses;
+                static_assert(TM % kPasses == 0, "whole row blocks per pass");
 #pragma unroll
-                for (int i = 0; i < TM; ++i) {
+                for (int pass = 0; pass < kPasses; ++pass) {
 #pragma unroll
-                    for (int j = 0; j < TN; ++j) {
-                        const float sbv = b_scale(j);
-                        const int col = wn * WTN + j * 32 + r32;
+                    for (int i = 0; i < TM; ++i) {
+                        if (i / kIPer != pass) continue;  // folds: i and pass are unrolled
 #pragma unroll
-                        for (int r = 0; r < 16; ++r)
-                            srow(wm * WTM + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3))[col] = value(i, j, r, sbv);
+                        for (int j = 0; j < TN; ++j) {
+                            const float sbv = b_scale(j);
+                            const int col = wn * WTN + j * 32 + e32;
+#pragma unroll
+                            for (int r = 0; r < 16; ++r)
+                                srow(wm * kHalf + (i - pass * kIPer) * 32 + 8 * (r >> 2) + 4 * eh + (r & 3))[col] =
+                                    value(i, j, r, sbv);
+                        }
                     }
-                }
-                __syncthreads();
-                constexpr int kPieces = BN / 8;  // 16-byte pieces per tile row
+                    __syncthreads();
+                    constexpr int kPieces = BN / 8;  // 16-byte pieces per tile row
 #pragma unroll 1
-                for (int q = tid; q < BM * kPieces; q += NT) {
-                    const int row = q / kPieces, pc = q % kPieces;
-                    const int64_t grow = m0 + row, gcol = n0 + pc * 8;
-                    if (grow < m_end && gcol < n_end)
-                        store_stream16(args.c + grow * args.N + gcol,
-                                       *reinterpret_cast<const uint4*>(srow(row) + pc * 8));
+                    for (int q = tid; q < kPassRows * kPieces; q += NT) {
+                        const int s = q / kPieces, pc = q % kPieces;
+                        const int row = kPasses == 1 ? s : (s / kHalf) * WTM + pass * kHalf + s % kHalf;
+                        const int64_t grow = m0 + row, gcol = n0 + pc * 8;
+                        if (grow < m_end && gcol < n_end)
+                            store_stream16(args.c + grow * args.N + gcol,
+                                           *reinterpret_cast<const uint4*>(srow(s) + pc * 8));
+                    }
+                    if (pass + 1 < kPasses) __syncthreads();  // the next pass reuses the staging rows
                 }
-            } else {
+            } else if constexpr (kPasses == 1) {
 #pragma unroll
                 for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -839,10 +894,15 @@ hipError_t launch_tile(const GemmProblem& p, hipStream_t stream, int mband) {
 }
 
 // Tile shapes and tile orders, chosen by measurement on MI355X (ragged
-// workloads of the benchmark): FP8 rowwise with many rows per group ->
-// 256 x 256 with eight waves (fewest operand bytes per FLOP that fit the
-// register file; 64-byte stages in four slots when K is a multiple of 64,
-// else 128-byte stages in two) in bands of 4 M tiles; MX formats with K a multiple of
+// workloads of the benchmark): FP8 rowwise with prepared weights -> 256 x
+// 384 with eight waves in three 64-byte-stage slots (a sixth fewer operand
+// bytes per FLOP than 256 x 256; its 192 accumulators per lane fit beside
+// the K loop only with the loop's offsets and fragment addresses recomputed
+// per stage and the epilogue staged in two passes; prefill shape 504.6 ->
+// 465.5 us, bit-identical) when that pads N no further than 256 columns
+// would; other FP8 rowwise with many rows per group ->
+// 256 x 256 with eight waves (64-byte stages in four slots when K is a
+// multiple of 64, else 128-byte stages in two) in bands of 4 M tiles; MX formats with K a multiple of
 // 1024 (LDS-staged scales) -> with at least 384 rows per group on average
 // the eight-wave 256 x 256 tile with 16-byte scale chunks, else the
 // eight-wave 192 x 256 tile in bands of 8 M tiles (at 170-270 rows per group
@@ -857,6 +917,7 @@ hipError_t launch_tile(const GemmProblem& p, hipStream_t stream, int mband) {
 // three slots.
 using TileLargeFp8 = Tile<256, 256, 2, 4, 4, 1, false, 64>;   // whole 64-byte stages
 using TileLargeFp8Prep = Tile<256, 256, 2, 4, 4, 1, false, 64, true>;  // the same, prepared weights
+using TileWideFp8Prep = Tile<256, 384, 2, 4, 3, 1, false, 64, true>;   // prepared weights, 384 columns (three slots fill 120 of the 160 KiB)
 using TileLargeFp8Tail = Tile<256, 256, 2, 4, 2>;              // K bytes not a multiple of 128
 using TileLargeMx = Tile<128, 256, 2, 2, 3>;
 using TileLargeMxKA = Tile<128, 256, 2, 2, 2>;
@@ -875,7 +936,7 @@ constexpr int64_t kTallRows = 384;
 // thread.
 __global__ __launch_bounds__(256) void prepare_weights_kernel(const uint8_t* __restrict__ b, int64_t E, int64_t N,
                                                               int64_t K, uint8_t* __restrict__ out) {
-    constexpr int BN = TileLargeFp8Prep::BN, SB = TileLargeFp8Prep::kSB;
+    constexpr int BN = kPrepRows, SB = TileLargeFp8Prep::kSB;
     const int64_t ntn = (N + BN - 1) / BN, nkt = K / SB;
     const int64_t pieces = E * ntn * nkt * BN * (SB / 16);
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < pieces; i += (int64_t)gridDim.x * blockDim.x) {
@@ -982,6 +1043,11 @@ hipError_t launch_grouped_gemm(const GemmProblem& p, hipStream_t stream) {
     if (p.b_prepared) {
         // the ring that reads prepared weights, whatever the rows per group
         if (p.fmt != 0 || swiglu || p.K % TileLargeFp8Prep::kSB != 0) return hipErrorInvalidValue;
+        // 384 columns when that pads N no further than 256 would (and rows
+        // of c start on 16 bytes, which its two-pass epilogue needs)
+        const int64_t wide_cols = (p.N + 383) / 384 * 384, square_cols = (p.N + 255) / 256 * 256;
+        if (p.N % 8 == 0 && wide_cols <= square_cols)
+            return launch_tile<TileWideFp8Prep, 0, false, true>(p, stream, kBandLarge);
         return launch_tile<TileLargeFp8Prep, 0, false, true>(p, stream, kBandLarge);
     }
     switch (p.fmt) {
@@ -999,7 +1065,7 @@ hipError_t launch_grouped_gemm(const GemmProblem& p, hipStream_t stream) {
 }
 
 int64_t prepared_weights_bytes(int64_t E, int64_t N, int64_t K) {
-    constexpr int BN = TileLargeFp8Prep::BN;
+    constexpr int BN = kPrepRows;
     return E * ((N + BN - 1) / BN) * BN * K;
 }
 

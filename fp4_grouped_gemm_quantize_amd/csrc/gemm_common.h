@@ -289,6 +289,27 @@ __device__ __forceinline__ TileCoord locate_tile(const GemmArgs& args, const uin
     return t;
 }
 
+// The coordinates are the same in every lane (they derive from the launch
+// arguments and the LDS prefix alone); read from the first lane, they sit in
+// scalar registers instead of taking vector registers through the K loop.
+__device__ __forceinline__ int64_t first_lane64(int64_t v) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)v);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | (uint64_t)lo);
+}
+__device__ __forceinline__ TileCoord uniform_coord(TileCoord t) {
+    t.g = __builtin_amdgcn_readfirstlane(t.g);
+    t.glo = first_lane64(t.glo);
+    t.e = __builtin_amdgcn_readfirstlane(t.e);
+    t.m0 = first_lane64(t.m0);
+    t.m_end = first_lane64(t.m_end);
+    t.n0 = first_lane64(t.n0);
+    t.n_end = first_lane64(t.n_end);
+    t.rows_in = __builtin_amdgcn_readfirstlane(t.rows_in);
+    t.cols_in = __builtin_amdgcn_readfirstlane(t.cols_in);
+    return t;
+}
+
 // Item W of a launch split as work_split describes.
 template <int BM, int BN>
 __device__ __forceinline__ TileCoord locate_item(const GemmArgs& args, const uint32_t* s_pre, const WorkSplit& ws,

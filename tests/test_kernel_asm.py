@@ -1,6 +1,7 @@
 """Checks on the generated gfx950 assembly of the GEMM kernels (CPU; hipcc
-cross-compiles).  The four-slot ring issues its direct-to-LDS loads from
-inline assembly and orders the LDS reads with its own counted vmcnt waits,
+cross-compiles).  The rings of 64-byte stages (the FP8 rowwise tiles: four
+slots at 256 x 256, three at 256 x 384) issue their direct-to-LDS loads from
+inline assembly and order the LDS reads with their own counted vmcnt waits,
 which is only sound while:
 
 * no other vector-memory instruction (register loads, stores, spill traffic)
@@ -44,24 +45,26 @@ def kernels(tmp_path_factory):
     return ks
 
 
-def four_slot(kernels):
+def asm_rings(kernels):
+    """The kernels whose ring streams 64-byte stages (assembly loads)."""
     out = {}
     for name, body in kernels.items():
         m = TILE.search(name)
-        if m and int(m.group(5)) == 4:
+        if m and m.group(8) == "64":
             out[m.groups()] = body
     return out
 
 
-def test_four_slot_kernels_exist(kernels):
-    fs = four_slot(kernels)
-    # FP8 rowwise, 256 x 256 with 64-byte stages: row-major and prepared weights
-    assert len(fs) == 2 and all(k[:2] == ("256", "256") for k in fs), sorted(fs)
-    assert sorted(k[8] for k in fs) == ["0", "1"], sorted(fs)
+def test_asm_ring_kernels_exist(kernels):
+    fs = asm_rings(kernels)
+    # FP8 rowwise: 256 x 256 in four slots on row-major and prepared weights,
+    # 256 x 384 in three slots on prepared weights
+    shapes = sorted((k[0], k[1], k[4], k[8]) for k in fs)
+    assert shapes == [("256", "256", "4", "0"), ("256", "256", "4", "1"), ("256", "384", "3", "1")], shapes
 
 
 def test_no_other_vector_memory_among_the_ring_loads(kernels):
-    for tile, body in four_slot(kernels).items():
+    for tile, body in asm_rings(kernels).items():
         dma = [i for i, l in enumerate(body) if "global_load_lds" in l]
         assert dma, tile
         inside = [body[i].strip() for i in range(dma[0], dma[-1] + 1) if VMEM.match(body[i]) and "lds" not in body[i]]
@@ -69,7 +72,7 @@ def test_no_other_vector_memory_among_the_ring_loads(kernels):
 
 
 def test_ring_loads_take_a_scalar_base_built_from_its_halves(kernels):
-    for tile, body in four_slot(kernels).items():
+    for tile, body in asm_rings(kernels).items():
         for i, l in enumerate(body):
             if "global_load_lds" not in l:
                 continue
@@ -86,7 +89,7 @@ def test_ring_loads_take_a_scalar_base_built_from_its_halves(kernels):
 
 
 def test_no_compiler_waits_before_fragment_reads(kernels):
-    for tile, body in four_slot(kernels).items():
+    for tile, body in asm_rings(kernels).items():
         mf = [i for i, l in enumerate(body) if "v_mfma" in l]
         lo, hi = mf[0], mf[-1]
         for i in range(lo, hi):

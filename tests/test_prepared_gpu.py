@@ -4,7 +4,12 @@ rearrangement of the same codes), and the grouped GEMM that reads it gives
 the oracle's results within the GEMM tolerance and bit-identical results to
 the GEMM on the row-major weights, on every reduced FP8 case whose K is a
 multiple of 64 (partial M and N tiles, one to fifteen 64-byte stages) and at
-the full prefill size.  Outputs sit between guard bytes."""
+the full prefill size.  The prepared path runs 256 x 384 tiles when N pads no
+further with 384 columns than with 256 (N = 384, 768, 1104, 1536 below; the
+last tile of N = 1104 has 336 columns), else 256 x 256 (N = 256, 512): both
+are covered, with small launches (every tile split into column halves), a
+launch of one whole round plus a split one, and the full prefill launch
+(whole tiles only).  Outputs sit between guard bytes."""
 import numpy as np
 import pytest
 import torch
@@ -17,6 +22,13 @@ from test_gemm_gpu import SENT_BF16, SMALL, check_all_rows, run_gemm
 pytestmark = pytest.mark.gpu
 
 FP8_CASES = [n for n, w in SMALL.items() if w.fmt == W.FP8_ROWWISE and w.K % 64 == 0]
+
+# shapes for the 256 x 384 tile beyond the reduced cases above
+WIDE = {
+    "wide_n1104_partial": W.WORKLOADS[3].scaled(tokens=96, E=16, N=1104, K=512),
+    "wide_n768_k64": W.WORKLOADS[3].scaled(tokens=64, E=12, top_k=4, N=768, K=64),
+    "wide_n1536_k128": W.WORKLOADS[3].scaled(tokens=128, E=16, N=1536, K=128),
+}
 
 
 def reference_layout(b: np.ndarray) -> np.ndarray:
@@ -69,6 +81,27 @@ def test_prepared_gemm_matches_oracle_and_plain_gemm(name):
     check_all_rows(case, c, f"{name} prepared")
     assert np.array_equal(c, run_gemm(case, hint=1 << 20)), "prepared and row-major weights disagree"
     assert np.array_equal(c, run_gemm(case, hint=0))
+
+
+@pytest.mark.parametrize("name", list(WIDE))
+def test_wide_tile_matches_oracle_and_plain_gemm(name):
+    case = GemmCase(WIDE[name])
+    c = run_prepared(case)
+    check_all_rows(case, c, f"{name} prepared")
+    assert np.array_equal(c, run_gemm(case, hint=1 << 20)), "prepared and row-major weights disagree"
+
+
+def test_wide_tile_whole_and_split_rounds():
+    """Every token routed to all 8 experts: 8 groups of 2,560 rows, 80 M tiles
+    by 4 N tiles = 320 tiles, so on 256 compute units one whole round runs and
+    the last 64 tiles split into 128 column halves."""
+    w = W.WORKLOADS[3].scaled(tokens=2560, E=8, top_k=8, N=1536, K=256)
+    case = GemmCase(w, gen_device="cuda")
+    c = run_prepared(case)
+    assert np.array_equal(c, run_gemm(case, hint=int(case.r.counts.max())))
+    rows = sample_rows(case.off, np.random.default_rng(5), per_group_extra=2, extra=16)
+    worst, exact = check_gemm_rows(c[rows], case.oracle_rows(rows), "whole and split rounds")
+    print(f"whole+split rounds: {rows.size} rows, max |err|/tol = {worst:.3g}, bf16-exact = {exact:.4f}")
 
 
 def test_prepared_gemm_full_prefill():
