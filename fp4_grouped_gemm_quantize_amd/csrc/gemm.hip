@@ -447,8 +447,8 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
             __asm__ volatile("" : "+v"(v));
             return v;
         };
-        // The four-slot ring issues its direct loads from inline assembly
-        // (see lds_dma16): its K loop issues no other vector-memory
+        // The rings of 64-byte stages issue their direct loads from inline
+        // assembly (see lds_dma16): their K loops issue no other vector-memory
         // instruction (FP8 rowwise: no scale loads; no register spills).
         constexpr bool kAsmDma = SB == 64;
         static_assert(!kAsmDma || !F::kMX, "assembly ring loads: FP8 rowwise only");
@@ -930,8 +930,8 @@ constexpr int64_t kTallRows = 384;
 
 // Prepared weights (FP8 rowwise, K a multiple of 64): element (e, n, k) of the
 // [E, N, K] codes goes to tile nt = n / 256, stage kt = k / 64, row r = n % 256
-// of a 256 x 64-byte block -- the block the four-slot ring copies to LDS as it
-// is -- at byte r * 64 + 16 * swz_chunk<64>(r, (k % 64) / 16) + k % 16, the
+// of a 256 x 64-byte block -- the block the 256 x 256 ring copies to LDS as
+// it is; the 256 x 384 ring copies one and a half of them -- at byte r * 64 + 16 * swz_chunk<64>(r, (k % 64) / 16) + k % 16, the
 // blocks ordered (e, nt, kt); rows past N are zero.  One 16-byte piece per
 // thread.
 __global__ __launch_bounds__(256) void prepare_weights_kernel(const uint8_t* __restrict__ b, int64_t E, int64_t N,

@@ -146,7 +146,7 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 }
 
 // A direct-to-LDS load, 16 bytes per lane (global_load_lds_dwordx4), issued
-// from inline assembly for the four-slot ring.  The compiler then does not
+// from inline assembly for the rings of 64-byte stages.  The compiler then does not
 // see an LDS write and adds no waits of its own before LDS reads (with the
 // builtin, its alias tracking of the loads in flight gave up at the ring
 // loop's head and drained them before every fourth stage); the ring's

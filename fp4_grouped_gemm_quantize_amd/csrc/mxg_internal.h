@@ -76,7 +76,7 @@ struct GemmProblem {
 hipError_t launch_grouped_gemm(const GemmProblem& p, hipStream_t stream);
 
 // FP8 rowwise weights [E, N, K] (K a multiple of 64) into the layout the
-// GEMM's four-slot ring loads as it is; out holds prepared_weights_bytes(E, N, K).
+// GEMM's 64-byte-stage rings load as it is; out holds prepared_weights_bytes(E, N, K).
 int64_t prepared_weights_bytes(int64_t E, int64_t N, int64_t K);
 hipError_t launch_prepare_weights(const void* b, int64_t E, int64_t N, int64_t K, void* out, hipStream_t stream);
 

@@ -242,11 +242,10 @@ mxg_status mx_grouped_matmul(mxg_format fmt, const void* a_q, const void* a_scal
  * of NvMxf4f8Strategy, prepare_weight_scales(), which rearranges weight
  * scales into its kernel's layout; the arithmetic is mx_grouped_matmul's.)
  *
- * The ring streams each row of a 256-column weight tile 64 bytes of K at a
- * time; in the plain [E, N, K] layout each such piece is half a 128-byte line
+ * The ring streams each row of a weight tile 64 bytes of K at a time; in the plain [E, N, K] layout each such piece is half a 128-byte line
  * of its own row, and the per-request cost of the load path, not its bytes,
- * sets the GEMM's pace.  Prepared, the 256 x 64-byte block of one tile and
- * stage is contiguous (16 KiB, rows in the order and 16-byte piece order the
+ * sets the GEMM's pace.  Prepared, the 256 x 64-byte block of 256 columns
+ * and one stage is contiguous (16 KiB, rows in the order and 16-byte piece order the
  * ring places them in LDS), so each load instruction reads whole lines.
  *
  * mx_prepared_weights_bytes(E, N, K): bytes of the prepared weights,
@@ -262,8 +261,11 @@ mxg_status mx_grouped_matmul(mxg_format fmt, const void* a_q, const void* a_scal
  *   reads it.  Asynchronous on `stream`.
  * mx_grouped_matmul_prepared(...): mx_grouped_matmul for MXG_FP8_E4M3_ROWWISE
  *   with b_prepared in place of b_q; every other argument as there (no tile
- *   hint: it always runs the 256 x 256 ring).  Results are bit-identical to
- *   mx_grouped_matmul on the weights the prepared ones came from.
+ *   hint: it runs 256-row tiles of 384 columns when that pads N no further
+ *   than 256 columns would and N % 8 == 0, else of 256 columns; a 384-column
+ *   tile reads one and a half 256-column blocks per stage).  Results are
+ *   bit-identical to mx_grouped_matmul on the weights the prepared ones came
+ *   from.
  *
  * Errors: INVALID_VALUE for null pointers, sizes <= 0 (total_rows /
  * num_groups < 0), misalignment (codes, prepared weights and c on 16 bytes,
