@@ -54,6 +54,9 @@
 //    tiles of an expert run in bands of a few M tiles (N outer inside a
 //    band), so the tiles on one XCD at a time form a block that shares A and
 //    weight panels in that XCD's L2.
+#include <cstdlib>
+#include <cstring>
+
 #include "gemm_common.h"
 
 namespace mxg {
@@ -918,6 +921,7 @@ hipError_t launch_tile(const GemmProblem& p, hipStream_t stream, int mband) {
 using TileLargeFp8 = Tile<256, 256, 2, 4, 4, 1, false, 64>;   // whole 64-byte stages
 using TileLargeFp8Prep = Tile<256, 256, 2, 4, 4, 1, false, 64, true>;  // the same, prepared weights
 using TileWideFp8Prep = Tile<256, 384, 2, 4, 3, 1, false, 64, true>;   // prepared weights, 384 columns (three slots fill 120 of the 160 KiB)
+using TileWideFp8 = Tile<256, 384, 2, 4, 3, 1, false, 64>;              // the same on row-major weights
 using TileLargeFp8Tail = Tile<256, 256, 2, 4, 2>;              // K bytes not a multiple of 128
 using TileLargeMx = Tile<128, 256, 2, 2, 3>;
 using TileLargeMxKA = Tile<128, 256, 2, 2, 2>;
@@ -955,6 +959,39 @@ __global__ __launch_bounds__(256) void prepare_weights_kernel(const uint8_t* __r
     }
 }
 
+// 256 x 384 or 256 x 256 FP8 tiles (both give the same bits).  Measured on
+// the prefill shape (N = 1536, K = 4096) from 8k to 64k rows, dense and
+// ragged: a 256 x 384 tile takes ~1.4x as long as a 256 x 256 one (1.5x the
+// work at a sixth fewer operand bytes per FLOP), and a persistent round costs
+// about as much whether its tiles are whole or split, so the wider tile pays
+// when its rounds, weighted 1.4, are fewer (dense 16k rows 0.74x, ragged 64k
+// 0.88x; dense 8k 1.26x, ragged 8k over 128 experts 1.06x).  The host does
+// not see the group sizes: the M tiles are estimated as T / 256 plus the
+// padding of each group, half a tile for groups of 256+ rows on average and
+// up to a whole one as the average falls to none (Zipf-routed 8k-64k rows
+// over 32 and 128 experts: estimates 48-320 against 48-314).  The wide tile needs
+// rows of c on 16 bytes (its two-pass epilogue) and is not used where it
+// pads N further than 256 columns do.  MXG_FP8_TILE=256x384 / 256x256
+// overrides the choice (tuning, tests); other values are ignored.
+bool wide_fp8_pays(const GemmProblem& p) {
+    if (p.N % 8 != 0) return false;
+    if (const char* v = getenv("MXG_FP8_TILE")) {
+        if (strcmp(v, "256x384") == 0) return true;
+        if (strcmp(v, "256x256") == 0) return false;
+    }
+    const int64_t ntn_w = (p.N + 383) / 384, ntn_s = (p.N + 255) / 256;
+    if (ntn_w * 384 > ntn_s * 256) return false;
+    const int64_t groups = p.G < p.T ? p.G : p.T;
+    if (groups <= 0) return false;
+    const int64_t avg = p.T / groups;
+    const int64_t pad = 128 + (avg < 256 ? 128 - avg / 2 : 0);  // 256ths of a tile per group
+    const int64_t mt = p.T / 256 + groups * pad / 256;
+    const int cus_q = device_cus();
+    const int64_t cus = cus_q > 0 ? cus_q : 256;
+    const int64_t rounds_w = (mt * ntn_w + cus - 1) / cus, rounds_s = (mt * ntn_s + cus - 1) / cus;
+    return 14 * rounds_w < 10 * rounds_s;
+}
+
 template <int FMT, bool SWIGLU>
 hipError_t launch_fmt(const GemmProblem& p, hipStream_t stream) {
     if constexpr (FMT == 3) {
@@ -968,7 +1005,10 @@ hipError_t launch_fmt(const GemmProblem& p, hipStream_t stream) {
         const int64_t rows = p.max_rows_hint > avg_rows ? (avg_rows + p.max_rows_hint) / 2 : avg_rows;
         if (rows >= 128) {
             if constexpr (FMT == 0) {
-                // whole 64-byte stages: the four-slot pipeline
+                // whole 64-byte stages: 256 x 384 where it pays, else the
+                // four-slot 256 x 256 pipeline
+                if (p.K % 64 == 0 && wide_fp8_pays(p))
+                    return launch_tile<TileWideFp8, FMT, SWIGLU, true>(p, stream, kBandLarge);
                 return p.K % 64 == 0 ? launch_tile<TileLargeFp8, FMT, SWIGLU, true>(p, stream, kBandLarge)
                                      : launch_tile<TileLargeFp8Tail, FMT, SWIGLU, false>(p, stream, kBandLarge);
             } else {
@@ -1043,11 +1083,7 @@ hipError_t launch_grouped_gemm(const GemmProblem& p, hipStream_t stream) {
     if (p.b_prepared) {
         // the ring that reads prepared weights, whatever the rows per group
         if (p.fmt != 0 || swiglu || p.K % TileLargeFp8Prep::kSB != 0) return hipErrorInvalidValue;
-        // 384 columns when that pads N no further than 256 would (and rows
-        // of c start on 16 bytes, which its two-pass epilogue needs)
-        const int64_t wide_cols = (p.N + 383) / 384 * 384, square_cols = (p.N + 255) / 256 * 256;
-        if (p.N % 8 == 0 && wide_cols <= square_cols)
-            return launch_tile<TileWideFp8Prep, 0, false, true>(p, stream, kBandLarge);
+        if (wide_fp8_pays(p)) return launch_tile<TileWideFp8Prep, 0, false, true>(p, stream, kBandLarge);
         return launch_tile<TileLargeFp8Prep, 0, false, true>(p, stream, kBandLarge);
     }
     switch (p.fmt) {

@@ -75,6 +75,12 @@
  *     malformed-routing convention of NvMxf4f8Strategy,
  *     prepare_swiglu_operands(), Raises: refuse instead of proceeding.)
  *     Without it, malformed routing is handled as described above.
+ *   - Tile override: the FP8 rowwise GEMMs run 256-row tiles of 384 or 256
+ *     columns where they use 256-row tiles at all (both give the same bits),
+ *     chosen from total_rows, num_groups, N and the device's compute units;
+ *     the environment variable MXG_FP8_TILE set to "256x384" or "256x256"
+ *     forces one (read at each call; other values are ignored; 256x384 still
+ *     needs N % 8 == 0).  For tuning and tests.
  */
 #ifndef MXG_H
 #define MXG_H
@@ -261,9 +267,9 @@ mxg_status mx_grouped_matmul(mxg_format fmt, const void* a_q, const void* a_scal
  *   reads it.  Asynchronous on `stream`.
  * mx_grouped_matmul_prepared(...): mx_grouped_matmul for MXG_FP8_E4M3_ROWWISE
  *   with b_prepared in place of b_q; every other argument as there (no tile
- *   hint: it runs 256-row tiles of 384 columns when that pads N no further
- *   than 256 columns would and N % 8 == 0, else of 256 columns; a 384-column
- *   tile reads one and a half 256-column blocks per stage).  Results are
+ *   hint: it always runs 256-row tiles, of 384 or 256 columns as described
+ *   under the tile override above; a 384-column tile reads one and a half
+ *   256-column blocks per stage).  Results are
  *   bit-identical to mx_grouped_matmul on the weights the prepared ones came
  *   from.
  *

@@ -63,11 +63,15 @@ SMALL = {
 
 # The row-count hint selects the tile shape: 0 lets small reduced problems use
 # the decode-regime tile, a large hint forces the prefill-regime tile (FP8:
-# 256 x 256 with eight waves, 64-byte stages in four slots when K is a
-# multiple of 64, else 128-byte stages in two; MX: 192 x 256 with eight waves when K is a
-# multiple of 1024, else 128 x 256), so both code paths see every case,
-# including partial M / N tiles and K tails.
+# 256 x 256 or 256 x 384 with eight waves, 64-byte stages when K is a
+# multiple of 64, else 256 x 256 with 128-byte stages in two slots; MX:
+# 192 x 256 with eight waves when K is a multiple of 1024, else 128 x 256),
+# so both code paths see every case, including partial M / N tiles and K
+# tails.  Which FP8 256-row tile runs is chosen from the problem's size (the
+# reduced cases take 256 x 256); MXG_FP8_TILE forces either one, and
+# test_fp8_256_row_tiles_agree runs both.
 HINTS = [0, 1 << 20]
+FP8_WIDE_CASES = [n for n, w in SMALL.items() if w.fmt == W.FP8_ROWWISE and w.K % 64 == 0 and w.N % 8 == 0]
 
 
 @pytest.mark.parametrize("hint", HINTS)
@@ -120,3 +124,16 @@ def test_gemm_mx_on_prefill_shape_sampled_rows(fmt):
     worst, exact = check_gemm_rows(c[rows], ref, f"prefill shape fmt {fmt}")
     print(f"prefill shape fmt {fmt}: {rows.size} rows, max |err|/tol = {worst:.3g}, bf16-exact = {exact:.4f}")
     assert not np.any(c == SENT_BF16)
+
+
+@pytest.mark.parametrize("name", FP8_WIDE_CASES)
+def test_fp8_256_row_tiles_agree(name, monkeypatch):
+    """FP8 rowwise on row-major weights through the 256 x 384 tile (forced) and
+    the 256 x 256 tile (forced): bit-identical, and within tolerance of the
+    oracle on every row."""
+    case = GemmCase(SMALL[name])
+    monkeypatch.setenv("MXG_FP8_TILE", "256x384")
+    wide = run_gemm(case, hint=1 << 20)
+    check_all_rows(case, wide, f"{name} 256x384")
+    monkeypatch.setenv("MXG_FP8_TILE", "256x256")
+    assert np.array_equal(wide, run_gemm(case, hint=1 << 20)), "256x384 and 256x256 tiles disagree"

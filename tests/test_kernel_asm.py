@@ -57,10 +57,11 @@ def asm_rings(kernels):
 
 def test_asm_ring_kernels_exist(kernels):
     fs = asm_rings(kernels)
-    # FP8 rowwise: 256 x 256 in four slots on row-major and prepared weights,
-    # 256 x 384 in three slots on prepared weights
+    # FP8 rowwise: 256 x 256 in four slots and 256 x 384 in three, each on
+    # row-major and on prepared weights
     shapes = sorted((k[0], k[1], k[4], k[8]) for k in fs)
-    assert shapes == [("256", "256", "4", "0"), ("256", "256", "4", "1"), ("256", "384", "3", "1")], shapes
+    assert shapes == [("256", "256", "4", "0"), ("256", "256", "4", "1"), ("256", "384", "3", "0"),
+                      ("256", "384", "3", "1")], shapes
 
 
 def test_no_other_vector_memory_among_the_ring_loads(kernels):

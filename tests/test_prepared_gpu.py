@@ -4,12 +4,13 @@ rearrangement of the same codes), and the grouped GEMM that reads it gives
 the oracle's results within the GEMM tolerance and bit-identical results to
 the GEMM on the row-major weights, on every reduced FP8 case whose K is a
 multiple of 64 (partial M and N tiles, one to fifteen 64-byte stages) and at
-the full prefill size.  The prepared path runs 256 x 384 tiles when N pads no
-further with 384 columns than with 256 (N = 384, 768, 1104, 1536 below; the
-last tile of N = 1104 has 336 columns), else 256 x 256 (N = 256, 512): both
-are covered, with small launches (every tile split into column halves), a
-launch of one whole round plus a split one, and the full prefill launch
-(whole tiles only).  Outputs sit between guard bytes."""
+the full prefill size.  The prepared path runs 256 x 384 or 256 x 256 tiles,
+chosen from the problem's size (the full prefill takes 256 x 384, the reduced
+cases 256 x 256); MXG_FP8_TILE forces either, so every reduced case runs
+through both, with N = 256 to 1536 (the last 256 x 384 tile of N = 1104 has
+336 columns), small launches (every tile split into column halves), a launch
+of whole rounds plus a split one, and the full prefill launch (whole tiles
+only).  Outputs sit between guard bytes."""
 import numpy as np
 import pytest
 import torch
@@ -74,42 +75,57 @@ def run_prepared(case: GemmCase):
     return g.numpy()
 
 
+TILES = ["256x256", "256x384"]
+
+
+@pytest.mark.parametrize("tile", TILES)
 @pytest.mark.parametrize("name", FP8_CASES)
-def test_prepared_gemm_matches_oracle_and_plain_gemm(name):
+def test_prepared_gemm_matches_oracle_and_plain_gemm(name, tile, monkeypatch):
     case = GemmCase(SMALL[name])
+    monkeypatch.setenv("MXG_FP8_TILE", tile)
     c = run_prepared(case)
-    check_all_rows(case, c, f"{name} prepared")
+    check_all_rows(case, c, f"{name} prepared {tile}")
+    monkeypatch.delenv("MXG_FP8_TILE")
     assert np.array_equal(c, run_gemm(case, hint=1 << 20)), "prepared and row-major weights disagree"
     assert np.array_equal(c, run_gemm(case, hint=0))
 
 
+@pytest.mark.parametrize("tile", TILES)
 @pytest.mark.parametrize("name", list(WIDE))
-def test_wide_tile_matches_oracle_and_plain_gemm(name):
+def test_wide_shapes_match_oracle_and_plain_gemm(name, tile, monkeypatch):
     case = GemmCase(WIDE[name])
+    monkeypatch.setenv("MXG_FP8_TILE", tile)
     c = run_prepared(case)
-    check_all_rows(case, c, f"{name} prepared")
+    check_all_rows(case, c, f"{name} prepared {tile}")
+    monkeypatch.setenv("MXG_FP8_TILE", "256x256" if tile == "256x384" else "256x384")
     assert np.array_equal(c, run_gemm(case, hint=1 << 20)), "prepared and row-major weights disagree"
 
 
-def test_wide_tile_whole_and_split_rounds():
-    """Every token routed to all 8 experts: 8 groups of 2,560 rows, 80 M tiles
-    by 4 N tiles = 320 tiles, so on 256 compute units one whole round runs and
-    the last 64 tiles split into 128 column halves."""
-    w = W.WORKLOADS[3].scaled(tokens=2560, E=8, top_k=8, N=1536, K=256)
+def test_wide_tile_whole_and_split_rounds(monkeypatch):
+    """Every token routed to all 8 experts: 8 groups of 14,336 rows, 448 M
+    tiles by 2 N tiles of 384 columns (N = 768) = 896 tiles, so on 256
+    compute units three whole rounds run and the last 128 tiles split into
+    256 column halves.  The size rule picks 256 x 384 here by itself
+    (estimated 4 rounds against 6 of 256 x 256); compared with the 256 x 256
+    tile on the row-major weights."""
+    w = W.WORKLOADS[3].scaled(tokens=14336, E=8, top_k=8, N=768, K=256)
     case = GemmCase(w, gen_device="cuda")
     c = run_prepared(case)
+    monkeypatch.setenv("MXG_FP8_TILE", "256x256")
     assert np.array_equal(c, run_gemm(case, hint=int(case.r.counts.max())))
     rows = sample_rows(case.off, np.random.default_rng(5), per_group_extra=2, extra=16)
     worst, exact = check_gemm_rows(c[rows], case.oracle_rows(rows), "whole and split rounds")
     print(f"whole+split rounds: {rows.size} rows, max |err|/tol = {worst:.3g}, bf16-exact = {exact:.4f}")
 
 
-def test_prepared_gemm_full_prefill():
-    """The prefill workload at full size: bit-identical to the row-major GEMM
-    on every output, and within tolerance of the oracle on sampled rows."""
+def test_prepared_gemm_full_prefill(monkeypatch):
+    """The prefill workload at full size (the size rule picks 256 x 384):
+    bit-identical to the row-major GEMM through 256 x 256 on every output, and
+    within tolerance of the oracle on sampled rows."""
     w = W.WORKLOADS[3]
     case = GemmCase(w, gen_device="cuda")
     c = run_prepared(case)
+    monkeypatch.setenv("MXG_FP8_TILE", "256x256")
     assert np.array_equal(c, run_gemm(case, hint=int(case.r.counts.max())))
     rows = sample_rows(case.off, np.random.default_rng(3), per_group_extra=1, extra=16)
     ref = case.oracle_rows(rows)
