@@ -26,6 +26,7 @@ FORMATS = {FP8_ROWWISE: "fp8_e4m3_rowwise", MXFP8: "mxfp8_e4m3", MXFP4: "mxfp4_e
 
 SUCCESS, ERROR_INVALID_VALUE, ERROR_NOT_SUPPORTED, ERROR_LAUNCH = 0, 1, 2, 3
 MAX_GROUPS = 1024
+MAX_K = 1 << 22  # largest K of the grouped GEMMs (MXG_MAX_K)
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmxg.so")

@@ -243,7 +243,7 @@ static mxg_status check_gemm_common(mxg_format fmt, const void* a_q, const void*
                                     int64_t K) {
     if (!valid_fmt(fmt)) return MXG_ERROR_INVALID_VALUE;
     if (K <= 0 || N <= 0 || num_experts <= 0 || total_rows < 0 || num_groups < 0) return MXG_ERROR_INVALID_VALUE;
-    if (K % 32 != 0 || num_groups > MXG_MAX_GROUPS) return MXG_ERROR_NOT_SUPPORTED;
+    if (K % 32 != 0 || K > MXG_MAX_K || num_groups > MXG_MAX_GROUPS) return MXG_ERROR_NOT_SUPPORTED;
     if (N > INT32_MAX / 2 || total_rows > INT32_MAX) return MXG_ERROR_NOT_SUPPORTED;
     if (total_rows == 0 || num_groups == 0) return MXG_SUCCESS;  // checked again by the caller: no-op
     if (!a_q || !a_scales || !b_q || !b_scales || !row_offsets || !expert_ids) return MXG_ERROR_INVALID_VALUE;
@@ -315,7 +315,7 @@ mxg_status mx_grouped_matmul_nvfp4(const void* a_q, const void* a_scales, const 
                                    int64_t total_rows, int64_t N, int64_t K, int64_t max_rows_per_group_hint,
                                    hipStream_t stream) {
     if (K <= 0 || N <= 0 || num_experts <= 0 || total_rows < 0 || num_groups < 0) return MXG_ERROR_INVALID_VALUE;
-    if (K % 512 != 0 || num_groups > MXG_MAX_GROUPS) return MXG_ERROR_NOT_SUPPORTED;
+    if (K % 512 != 0 || K > MXG_MAX_K || num_groups > MXG_MAX_GROUPS) return MXG_ERROR_NOT_SUPPORTED;
     if (N > INT32_MAX / 2 || total_rows > INT32_MAX) return MXG_ERROR_NOT_SUPPORTED;
     if (total_rows == 0 || num_groups == 0) return MXG_SUCCESS;  // nothing is read or written
     if (!a_q || !a_scales || !b_q || !b_scales || !expert_scales || !c_bf16 || !row_offsets || !expert_ids)
@@ -336,7 +336,7 @@ mxg_status mx_grouped_matmul_nvfp4_padded(const void* a_q, const void* a_scales,
                                           hipStream_t stream) {
     if (K <= 0 || N <= 0 || num_experts <= 0 || total_rows < 0 || num_groups < 0 || a_scale_rows < 0)
         return MXG_ERROR_INVALID_VALUE;
-    if (K % 512 != 0 || num_groups > MXG_MAX_GROUPS) return MXG_ERROR_NOT_SUPPORTED;
+    if (K % 512 != 0 || K > MXG_MAX_K || num_groups > MXG_MAX_GROUPS) return MXG_ERROR_NOT_SUPPORTED;
     if (N > INT32_MAX / 2 || total_rows > INT32_MAX) return MXG_ERROR_NOT_SUPPORTED;
     if (total_rows == 0 || num_groups == 0) return MXG_SUCCESS;  // nothing is read or written
     if (!a_q || !a_scales || !a_scales_offsets || !b_q || !b_scales || !expert_scales || !c_bf16 || !row_offsets ||
@@ -410,7 +410,7 @@ mxg_status mx_grouped_matmul_swiglu_nvfp4(const void* a_q, const void* a_scales,
                                           int32_t num_groups, int32_t num_experts, int64_t total_rows, int64_t I,
                                           int64_t K, int64_t max_rows_per_group_hint, hipStream_t stream) {
     if (K <= 0 || I <= 0 || num_experts <= 0 || total_rows < 0 || num_groups < 0) return MXG_ERROR_INVALID_VALUE;
-    if (K % 512 != 0 || I % 32 != 0 || num_groups > MXG_MAX_GROUPS) return MXG_ERROR_NOT_SUPPORTED;
+    if (K % 512 != 0 || K > MXG_MAX_K || I % 32 != 0 || num_groups > MXG_MAX_GROUPS) return MXG_ERROR_NOT_SUPPORTED;
     if (I > INT32_MAX / 4 || total_rows > INT32_MAX) return MXG_ERROR_NOT_SUPPORTED;
     if (total_rows == 0 || num_groups == 0) return MXG_SUCCESS;  // nothing is read or written
     if (!a_q || !a_scales || !w_q || !w_scales || !expert_scales || !y_tensor_scales || !y_q || !y_scales ||

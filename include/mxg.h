@@ -95,7 +95,7 @@ extern "C" {
 typedef enum {
     MXG_SUCCESS = 0,
     MXG_ERROR_INVALID_VALUE = 1, /* null pointer, bad enum, bad size, misaligned pointer */
-    MXG_ERROR_NOT_SUPPORTED = 2, /* K or I not a multiple of 32, too many groups, format not offered */
+    MXG_ERROR_NOT_SUPPORTED = 2, /* K or I not a multiple of 32, K past MXG_MAX_K, too many groups, format not offered */
     MXG_ERROR_LAUNCH = 3         /* the HIP runtime refused a launch */
 } mxg_status;
 
@@ -107,6 +107,12 @@ typedef enum {
 
 /* Largest num_groups any entry point accepts. */
 #define MXG_MAX_GROUPS 1024
+
+/* Largest K (elements per row) the grouped GEMM entry points accept: the
+ * operand loads address a tile's rows from 32-bit offsets (up to 384 rows or,
+ * on prepared weights, two 256-column blocks of K * 256 bytes).  Larger K
+ * returns MXG_ERROR_NOT_SUPPORTED. */
+#define MXG_MAX_K (1 << 22)
 
 /*
  * mx_grouped_quantize -- per-expert dynamic quantization of BF16 rows.
@@ -231,8 +237,9 @@ mxg_status mx_grouped_quantize_scatter(mxg_format fmt, const void* x_tokens, int
  * Errors: INVALID_VALUE for null pointers, a bad fmt, K/N/num_experts <= 0,
  * total_rows/num_groups < 0, misalignment (codes and c on 16 bytes; rowwise
  * fp32 scales on 4; MX scale tensors on 16, since they are streamed in
- * 16-byte pieces); NOT_SUPPORTED for K % 32 != 0 or num_groups >
- * MXG_MAX_GROUPS.  The same pointer rules hold for mx_grouped_matmul_swiglu.
+ * 16-byte pieces); NOT_SUPPORTED for K % 32 != 0, K > MXG_MAX_K or
+ * num_groups > MXG_MAX_GROUPS.  The same pointer rules hold for
+ * mx_grouped_matmul_swiglu.
  */
 mxg_status mx_grouped_matmul(mxg_format fmt, const void* a_q, const void* a_scales, const void* b_q,
                              const void* b_scales, void* c_bf16, const uint32_t* row_offsets,
@@ -276,8 +283,8 @@ mxg_status mx_grouped_matmul(mxg_format fmt, const void* a_q, const void* a_scal
  * Errors: INVALID_VALUE for null pointers, sizes <= 0 (total_rows /
  * num_groups < 0), misalignment (codes, prepared weights and c on 16 bytes,
  * scales on 4); NOT_SUPPORTED for K % 64 != 0, num_groups > MXG_MAX_GROUPS,
- * N > INT32_MAX / 2 or total_rows > INT32_MAX.  total_rows or num_groups of
- * 0 is a no-op.
+ * N > INT32_MAX / 2 or total_rows > INT32_MAX, and for the GEMM also
+ * K > MXG_MAX_K.  total_rows or num_groups of 0 is a no-op.
  */
 int64_t mx_prepared_weights_bytes(int64_t num_experts, int64_t N, int64_t K);
 mxg_status mx_prepare_weights_fp8(const void* b_q, int32_t num_experts, int64_t N, int64_t K, void* b_prepared,
@@ -311,8 +318,8 @@ mxg_status mx_grouped_matmul_prepared(const void* a_q, const void* a_scales, con
  *
  * Errors: INVALID_VALUE for a null pointer, K/N <= 0, num_experts <= 0,
  * total_rows/num_groups < 0, misalignment (codes, scales and c on 16 bytes);
- * NOT_SUPPORTED for K % 512 != 0, num_groups > MXG_MAX_GROUPS or sizes past
- * the int32 range.
+ * NOT_SUPPORTED for K % 512 != 0, K > MXG_MAX_K, num_groups > MXG_MAX_GROUPS
+ * or sizes past the int32 range.
  */
 mxg_status mx_grouped_matmul_nvfp4(const void* a_q, const void* a_scales, const void* b_q, const void* b_scales,
                                    const float* expert_scales, void* c_bf16, const uint32_t* row_offsets,

@@ -112,6 +112,10 @@ int main() {
     CALL(MXG_ERROR_NOT_SUPPORTED, false,
          mx_grouped_matmul(F8, q, s, b, bs, c, off, ids, G, E, (int64_t)INT32_MAX + 1, N, K, 0, nullptr));
     CALL(MXG_ERROR_INVALID_VALUE, false, mx_grouped_matmul(F8, q, s, b, bs, c, off, ids, G, 0, T, N, K, 0, nullptr));
+    CALL(MXG_ERROR_NOT_SUPPORTED, false,
+         mx_grouped_matmul(MX8, q, s, b, bs, c, off, ids, G, E, T, N, MXG_MAX_K + 512, 0, nullptr));
+    CALL(MXG_ERROR_NOT_SUPPORTED, false,
+         mx_grouped_matmul_prepared(q, s, b, bs, c, off, ids, G, E, T, N, MXG_MAX_K + 512, nullptr));
     CALL(MXG_SUCCESS, true, mx_grouped_matmul_prepared(q, s, b, bs, c, off, ids, G, E, T, N, K, nullptr));
     EXPECT(g_stub.gemm.b_prepared && g_stub.gemm.fmt == 0 && g_stub.gemm.b == b);
     CALL(MXG_ERROR_NOT_SUPPORTED, false, mx_grouped_matmul_prepared(q, s, b, bs, c, off, ids, G, E, T, N, 96, nullptr));

@@ -345,3 +345,21 @@ def test_prepared_weights_size_and_argument_errors():
     assert mm(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 0, 4, 96, 128, None) == mxg.ERROR_INVALID_VALUE
     # no rows: nothing is read, written or launched
     assert mm(None, None, None, None, None, None, None, 1, 3, 0, 96, 128, None) == mxg.SUCCESS
+
+
+def test_gemm_k_past_the_limit_is_not_supported():
+    """Every grouped GEMM entry point refuses K > MXG_MAX_K (its operand loads
+    use 32-bit offsets within a tile) before it reads a pointer."""
+    L = mxg.lib()
+    K = mxg.MAX_K + 512  # a multiple of 32, 64 and 512: only the limit is broken
+    NS = mxg.ERROR_NOT_SUPPORTED
+    assert mxg.MAX_K == 1 << 22
+    for fmt in (mxg.FP8_ROWWISE, mxg.MXFP8, mxg.MXFP4):
+        assert L.mx_grouped_matmul(fmt, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 3, 4, 96, K, 0, None) == NS
+    for fmt in (mxg.MXFP8, mxg.MXFP4):
+        assert L.mx_grouped_matmul_swiglu(fmt, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 3, 4, 64, K, 0,
+                                          None) == NS
+    assert L.mx_grouped_matmul_prepared(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 3, 4, 96, K, None) == NS
+    assert L.mx_grouped_matmul_nvfp4(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 3, 4, 96, K, 0, None) == NS
+    assert L.mx_grouped_matmul_swiglu_nvfp4(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 3, 4,
+                                            64, K, 0, None) == NS
