@@ -478,7 +478,9 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
                     // (the lane term passes through the empty asm, the rest is uniform)
                     const int q = wave + NW * j;
                     const int c = (int)(n0 % kPrepRows) + (q * kRPI < cols_in ? q : (cols_in - 1) / kRPI) * kRPI;
-                    off = opaque((uint32_t)lane * 16u) + (uint32_t)((c / kPrepRows) * nkt * (kPrepRows * SB) + (c % kPrepRows) * SB);
+                    // (unsigned: two blocks of K * 256 bytes reach 2^31 at K = MXG_MAX_K)
+                    off = opaque((uint32_t)lane * 16u) + (uint32_t)(c / kPrepRows) * (uint32_t)nkt * (uint32_t)(kPrepRows * SB) +
+                          (uint32_t)((c % kPrepRows) * SB);
                 }
                 if constexpr (kAsmDma)
                     lds_dma16<TL::kStreamB>(bk, off, lds_addr(slot + kAStage + (wave + NW * j) * 1024));
