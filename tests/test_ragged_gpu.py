@@ -2,6 +2,9 @@
 empty groups, a single group, one-row groups, permuted / repeated / subset
 expert ids, out-of-range ids and malformed offsets (skipped, never read out of
 bounds), uncovered rows (left untouched) and N / K tails."""
+import contextlib
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -25,19 +28,48 @@ def random_operands(rng, fmt, T, E, N, K):
     return a, sa, b, sb
 
 
+@contextlib.contextmanager
+def fp8_tile(tile):
+    """MXG_FP8_TILE set for the duration (None: the library's own choice)."""
+    old = os.environ.get("MXG_FP8_TILE")
+    if tile is None:
+        os.environ.pop("MXG_FP8_TILE", None)
+    else:
+        os.environ["MXG_FP8_TILE"] = tile
+    try:
+        yield
+    finally:
+        if old is None:
+            os.environ.pop("MXG_FP8_TILE", None)
+        else:
+            os.environ["MXG_FP8_TILE"] = old
+
+
 def run_case(fmt, a, sa, b, sb, off, ids, N, K):
     """Both tile regimes (hint 0 and a hint that forces the large tile) must
-    agree bit for bit and match the oracle; uncovered rows keep the sentinel."""
+    agree bit for bit and match the oracle; uncovered rows keep the sentinel.
+    FP8 rowwise with K % 64 == 0 and N % 8 == 0 also runs the large tile as
+    256 x 384 (forced) and the prepared weights under both 256-row tiles."""
     T = a.shape[0]
+    runs = [(hint, None, False) for hint in (0, 1 << 20)]
+    if fmt == 0 and K % 64 == 0 and N % 8 == 0:
+        runs += [(1 << 20, "256x384", False), (0, "256x256", True), (0, "256x384", True)]
     outs = []
-    for hint in (0, 1 << 20):
+    for hint, tile, prepared in runs:
         g = Guarded(np.full((T, N), SENT, np.uint16))
-        mxg.mx_grouped_matmul(fmt, to_gpu(a), to_gpu(sa), to_gpu(b), to_gpu(sb), g.view(torch.bfloat16),
-                              offsets_gpu(off), ids_gpu(ids), hint)
-        torch.cuda.synchronize()
-        g.check(f"fmt {fmt} hint {hint}")
+        with fp8_tile(tile):
+            if prepared:
+                bp = mxg.prepare_weights_fp8(to_gpu(b))
+                mxg.mx_grouped_matmul_prepared(to_gpu(a), to_gpu(sa), bp, to_gpu(sb), g.view(torch.bfloat16),
+                                               offsets_gpu(off), ids_gpu(ids))
+            else:
+                mxg.mx_grouped_matmul(fmt, to_gpu(a), to_gpu(sa), to_gpu(b), to_gpu(sb), g.view(torch.bfloat16),
+                                      offsets_gpu(off), ids_gpu(ids), hint)
+            torch.cuda.synchronize()
+        label = f"fmt {fmt} hint {hint} tile {tile or 'chosen'}{' prepared' if prepared else ''}"
+        g.check(label)
         outs.append(g.numpy())
-    assert np.array_equal(outs[0], outs[1]), "tile regimes disagree"
+        assert np.array_equal(outs[0], outs[-1]), f"{label} disagrees with the first run"
     c = outs[0]
     ref = oracle.gemm_rows(fmt, a, sa, b, sb, off, ids, N, K, np.arange(T))
     cov = ref["group"] >= 0
