@@ -32,9 +32,9 @@
 //    assembly (lds_dma16), so that the only waits before its fragment reads
 //    are the ring's own counted ones (4-5 % faster than with the builtin,
 //    whose load tracking made the compiler drain the ring every fourth
-//    stage).  The 256 x 384 tile for prepared weights streams 64-byte
-//    stages through three slots (four would fill all of LDS), the same way.  The 16-byte chunks of a row are
-//    XOR-swizzled (see swz_chunk) so the 16-byte fragment reads of 16
+//    stage).  The 256 x 384 FP8 tile streams 64-byte stages through three
+//    slots (four would fill all of LDS), the same way.  The 16-byte chunks
+//    of a row are XOR-swizzled (see swz_chunk) so the 16-byte fragment reads of 16
 //    consecutive rows hit distinct bank groups; the swizzle is realised by
 //    choosing which global chunk each lane fetches.  A stage that runs past
 //    the end of K (only the last one, when K bytes are not a multiple of the
@@ -419,9 +419,10 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
         static_assert(NW % 2 == 0, "per-lane chunk independent of the load index");
         constexpr bool kLeanOffsets = F::kMX && NW >= 8;
         const uint8_t* a_base = args.a + m0 * row_bytes;
-        // Prepared weights: the tile's stage kt is the 256 x 64-byte image at
-        // ((e * ntiles_n + n0 / BN) * nkt + kt) * BN * SB (a half tile starts
-        // at its row n0 % BN of it); one load instruction reads 1 KiB of it.
+        // Prepared weights: stage kt of 256-column block nb is the 256 x
+        // 64-byte image at ((e * ceil(N / 256) + nb) * nkt + kt) * 16 KiB; the
+        // tile starts at row n0 % 256 of block n0 / 256 and a 384-column tile
+        // runs into the next block.  One load instruction reads 1 KiB.
         static_assert(!TL::kBPrep || (!F::kMX && SB == 64), "prepared weights: FP8 64-byte-stage ring");
         const int64_t prep_ntn = (args.N + kPrepRows - 1) / kPrepRows;
         const uint8_t* b_base = TL::kBPrep
@@ -472,13 +473,13 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
             for (int j = 0; j < B_J; ++j) {
                 uint32_t off = kLeanOffsets ? op_off(rb, j, cols_in) : opaque(b_off[j]);
                 if constexpr (TL::kBPrep) {
-                    // load groups wholly past the tile's columns re-read its
+                    // Load groups wholly past the tile's columns re-read its
                     // last real group; a group lies in one 256-column block
-                    // (n0 and kRPI are multiples of 16)
-                    // (the lane term passes through the empty asm, the rest is uniform)
+                    // (n0 and kRPI are multiples of 16).  The lane term passes
+                    // through the empty asm, the rest is uniform; unsigned, as
+                    // two blocks of K * 256 bytes reach 2^31 at K = MXG_MAX_K.
                     const int q = wave + NW * j;
                     const int c = (int)(n0 % kPrepRows) + (q * kRPI < cols_in ? q : (cols_in - 1) / kRPI) * kRPI;
-                    // (unsigned: two blocks of K * 256 bytes reach 2^31 at K = MXG_MAX_K)
                     off = opaque((uint32_t)lane * 16u) + (uint32_t)(c / kPrepRows) * (uint32_t)nkt * (uint32_t)(kPrepRows * SB) +
                           (uint32_t)((c % kPrepRows) * SB);
                 }
@@ -899,15 +900,15 @@ hipError_t launch_tile(const GemmProblem& p, hipStream_t stream, int mband) {
 }
 
 // Tile shapes and tile orders, chosen by measurement on MI355X (ragged
-// workloads of the benchmark): FP8 rowwise with prepared weights -> 256 x
-// 384 with eight waves in three 64-byte-stage slots (a sixth fewer operand
-// bytes per FLOP than 256 x 256; its 192 accumulators per lane fit beside
-// the K loop only with the loop's offsets and fragment addresses recomputed
-// per stage and the epilogue staged in two passes; prefill shape 504.6 ->
-// 465.5 us, bit-identical) when that pads N no further than 256 columns
-// would; other FP8 rowwise with many rows per group ->
-// 256 x 256 with eight waves (64-byte stages in four slots when K is a
-// multiple of 64, else 128-byte stages in two) in bands of 4 M tiles; MX formats with K a multiple of
+// workloads of the benchmark): FP8 rowwise with many rows per group (and
+// prepared weights always) -> 256-row tiles with eight waves in bands of 4 M
+// tiles: 256 x 384 in three 64-byte-stage slots (a sixth fewer operand bytes
+// per FLOP than 256 x 256; its 192 accumulators per lane fit beside the K
+// loop only with the loop's offsets and fragment addresses recomputed per
+// stage and the epilogue staged in two passes; prefill shape 504.6 -> 465.5
+// us, bit-identical) where wide_fp8_pays says so, else 256 x 256 (64-byte
+// stages in four slots when K is a multiple of 64, else 128-byte stages in
+// two); MX formats with K a multiple of
 // 1024 (LDS-staged scales) -> with at least 384 rows per group on average
 // the eight-wave 256 x 256 tile with 16-byte scale chunks, else the
 // eight-wave 192 x 256 tile in bands of 8 M tiles (at 170-270 rows per group
@@ -922,7 +923,7 @@ hipError_t launch_tile(const GemmProblem& p, hipStream_t stream, int mband) {
 // three slots.
 using TileLargeFp8 = Tile<256, 256, 2, 4, 4, 1, false, 64>;   // whole 64-byte stages
 using TileLargeFp8Prep = Tile<256, 256, 2, 4, 4, 1, false, 64, true>;  // the same, prepared weights
-using TileWideFp8Prep = Tile<256, 384, 2, 4, 3, 1, false, 64, true>;   // prepared weights, 384 columns (three slots fill 120 of the 160 KiB)
+using TileWideFp8Prep = Tile<256, 384, 2, 4, 3, 1, false, 64, true>;   // 384 columns, prepared weights (120 KiB ring)
 using TileWideFp8 = Tile<256, 384, 2, 4, 3, 1, false, 64>;              // the same on row-major weights
 using TileLargeFp8Tail = Tile<256, 256, 2, 4, 2>;              // K bytes not a multiple of 128
 using TileLargeMx = Tile<128, 256, 2, 2, 3>;
@@ -936,9 +937,10 @@ constexpr int64_t kTallRows = 384;
 
 // Prepared weights (FP8 rowwise, K a multiple of 64): element (e, n, k) of the
 // [E, N, K] codes goes to tile nt = n / 256, stage kt = k / 64, row r = n % 256
-// of a 256 x 64-byte block -- the block the 256 x 256 ring copies to LDS as
-// it is; the 256 x 384 ring copies one and a half of them -- at byte r * 64 + 16 * swz_chunk<64>(r, (k % 64) / 16) + k % 16, the
-// blocks ordered (e, nt, kt); rows past N are zero.  One 16-byte piece per
+// of a 256 x 64-byte block (the block the 256 x 256 ring copies to LDS as
+// it is; the 256 x 384 ring copies one and a half of them), at byte r * 64 +
+// 16 * swz_chunk<64>(r, (k % 64) / 16) + k % 16, the blocks ordered (e, nt,
+// kt); rows past N are zero.  One 16-byte piece per
 // thread.
 __global__ __launch_bounds__(256) void prepare_weights_kernel(const uint8_t* __restrict__ b, int64_t E, int64_t N,
                                                               int64_t K, uint8_t* __restrict__ out) {
@@ -971,9 +973,9 @@ __global__ __launch_bounds__(256) void prepare_weights_kernel(const uint8_t* __r
 // not see the group sizes: the M tiles are estimated as T / 256 plus the
 // padding of each group, half a tile for groups of 256+ rows on average and
 // up to a whole one as the average falls to none (Zipf-routed 8k-64k rows
-// over 32 and 128 experts: estimates 48-320 against 48-314).  The wide tile needs
-// rows of c on 16 bytes (its two-pass epilogue) and is not used where it
-// pads N further than 256 columns do.  MXG_FP8_TILE=256x384 / 256x256
+// over 32 and 128 experts: estimates 48-320 against 48-314).  The wide tile
+// needs rows of c on 16 bytes (its two-pass epilogue) and is not used where
+// it pads N further than 256 columns do.  MXG_FP8_TILE=256x384 / 256x256
 // overrides the choice (tuning, tests); other values are ignored.
 bool wide_fp8_pays(const GemmProblem& p) {
     if (p.N % 8 != 0) return false;
