@@ -36,7 +36,7 @@ EXPORTED = ("mx_grouped_quantize", "mx_grouped_quantize_gather", "mx_grouped_qua
             "mx_grouped_matmul_swiglu_nvfp4", "mx_silu_quantize_nvfp4", "mx_grouped_quantize_padded",
             "mx_grouped_matmul_padded", "mx_grouped_matmul_swiglu_padded",
             "mx_grouped_quantize_nvfp4_padded", "mx_grouped_matmul_nvfp4_padded", "mx_prepared_weights_bytes",
-            "mx_prepare_weights_fp8", "mx_grouped_matmul_prepared", "mxg_clock_probe",
+            "mx_prepare_weights_fp8", "mx_grouped_matmul_prepared", "mxg_clock_probe", "mxg_fp8_tile",
             "mxg_validation_message", "mxg_routing_violation", "mxg_status_string")
 
 
@@ -103,6 +103,8 @@ def lib() -> ctypes.CDLL:
         L.mxg_routing_violation.restype = ctypes.c_int
         L.mxg_clock_probe.argtypes = [_P, _I64, _P]
         L.mxg_clock_probe.restype = ctypes.c_int
+        L.mxg_fp8_tile.argtypes = [_I32, _I64, _I64, _I64, _I64, _I32]
+        L.mxg_fp8_tile.restype = ctypes.c_int32
         L.mxg_status_string.argtypes = [ctypes.c_int]
         L.mxg_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -415,6 +417,14 @@ def mx_grouped_matmul(fmt: int, a_q, a_scales, b_q, b_scales, c, row_offsets, ex
     _check(lib().mx_grouped_matmul(fmt, _ptr(a_q), _ptr(a_scales), _ptr(b_q), _ptr(b_scales), _ptr(c),
                                    _ptr(row_offsets), _ptr(expert_ids), G, E, T, N, K,
                                    int(max_rows_per_group_hint), _stream(a_q)), "mx_grouped_matmul")
+
+
+def fp8_tile(num_groups: int, total_rows: int, N: int, K: int, max_rows_per_group_hint: int = 0,
+             prepared: bool = False) -> int:
+    """The tile an FP8 rowwise grouped GEMM of these sizes would run: 384 or 256 (256-row
+    tiles of that many columns), 32 (the decode-regime tile), 0 (nothing / refused)."""
+    return int(lib().mxg_fp8_tile(int(num_groups), int(total_rows), int(N), int(K),
+                                  int(max_rows_per_group_hint), 1 if prepared else 0))
 
 
 def prepared_weights_bytes(num_experts: int, N: int, K: int) -> int:

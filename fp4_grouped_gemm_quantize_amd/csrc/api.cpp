@@ -272,6 +272,22 @@ mxg_status mx_grouped_matmul(mxg_format fmt, const void* a_q, const void* a_scal
     return launch_gemm_checked(p, stream);
 }
 
+int32_t mxg_fp8_tile(int32_t num_groups, int64_t total_rows, int64_t N, int64_t K, int64_t max_rows_per_group_hint,
+                     int32_t prepared) {
+    if (num_groups <= 0 || total_rows <= 0 || N <= 0 || K <= 0) return 0;
+    if (K % 32 != 0 || K > MXG_MAX_K || num_groups > MXG_MAX_GROUPS || N > INT32_MAX / 2 || total_rows > INT32_MAX)
+        return 0;
+    mxg::GemmProblem p{};
+    p.fmt = MXG_FP8_E4M3_ROWWISE;
+    p.G = num_groups;
+    p.T = total_rows;
+    p.N = N;
+    p.K = K;
+    p.max_rows_hint = max_rows_per_group_hint;
+    p.b_prepared = prepared != 0;
+    return mxg::fp8_tile_choice(p);
+}
+
 // E * ceil(N / 256) * 256 * K fits in int64
 static bool prepared_size_fits(int64_t num_experts, int64_t N, int64_t K) {
     const int64_t rows = (N + 255) / 256 * 256;

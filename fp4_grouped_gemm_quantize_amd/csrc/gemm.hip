@@ -996,36 +996,58 @@ bool wide_fp8_pays(const GemmProblem& p) {
     return 14 * rounds_w < 10 * rounds_s;
 }
 
+// Rows per group that decide the regime: the average over non-empty groups,
+// moved halfway to the optional host hint (largest group) when that is larger
+// (the hint can only move a problem to the larger tile).
+int64_t regime_rows(const GemmProblem& p) {
+    const int64_t groups = p.G < p.T ? p.G : p.T;
+    const int64_t avg_rows = groups > 0 ? p.T / groups : p.T;
+    return p.max_rows_hint > avg_rows ? (avg_rows + p.max_rows_hint) / 2 : avg_rows;
+}
+
+}  // namespace
+
+// The FP8 rowwise tile launch_grouped_gemm runs: 384 or 256 (256-row tiles of
+// that many columns), 32 (the decode-regime 32 x 256 tile), 0 for anything
+// else (other formats, the fused epilogue, prepared weights with K % 64 != 0).
+int fp8_tile_choice(const GemmProblem& p) {
+    if (p.fmt != 0 || p.yq != nullptr) return 0;
+    if (p.b_prepared) return p.K % 64 != 0 ? 0 : wide_fp8_pays(p) ? 384 : 256;
+    if (regime_rows(p) < 128) return 32;
+    return p.K % 64 == 0 && wide_fp8_pays(p) ? 384 : 256;
+}
+
+namespace {
+
 template <int FMT, bool SWIGLU>
 hipError_t launch_fmt(const GemmProblem& p, hipStream_t stream) {
     if constexpr (FMT == 3) {
         // NVFP4: the 128 x 256 tile with LDS-staged scales (K a multiple of 512)
         return launch_tile<TileLargeMxKA, FMT, SWIGLU, true>(p, stream, kBandMx);
     } else {
-        // Average rows per non-empty group decides the regime; the optional host
-        // hint (largest group) can only move a problem to the larger tile.
-        const int64_t groups = p.G < p.T ? p.G : p.T;
-        const int64_t avg_rows = groups > 0 ? p.T / groups : p.T;
-        const int64_t rows = p.max_rows_hint > avg_rows ? (avg_rows + p.max_rows_hint) / 2 : avg_rows;
-        if (rows >= 128) {
-            if constexpr (FMT == 0) {
-                // whole 64-byte stages: 256 x 384 where it pays, else the
-                // four-slot 256 x 256 pipeline
-                if (p.K % 64 == 0 && wide_fp8_pays(p))
-                    return launch_tile<TileWideFp8, FMT, SWIGLU, true>(p, stream, kBandLarge);
+        if constexpr (FMT == 0) {
+            // 256 x 384 where it pays, else 256 x 256 (whole 64-byte stages
+            // in the four-slot pipeline, or 128-byte stages with a K tail);
+            // few rows per group: the 32 x 256 decode tile
+            const int choice = fp8_tile_choice(p);
+            if (choice == 384) return launch_tile<TileWideFp8, FMT, SWIGLU, true>(p, stream, kBandLarge);
+            if (choice == 256)
                 return p.K % 64 == 0 ? launch_tile<TileLargeFp8, FMT, SWIGLU, true>(p, stream, kBandLarge)
                                      : launch_tile<TileLargeFp8Tail, FMT, SWIGLU, false>(p, stream, kBandLarge);
-            } else {
+            return launch_tile<TileSmallFp8, FMT, SWIGLU, false>(p, stream, kBandNOuter);
+        } else {
+            if (regime_rows(p) >= 128) {
                 // whole 128-byte stages and whole 32-byte scale chunks (LDS-staged scales)
+                const int64_t groups = p.G < p.T ? p.G : p.T;
+                const int64_t avg_rows = groups > 0 ? p.T / groups : p.T;
                 const bool ka = p.K % 1024 == 0;
                 if (ka && avg_rows >= kTallRows)
                     return launch_tile<TileLargeMxKA8, FMT, SWIGLU, true>(p, stream, kBandLarge);
                 return ka ? launch_tile<TileMx192, FMT, SWIGLU, true>(p, stream, kBandMx)
                           : launch_tile<TileLargeMx, FMT, SWIGLU, false>(p, stream, kBandMx);
             }
+            return launch_tile<TileSmall, FMT, SWIGLU, false>(p, stream, kBandNOuter);
         }
-        if constexpr (FMT == 0) return launch_tile<TileSmallFp8, FMT, SWIGLU, false>(p, stream, kBandNOuter);
-        else return launch_tile<TileSmall, FMT, SWIGLU, false>(p, stream, kBandNOuter);
     }
 }
 
@@ -1086,9 +1108,10 @@ hipError_t launch_grouped_gemm(const GemmProblem& p, hipStream_t stream) {
     const bool swiglu = p.yq != nullptr;
     if (p.b_prepared) {
         // the ring that reads prepared weights, whatever the rows per group
-        if (p.fmt != 0 || swiglu || p.K % TileLargeFp8Prep::kSB != 0) return hipErrorInvalidValue;
-        if (wide_fp8_pays(p)) return launch_tile<TileWideFp8Prep, 0, false, true>(p, stream, kBandLarge);
-        return launch_tile<TileLargeFp8Prep, 0, false, true>(p, stream, kBandLarge);
+        const int choice = fp8_tile_choice(p);
+        if (choice == 384) return launch_tile<TileWideFp8Prep, 0, false, true>(p, stream, kBandLarge);
+        if (choice == 256) return launch_tile<TileLargeFp8Prep, 0, false, true>(p, stream, kBandLarge);
+        return hipErrorInvalidValue;
     }
     switch (p.fmt) {
         case 0:

@@ -75,6 +75,10 @@ struct GemmProblem {
 
 hipError_t launch_grouped_gemm(const GemmProblem& p, hipStream_t stream);
 
+// The FP8 rowwise tile launch_grouped_gemm runs for p: 384 or 256 (256-row
+// tiles of that many columns), 32 (the 32 x 256 decode tile), 0 otherwise.
+int fp8_tile_choice(const GemmProblem& p);
+
 // FP8 rowwise weights [E, N, K] (K a multiple of 64) into the layout the
 // GEMM's 64-byte-stage rings load as it is; out holds prepared_weights_bytes(E, N, K).
 int64_t prepared_weights_bytes(int64_t E, int64_t N, int64_t K);

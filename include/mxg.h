@@ -80,7 +80,8 @@
  *     chosen from total_rows, num_groups, N and the device's compute units;
  *     the environment variable MXG_FP8_TILE set to "256x384" or "256x256"
  *     forces one (read at each call; other values are ignored; 256x384 still
- *     needs N % 8 == 0).  For tuning and tests.
+ *     needs N % 8 == 0).  For tuning and tests; mxg_fp8_tile reports the
+ *     choice.
  */
 #ifndef MXG_H
 #define MXG_H
@@ -578,6 +579,21 @@ mxg_status mx_moe_combine(const void* y_bf16, int64_t total_rows, int64_t H, con
  * outside [1, MXG_CLOCK_PROBE_MAX_US].
  */
 #define MXG_CLOCK_PROBE_MAX_US 10000000
+
+/*
+ * mxg_fp8_tile -- which tile an FP8 rowwise grouped GEMM of this size would
+ * run (not a step of the path: for tuning and for tests of the choice).  The
+ * host sees only the sizes, as the GEMM does: num_groups, total_rows, N, K,
+ * the hint of mx_grouped_matmul and whether the weights are prepared
+ * (mx_grouped_matmul_prepared).  Returns 384 or 256 for 256-row tiles of that
+ * many columns, 32 for the 32 x 256 tile of the few-rows-per-group regime,
+ * and 0 where such a call would launch nothing or be refused (sizes <= 0, K
+ * not a multiple of 32 (of 64 for prepared weights) or past MXG_MAX_K, too
+ * many groups).  Follows MXG_FP8_TILE and the device's compute units as the
+ * GEMM does (256 when no device is visible).  Touches no device memory.
+ */
+int32_t mxg_fp8_tile(int32_t num_groups, int64_t total_rows, int64_t N, int64_t K,
+                     int64_t max_rows_per_group_hint, int32_t prepared);
 mxg_status mxg_clock_probe(unsigned long long* out, int64_t window_us, hipStream_t stream);
 
 /*

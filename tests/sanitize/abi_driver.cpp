@@ -116,6 +116,10 @@ int main() {
          mx_grouped_matmul(MX8, q, s, b, bs, c, off, ids, G, E, T, N, MXG_MAX_K + 512, 0, nullptr));
     CALL(MXG_ERROR_NOT_SUPPORTED, false,
          mx_grouped_matmul_prepared(q, s, b, bs, c, off, ids, G, E, T, N, MXG_MAX_K + 512, nullptr));
+    EXPECT(mxg_fp8_tile(G, T, N, K, 17, 1) == 256 && g_stub.gemm.b_prepared && g_stub.gemm.max_rows_hint == 17 &&
+           g_stub.gemm.T == T && g_stub.gemm.N == N && g_stub.gemm.K == K && g_stub.gemm.fmt == 0);
+    EXPECT(mxg_fp8_tile(0, T, N, K, 0, 0) == 0 && mxg_fp8_tile(G, T, N, 48, 0, 0) == 0 &&
+           mxg_fp8_tile(G, T, N, MXG_MAX_K + 512, 0, 0) == 0 && mxg_fp8_tile(G, -1, N, K, 0, 0) == 0);
     CALL(MXG_SUCCESS, true, mx_grouped_matmul_prepared(q, s, b, bs, c, off, ids, G, E, T, N, K, nullptr));
     EXPECT(g_stub.gemm.b_prepared && g_stub.gemm.fmt == 0 && g_stub.gemm.b == b);
     CALL(MXG_ERROR_NOT_SUPPORTED, false, mx_grouped_matmul_prepared(q, s, b, bs, c, off, ids, G, E, T, N, 96, nullptr));

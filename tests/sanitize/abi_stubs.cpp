@@ -58,6 +58,10 @@ hipError_t launch_grouped_gemm(const GemmProblem& p, hipStream_t) {
 }
 hipError_t launch_clock_probe(unsigned long long*, unsigned long long, hipStream_t) { return record("clock_probe"); }
 int64_t prepared_weights_bytes(int64_t E, int64_t N, int64_t K) { return E * ((N + 255) / 256) * 256 * K; }
+int fp8_tile_choice(const GemmProblem& p) {
+    g_stub.gemm = p;
+    return 256;
+}
 hipError_t launch_prepare_weights(const void*, int64_t, int64_t, int64_t, void*, hipStream_t) {
     return record("prepare_weights");
 }

@@ -363,3 +363,45 @@ def test_gemm_k_past_the_limit_is_not_supported():
     assert L.mx_grouped_matmul_nvfp4(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 3, 4, 96, K, 0, None) == NS
     assert L.mx_grouped_matmul_swiglu_nvfp4(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 3, 4,
                                             64, K, 0, None) == NS
+
+
+def test_fp8_tile_choice(monkeypatch):
+    """The FP8 tile rule on the shapes it was measured on (N = 1536, K = 4096;
+    256 compute units when no device is visible, as here): 256x384 where its
+    persistent rounds, weighted 1.4, are fewer, else 256x256; the decode
+    regime's 32-row tile for few rows per group; MXG_FP8_TILE forces the
+    256-row tile's width (never 384 with N % 8 != 0); malformed sizes give 0."""
+    monkeypatch.delenv("MXG_FP8_TILE", raising=False)
+    t = mxg.fp8_tile
+    # dense: 8k rows fill fewer compute units with 384 columns
+    assert t(1, 8192, 1536, 4096, prepared=True) == 256
+    assert t(1, 16384, 1536, 4096, prepared=True) == 384
+    assert t(1, 65536, 1536, 4096, prepared=True) == 384
+    # Zipf-routed over 128 experts: 8k and 16k rows stay 256 wide, the 64k prefill goes 384
+    assert t(128, 8192, 1536, 4096, prepared=True) == 256
+    assert t(128, 16384, 1536, 4096, prepared=True) == 256
+    assert t(128, 65536, 1536, 4096, prepared=True) == 384
+    assert t(128, 65536, 1536, 4096, max_rows_per_group_hint=7408) == 384  # row-major, the bench's hint
+    assert t(32, 8192, 1536, 4096, prepared=True) == 384
+    # the split-round test shape (N = 768)
+    assert t(8, 114688, 768, 256, prepared=True) == 384
+    # 384 columns would pad N = 1024 to 1152 (256: no padding)
+    assert t(1, 1 << 20, 1024, 4096, prepared=True) == 256
+    # few rows per group: the decode tile, unless the hint moves the problem up
+    assert t(64, 1024, 2048, 7168) == 32
+    assert t(64, 1024, 2048, 7168, max_rows_per_group_hint=1 << 20) in (256, 384)
+    # K not a multiple of 64: the 128-byte-stage 256 x 256 tile; prepared weights refuse it
+    assert t(1, 65536, 1536, 4000) == 256
+    assert t(1, 65536, 1536, 4000, prepared=True) == 0
+    # malformed sizes
+    for args in [(0, 64, 256, 256), (1, 0, 256, 256), (1, 64, 0, 256), (1, 64, 256, 48),
+                 (1, 64, 256, mxg.MAX_K + 32), (mxg.MAX_GROUPS + 1, 64, 256, 256)]:
+        assert t(*args) == 0, args
+    # the override
+    monkeypatch.setenv("MXG_FP8_TILE", "256x384")
+    assert t(1, 8192, 1536, 4096, prepared=True) == 384
+    assert t(1, 8192, 1540, 4096, prepared=True) == 256  # N % 8 != 0
+    monkeypatch.setenv("MXG_FP8_TILE", "256x256")
+    assert t(128, 65536, 1536, 4096, prepared=True) == 256
+    monkeypatch.setenv("MXG_FP8_TILE", "something else")
+    assert t(128, 65536, 1536, 4096, prepared=True) == 384

@@ -110,6 +110,8 @@ def test_wide_tile_whole_and_split_rounds(monkeypatch):
     tile on the row-major weights."""
     w = W.WORKLOADS[3].scaled(tokens=14336, E=8, top_k=8, N=768, K=256)
     case = GemmCase(w, gen_device="cuda")
+    monkeypatch.delenv("MXG_FP8_TILE", raising=False)
+    assert mxg.fp8_tile(len(case.ids), case.T, w.N, w.K, prepared=True) == 384
     c = run_prepared(case)
     monkeypatch.setenv("MXG_FP8_TILE", "256x256")
     assert np.array_equal(c, run_gemm(case, hint=int(case.r.counts.max())))
@@ -124,6 +126,8 @@ def test_prepared_gemm_full_prefill(monkeypatch):
     within tolerance of the oracle on sampled rows."""
     w = W.WORKLOADS[3]
     case = GemmCase(w, gen_device="cuda")
+    monkeypatch.delenv("MXG_FP8_TILE", raising=False)
+    assert mxg.fp8_tile(len(case.ids), case.T, w.N, w.K, prepared=True) == 384
     c = run_prepared(case)
     monkeypatch.setenv("MXG_FP8_TILE", "256x256")
     assert np.array_equal(c, run_gemm(case, hint=int(case.r.counts.max())))
