@@ -29,6 +29,9 @@ WIDE = {
     "wide_n1104_partial": W.WORKLOADS[3].scaled(tokens=96, E=16, N=1104, K=512),
     "wide_n768_k64": W.WORKLOADS[3].scaled(tokens=64, E=12, top_k=4, N=768, K=64),
     "wide_n1536_k128": W.WORKLOADS[3].scaled(tokens=128, E=16, N=1536, K=128),
+    # last 384-column tile 232 columns wide: its last 16-column load group
+    # reaches 8 columns past N (zero rows of the prepared block)
+    "wide_n1000": W.WORKLOADS[3].scaled(tokens=64, E=8, top_k=4, N=1000, K=128),
 }
 
 

@@ -105,7 +105,8 @@ def test_groupings(fmt, name, K):
 
 
 @pytest.mark.parametrize("fmt", [0, 1, 2])
-@pytest.mark.parametrize("N,K", [(32, 32), (96, 64), (129, 160), (1000, 96), (300, 512), (300, 1024), (40, 3072)])
+@pytest.mark.parametrize("N,K", [(32, 32), (96, 64), (129, 160), (1000, 96), (1000, 128), (300, 512), (300, 1024),
+                                 (40, 3072)])
 def test_shape_tails(fmt, N, K):
     rng = np.random.default_rng(N * K + fmt)
     T, E = 77, 3
