@@ -553,10 +553,17 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
         // LDS-staged scales: chunk c (32 bytes per row from block 32c) into
         // buffer `buf`, rows 0 .. BM-1 of A then BM .. BM+BN-1 of B, row r at
         // byte 32r; 32-row group q is loaded by wave q % NW (lane l: row
-        // 32q + l/2, bytes 16(l%2) ..).
+        // 32q + l/2).  With 32-byte chunks the two 16-byte halves of a row
+        // trade places when bit 3 of the row is set (lane l fetches half
+        // (l % 2) ^ ((l >> 4) & 1)): the 32 rows a 4-byte scale read covers
+        // then fall on 16 bank groups instead of 8 (two-way instead of
+        // four-way LDS bank conflicts, the least a 4-byte read of one word
+        // per row allows).
         constexpr int kSclRowsPerLoad = 1024 / kSclBytes;
         constexpr int kSclGroups = kSclRows / kSclRowsPerLoad;
         constexpr int kSclPerWave = (kSclGroups + NW - 1) / NW;
+        static_assert(!kLdsScales || (WTM % 32 == 0 && WTN % 32 == 0),
+                      "LDS scales: wave row blocks start on 32-row boundaries");
         const uint8_t* scl_base[kSclPerWave];
         uint32_t scl_off[kSclPerWave];
         if constexpr (kLdsScales) {
@@ -565,10 +572,11 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
                 const int q = wave + NW * k;
                 const int r = q * kSclRowsPerLoad + lane / (kSclBytes / 16);
                 const bool in_a = q * kSclRowsPerLoad < BM;  // wave-uniform
+                const int half = kSclBytes == 32 ? (lane % 2) ^ ((lane >> 4) & 1) : 0;
                 scl_base[k] = in_a ? sa_base : sb_base;
                 scl_off[k] = (in_a ? (uint32_t)((r < rows_sc ? r : rows_sc - 1) * nblk)
                                    : (uint32_t)((r - BM < cols_in ? r - BM : cols_in - 1) * nblk)) +
-                             16 * (lane % (kSclBytes / 16));
+                             16 * half;
             }
         }
         auto issue_scales = [&](int c, uint8_t* buf) {
@@ -578,18 +586,23 @@ __global__ __launch_bounds__(TL::kThreads, TL::kMinBlocks) void grouped_gemm_ker
                     __builtin_amdgcn_global_load_lds((gptr_t)(scl_base[k] + kSclBytes * c + opaque(scl_off[k])),
                                                      (lptr_t)(buf + (wave + NW * k) * 1024), 16, 0, 0);
         };
-        // this lane's scale words for position `pos` (stage within a chunk)
+        // this lane's scale words for position `pos` (stage within a chunk);
+        // the row's bit 3 is r32's (row blocks start on 32-row boundaries), so
+        // byte b of the chunk sits at b + sx in the first half, b - sx in the
+        // second
+        const int sx = kLdsScales && kSclBytes == 32 ? ((r32 >> 3) & 1) * 16 : 0;
         auto read_scales = [&](const uint8_t* buf, int pos, uint32_t (&xa)[TM][kWords], uint32_t (&xb)[TN][kWords]) {
 #pragma unroll
             for (int w = 0; w < kWords; ++w) {
+                const int b = (pos * kWords + w) * 4;
+                const int bs = b < 16 ? b + sx : b - sx;
 #pragma unroll
                 for (int i = 0; i < TM; ++i)
-                    xa[i][w] = *reinterpret_cast<const uint32_t*>(buf + (wm * WTM + i * 32 + r32) * kSclBytes +
-                                                                  (pos * kWords + w) * 4);
+                    xa[i][w] = *reinterpret_cast<const uint32_t*>(buf + (wm * WTM + i * 32 + r32) * kSclBytes + bs);
 #pragma unroll
                 for (int j = 0; j < TN; ++j)
                     xb[j][w] = *reinterpret_cast<const uint32_t*>(buf + (BM + wn * WTN + j * 32 + r32) * kSclBytes +
-                                                                  (pos * kWords + w) * 4);
+                                                                  bs);
             }
         };
         auto load_scales = [&](int kt, uint32_t (&xa)[TM][kWords], uint32_t (&xb)[TN][kWords]) {
