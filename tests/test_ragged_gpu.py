@@ -114,15 +114,30 @@ def test_shape_tails(fmt, N, K):
     run_case(fmt, a, sa, b, sb, np.array([0, 20, 21, 77], np.uint32), np.array([2, 0, 1], np.int32), N, K)
 
 
-def test_many_groups():
-    """The largest group count (1024 groups, many of them empty)."""
-    rng = np.random.default_rng(99)
-    G, E, T, N, K = 1024, 8, 600, 64, 64
-    counts = rng.multinomial(T, np.ones(G) / G)
+@pytest.mark.parametrize("fmt", [0, 1, 2])
+@pytest.mark.parametrize("spread", ["sparse", "skewed"])
+def test_many_groups(fmt, spread):
+    """The largest group count, 1024 groups.  Sparse: 600 rows over all of
+    them (most groups empty or a row or two).  Skewed: 3000 rows drawn with
+    weights 1/k^1.2 over a shuffled group order (437 non-empty groups, the
+    largest 707 rows, so a few span several 256-row tiles), N = 400 and
+    K = 1024: every tile regime has more than one column tile (the 256 x 384
+    tile a partial last one), the MX formats stage their scales through LDS,
+    and FP8 also runs the 256 x 384 and prepared-weight tiles (run_case)."""
+    rng = np.random.default_rng(99 if spread == "sparse" else 100)
+    G, E = 1024, 8
+    if spread == "sparse":
+        T, N, K = 600, 64, 64
+        counts = rng.multinomial(T, np.ones(G) / G)
+    else:
+        T, N, K = 3000, 400, 1024
+        p = 1.0 / np.arange(1, G + 1) ** 1.2
+        rng.shuffle(p)
+        counts = rng.multinomial(T, p / p.sum())
     off = np.r_[0, np.cumsum(counts)].astype(np.uint32)
     ids = rng.integers(0, E, G).astype(np.int32)
-    a, sa, b, sb = random_operands(rng, 2, T, E, N, K)
-    cov = run_case(2, a, sa, b, sb, off, ids, N, K)
+    a, sa, b, sb = random_operands(rng, fmt, T, E, N, K)
+    cov = run_case(fmt, a, sa, b, sb, off, ids, N, K)
     assert cov.all()
 
 
