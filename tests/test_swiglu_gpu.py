@@ -119,3 +119,55 @@ def test_fused_full_size_sampled_rows():
     assert np.array_equal(yq, yq2) and np.array_equal(ys, ys2), "fused and chained paths differ"
     rows = sample_rows(case.off, np.random.default_rng(5), per_group_extra=1, extra=16)
     check_against_oracle(case, yq, ys, rows)
+
+
+# Sparse and malformed routings (as in the GEMM's ragged suite): the fused
+# kernel writes exactly the rows a valid group covers -- groups with an id
+# outside [0, E) or inverted offsets are skipped, offsets past the end are
+# clamped to T, rows no group covers keep their bytes.
+FUSED_GROUPINGS = {
+    "empty_groups": ([0, 0, 50, 50, 50, 130, 130], [0, 1, 2, 3, 1, 0]),
+    "subset_with_gaps": ([5, 40, 40, 90], [1, 1, 2]),
+    "out_of_range_ids": ([0, 40, 80, 130], [4, -1, 1]),
+    "inverted_and_past_end": ([60, 20, 100, 500], [0, 1, 2]),
+}
+
+
+@pytest.mark.parametrize("hint", [0, 1 << 20])
+@pytest.mark.parametrize("K", [640, 1024])
+@pytest.mark.parametrize("fmt", [W.MXFP8, W.MXFP4])
+@pytest.mark.parametrize("name", list(FUSED_GROUPINGS))
+def test_fused_sparse_and_malformed_routing(name, fmt, K, hint):
+    """K = 640 loads the scales per lane, K = 1024 stages them through LDS;
+    hint 0 runs the small-group tile, the large hint the large one.  On the
+    covered rows the fused result equals the chained GEMM + activation byte
+    for byte and is reachable from the oracle's gate/up intervals."""
+    from test_ragged_gpu import random_operands
+
+    rng = np.random.default_rng(len(name) * 31 + fmt * 7 + K)
+    T, E, N = 130, 4, 256
+    I = N // 2
+    a, sa, b, sb = random_operands(rng, fmt, T, E, N, K)
+    off = np.array(FUSED_GROUPINGS[name][0], np.uint32)
+    ids = np.array(FUSED_GROUPINGS[name][1], np.int32)
+    off_d, ids_d = offsets_gpu(off), torch.from_numpy(ids).cuda()
+    gq = Guarded(np.full((T, I // 2), 0xA5, np.uint8))
+    gs = Guarded(np.full((T, I // 32), 0x5A, np.uint8))
+    mxg.mx_grouped_matmul_swiglu(fmt, to_gpu(a), to_gpu(sa), to_gpu(b), to_gpu(sb), gq.view(), gs.view(), off_d,
+                                 ids_d, hint)
+    c = torch.zeros((T, N), dtype=torch.bfloat16, device="cuda")
+    mxg.mx_grouped_matmul(fmt, to_gpu(a), to_gpu(sa), to_gpu(b), to_gpu(sb), c, off_d, ids_d, hint)
+    yq2 = torch.full((T, I // 2), 0xA5, dtype=torch.uint8, device="cuda")
+    ys2 = torch.full((T, I // 32), 0x5A, dtype=torch.uint8, device="cuda")
+    mxg.mx_silu_quantize(c, yq2, ys2, off_d)
+    torch.cuda.synchronize()
+    gq.check("fused codes")
+    gs.check("fused scales")
+    yq, ys = gq.numpy(), gs.numpy()
+    ref = oracle.gemm_swiglu_rows(fmt, a, sa, b, sb, off, ids, I, K, np.arange(T))
+    cov = ref["group"] >= 0
+    assert np.all(yq[~cov] == 0xA5) and np.all(ys[~cov] == 0x5A), "a row no valid group covers was written"
+    assert np.array_equal(yq[cov], yq2.cpu().numpy()[cov]) and np.array_equal(ys[cov], ys2.cpu().numpy()[cov]), \
+        "fused and chained paths differ on covered rows"
+    if cov.any():
+        check_swiglu_interval(yq[cov], ys[cov], ref["gu_exact"][cov], ref["gu_bound"][cov])
