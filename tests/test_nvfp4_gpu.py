@@ -192,6 +192,42 @@ def test_nvfp4_gemm_random_codes_and_bad_expert_ids():
     check_gemm_rows(c[cov], {k: v[cov] for k, v in ref.items() if k != "group"}, "random codes")
 
 
+# Sparse and malformed routings (as in the MX / FP8 ragged suite): groups
+# with an id outside [0, E) or inverted offsets are skipped, offsets past the
+# end are clamped to T, rows no valid group covers keep the sentinel.
+NV_GROUPINGS = {
+    "empty_groups": ([0, 0, 50, 50, 50, 130, 130], [0, 1, 2, 3, 1, 0]),
+    "subset_with_gaps": ([5, 40, 40, 90], [1, 1, 2]),
+    "out_of_range_ids": ([0, 40, 80, 130], [4, -1, 1]),
+    "inverted_and_past_end": ([60, 20, 100, 500], [0, 1, 2]),
+}
+
+
+@pytest.mark.parametrize("K", [512, 1024])
+@pytest.mark.parametrize("name", list(NV_GROUPINGS))
+def test_nvfp4_gemm_sparse_and_malformed_routing(name, K):
+    rng = np.random.default_rng(len(name) * 13 + K)
+    T, E, N = 130, 4, 288
+    a = rng.integers(0, 256, size=(T, K // 2), dtype=np.uint8)
+    sa = rng.integers(0x28, 0x48, size=(T, K // 16), dtype=np.uint8)
+    b = rng.integers(0, 256, size=(E, N, K // 2), dtype=np.uint8)
+    sb = rng.integers(0x28, 0x48, size=(E, N, K // 16), dtype=np.uint8)
+    es = rng.uniform(0.25, 4.0, size=E).astype(np.float32)
+    off = np.array(NV_GROUPINGS[name][0], np.uint32)
+    ids = np.array(NV_GROUPINGS[name][1], np.int32)
+    g = Guarded(np.full((T, N), SENT_BF16, np.uint16))
+    mxg.mx_grouped_matmul_nvfp4(to_gpu(a), to_gpu(sa), to_gpu(b), to_gpu(sb), to_gpu(es), g.view(torch.bfloat16),
+                                offsets_gpu(off), to_gpu(ids))
+    torch.cuda.synchronize()
+    g.check("NVFP4 c")
+    c = g.numpy()
+    ref = oracle.gemm_rows_nvfp4(a, sa, b, sb, es, off, ids, N, K, np.arange(T))
+    cov = ref["group"] >= 0
+    assert np.all(c[~cov] == SENT_BF16), "a row no valid group covers was written"
+    if cov.any():
+        check_gemm_rows(c[cov], {k: v[cov] for k, v in ref.items() if k != "group"}, name)
+
+
 def test_nvfp4_gemm_full_size_sampled_rows():
     """The mxfp4_swiglu routing at full size (32,768 routed rows, 128 experts,
     K = 7168) as a plain NVFP4 GEMM with N = 4096; seeded random operands,
