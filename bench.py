@@ -278,7 +278,7 @@ def cpu_baseline(w, r, x_gpu, target_s):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "the benchmark measures one GPU: the kernels run on one device and there is no multi-GPU path; --gpus must be 1"}))
         sys.exit(2)
     import numpy as np
     import torch
